@@ -1,0 +1,223 @@
+"""Plain CPU oracle for C = alpha*op(A)*op(B) + beta*C (test infrastructure).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by __graft_entry__.smoke() and by
+bench.py's cpu_baseline leg, never by the library under dense_gemm_tiled_amd/,
+and it never imports that library.  The arithmetic lives in oracle_gemm.c (a
+triple loop accumulating in fp64, int64 for int8); this module only compiles it
+with gcc and marshals numpy arrays.
+
+The definition it evaluates comes from tensorcore "GEMM" (sections "Surface",
+"Transposes", "Numerical guarantees"), Phobos "Matrix products" (sgemm/hgemm
+epilogue, matmul_t) and tessl "Architecture" ("Integer GEMM", "Fused
+Epilogue"); the C file's header states it in full.
+
+Every function of this oracle is pinned by tests/test_oracle.py against facts
+the pages and the mathematics fix (exhaustive codec round trips, ties-to-even,
+exact-rational brute force, identities, alpha/beta closed forms, int8
+extremes); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle_gemm.c")
+_LIB = os.path.join(_HERE, "liboracle_gemm.so")
+
+# dtype names -> the oracle's own codes (see the enum in oracle_gemm.c)
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "i32": 4}
+STORAGE = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16,
+           "i8": np.int8, "i32": np.int32}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle_gemm.c into liboracle_gemm.so with gcc (OpenMP)."""
+    if not force and os.path.exists(_LIB) and \
+            os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+           "-ffp-contract=off", "-fno-fast-math", "-march=x86-64-v2",
+           _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    i64, i32, f64, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
+    lib.oracle_gemm.restype = i32
+    lib.oracle_gemm.argtypes = [i64, i64, i64, i32, i32, i32, i32, f64, f64,
+                                vp, i64, vp, i64, vp, i64, vp, vp,
+                                i64, i64, i64, i64]
+    lib.oracle_gemm_points.restype = i32
+    lib.oracle_gemm_points.argtypes = [i64, i64, i64, i32, i32, i32, i32, f64, f64,
+                                       vp, i64, vp, i64, vp, i64, i64, i64, i64,
+                                       i64, vp, vp, vp, vp, vp]
+    for name in ("oracle_decode_bf16", "oracle_decode_f16"):
+        getattr(lib, name).restype = f64
+        getattr(lib, name).argtypes = [ctypes.c_uint16]
+    for name in ("oracle_round_f32", "oracle_round_bf16", "oracle_round_f16"):
+        getattr(lib, name).restype = f64
+        getattr(lib, name).argtypes = [f64]
+    for name in ("oracle_encode_bf16", "oracle_encode_f16"):
+        getattr(lib, name).restype = ctypes.c_uint16
+        getattr(lib, name).argtypes = [f64]
+    lib.oracle_encode_f32.restype = ctypes.c_float
+    lib.oracle_encode_f32.argtypes = [f64]
+    lib.oracle_decode_array.restype = None
+    lib.oracle_decode_array.argtypes = [vp, i32, i64, vp]
+    lib.oracle_encode_array.restype = None
+    lib.oracle_encode_array.argtypes = [vp, i32, i64, vp]
+    lib.oracle_num_threads.restype = i32
+    lib.oracle_num_threads.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+# ---------------------------------------------------------------- codecs
+def decode(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored values (raw bits for f16/bf16) -> float64, elementwise."""
+    if dtype not in DTYPES:
+        raise ValueError(dtype)
+    flat = np.ascontiguousarray(bits).ravel().view(STORAGE[dtype])
+    out = np.empty(flat.size, dtype=np.float64)
+    _load().oracle_decode_array(_ptr(flat), DTYPES[dtype], flat.size, _ptr(out))
+    return out.reshape(np.shape(bits))
+
+
+def round_to(values: np.ndarray, dtype: str) -> np.ndarray:
+    """float64 -> nearest (ties to even) value of dtype, as float64."""
+    lib = _load()
+    fn = {"f32": lib.oracle_round_f32, "bf16": lib.oracle_round_bf16,
+          "f16": lib.oracle_round_f16}[dtype]
+    flat = np.asarray(values, dtype=np.float64).ravel()
+    return np.array([fn(float(v)) for v in flat]).reshape(np.shape(values))
+
+
+def encode(values: np.ndarray, dtype: str) -> np.ndarray:
+    """float64 -> stored bit patterns of dtype (rounded to nearest even)."""
+    if dtype not in ("bf16", "f16", "f32"):
+        raise ValueError(dtype)
+    flat = np.ascontiguousarray(np.asarray(values, dtype=np.float64).ravel())
+    out = np.empty(flat.size, dtype=STORAGE[dtype])
+    _load().oracle_encode_array(_ptr(flat), DTYPES[dtype], flat.size, _ptr(out))
+    return out.reshape(np.shape(values))
+
+
+# ---------------------------------------------------------------- GEMM
+def _c_dtype_ok(a_dtype: str, c_dtype: str) -> None:
+    if a_dtype not in DTYPES or c_dtype not in DTYPES:
+        raise ValueError("unknown dtype %s/%s" % (a_dtype, c_dtype))
+
+
+def gemm(A: np.ndarray, B: np.ndarray, C_in: Optional[np.ndarray], *,
+         M: int, N: int, K: int, a_dtype: str, c_dtype: str,
+         transpose_a: bool = False, transpose_b: bool = False,
+         alpha: float = 1.0, beta: float = 0.0,
+         lda: int = 0, ldb: int = 0, ldc: int = 0,
+         batch: int = 1, stride_a: int = 0, stride_b: int = 0,
+         stride_c: int = 0, C_like: Optional[np.ndarray] = None,
+         want_value: bool = True) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+    """Evaluate the whole product.
+
+    A, B, C_in are flat-or-shaped numpy arrays of stored values (uint16 bit
+    patterns for f16/bf16).  Leading dims 0 mean contiguous.  Returns
+    (C_out, value) where C_out has C_in's layout (or C_like's when C_in is None)
+    holding round_c(value) inside the M x N extent, and value is the unrounded
+    fp64 result as a dense [batch, M, N] array (None unless want_value).
+    """
+    _c_dtype_ok(a_dtype, c_dtype)
+    lda = lda or (M if transpose_a else K)
+    ldb = ldb or (K if transpose_b else N)
+    ldc = ldc or N
+    A = np.ascontiguousarray(A)
+    B = np.ascontiguousarray(B)
+    if C_in is not None:
+        C_in = np.ascontiguousarray(C_in)
+        C_out = C_in.copy()
+    else:
+        if C_like is None:
+            size = (batch - 1) * stride_c + (M - 1) * ldc + N
+            C_like = np.zeros(size, dtype=STORAGE[c_dtype])
+        C_out = np.ascontiguousarray(C_like).copy()
+    value = np.empty((batch, M, N), dtype=np.float64) if want_value else None
+    rc = _load().oracle_gemm(M, N, K, DTYPES[a_dtype], DTYPES[c_dtype],
+                             int(bool(transpose_a)), int(bool(transpose_b)),
+                             float(alpha), float(beta), _ptr(A), lda, _ptr(B), ldb,
+                             _ptr(C_in), ldc, _ptr(C_out), _ptr(value),
+                             batch, stride_a, stride_b, stride_c)
+    if rc != 0:
+        raise ValueError("oracle_gemm rejected its arguments (code %d)" % rc)
+    return C_out, value
+
+
+def gemm_points(A: np.ndarray, B: np.ndarray, C_in: Optional[np.ndarray],
+                points: Sequence[Tuple[int, int, int]], *,
+                M: int, N: int, K: int, a_dtype: str, c_dtype: str,
+                transpose_a: bool = False, transpose_b: bool = False,
+                alpha: float = 1.0, beta: float = 0.0,
+                lda: int = 0, ldb: int = 0, ldc: int = 0,
+                stride_a: int = 0, stride_b: int = 0, stride_c: int = 0
+                ) -> Tuple[np.ndarray, np.ndarray]:
+    """Evaluate the definition only at the given (z, i, j) outputs.
+
+    Returns (rounded, value): rounded holds c_dtype stored values, value the
+    unrounded fp64 results (exact sums for int8).
+    """
+    _c_dtype_ok(a_dtype, c_dtype)
+    lda = lda or (M if transpose_a else K)
+    ldb = ldb or (K if transpose_b else N)
+    ldc = ldc or N
+    pts = np.asarray(points, dtype=np.int64).reshape(-1, 3)
+    zs = np.ascontiguousarray(pts[:, 0])
+    is_ = np.ascontiguousarray(pts[:, 1])
+    js = np.ascontiguousarray(pts[:, 2])
+    A = np.ascontiguousarray(A)
+    B = np.ascontiguousarray(B)
+    C_in = None if C_in is None else np.ascontiguousarray(C_in)
+    value = np.empty(len(pts), dtype=np.float64)
+    rounded = np.empty(len(pts), dtype=STORAGE[c_dtype])
+    rc = _load().oracle_gemm_points(M, N, K, DTYPES[a_dtype], DTYPES[c_dtype],
+                                    int(bool(transpose_a)), int(bool(transpose_b)),
+                                    float(alpha), float(beta), _ptr(A), lda, _ptr(B),
+                                    ldb, _ptr(C_in), ldc, stride_a, stride_b, stride_c,
+                                    len(pts), _ptr(zs), _ptr(is_), _ptr(js),
+                                    _ptr(value), _ptr(rounded))
+    if rc != 0:
+        raise ValueError("oracle_gemm_points rejected its arguments (code %d)" % rc)
+    return rounded, value
+
+
+def rel_frobenius(got: np.ndarray, ref: np.ndarray) -> float:
+    """||got - ref||_F / ||ref||_F in fp64 (the error measure of tensorcore
+    "GEMM", section "Numerical guarantees", with epsilon = 0: a zero reference
+    demands an exactly zero result, reported as 0 or inf)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    num = float(np.linalg.norm((got - ref).ravel()))
+    den = float(np.linalg.norm(ref.ravel()))
+    if den == 0.0:
+        return 0.0 if num == 0.0 else float("inf")
+    return num / den

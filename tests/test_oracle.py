@@ -1,0 +1,432 @@
+"""Pins of the CPU oracle against facts fixed outside it (no GPU needed).
+
+Each test checks the oracle against something it does not share code with:
+library codecs used as a special case (numpy float16, torch bfloat16), brute
+force over every value of a format, exact rational arithmetic (fractions) on
+tiny problems, closed forms (identity, permutation, alpha/beta), and the
+integer extremes the tessl "Architecture" page names in "Integer GEMM".
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+FLOAT_TYPES = ("f32", "f16", "bf16")
+
+
+# ----------------------------------------------------------------- helpers
+def lib_decode(bits, dtype):
+    """Decode with a library (independent of the oracle's decoders)."""
+    bits = np.asarray(bits)
+    if dtype == "f16":
+        return bits.astype(np.uint16).view(np.float16).astype(np.float64)
+    if dtype == "bf16":
+        t = torch.from_numpy(bits.astype(np.uint16).view(np.int16).copy())
+        return t.view(torch.bfloat16).to(torch.float64).numpy()
+    if dtype == "f32":
+        return bits.astype(np.float32).astype(np.float64)
+    return bits.astype(np.float64)
+
+
+def finite_values(dtype):
+    """Every finite value of a 16-bit format, sorted, with its bit pattern."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = lib_decode(bits, dtype)
+    ok = np.isfinite(vals)
+    vals, bits = vals[ok], bits[ok]
+    order = np.lexsort((bits, vals))
+    return vals[order], bits[order]
+
+
+FORMAT = {  # significand bits (with hidden bit), max finite exponent
+    "f16": (11, 15), "bf16": (8, 127), "f32": (24, 127)}
+
+
+def nearest_by_search(x, dtype, table):
+    """Round x to dtype by searching the enumerated finite values: nearest by
+    exact distance, ties to the pattern whose last significand bit is 0, and
+    +-inf beyond max + half an ulp (IEEE's unbounded-exponent rule)."""
+    vals, bits = table
+    p, emax = FORMAT[dtype]
+    maxf = float(vals[-1])
+    half_ulp_top = Fraction(2) ** (emax - p)        # half an ulp at the top binade
+    fx = Fraction(x)
+    if fx >= Fraction(maxf) + half_ulp_top:
+        return math.inf
+    if fx <= -Fraction(maxf) - half_ulp_top:
+        return -math.inf
+    k = int(np.searchsorted(vals, x))
+    cands = [c for c in (k - 1, k, k + 1) if 0 <= c < len(vals)]
+    best = None
+    for c in cands:
+        d = abs(Fraction(float(vals[c])) - fx)
+        key = (d, int(bits[c]) & 1)                  # even last bit wins a tie
+        if best is None or key < best[0]:
+            best = (key, c)
+    v = float(vals[best[1]])
+    if v == 0.0:
+        return math.copysign(0.0, x)
+    return v
+
+
+def nan_like(x, dtype):
+    if dtype == "f32":
+        return np.full_like(x, np.nan)
+    return np.full_like(x, 0x7E00 if dtype == "f16" else 0x7FC0)
+
+
+def exact_gemm(A, B, C, M, N, K, ta, tb, alpha, beta, lda, ldb, ldc):
+    """The definition in exact rational arithmetic (tiny sizes only)."""
+    out = [[None] * N for _ in range(M)]
+    for i in range(M):
+        for j in range(N):
+            s = Fraction(0)
+            for k in range(K):
+                a = A[k * lda + i] if ta else A[i * lda + k]
+                b = B[j * ldb + k] if tb else B[k * ldb + j]
+                s += Fraction(float(a)) * Fraction(float(b))
+            v = Fraction(alpha) * s
+            if beta != 0:
+                v += Fraction(beta) * Fraction(float(C[i * ldc + j]))
+            out[i][j] = v
+    return out
+
+
+def draw(rng, dtype, shape, kind="normal"):
+    if dtype == "i8":
+        return rng.integers(-128, 128, size=shape, dtype=np.int8)
+    if kind == "small_int":
+        x = rng.integers(-4, 5, size=shape).astype(np.float64)
+    else:
+        x = rng.normal(0, 1, size=shape)
+    if dtype == "f32":
+        return x.astype(np.float32)
+    if dtype == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    t = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+# ----------------------------------------------------------------- codecs
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_decode_exhaustive_matches_library(dtype):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.decode(bits, dtype)
+    ref = lib_decode(bits, dtype)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_encode_roundtrip_exhaustive(dtype):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = lib_decode(bits, dtype)
+    ok = ~np.isnan(vals)
+    back = oracle.encode(vals[ok], dtype)
+    assert np.array_equal(back, bits[ok])
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_round_ties_to_even_at_every_midpoint(dtype):
+    vals, bits = finite_values(dtype)
+    pos = vals > 0
+    v, b = vals[pos], bits[pos]
+    lo, hi = v[:-1], v[1:]
+    mid = (lo + hi) / 2.0                    # exact in fp64 (few bits)
+    even_lo = (b[:-1] & 1) == 0
+    expect = np.where(even_lo, lo, hi)
+    got = oracle.round_to(mid, dtype)
+    assert np.array_equal(got, expect)
+    assert np.array_equal(oracle.round_to(-mid, dtype), -expect)
+    # just below / above a midpoint go to the nearer neighbour
+    below = np.nextafter(mid, -np.inf)
+    above = np.nextafter(mid, np.inf)
+    assert np.array_equal(oracle.round_to(below, dtype), lo)
+    assert np.array_equal(oracle.round_to(above, dtype), hi)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_round_matches_enumerated_nearest(dtype):
+    table = finite_values(dtype)
+    rng = np.random.default_rng(11)
+    p, emax = FORMAT[dtype]
+    xs = np.concatenate([
+        rng.normal(0, 1, 400),
+        rng.normal(0, 1, 300) * np.exp2(rng.integers(-30 if dtype == "f16" else -140,
+                                                     emax + 2, 300)),
+        rng.uniform(-1, 1, 100) * float(table[0][-1]) * 1.01,
+    ])
+    got = oracle.round_to(xs, dtype)
+    ref = np.array([nearest_by_search(float(x), dtype, table) for x in xs])
+    assert np.array_equal(got, ref)
+
+
+def test_f16_round_matches_numpy_direct_cast():
+    rng = np.random.default_rng(3)
+    xs = np.concatenate([rng.normal(0, 1, 20000),
+                         rng.normal(0, 1, 20000) * np.exp2(rng.integers(-28, 17, 20000))])
+    got = oracle.encode(xs, "f16")
+    with np.errstate(over="ignore"):
+        ref = xs.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_f32_round_matches_hardware_cast():
+    rng = np.random.default_rng(4)
+    xs = rng.normal(0, 1, 50000) * np.exp2(rng.integers(-150, 129, 50000))
+    got = oracle.round_to(xs, "f32")
+    with np.errstate(over="ignore"):
+        ref = xs.astype(np.float32).astype(np.float64)
+    assert np.array_equal(got, ref)
+
+
+def test_overflow_and_specials():
+    assert oracle.round_to(np.array([65520.0]), "f16")[0] == math.inf     # tie -> even -> inf
+    assert oracle.round_to(np.array([65519.0]), "f16")[0] == 65504.0
+    assert oracle.encode(np.array([-1e9]), "f16")[0] == 0xFC00
+    assert oracle.encode(np.array([3.5e38]), "bf16")[0] == 0x7F80
+    assert oracle.encode(np.array([2.0 ** -25]), "f16")[0] == 0x0000         # tie -> even zero
+    assert oracle.encode(np.array([2.0 ** -25 * 1.5]), "f16")[0] == 0x0001
+    assert oracle.encode(np.array([-0.0]), "bf16")[0] == 0x8000
+
+
+# ----------------------------------------------------------------- GEMM vs exact rationals
+LAYOUTS = [(False, False), (True, False), (False, True), (True, True)]
+
+
+def _tiny_case(rng, dtype, ta, tb, M, N, K, pad, kind):
+    lda = (M if ta else K) + pad
+    ldb = (K if tb else N) + pad
+    ldc = N + pad
+    A = draw(rng, dtype, ((K if ta else M) * lda,), kind)
+    B = draw(rng, dtype, ((N if tb else K) * ldb,), kind)
+    return A, B, lda, ldb, ldc
+
+
+@pytest.mark.parametrize("dtype", FLOAT_TYPES)
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+@pytest.mark.parametrize("alpha,beta", [(1.0, 0.0), (0.5, 1.0), (-2.0, 0.25)])
+def test_tiny_float_gemm_against_exact_rationals(dtype, ta, tb, alpha, beta):
+    rng = np.random.default_rng(hash((dtype, ta, tb, alpha)) % 2**32)
+    M, N, K, pad = 7, 5, 8, 3
+    A, B, lda, ldb, ldc = _tiny_case(rng, dtype, ta, tb, M, N, K, pad, "normal")
+    C_in = draw(rng, dtype, (M * ldc,), "normal")
+    Ad, Bd, Cd = (lib_decode(x, dtype) for x in (A, B, C_in))
+    exact = exact_gemm(Ad, Bd, Cd, M, N, K, ta, tb, alpha, beta, lda, ldb, ldc)
+    C_out, value = oracle.gemm(A, B, C_in, M=M, N=N, K=K, a_dtype=dtype, c_dtype=dtype,
+                               transpose_a=ta, transpose_b=tb, alpha=alpha, beta=beta,
+                               lda=lda, ldb=ldb, ldc=ldc)
+    table = finite_values(dtype) if dtype != "f32" else None
+    got = lib_decode(C_out, dtype)
+    for i in range(M):
+        for j in range(N):
+            ex = exact[i][j]
+            # fp64 sum of K exact products: error within K*2^-53*sum|terms|
+            bound = Fraction(K + 2) * Fraction(2) ** -53 * (abs(ex) + 64)
+            assert abs(Fraction(value[0, i, j]) - ex) <= bound
+            if dtype == "f32":
+                want = float(np.float64(float(ex)).astype(np.float32))
+            else:
+                want = nearest_by_search(float(ex), dtype, table)
+            assert got[i * ldc + j] == want, (i, j)
+    # padding columns of C are untouched
+    for i in range(M):
+        for j in range(N, ldc):
+            assert C_out[i * ldc + j] == C_in[i * ldc + j] or (
+                np.isnan(got[i * ldc + j]) and np.isnan(lib_decode(C_in[i * ldc + j], dtype)))
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_tiny_int8_gemm_against_exact_integers(ta, tb):
+    rng = np.random.default_rng(77)
+    M, N, K, pad = 6, 9, 13, 2
+    A, B, lda, ldb, ldc = _tiny_case(rng, "i8", ta, tb, M, N, K, pad, "")
+    C_out, value = oracle.gemm(A, B, None, M=M, N=N, K=K, a_dtype="i8", c_dtype="i32",
+                               transpose_a=ta, transpose_b=tb, lda=lda, ldb=ldb, ldc=ldc,
+                               C_like=np.full(M * ldc, 99, dtype=np.int32))
+    exact = exact_gemm(A.astype(np.int64), B.astype(np.int64), None, M, N, K, ta, tb,
+                       1, 0, lda, ldb, ldc)
+    for i in range(M):
+        for j in range(N):
+            assert C_out[i * ldc + j] == exact[i][j]
+            assert value[0, i, j] == exact[i][j]
+        for j in range(N, ldc):
+            assert C_out[i * ldc + j] == 99
+
+
+@pytest.mark.parametrize("dtype", FLOAT_TYPES + ("i8",))
+def test_small_integer_inputs_are_exact(dtype):
+    """Integer-valued inputs keep every fp64 partial sum exact, so the oracle
+    value equals the exact integer sum."""
+    rng = np.random.default_rng(5)
+    M, N, K = 9, 11, 40
+    A = draw(rng, dtype, (M * K,), "small_int")
+    B = draw(rng, dtype, (K * N,), "small_int")
+    c_dtype = "i32" if dtype == "i8" else dtype
+    _, value = oracle.gemm(A, B, None, M=M, N=N, K=K, a_dtype=dtype, c_dtype=c_dtype)
+    Ad = lib_decode(A, dtype).reshape(M, K).astype(np.int64)
+    Bd = lib_decode(B, dtype).reshape(K, N).astype(np.int64)
+    assert np.array_equal(value[0], (Ad @ Bd).astype(np.float64))
+
+
+# ----------------------------------------------------------------- closed forms
+@pytest.mark.parametrize("dtype", FLOAT_TYPES + ("i8",))
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_identity_and_permutation(dtype, ta, tb):
+    rng = np.random.default_rng(9)
+    n = 12
+    one = {"f32": np.float32(1), "f16": np.float16(1).view(np.uint16),
+           "bf16": np.uint16(0x3F80), "i8": np.int8(1)}[dtype]
+    perm = rng.permutation(n)
+    P = np.zeros((n, n), dtype=draw(rng, dtype, (1,)).dtype)
+    P[np.arange(n), perm] = one                  # (P @ X)[i] = X[perm[i]]
+    X = draw(rng, dtype, (n, n))
+    c_dtype = "i32" if dtype == "i8" else dtype
+    A = P.T.copy() if ta else P
+    B = X.T.copy() if tb else X
+    C_out, _ = oracle.gemm(A, B, None, M=n, N=n, K=n, a_dtype=dtype, c_dtype=c_dtype,
+                           transpose_a=ta, transpose_b=tb)
+    C_out = C_out.reshape(n, n)
+    if dtype == "i8":
+        assert np.array_equal(C_out, X[perm].astype(np.int32))
+    else:
+        assert np.array_equal(C_out, X[perm])
+
+
+@pytest.mark.parametrize("dtype", FLOAT_TYPES + ("i8",))
+def test_transposed_storage_equals_plain(dtype):
+    rng = np.random.default_rng(10)
+    M, N, K = 10, 7, 33
+    A = draw(rng, dtype, (M, K))
+    B = draw(rng, dtype, (K, N))
+    c_dtype = "i32" if dtype == "i8" else dtype
+    ref, _ = oracle.gemm(A, B, None, M=M, N=N, K=K, a_dtype=dtype, c_dtype=c_dtype)
+    for ta, tb in LAYOUTS[1:]:
+        As = A.T.copy() if ta else A
+        Bs = B.T.copy() if tb else B
+        got, _ = oracle.gemm(As, Bs, None, M=M, N=N, K=K, a_dtype=dtype, c_dtype=c_dtype,
+                             transpose_a=ta, transpose_b=tb)
+        assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("dtype", FLOAT_TYPES)
+def test_alpha_beta_closed_forms(dtype):
+    rng = np.random.default_rng(12)
+    M, N, K = 8, 6, 16
+    A = draw(rng, dtype, (M, K))
+    B = draw(rng, dtype, (K, N))
+    C = draw(rng, dtype, (M, N))
+    Cd = lib_decode(C, dtype)
+    kw = dict(M=M, N=N, K=K, a_dtype=dtype, c_dtype=dtype)
+    # alpha = 0: C = round(beta*C_in) and A, B are never read (NaN operands)
+    out, val = oracle.gemm(nan_like(A, dtype), nan_like(B, dtype), C,
+                           alpha=0.0, beta=0.75, **kw)
+    assert np.array_equal(val[0], 0.75 * Cd)
+    # alpha = 0, beta = 1: C unchanged bit for bit
+    out, _ = oracle.gemm(A, B, C, alpha=0.0, beta=1.0, **kw)
+    assert np.array_equal(out, C)
+    # alpha = 2 doubles the alpha = 1 value exactly (a power-of-two scale)
+    _, v1 = oracle.gemm(A, B, None, alpha=1.0, beta=0.0, **kw)
+    _, v2 = oracle.gemm(A, B, None, alpha=2.0, beta=0.0, **kw)
+    assert np.array_equal(v2, 2.0 * v1)
+    # beta = 0: C_in is not read, so NaNs there do not leak
+    o_nan, v_nan = oracle.gemm(A, B, nan_like(C, dtype), alpha=1.0, beta=0.0, **kw)
+    assert np.array_equal(v_nan, v1)
+    assert not np.isnan(lib_decode(o_nan, dtype)).any()
+
+
+def test_linearity_in_b():
+    rng = np.random.default_rng(13)
+    M, N, K = 9, 8, 64
+    A = rng.normal(0, 1, (M, K)).astype(np.float32)
+    # B1, B2 with few significand bits so that B1 + B2 is exact in fp32
+    B1 = (np.round(rng.normal(0, 1, (K, N)) * 64) / 64).astype(np.float32)
+    B2 = (np.round(rng.normal(0, 1, (K, N)) * 64) / 64).astype(np.float32)
+    kw = dict(M=M, N=N, K=K, a_dtype="f32", c_dtype="f32")
+    _, v12 = oracle.gemm(A, B1 + B2, None, **kw)
+    _, v1 = oracle.gemm(A, B1, None, **kw)
+    _, v2 = oracle.gemm(A, B2, None, **kw)
+    absum = np.abs(A).astype(np.float64) @ (np.abs(B1) + np.abs(B2)).astype(np.float64)
+    bound = 3 * K * 2.0 ** -53 * absum
+    assert np.all(np.abs(v12[0] - v1[0] - v2[0]) <= bound)
+    # a dropped or doubled term would break it by far more than the bound
+    assert np.abs(v12[0] - v1[0]).max() > 1e3 * bound.max()
+
+
+# ----------------------------------------------------------------- integer extremes
+@pytest.mark.parametrize("K", [1, 4096, 131071])
+def test_int8_extremes(K):
+    """All (-128)*(-128) gives 16384*K; 127*(-128) gives -16256*K.  At
+    K = 131071 the first is 2147467264, still below 2^31 - 1."""
+    M, N = 2, 3
+    A = np.full((M, K), -128, dtype=np.int8)
+    B = np.full((K, N), -128, dtype=np.int8)
+    out, val = oracle.gemm(A, B, None, M=M, N=N, K=K, a_dtype="i8", c_dtype="i32")
+    assert np.all(out == 16384 * K) and np.all(val == 16384 * K)
+    A[:] = 127
+    out, _ = oracle.gemm(A, B, None, M=M, N=N, K=K, a_dtype="i8", c_dtype="i32")
+    assert np.all(out == -16256 * K)
+    if K == 131071:
+        assert 16384 * K <= 2 ** 31 - 1 < 16384 * (K + 1)
+
+
+# ----------------------------------------------------------------- worked example
+def test_foundry_quickstart_2x2():
+    with open(os.path.join(GOLDEN, "foundry_quickstart_2x2.json")) as f:
+        g = json.load(f)
+    A = np.array(g["A"], dtype=np.float32)
+    B = np.array(g["B"], dtype=np.float32)
+    C = np.array(g["C"], dtype=np.float32)
+    out, _ = oracle.gemm(A, B, C, M=g["M"], N=g["N"], K=g["K"], a_dtype="f32",
+                         c_dtype="f32", alpha=g["alpha"], beta=g["beta"])
+    exact = exact_gemm(A, B, C, 2, 2, 2, False, False, g["alpha"], g["beta"], 2, 2, 2)
+    assert out.tolist() == [float(exact[i][j]) for i in range(2) for j in range(2)]
+    assert out.tolist() == [19.0, 22.0, 43.0, 50.0]
+
+
+# ----------------------------------------------------------------- batched and points
+@pytest.mark.parametrize("dtype", ["bf16", "i8"])
+def test_batched_equals_per_problem_and_points(dtype):
+    rng = np.random.default_rng(14)
+    b, M, N, K = 3, 5, 7, 20
+    A = draw(rng, dtype, (b, K, M))      # TN
+    B = draw(rng, dtype, (b, K, N))
+    c_dtype = "i32" if dtype == "i8" else "f32"
+    kw = dict(M=M, N=N, K=K, a_dtype=dtype, c_dtype=c_dtype, transpose_a=True)
+    out, val = oracle.gemm(A, B, None, batch=b, stride_a=K * M, stride_b=K * N,
+                           stride_c=M * N, **kw)
+    out = out.reshape(b, M, N)
+    for z in range(b):
+        o1, v1 = oracle.gemm(A[z], B[z], None, **kw)
+        assert np.array_equal(o1.reshape(M, N), out[z])
+        assert np.array_equal(v1[0], val[z])
+    pts = [(z, i, j) for z in range(b) for i in range(M) for j in range(N)]
+    r, v = oracle.gemm_points(A, B, None, pts, stride_a=K * M, stride_b=K * N,
+                              stride_c=M * N, **kw)
+    assert np.array_equal(r.reshape(b, M, N), out)
+    assert np.array_equal(v.reshape(b, M, N), val)
+
+
+def test_rejects_bad_arguments():
+    A = np.zeros(4, dtype=np.int8)
+    with pytest.raises(ValueError):
+        oracle.gemm(A, A, None, M=2, N=2, K=2, a_dtype="i8", c_dtype="i32", alpha=2.0)
+    with pytest.raises(ValueError):
+        oracle.gemm(A, A, None, M=0, N=2, K=2, a_dtype="i8", c_dtype="i32")
+    with pytest.raises(ValueError):
+        oracle.gemm(A, A, None, M=2, N=2, K=2, a_dtype="i8", c_dtype="f16")
+
+
+def test_rel_frobenius():
+    assert oracle.rel_frobenius(np.zeros(3), np.zeros(3)) == 0.0
+    assert oracle.rel_frobenius(np.ones(3), np.zeros(3)) == math.inf
+    assert oracle.rel_frobenius(np.array([3.0, 4.0]), np.array([3.0, 0.0])) == pytest.approx(4 / 3)
