@@ -1,0 +1,147 @@
+// epilogue_kernels.hip -- the split-K reduction, the alpha == 0 kernel, and
+// the dispatch from (input type, layout) to the per-object launchers.
+#include "gemm_kernel.hpp"
+
+namespace tcg {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Split-K reduction: C = round(alpha * sum_s partial[s] + beta * C_old), the
+// slices summed in ascending s so the result is the same on every run.
+// One thread per 4 consecutive outputs of a row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const EpilogueArgs a) {
+    const int nq = (a.N + 3) / 4;
+    const int64_t total = (int64_t)a.batch * a.M * nq;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total) return;
+    const int z = (int)(idx / ((int64_t)a.M * nq));
+    const int64_t rem = idx - (int64_t)z * a.M * nq;
+    const int m = (int)(rem / nq), n = (int)(rem % nq) * 4;
+    const int nvalid = a.N - n;
+    const int64_t plane = (int64_t)a.M * a.N;
+    const char *wsz = static_cast<const char *>(a.ws) + (int64_t)z * a.splits * plane * 4;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(wsz, (int64_t)a.splits * plane * 4);
+    const int CES = dt_size(a.c_dtype);
+    char *Cz = static_cast<char *>(a.C) + z * a.stride_c * CES;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cz, a.c_extent);
+    const int coff = (m * a.ldc + n) * CES;
+    const bool wvec = (a.N % 4) == 0;
+    const bool cvec = a.c_vec_ok != 0;
+    if (a.acc_is_int) {
+        int s4[4] = {0, 0, 0, 0};
+        for (int s = 0; s < a.splits; ++s) {
+            const int off = (int)((s * plane + (int64_t)m * a.N + n) * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (e < nvalid) s4[e] += (int)__builtin_amdgcn_raw_buffer_load_b32(rw, off + 4 * e, 0, 0);
+        }
+        store_i4(rc, coff, nvalid, cvec, s4);
+        return;
+    }
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < a.splits; ++s) {
+        const int off = (int)((s * plane + (int64_t)m * a.N + n) * 4);
+        if (wvec && nvalid >= 4) {
+            u32x4 w = ld128(rw, off);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s4[e] += __builtin_bit_cast(float, w[e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (e < nvalid)
+                    s4[e] += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, off + 4 * e, 0, 0));
+        }
+    }
+    switch (a.c_dtype) {
+    case DT_F32: finish4<DT_F32>(rc, coff, nvalid, cvec, a.alpha, a.beta, s4); break;
+    case DT_BF16: finish4<DT_BF16>(rc, coff, nvalid, cvec, a.alpha, a.beta, s4); break;
+    default: finish4<DT_F16>(rc, coff, nvalid, cvec, a.alpha, a.beta, s4); break;
+    }
+}
+
+// alpha == 0: C = beta * C (beta == 0 writes zeros without reading C).
+__global__ __launch_bounds__(256) void scale_c_kernel(const EpilogueArgs a) {
+    const int nq = (a.N + 3) / 4;
+    const int64_t total = (int64_t)a.batch * a.M * nq;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total) return;
+    const int z = (int)(idx / ((int64_t)a.M * nq));
+    const int64_t rem = idx - (int64_t)z * a.M * nq;
+    const int m = (int)(rem / nq), n = (int)(rem % nq) * 4;
+    const int nvalid = a.N - n;
+    const int CES = dt_size(a.c_dtype);
+    char *Cz = static_cast<char *>(a.C) + z * a.stride_c * CES;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cz, a.c_extent);
+    const int coff = (m * a.ldc + n) * CES;
+    const bool cvec = a.c_vec_ok != 0;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    // alpha = 1 on zeros keeps them zero; finish4 then adds beta * C_old.
+    switch (a.c_dtype) {
+    case DT_F32: finish4<DT_F32>(rc, coff, nvalid, cvec, 1.f, a.beta, v); break;
+    case DT_BF16: finish4<DT_BF16>(rc, coff, nvalid, cvec, 1.f, a.beta, v); break;
+    case DT_F16: finish4<DT_F16>(rc, coff, nvalid, cvec, 1.f, a.beta, v); break;
+    default: {
+        int iv[4] = {0, 0, 0, 0};
+        store_i4(rc, coff, nvalid, cvec, iv);
+    }
+    }
+}
+
+using Launcher = hipError_t (*)(int, int, const GemmArgs &, int64_t, hipStream_t);
+
+// [input type][transpose_a * 2 + transpose_b]
+const Launcher kLaunchers[4][4] = {
+    {tcg_launch_f32_nn, tcg_launch_f32_nt, tcg_launch_f32_tn, tcg_launch_f32_tt},
+    {tcg_launch_f16_nn, tcg_launch_f16_nt, tcg_launch_f16_tn, tcg_launch_f16_tt},
+    {tcg_launch_bf16_nn, tcg_launch_bf16_nt, tcg_launch_bf16_tn, tcg_launch_bf16_tt},
+    {tcg_launch_i8_nn, tcg_launch_i8_nt, tcg_launch_i8_tn, tcg_launch_i8_tt}};
+
+const char *const kDtName[4] = {"f32", "f16", "bf16", "i8"};
+const char *const kLayoutName[2][2] = {{"nn", "nt"}, {"tn", "tt"}};
+const char *const kTileName[NUM_TILE_CLASSES] = {"256x256", "128x128", "64x64"};
+
+char g_names[4][2][2][NUM_TILE_CLASSES][64];
+bool g_names_ready = false;
+
+}  // namespace
+}  // namespace tcg
+
+using namespace tcg;
+
+hipError_t tcg_launch_gemm(int dt, bool ta, bool tb, int cls, int out, const GemmArgs &args,
+                           int64_t grid, hipStream_t stream) {
+    if (dt < 0 || dt > 3 || cls < 0 || cls >= NUM_TILE_CLASSES || grid <= 0 || grid > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    return kLaunchers[dt][(ta ? 2 : 0) + (tb ? 1 : 0)](cls, out, args, grid, stream);
+}
+
+hipError_t tcg_launch_splitk_reduce(const EpilogueArgs &args, hipStream_t stream) {
+    const int64_t total = (int64_t)args.batch * args.M * ((args.N + 3) / 4);
+    const int64_t blocks = (total + 255) / 256;
+    if (blocks <= 0 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, args);
+    return hipGetLastError();
+}
+
+hipError_t tcg_launch_scale_c(const EpilogueArgs &args, hipStream_t stream) {
+    const int64_t total = (int64_t)args.batch * args.M * ((args.N + 3) / 4);
+    const int64_t blocks = (total + 255) / 256;
+    if (blocks <= 0 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(scale_c_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, args);
+    return hipGetLastError();
+}
+
+const char *tcg_kernel_name(int dt, bool ta, bool tb, int cls) {
+    if (dt < 0 || dt > 3 || cls < 0 || cls >= NUM_TILE_CLASSES) return "";
+    if (!g_names_ready) {
+        for (int d = 0; d < 4; ++d)
+            for (int a = 0; a < 2; ++a)
+                for (int b = 0; b < 2; ++b)
+                    for (int c = 0; c < NUM_TILE_CLASSES; ++c)
+                        snprintf(g_names[d][a][b][c], sizeof g_names[d][a][b][c], "gemm_%s_%s_%s",
+                                 kDtName[d], kLayoutName[a][b], kTileName[c]);
+        g_names_ready = true;
+    }
+    return g_names[dt][ta ? 1 : 0][tb ? 1 : 0][cls];
+}

@@ -1,0 +1,59 @@
+// gemm_inst.hip -- instantiates the GEMM kernel for one input type and one
+// layout and exports that object's launcher.  The build compiles this file
+// once per (TCG_DT, TCG_TA, TCG_TB) with TCG_LAUNCHER naming the launcher,
+// so the 16 objects compile in parallel.
+#include "gemm_kernel.hpp"
+
+#if !defined(TCG_DT) || !defined(TCG_TA) || !defined(TCG_TB) || !defined(TCG_LAUNCHER)
+#error "the build defines TCG_DT, TCG_TA, TCG_TB and TCG_LAUNCHER"
+#endif
+
+namespace tcg {
+namespace {
+
+// Output types that exist for this input type (include/tcgemm.h lists the
+// supported tuples); split-K partials only for the 64x64 class, the only
+// class the planner splits.
+constexpr bool out_ok(int cls, int out) {
+    if (out == OUT_PARTIAL) return cls == TILE_64;
+    if (TCG_DT == DT_I8) return out == DT_I32;
+    if (TCG_DT == DT_F32) return out == DT_F32;
+    return out == TCG_DT || out == DT_F32;
+}
+
+template <int CLS, int OUT>
+hipError_t launch_one(const GemmArgs &args, int64_t grid, hipStream_t stream) {
+    if constexpr (out_ok(CLS, OUT)) {
+        hipLaunchKernelGGL((gemm_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, CLS, OUT>),
+                           dim3((unsigned)grid), dim3(256), 0, stream, args);
+        return hipGetLastError();
+    } else {
+        return hipErrorInvalidValue;
+    }
+}
+
+template <int CLS>
+hipError_t launch_cls(int out, const GemmArgs &args, int64_t grid, hipStream_t stream) {
+    switch (out) {
+    case DT_F32: return launch_one<CLS, DT_F32>(args, grid, stream);
+    case DT_F16: return launch_one<CLS, DT_F16>(args, grid, stream);
+    case DT_BF16: return launch_one<CLS, DT_BF16>(args, grid, stream);
+    case DT_I32: return launch_one<CLS, DT_I32>(args, grid, stream);
+    case OUT_PARTIAL: return launch_one<CLS, OUT_PARTIAL>(args, grid, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+}  // namespace tcg
+
+hipError_t TCG_LAUNCHER(int cls, int out, const tcg::GemmArgs &args, int64_t grid,
+                        hipStream_t stream) {
+    using namespace tcg;
+    switch (cls) {
+    case TILE_256: return launch_cls<TILE_256>(out, args, grid, stream);
+    case TILE_128: return launch_cls<TILE_128>(out, args, grid, stream);
+    case TILE_64: return launch_cls<TILE_64>(out, args, grid, stream);
+    default: return hipErrorInvalidValue;
+    }
+}

@@ -1,0 +1,565 @@
+// gemm_kernel.hpp -- the dense GEMM kernel template for gfx950 (MI355X, CDNA4).
+// Instantiated by gemm_inst.hip (one object per input type and layout).
+//
+// Computes C = alpha * op(A) @ op(B) + beta * C in BLAS row-major layout
+// (tensorcore "GEMM", section "Surface"), as a K-tiled loop that stages a
+// slice of each operand and accumulates their product (Phobos "Matrix
+// products", matmul / matmul_t), with the accumulator held in registers for
+// the whole K loop and C written exactly once (tessl "Architecture", section
+// "Cooperative Destination Accumulation").
+//
+// Structure of one workgroup (256 threads = 4 wave64s, 2 x 2):
+//   * tile (tm, tn, group) from tile_of_workgroup(): XCD-aware regrouping,
+//     then the column-panel band order;
+//   * per K-tile: every thread loads its share of the A and B tiles from HBM
+//     into registers (buffer loads; transposed operands are transposed in
+//     registers), writes them to one of two LDS stages, and the waves run MFMA
+//     on the other stage -- one barrier per K-tile;
+//   * LDS holds both operands K-contiguous: one 128-byte row of K per M (or
+//     N) index, its 16-byte chunks XOR-swizzled by the row so that fragment
+//     reads and transposed writes do not collide in banks;
+//   * each wave owns a (BM/2) x (BN/2) block of C as 16x16 MFMA blocks;
+//     operands enter the MFMA swapped (B block as src0, A block as src1) so
+//     each lane ends up with 4 consecutive columns of one C row;
+//   * epilogue: alpha*acc + beta*C_old (C read only when beta != 0), rounded
+//     once to the output type, masked to the M x N extent -- or, for split-K,
+//     the raw fp32/int32 partial to the workspace.
+//
+// Ragged edges (tessl "Architecture", "Edge-Slice Support"): tiles that reach
+// past M, N or K take a checked load path that zero-fills everything outside
+// the operand, element by element where a 16-byte chunk straddles the end.
+// Every global access is a buffer access whose range is the operand's own
+// extent, so an access outside it reads 0 or is dropped instead of faulting.
+
+#pragma once
+
+#include <type_traits>
+
+#include "tc_internal.h"
+
+namespace tcg {
+namespace {
+
+typedef uint32_t u32;
+typedef u32 u32x4 __attribute__((ext_vector_type(4)));
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// Word 3 of a gfx9-family buffer resource: raw (untyped) 32-bit data.
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    int32_t n = bytes <= 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, kRsrcWord3);
+}
+
+__device__ inline u32x4 ld128(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// Load the first `nvalid` elements (of 16 / ES) of a 16-byte chunk one by
+// one; the rest of the chunk is zero.  Used where a chunk straddles the end
+// of a row or of the operand.
+template <int ES>
+__device__ inline u32x4 ld_partial(__amdgpu_buffer_rsrc_t r, int off, int nvalid) {
+    u32 w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 16 / ES; ++e) {
+        if (e < nvalid) {
+            u32 x;
+            if constexpr (ES == 4) {
+                x = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * e, 0, 0);
+            } else if constexpr (ES == 2) {
+                x = __builtin_amdgcn_raw_buffer_load_b16(r, off + 2 * e, 0, 0);
+            } else {
+                x = __builtin_amdgcn_raw_buffer_load_b8(r, off + e, 0, 0);
+            }
+            const int bit = e * ES * 8;
+            w[bit >> 5] |= x << (bit & 31);
+        }
+    }
+    return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// LDS tile layout: row r (an M or N index) holds 128 bytes of K as 8 chunks
+// of 16 bytes; chunk c is stored at position c ^ swz(r).  swz mixes the low
+// three bits of the row with the next three, so 8 consecutive rows read at
+// one chunk (fragment reads) and rows 8 apart written at one chunk
+// (transposed writes) both land on 8 different 16-byte bank groups.
+__device__ inline int swz(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ inline int lds_off(int row, int chunk) {
+    return row * kLdsRowBytes + ((chunk ^ swz(row)) << 4);
+}
+
+// ---------------------------------------------------------------------------
+// Operand tile loaders.  A tile is R rows (M or N indices) x 128 bytes of K.
+// ---------------------------------------------------------------------------
+
+// K-contiguous operand (A not transposed, B transposed): global row r has the
+// tile's K slice at bytes [0, 128) from the tile origin.  8 threads cover one
+// 128-byte row, so a wave reads 8 full rows.
+template <int ES, int R, int THREADS>
+struct RowLoader {
+    static constexpr int kChunks = R * 8;
+    static constexpr int kPer = (kChunks + THREADS - 1) / THREADS;
+    u32x4 v[kPer];
+
+    template <bool CHECK>
+    __device__ inline void load(__amdgpu_buffer_rsrc_t r, int tid, int ld_bytes,
+                                int rows_valid, int k_valid) {
+        constexpr int EPC = 16 / ES;
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int q = tid + u * THREADS;
+            if (kChunks % THREADS != 0 && q >= kChunks) break;
+            const int row = q >> 3, c = q & 7;
+            const int off = row * ld_bytes + c * 16;
+            if constexpr (!CHECK) {
+                v[u] = ld128(r, off);
+            } else {
+                const int k0 = c * EPC;
+                if (row < rows_valid && k0 + EPC <= k_valid) {
+                    v[u] = ld128(r, off);
+                } else if (row >= rows_valid || k0 >= k_valid) {
+                    v[u] = u32x4{0u, 0u, 0u, 0u};
+                } else {
+                    v[u] = ld_partial<ES>(r, off, k_valid - k0);
+                }
+            }
+        }
+    }
+
+    __device__ inline void store(char *s, int tid) const {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int q = tid + u * THREADS;
+            if (kChunks % THREADS != 0 && q >= kChunks) break;
+            *reinterpret_cast<u32x4 *>(s + lds_off(q >> 3, q & 7)) = v[u];
+        }
+    }
+};
+
+// M/N-contiguous operand (A transposed, B not transposed): global row k holds
+// the tile's R M/N values.  Each thread loads a block of KB rows x 16 bytes
+// and transposes it in registers so that LDS again holds K-contiguous rows.
+// Threads with consecutive ids take consecutive 16-byte chunks of one k row.
+template <int ES, int R, int THREADS>
+struct ColLoader {
+    static constexpr int EPC = 16 / ES;             // M/N values per chunk
+    static constexpr int KB = (ES == 4) ? 4 : 8;    // k rows per block
+    static constexpr int BKE = kLdsRowBytes / ES;   // k values per tile
+    static constexpr int NMB = R / EPC;
+    static constexpr int NKB = BKE / KB;
+    static constexpr int kBlocks = NMB * NKB;
+    static constexpr int kPer = (kBlocks + THREADS - 1) / THREADS;
+    static_assert(R % EPC == 0, "tile rows must hold whole chunks");
+    u32x4 in[kPer][KB];
+
+    template <bool CHECK>
+    __device__ inline void load(__amdgpu_buffer_rsrc_t r, int tid, int ld_bytes,
+                                int mn_valid, int k_valid) {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int q = tid + u * THREADS;
+            if (kBlocks % THREADS != 0 && q >= kBlocks) break;
+            const int mb = q % NMB, kb = q / NMB;
+#pragma unroll
+            for (int j = 0; j < KB; ++j) {
+                const int krow = kb * KB + j;
+                const int off = krow * ld_bytes + mb * 16;
+                if constexpr (!CHECK) {
+                    in[u][j] = ld128(r, off);
+                } else {
+                    const int mn0 = mb * EPC;
+                    if (krow < k_valid && mn0 + EPC <= mn_valid) {
+                        in[u][j] = ld128(r, off);
+                    } else if (krow >= k_valid || mn0 >= mn_valid) {
+                        in[u][j] = u32x4{0u, 0u, 0u, 0u};
+                    } else {
+                        in[u][j] = ld_partial<ES>(r, off, mn_valid - mn0);
+                    }
+                }
+            }
+        }
+    }
+
+    __device__ inline void store(char *s, int tid) const {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int q = tid + u * THREADS;
+            if (kBlocks % THREADS != 0 && q >= kBlocks) break;
+            const int mb = q % NMB, kb = q / NMB;
+            if constexpr (ES == 4) {
+                // 4 k rows x 4 values: column e is word e of each row.
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    u32x4 o = {in[u][0][e], in[u][1][e], in[u][2][e], in[u][3][e]};
+                    *reinterpret_cast<u32x4 *>(s + lds_off(mb * 4 + e, kb)) = o;
+                }
+            } else if constexpr (ES == 2) {
+                // 8 k rows x 8 halves: column e takes half (e & 1) of word e/2
+                // of rows 2p and 2p+1 into word p.
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    u32x4 o;
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const u32 x0 = in[u][2 * p][e >> 1], x1 = in[u][2 * p + 1][e >> 1];
+                        o[p] = (e & 1) ? ((x0 >> 16) | (x1 & 0xFFFF0000u))
+                                       : ((x0 & 0xFFFFu) | (x1 << 16));
+                    }
+                    *reinterpret_cast<u32x4 *>(s + lds_off(mb * 8 + e, kb)) = o;
+                }
+            } else {
+                // 8 k rows x 16 bytes: column c gathers byte c of each row,
+                // rows 0-3 into the low word and rows 4-7 into the high word;
+                // the 8 bytes go to byte offset 8*kb of the 128-byte row.
+#pragma unroll
+                for (int c = 0; c < 16; ++c) {
+                    const int w = c >> 2, sh = (c & 3) * 8;
+                    u32 lo = 0, hi = 0;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        lo |= ((in[u][j][w] >> sh) & 0xFFu) << (8 * j);
+                        hi |= ((in[u][j + 4][w] >> sh) & 0xFFu) << (8 * j);
+                    }
+                    *reinterpret_cast<u32x2 *>(s + lds_off(mb * 16 + c, kb >> 1) +
+                                               ((kb & 1) << 3)) = u32x2{lo, hi};
+                }
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// MFMA step: one 16x16 output block, one 16-byte K chunk per lane.
+// Lane l supplies row (l % 16) of its operand and chunk (l / 16) of the
+// current 64-byte half of the LDS row; both operands use the same lane -> k
+// mapping, so the instruction contracts matching k.
+// ---------------------------------------------------------------------------
+template <int DT>
+struct Mma;
+
+template <>
+struct Mma<DT_BF16> {
+    using Acc = f32x4;
+    __device__ static inline void run(Acc &acc, u32x4 b, u32x4 a) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b),
+                                                      __builtin_bit_cast(bf16x8, a), acc, 0, 0, 0);
+    }
+};
+
+template <>
+struct Mma<DT_F16> {
+    using Acc = f32x4;
+    __device__ static inline void run(Acc &acc, u32x4 b, u32x4 a) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, b),
+                                                     __builtin_bit_cast(f16x8, a), acc, 0, 0, 0);
+    }
+};
+
+template <>
+struct Mma<DT_I8> {
+    using Acc = i32x4;
+    __device__ static inline void run(Acc &acc, u32x4 b, u32x4 a) {
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, b),
+                                                    __builtin_bit_cast(i32x4, a), acc, 0, 0, 0);
+    }
+};
+
+// fp32: a 16-byte chunk holds 4 k values; element e of every lane's chunk
+// feeds the e-th 16x16x4 instruction, which therefore contracts the k set
+// {4g + e : g = 0..3} -- the four instructions together cover all 16.
+template <>
+struct Mma<DT_F32> {
+    using Acc = f32x4;
+    __device__ static inline void run(Acc &acc, u32x4 b, u32x4 a) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, b[e]),
+                                                       __builtin_bit_cast(float, a[e]), acc,
+                                                       0, 0, 0);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Output conversion and the shared epilogue of the GEMM and reduce kernels.
+// ---------------------------------------------------------------------------
+__device__ inline u32 to_bf16_bits(float x) {
+    return (u32)__builtin_bit_cast(unsigned short, static_cast<__bf16>(x));
+}
+__device__ inline u32 to_f16_bits(float x) {
+    return (u32)__builtin_bit_cast(unsigned short, static_cast<_Float16>(x));
+}
+__device__ inline float from_bf16_bits(u32 h) { return __builtin_bit_cast(float, h << 16); }
+__device__ inline float from_f16_bits(u32 h) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)h);
+}
+
+// Read up to 4 consecutive C values (n < nvalid) as float.
+template <int CDT>
+__device__ inline void load_c4(__amdgpu_buffer_rsrc_t r, int off, int nvalid, bool vec,
+                               float (&o)[4]) {
+    if constexpr (CDT == DT_F32) {
+        if (vec && nvalid >= 4) {
+            u32x4 w = ld128(r, off);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = __builtin_bit_cast(float, w[e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o[e] = e < nvalid ? __builtin_bit_cast(
+                                        float, __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * e, 0, 0))
+                                  : 0.f;
+        }
+    } else {
+        u32 h[4];
+        if (vec && nvalid >= 4) {
+            u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+            h[0] = w[0] & 0xFFFFu; h[1] = w[0] >> 16; h[2] = w[1] & 0xFFFFu; h[3] = w[1] >> 16;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                h[e] = e < nvalid ? (u32)__builtin_amdgcn_raw_buffer_load_b16(r, off + 2 * e, 0, 0)
+                                  : 0u;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            o[e] = (CDT == DT_BF16) ? from_bf16_bits(h[e]) : from_f16_bits(h[e]);
+    }
+}
+
+// Store up to 4 consecutive values (n < nvalid) converted to CDT.
+template <int CDT>
+__device__ inline void store_c4(__amdgpu_buffer_rsrc_t r, int off, int nvalid, bool vec,
+                                const float (&v)[4]) {
+    if constexpr (CDT == DT_F32) {
+        if (vec && nvalid >= 4) {
+            u32x4 w = {__builtin_bit_cast(u32, v[0]), __builtin_bit_cast(u32, v[1]),
+                       __builtin_bit_cast(u32, v[2]), __builtin_bit_cast(u32, v[3])};
+            __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 0);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (e < nvalid)
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(u32, v[e]), r,
+                                                          off + 4 * e, 0, 0);
+        }
+    } else {
+        u32 h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            h[e] = (CDT == DT_BF16) ? to_bf16_bits(v[e]) : to_f16_bits(v[e]);
+        if (vec && nvalid >= 4) {
+            u32x2 w = {h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+            __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, 0);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (e < nvalid)
+                    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)h[e], r, off + 2 * e, 0, 0);
+        }
+    }
+}
+
+__device__ inline void store_i4(__amdgpu_buffer_rsrc_t r, int off, int nvalid, bool vec,
+                                const int (&v)[4]) {
+    if (vec && nvalid >= 4) {
+        u32x4 w = {(u32)v[0], (u32)v[1], (u32)v[2], (u32)v[3]};
+        __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 0);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (e < nvalid) __builtin_amdgcn_raw_buffer_store_b32((u32)v[e], r, off + 4 * e, 0, 0);
+    }
+}
+
+// alpha * acc + beta * C_old for 4 values, C_old read only when beta != 0.
+template <int CDT>
+__device__ inline void finish4(__amdgpu_buffer_rsrc_t rc, int off, int nvalid, bool vec,
+                               float alpha, float beta, float (&v)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] *= alpha;
+    if (beta != 0.f) {
+        float old[4];
+        load_c4<CDT>(rc, off, nvalid, vec, old);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(beta, old[e], v[e]);
+    }
+    store_c4<CDT>(rc, off, nvalid, vec, v);
+}
+
+// ---------------------------------------------------------------------------
+// The GEMM kernel.
+// ---------------------------------------------------------------------------
+template <int CLS>
+struct Occupancy {
+    // waves per SIMD (= workgroups per CU) the tile class is sized for.
+    // LDS per workgroup: 2 stages x (BM + BN) x 128 B = 128 / 64 / 32 KiB.
+    // 2 waves per SIMD leave 256 VGPRs per lane for the staging registers
+    // of both operands.
+    static constexpr int value = CLS == TILE_256 ? 1 : 2;
+};
+
+// OUT is the output element type (DT_F32 / DT_F16 / DT_BF16 / DT_I32), or
+// OUT_PARTIAL to write raw split-K partial sums to the workspace.
+template <int DT, bool TA, bool TB, int CLS, int OUT>
+__global__ __launch_bounds__(256, Occupancy<CLS>::value) void gemm_kernel(const GemmArgs args) {
+    constexpr TileShape TS = tile_shape(CLS);
+    constexpr int BM = TS.bm, BN = TS.bn, WM = TS.wm, WN = TS.wn;
+    constexpr int THREADS = WM * WN * 64;
+    static_assert(THREADS == 256, "launch uses 256 threads");
+    constexpr int ES = dt_size(DT);
+    constexpr int BK = kLdsRowBytes / ES;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FM = WTM / 16, FN = WTN / 16;
+    constexpr int STAGE = (BM + BN) * kLdsRowBytes;
+    using Acc = typename Mma<DT>::Acc;
+
+    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+
+    int32_t tm, tn, g;
+    tile_of_workgroup(args.tiles_m, args.tiles_n, args.band, blockIdx.x, gridDim.x, &tm, &tn, &g);
+    const int z = g / args.splits, sidx = g % args.splits;
+    const int M = args.M, N = args.N, K = args.K;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int k_lo = sidx * args.k_per_split;
+    const int k_hi = min(K, k_lo + args.k_per_split);
+    const int nkt = (k_hi - k_lo + BK - 1) / BK;
+
+    const char *Ab = static_cast<const char *>(args.A) + z * args.stride_a * ES;
+    const char *Bb = static_cast<const char *>(args.B) + z * args.stride_b * ES;
+    const int lda_b = args.lda * ES, ldb_b = args.ldb * ES;
+    const bool mn_interior = (m0 + BM <= M) && (n0 + BN <= N);
+
+    using LoadA = std::conditional_t<TA, ColLoader<ES, BM, THREADS>, RowLoader<ES, BM, THREADS>>;
+    using LoadB = std::conditional_t<TB, RowLoader<ES, BN, THREADS>, ColLoader<ES, BN, THREADS>>;
+    LoadA la;
+    LoadB lb;
+
+    auto load_tile = [&](int k0) {
+        const int64_t a_org = TA ? ((int64_t)k0 * args.lda + m0) * ES
+                                 : ((int64_t)m0 * args.lda + k0) * ES;
+        const int64_t b_org = TB ? ((int64_t)n0 * args.ldb + k0) * ES
+                                 : ((int64_t)k0 * args.ldb + n0) * ES;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + a_org, args.a_extent - a_org);
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + b_org, args.b_extent - b_org);
+        if (mn_interior && k0 + BK <= K) {
+            la.template load<false>(ra, tid, lda_b, BM, BK);
+            lb.template load<false>(rb, tid, ldb_b, BN, BK);
+        } else {
+            la.template load<true>(ra, tid, lda_b, M - m0, K - k0);
+            lb.template load<true>(rb, tid, ldb_b, N - n0, K - k0);
+        }
+    };
+
+    Acc acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+
+    if (nkt > 0) {
+        load_tile(k_lo);
+        la.store(smem, tid);
+        lb.store(smem + BM * kLdsRowBytes, tid);
+        __syncthreads();
+    }
+
+    const int frag_row = lane & 15, frag_chunk = lane >> 4;
+    for (int kt = 0; kt < nkt; ++kt) {
+        char *sa = smem + (kt & 1) * STAGE;
+        char *sb = sa + BM * kLdsRowBytes;
+        if (kt + 1 < nkt) load_tile(k_lo + (kt + 1) * BK);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            u32x4 af[FM], bf[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                af[i] = *reinterpret_cast<const u32x4 *>(
+                    sa + lds_off(wm * WTM + i * 16 + frag_row, ks * 4 + frag_chunk));
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                bf[j] = *reinterpret_cast<const u32x4 *>(
+                    sb + lds_off(wn * WTN + j * 16 + frag_row, ks * 4 + frag_chunk));
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) Mma<DT>::run(acc[i][j], bf[j], af[i]);
+        }
+        if (kt + 1 < nkt) {
+            char *na = smem + ((kt + 1) & 1) * STAGE;
+            la.store(na, tid);
+            lb.store(na + BM * kLdsRowBytes, tid);
+        }
+        __syncthreads();
+    }
+
+    // ---- epilogue: lane holds C[m][n .. n+3] of each 16x16 block
+    const int ml0 = wm * WTM + (lane & 15);
+    const int nl0 = wn * WTN + 4 * (lane >> 4);
+    if constexpr (OUT == OUT_PARTIAL) {
+        // raw fp32 / int32 partial sums of this K slice: workspace plane g
+        char *wsb = static_cast<char *>(args.ws) +
+                    ((int64_t)g * M * N + (int64_t)m0 * N + n0) * 4;
+        const int64_t ws_ext = (int64_t)(M - m0) * N * 4 - (int64_t)n0 * 4;
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(wsb, ws_ext);
+        const bool vec = (N % 4) == 0;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int ml = ml0 + i * 16;
+            if (m0 + ml >= M) continue;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int nl = nl0 + j * 16;
+                const int nvalid = N - (n0 + nl);
+                if (nvalid <= 0) continue;
+                int v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = __builtin_bit_cast(int, acc[i][j][e]);
+                store_i4(rw, (ml * N + nl) * 4, nvalid, vec, v);
+            }
+        }
+    } else {
+        constexpr int CES = dt_size(OUT);
+        const int64_t c_org = ((int64_t)m0 * args.ldc + n0) * CES;
+        char *Cb = static_cast<char *>(args.C) + z * args.stride_c * CES + c_org;
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cb, args.c_extent - c_org);
+        const bool vec = args.c_vec_ok != 0;
+        const int ldc = args.ldc;
+        const float alpha = args.alpha, beta = args.beta;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int ml = ml0 + i * 16;
+            if (m0 + ml >= M) continue;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int nl = nl0 + j * 16;
+                const int nvalid = N - (n0 + nl);
+                if (nvalid <= 0) continue;
+                const int off = (ml * ldc + nl) * CES;
+                if constexpr (OUT == DT_I32) {
+                    int v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e];
+                    store_i4(rc, off, nvalid, vec, v);
+                } else {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e];
+                    finish4<OUT>(rc, off, nvalid, vec, alpha, beta, v);
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+}  // namespace tcg

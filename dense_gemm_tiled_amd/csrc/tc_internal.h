@@ -1,0 +1,134 @@
+// tc_internal.h -- definitions shared by the host planner (tcgemm.cpp) and
+// the gfx950 kernels (gemm_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tcg {
+
+// Element type codes; identical to tc_dtype_t in include/tcgemm.h.
+enum Dt : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3, DT_I32 = 4 };
+
+__host__ __device__ constexpr int dt_size(int dt) {
+    return dt == DT_F32 ? 4 : dt == DT_I32 ? 4 : dt == DT_I8 ? 1 : 2;
+}
+
+// Tile classes.  Every class keeps one LDS row of an operand tile at 128
+// bytes of K (64 bf16/f16, 128 int8, 32 f32), so the swizzle and the MFMA
+// fragment reads are the same for every element type.
+enum TileClass : int { TILE_256 = 0, TILE_128 = 1, TILE_64 = 2, NUM_TILE_CLASSES = 3 };
+
+struct TileShape {
+    int bm, bn, wm, wn;   // tile rows/cols, waves along m/n (4 waves = 256 threads)
+};
+
+__host__ __device__ constexpr TileShape tile_shape(int cls) {
+    return cls == TILE_256 ? TileShape{256, 256, 2, 2}
+         : cls == TILE_128 ? TileShape{128, 128, 2, 2}
+                           : TileShape{64, 64, 2, 2};
+}
+
+constexpr int kLdsRowBytes = 128;      // bytes of K per LDS tile row
+constexpr int kXcds = 8;               // MI355X: 8 XCDs x 32 CUs
+
+// Output selector of the GEMM kernel beyond the element types: raw partial
+// sums of one split-K slice (fp32, or int32 for int8 inputs).
+constexpr int OUT_PARTIAL = 5;
+
+// Everything a GEMM launch needs; passed by value as the kernel argument.
+struct GemmArgs {
+    const void *A;
+    const void *B;
+    void *C;
+    void *ws;                  // split-K partials [batch][splits][M][N] (4-byte elements)
+    int64_t stride_a, stride_b, stride_c;   // elements between batch problems
+    int64_t a_extent, b_extent, c_extent;   // bytes spanned by one problem's operand
+    int32_t M, N, K;
+    int32_t lda, ldb, ldc;     // elements
+    int32_t c_dtype;
+    float alpha, beta;
+    int32_t tiles_m, tiles_n;
+    int32_t splits, k_per_split;   // k_per_split is a multiple of the tile K
+    int32_t groups;                // batch * splits
+    int32_t band;                  // tile-order band height (<= 0: row-major)
+    int32_t c_vec_ok;              // C rows allow 4-element vector access
+};
+
+// Arguments of the split-K reduction and of the alpha == 0 scaling kernel.
+struct EpilogueArgs {
+    const void *ws;
+    void *C;
+    int64_t stride_c;
+    int64_t c_extent;
+    int32_t M, N, ldc;
+    int32_t batch, splits;
+    int32_t c_dtype;
+    int32_t acc_is_int;
+    int32_t c_vec_ok;          // C rows allow 4-element vector access
+    float alpha, beta;
+};
+
+// Workgroup -> (tile_m, tile_n, group).
+//
+// Step 1, XCD regrouping: the hardware hands consecutive workgroup ids to the
+// 8 XCDs in turn, so XCD x runs ids x, x+8, x+16, ...  Those are renumbered to
+// one contiguous range of logical ids per XCD (a bijection also when n_wg is
+// not a multiple of 8), so that the tiles one XCD runs together share operand
+// panels in that XCD's L2.
+//
+// Step 2, group: logical ids are group-major (group = batch element x split
+// slice), so one XCD's range stays inside one problem where it can.
+//
+// Step 3, band order inside a group (tessl "Architecture", "Column-Panel Grid
+// Swizzling"): the tile grid is cut into bands of `band` tile rows; inside a
+// band consecutive ids walk down a column of the band before moving right, so
+// a run of ids touches few B column panels and few A row panels.
+__host__ __device__ inline void tile_of_workgroup(int32_t tiles_m, int32_t tiles_n,
+                                                  int32_t band, int64_t wg, int64_t n_wg,
+                                                  int32_t *tm, int32_t *tn, int32_t *g) {
+    int64_t q = n_wg / kXcds, r = n_wg % kXcds;
+    int64_t xcd = wg % kXcds, j = wg / kXcds;
+    int64_t logical = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + j;
+    int64_t tiles = (int64_t)tiles_m * tiles_n;
+    int64_t t = logical % tiles;
+    *g = (int32_t)(logical / tiles);
+    if (band <= 0) {
+        *tm = (int32_t)(t / tiles_n);
+        *tn = (int32_t)(t % tiles_n);
+        return;
+    }
+    int64_t per_band = (int64_t)band * tiles_n;
+    int64_t b = t / per_band;
+    int64_t rem = t - b * per_band;
+    int64_t h = tiles_m - b * band;
+    if (h > band) h = band;
+    *tm = (int32_t)(b * band + rem % h);
+    *tn = (int32_t)(rem / h);
+}
+
+}  // namespace tcg
+
+// Launchers (epilogue_kernels.hip and gemm_inst.hip).  They return
+// hipSuccess or the launch error; hipErrorInvalidValue for a combination
+// that has no instantiation.  `cls` is a TileClass, `dt` the input Dt, `out`
+// the output Dt or OUT_PARTIAL.
+hipError_t tcg_launch_gemm(int dt, bool ta, bool tb, int cls, int out, const tcg::GemmArgs &args,
+                           int64_t grid, hipStream_t stream);
+hipError_t tcg_launch_splitk_reduce(const tcg::EpilogueArgs &args, hipStream_t stream);
+hipError_t tcg_launch_scale_c(const tcg::EpilogueArgs &args, hipStream_t stream);
+const char *tcg_kernel_name(int dt, bool ta, bool tb, int cls);
+
+// One launcher per (input type, layout) object; each dispatches on (cls, out).
+#define TCG_DECLARE_LAUNCHER(NAME)                                                       \
+    hipError_t NAME(int cls, int out, const tcg::GemmArgs &args, int64_t grid,           \
+                    hipStream_t stream);
+TCG_DECLARE_LAUNCHER(tcg_launch_f32_nn) TCG_DECLARE_LAUNCHER(tcg_launch_f32_nt)
+TCG_DECLARE_LAUNCHER(tcg_launch_f32_tn) TCG_DECLARE_LAUNCHER(tcg_launch_f32_tt)
+TCG_DECLARE_LAUNCHER(tcg_launch_f16_nn) TCG_DECLARE_LAUNCHER(tcg_launch_f16_nt)
+TCG_DECLARE_LAUNCHER(tcg_launch_f16_tn) TCG_DECLARE_LAUNCHER(tcg_launch_f16_tt)
+TCG_DECLARE_LAUNCHER(tcg_launch_bf16_nn) TCG_DECLARE_LAUNCHER(tcg_launch_bf16_nt)
+TCG_DECLARE_LAUNCHER(tcg_launch_bf16_tn) TCG_DECLARE_LAUNCHER(tcg_launch_bf16_tt)
+TCG_DECLARE_LAUNCHER(tcg_launch_i8_nn) TCG_DECLARE_LAUNCHER(tcg_launch_i8_nt)
+TCG_DECLARE_LAUNCHER(tcg_launch_i8_tn) TCG_DECLARE_LAUNCHER(tcg_launch_i8_tt)
+#undef TCG_DECLARE_LAUNCHER

@@ -1,0 +1,589 @@
+// tcgemm.cpp -- host side of libtcgemm.so: the C ABI declared in
+// include/tcgemm.h.
+//
+// Call path (tessl "Architecture", "GEMM Pipeline & Kernel Selection"):
+// normalize leading dims -> validate everything with checked 64-bit
+// arithmetic -> plan (kernel by dtype x layout, tile class by shape, split-K
+// when the output has too few tiles to fill the GPU) -> enqueue.  Validation
+// returns before anything is enqueued, so a refused call leaves the dispatch
+// count unchanged (same page, "The Kernel Library and the nn Boundary").
+
+#include "tcgemm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "tc_internal.h"
+
+using namespace tcg;
+
+struct tc_stream {
+    tc_context *ctx = nullptr;
+    hipStream_t stream = nullptr;
+    bool owned = false;
+    void *ws = nullptr;          // split-K workspace (device memory)
+    int64_t ws_bytes = 0;
+};
+
+struct tc_context {
+    int device = -1;             // bound at the first launch
+    tc_stream *internal = nullptr;
+    uint64_t dispatches = 0;
+    std::string last_kernel;
+    std::string last_error;
+};
+
+namespace {
+
+constexpr int64_t kMaxIndex = 0x7FFFFFFF;          // every element index fits int32
+constexpr int64_t kMaxTileSpanBytes = 0x7FFFFFFF;  // byte offsets inside one tile fit int32
+constexpr int32_t kMaxInt8K = 131071;              // 16384 * 131072 = 2^31 would wrap
+constexpr int kMaxTileRows = 256;
+
+std::string g_plan_error;   // error text of tc_gemm_plan(NULL, ...)
+
+// Everything validation derives from a descriptor.
+struct Problem {
+    int32_t M, N, K, batch;
+    int dt, cdt;
+    bool ta, tb;
+    float alpha, beta;
+    int64_t lda, ldb, ldc;
+    int64_t stride_a, stride_b, stride_c;
+    int64_t a_ext, b_ext, c_ext;          // elements spanned by one problem
+    int64_t a_total, b_total, c_total;    // bytes spanned by all problems
+};
+
+struct Plan {
+    int cls;
+    int bm, bn, bk;
+    int32_t tiles_m, tiles_n;
+    int32_t splits, k_per_split;
+    int64_t grid;
+    int64_t ws_bytes;
+    int32_t band;
+};
+
+tc_status_t fail(std::string *err, tc_status_t st, const char *fmt, ...) {
+    if (err) {
+        char buf[512];
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(buf, sizeof buf, fmt, ap);
+        va_end(ap);
+        *err = buf;
+    }
+    return st;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_mul_overflow(a, b, out); }
+bool add_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_add_overflow(a, b, out); }
+
+// Elements spanned by a rows x cols matrix with leading dim ld; -1 on overflow.
+int64_t span(int64_t rows, int64_t cols, int64_t ld) {
+    int64_t t, r;
+    if (!mul_ok(rows - 1, ld, &t) || !add_ok(t, cols, &r)) return -1;
+    return r;
+}
+
+// Bytes spanned by `batch` problems of `ext` elements at `stride`; -1 on overflow.
+int64_t total_bytes(int64_t batch, int64_t stride, int64_t ext, int es) {
+    int64_t t, r, b;
+    if (!mul_ok(batch - 1, stride, &t) || !add_ok(t, ext, &r) || !mul_ok(r, es, &b)) return -1;
+    return b;
+}
+
+const char *dt_name(int dt) {
+    switch (dt) {
+    case TC_F32: return "f32";
+    case TC_F16: return "f16";
+    case TC_BF16: return "bf16";
+    case TC_I8: return "i8";
+    case TC_I32: return "i32";
+    default: return "?";
+    }
+}
+
+tc_status_t validate(const tc_gemm_batched_desc *bd, Problem *p, std::string *err) {
+    if (!bd) return fail(err, TC_ERR_INVALID_ARGUMENT, "descriptor is NULL");
+    const tc_gemm_desc &d = bd->base;
+    if (d.M < 1 || d.N < 1 || d.K < 1)
+        return fail(err, TC_ERR_INVALID_ARGUMENT, "dims must be >= 1 (M=%d N=%d K=%d)", d.M, d.N, d.K);
+    if (bd->batch < 1) return fail(err, TC_ERR_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", bd->batch);
+
+    // supported (a, b, c, accum) tuples
+    const int a = d.a_dtype, b = d.b_dtype, c = d.c_dtype, acc = d.accum_dtype;
+    bool ok = false;
+    if (a != b) {
+        ok = false;
+    } else if (a == TC_F32) {
+        ok = c == TC_F32 && acc == TC_F32;
+    } else if (a == TC_F16 || a == TC_BF16) {
+        ok = (c == a || c == TC_F32) && acc == TC_F32;
+    } else if (a == TC_I8) {
+        ok = c == TC_I32 && acc == TC_I32;
+    }
+    if (!ok)
+        return fail(err, TC_ERR_UNSUPPORTED, "unsupported dtypes a=%s b=%s c=%s accum=%s", dt_name(a),
+                    dt_name(b), dt_name(c), dt_name(acc));
+
+    p->M = d.M; p->N = d.N; p->K = d.K; p->batch = bd->batch;
+    p->dt = a; p->cdt = c;
+    p->ta = d.transpose_a; p->tb = d.transpose_b;
+    p->alpha = d.alpha; p->beta = d.beta;
+
+    // leading dims: 0 means contiguous (tensorcore "GEMM", "Surface")
+    const int64_t a_rows = p->ta ? d.K : d.M, a_cols = p->ta ? d.M : d.K;
+    const int64_t b_rows = p->tb ? d.N : d.K, b_cols = p->tb ? d.K : d.N;
+    p->lda = d.lda == 0 ? a_cols : d.lda;
+    p->ldb = d.ldb == 0 ? b_cols : d.ldb;
+    p->ldc = d.ldc == 0 ? d.N : d.ldc;
+    if (p->lda < a_cols)
+        return fail(err, TC_ERR_INVALID_ARGUMENT, "lda=%lld < %lld", (long long)p->lda, (long long)a_cols);
+    if (p->ldb < b_cols)
+        return fail(err, TC_ERR_INVALID_ARGUMENT, "ldb=%lld < %lld", (long long)p->ldb, (long long)b_cols);
+    if (p->ldc < d.N)
+        return fail(err, TC_ERR_INVALID_ARGUMENT, "ldc=%lld < N=%d", (long long)p->ldc, d.N);
+
+    if (!std::isfinite(d.alpha) || !std::isfinite(d.beta))
+        return fail(err, TC_ERR_INVALID_ARGUMENT, "alpha and beta must be finite");
+
+    if (a == TC_I8) {
+        if (d.alpha != 1.0f || d.beta != 0.0f)
+            return fail(err, TC_ERR_UNSUPPORTED, "int8 GEMM needs alpha = 1 and beta = 0");
+        if (d.K > kMaxInt8K)
+            return fail(err, TC_ERR_OVERFLOW, "int8 K=%d > %d: an int32 sum could wrap", d.K, kMaxInt8K);
+    }
+
+    const int es = dt_size(a), ces = dt_size(c);
+    p->a_ext = span(a_rows, a_cols, p->lda);
+    p->b_ext = span(b_rows, b_cols, p->ldb);
+    p->c_ext = span(d.M, d.N, p->ldc);
+    if (p->a_ext < 0 || p->a_ext > kMaxIndex) return fail(err, TC_ERR_OVERFLOW, "A spans more than 2^31-1 elements");
+    if (p->b_ext < 0 || p->b_ext > kMaxIndex) return fail(err, TC_ERR_OVERFLOW, "B spans more than 2^31-1 elements");
+    if (p->c_ext < 0 || p->c_ext > kMaxIndex) return fail(err, TC_ERR_OVERFLOW, "C spans more than 2^31-1 elements");
+    // byte offsets inside one tile are 32-bit
+    if ((int64_t)kMaxTileRows * p->lda * es + 256 > kMaxTileSpanBytes ||
+        (int64_t)kMaxTileRows * p->ldb * es + 256 > kMaxTileSpanBytes ||
+        (int64_t)kMaxTileRows * p->ldc * ces + 256 > kMaxTileSpanBytes)
+        return fail(err, TC_ERR_OVERFLOW, "a leading dimension exceeds 8 MiB per row");
+
+    p->stride_a = bd->batch > 1 ? bd->stride_a : 0;
+    p->stride_b = bd->batch > 1 ? bd->stride_b : 0;
+    p->stride_c = bd->batch > 1 ? bd->stride_c : 0;
+    if (p->stride_a < 0 || p->stride_b < 0 || p->stride_c < 0)
+        return fail(err, TC_ERR_INVALID_ARGUMENT, "batch strides must be >= 0");
+    if (bd->batch > 1 && p->stride_c < p->c_ext)
+        return fail(err, TC_ERR_ALIASING, "stride_c=%lld < C extent %lld: batch outputs overlap",
+                    (long long)p->stride_c, (long long)p->c_ext);
+    p->a_total = total_bytes(bd->batch, p->stride_a, p->a_ext, es);
+    p->b_total = total_bytes(bd->batch, p->stride_b, p->b_ext, es);
+    p->c_total = total_bytes(bd->batch, p->stride_c, p->c_ext, ces);
+    if (p->a_total < 0 || p->b_total < 0 || p->c_total < 0)
+        return fail(err, TC_ERR_OVERFLOW, "batched extent overflows 64 bits");
+    return TC_OK;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Tile class and split-K choice.  MI355X has 256 CUs; a launch wants at least
+// about one workgroup per CU.  The big tile is used when it alone fills the
+// chip; otherwise the smaller classes, then split-K for tall-K outputs with
+// few tiles (the case tessl "Architecture" routes to split-K: K >= 2048 with
+// small M and N).
+//
+// Tuning overrides (environment, read at every call; unset in normal use):
+// TCGEMM_TILE=256|128|64 forces a tile class, TCGEMM_SPLITS=S forces split-K
+// with S slices (on the 64x64 class, the one with a partial-sum output),
+// TCGEMM_BAND=h sets the band height of the tile order (0: row-major).
+void make_plan(const Problem &p, Plan *pl) {
+    const int es = dt_size(p.dt);
+    const int bk = kLdsRowBytes / es;
+    int cls = TILE_64;
+    for (int c = TILE_256; c <= TILE_64; ++c) {
+        const TileShape ts = tile_shape(c);
+        const int64_t tiles = ceil_div(p.M, ts.bm) * ceil_div(p.N, ts.bn) * p.batch;
+        if (tiles >= 192 || c == TILE_64) { cls = c; break; }
+    }
+    int64_t forced_splits = 0;
+    if (const char *env = getenv("TCGEMM_TILE")) {
+        const int v = atoi(env);
+        cls = v == 256 ? TILE_256 : v == 128 ? TILE_128 : v == 64 ? TILE_64 : cls;
+    }
+    if (const char *env = getenv("TCGEMM_SPLITS")) {
+        forced_splits = atoi(env);
+        if (forced_splits > 1) cls = TILE_64;
+    }
+    const TileShape ts = tile_shape(cls);
+    pl->cls = cls;
+    pl->bm = ts.bm; pl->bn = ts.bn; pl->bk = bk;
+    pl->tiles_m = (int32_t)ceil_div(p.M, ts.bm);
+    pl->tiles_n = (int32_t)ceil_div(p.N, ts.bn);
+    const int64_t tiles = (int64_t)pl->tiles_m * pl->tiles_n * p.batch;
+    const int64_t ktiles = ceil_div(p.K, bk);
+
+    int64_t splits = 1;
+    if (cls == TILE_64 && tiles < 128 && ktiles >= 16 && p.alpha != 0.0f) {
+        splits = ceil_div(256, tiles);
+        if (splits > ktiles / 8) splits = ktiles / 8;      // keep >= 8 K-tiles per slice
+        if (splits > 16) splits = 16;
+        if (splits < 1) splits = 1;
+    }
+    if (forced_splits > 0 && p.alpha != 0.0f) splits = forced_splits > ktiles ? ktiles : forced_splits;
+    int64_t kps = ceil_div(ceil_div(p.K, splits), bk) * bk;
+    splits = ceil_div(p.K, kps);                            // every slice non-empty
+    int64_t ws = 0;
+    if (splits > 1) {
+        ws = splits * p.batch * (int64_t)p.M * p.N * 4;
+        if ((int64_t)splits * p.M * p.N * 4 > 0x7FFFFFFF) {  // reduce-kernel offsets are 32-bit
+            splits = 1;
+            kps = ceil_div(p.K, bk) * bk;
+            ws = 0;
+        }
+    }
+    pl->splits = (int32_t)splits;
+    pl->k_per_split = (int32_t)kps;
+    pl->grid = tiles * splits;
+    pl->ws_bytes = ws;
+    pl->band = 8;
+    if (const char *env = getenv("TCGEMM_BAND")) pl->band = atoi(env);   // tuning knob
+}
+
+void fill_info(const Problem &p, const Plan &pl, tc_plan_info *info) {
+    if (!info) return;
+    memset(info, 0, sizeof *info);
+    snprintf(info->kernel, sizeof info->kernel, "%s%s", tcg_kernel_name(p.dt, p.ta, p.tb, pl.cls),
+             pl.splits > 1 ? "+splitk_reduce" : "");
+    if (p.alpha == 0.0f) snprintf(info->kernel, sizeof info->kernel, "scale_c");
+    info->tile_m = pl.bm; info->tile_n = pl.bn; info->tile_k = pl.bk;
+    info->threads = 256;
+    info->tiles_m = pl.tiles_m; info->tiles_n = pl.tiles_n;
+    info->splits = pl.splits; info->k_per_split = pl.k_per_split;
+    info->grid = p.alpha == 0.0f ? 0 : pl.grid;
+    info->workspace_bytes = p.alpha == 0.0f ? 0 : pl.ws_bytes;
+    info->launches = p.alpha == 0.0f ? 1 : (pl.splits > 1 ? 2 : 1);
+    info->band = pl.band;
+}
+
+bool ranges_overlap(const void *a, int64_t an, const void *b, int64_t bn) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)bn && b0 < a0 + (uintptr_t)an;
+}
+
+tc_status_t check_allocation(const char *name, const void *ptr, int64_t bytes, std::string *err) {
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    hipError_t e = hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)ptr);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(err, TC_ERR_INVALID_ARGUMENT, "%s=%p is not device memory (%s)", name, ptr,
+                    hipGetErrorString(e));
+    }
+    const uintptr_t b0 = (uintptr_t)base, p0 = (uintptr_t)ptr;
+    if (p0 < b0 || p0 + (uintptr_t)bytes > b0 + size)
+        return fail(err, TC_ERR_INVALID_ARGUMENT,
+                    "%s needs %lld bytes from %p but its allocation ends %lld bytes after it", name,
+                    (long long)bytes, ptr, (long long)(b0 + size - p0));
+    return TC_OK;
+}
+
+tc_status_t bind_device(tc_context *ctx) {
+    if (ctx->device >= 0) return hipSetDevice(ctx->device) == hipSuccess ? TC_OK : TC_ERR_DEVICE;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        ctx->last_error = std::string("no HIP device: ") + hipGetErrorString(e);
+        return TC_ERR_DEVICE;
+    }
+    ctx->device = dev;
+    return TC_OK;
+}
+
+tc_status_t ensure_workspace(tc_stream *s, int64_t bytes, std::string *err) {
+    if (bytes <= s->ws_bytes) return TC_OK;
+    if (s->ws) {
+        // the old buffer may still be in use by work queued on this stream
+        if (hipStreamSynchronize(s->stream) != hipSuccess)
+            return fail(err, TC_ERR_DEVICE, "hipStreamSynchronize failed while growing the workspace");
+        (void)hipFree(s->ws);
+        s->ws = nullptr;
+        s->ws_bytes = 0;
+    }
+    const int64_t want = ((bytes + (1 << 20) - 1) >> 20) << 20;
+    hipError_t e = hipMalloc(&s->ws, (size_t)want);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        s->ws = nullptr;
+        return fail(err, TC_ERR_OUT_OF_MEMORY, "split-K workspace of %lld bytes: %s", (long long)want,
+                    hipGetErrorString(e));
+    }
+    s->ws_bytes = want;
+    return TC_OK;
+}
+
+tc_status_t create_stream(tc_context *ctx, tc_stream **out, hipStream_t existing) {
+    tc_stream *s = new (std::nothrow) tc_stream();
+    if (!s) return TC_ERR_OUT_OF_MEMORY;
+    s->ctx = ctx;
+    if (existing) {
+        s->stream = existing;
+        s->owned = false;
+    } else {
+        hipError_t e = hipStreamCreate(&s->stream);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            ctx->last_error = std::string("hipStreamCreate: ") + hipGetErrorString(e);
+            delete s;
+            return TC_ERR_DEVICE;
+        }
+        s->owned = true;
+    }
+    *out = s;
+    return TC_OK;
+}
+
+// Validate, plan and enqueue one (batched) GEMM on stream s.
+tc_status_t run(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A, const void *B,
+                void *C, tc_stream *s, bool sync) {
+    if (!ctx) return TC_ERR_INVALID_ARGUMENT;
+    ctx->last_error.clear();
+    std::string *err = &ctx->last_error;
+    if (!A || !B || !C) return fail(err, TC_ERR_INVALID_ARGUMENT, "A, B and C must be non-NULL");
+    Problem p;
+    tc_status_t st = validate(bd, &p, err);
+    if (st != TC_OK) return st;
+    if (ranges_overlap(C, p.c_total, A, p.a_total) || ranges_overlap(C, p.c_total, B, p.b_total))
+        return fail(err, TC_ERR_ALIASING, "C overlaps A or B");
+    Plan pl;
+    make_plan(p, &pl);
+
+    st = bind_device(ctx);
+    if (st != TC_OK) return st;
+    if ((st = check_allocation("A", A, p.a_total, err)) != TC_OK) return st;
+    if ((st = check_allocation("B", B, p.b_total, err)) != TC_OK) return st;
+    if ((st = check_allocation("C", C, p.c_total, err)) != TC_OK) return st;
+
+    if (!s) {
+        if (!ctx->internal && (st = create_stream(ctx, &ctx->internal, nullptr)) != TC_OK) return st;
+        s = ctx->internal;
+    }
+    const bool use_splitk = p.alpha != 0.0f && pl.splits > 1;
+    if (use_splitk && (st = ensure_workspace(s, pl.ws_bytes, err)) != TC_OK) return st;
+
+    const int ces = dt_size(p.cdt);
+    const bool c_vec_ok = (p.ldc % 4 == 0) && (p.stride_c % 4 == 0) && ((uintptr_t)C % 16 == 0);
+    EpilogueArgs ea;
+    memset(&ea, 0, sizeof ea);
+    ea.C = C;
+    ea.stride_c = p.stride_c;
+    ea.c_extent = p.c_ext * ces;
+    ea.M = p.M; ea.N = p.N; ea.ldc = (int32_t)p.ldc;
+    ea.batch = p.batch;
+    ea.c_dtype = p.cdt;
+    ea.acc_is_int = p.dt == TC_I8;
+    ea.alpha = p.alpha; ea.beta = p.beta;
+    ea.c_vec_ok = c_vec_ok;
+
+    hipError_t e;
+    std::string name;
+    if (p.alpha == 0.0f) {
+        e = tcg_launch_scale_c(ea, s->stream);
+        name = "scale_c";
+        if (e == hipSuccess) ctx->dispatches += 1;
+    } else {
+        GemmArgs ga;
+        memset(&ga, 0, sizeof ga);
+        ga.A = A; ga.B = B; ga.C = C;
+        ga.ws = use_splitk ? s->ws : nullptr;
+        ga.stride_a = p.stride_a; ga.stride_b = p.stride_b; ga.stride_c = p.stride_c;
+        ga.a_extent = p.a_ext * dt_size(p.dt);
+        ga.b_extent = p.b_ext * dt_size(p.dt);
+        ga.c_extent = p.c_ext * ces;
+        ga.M = p.M; ga.N = p.N; ga.K = p.K;
+        ga.lda = (int32_t)p.lda; ga.ldb = (int32_t)p.ldb; ga.ldc = (int32_t)p.ldc;
+        ga.c_dtype = p.cdt;
+        ga.alpha = p.alpha; ga.beta = p.beta;
+        ga.tiles_m = pl.tiles_m; ga.tiles_n = pl.tiles_n;
+        ga.splits = pl.splits; ga.k_per_split = pl.k_per_split;
+        ga.groups = p.batch * pl.splits;
+        ga.band = pl.band;
+        ga.c_vec_ok = c_vec_ok;
+        e = tcg_launch_gemm(p.dt, p.ta, p.tb, pl.cls, use_splitk ? OUT_PARTIAL : p.cdt, ga,
+                            pl.grid, s->stream);
+        name = tcg_kernel_name(p.dt, p.ta, p.tb, pl.cls);
+        if (e == hipSuccess) {
+            ctx->dispatches += 1;
+            if (use_splitk) {
+                ea.ws = s->ws;
+                ea.splits = pl.splits;
+                e = tcg_launch_splitk_reduce(ea, s->stream);
+                name += "+splitk_reduce";
+                if (e == hipSuccess) ctx->dispatches += 1;
+            }
+        }
+    }
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(err, TC_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    }
+    ctx->last_kernel = name;
+    if (sync) {
+        e = hipStreamSynchronize(s->stream);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(err, TC_ERR_DEVICE, "hipStreamSynchronize: %s", hipGetErrorString(e));
+        }
+    }
+    return TC_OK;
+}
+
+tc_gemm_batched_desc single(const tc_gemm_desc *d) {
+    tc_gemm_batched_desc bd;
+    memset(&bd, 0, sizeof bd);
+    if (d) bd.base = *d;
+    bd.batch = 1;
+    return bd;
+}
+
+}  // namespace
+
+extern "C" {
+
+tc_status_t tc_context_create(tc_context **out) {
+    if (!out) return TC_ERR_INVALID_ARGUMENT;
+    *out = new (std::nothrow) tc_context();
+    return *out ? TC_OK : TC_ERR_OUT_OF_MEMORY;
+}
+
+void tc_context_destroy(tc_context *ctx) {
+    if (!ctx) return;
+    if (ctx->internal) tc_stream_destroy(ctx->internal);
+    delete ctx;
+}
+
+tc_status_t tc_stream_create(tc_context *ctx, tc_stream **out) {
+    if (!ctx || !out) return TC_ERR_INVALID_ARGUMENT;
+    tc_status_t st = bind_device(ctx);
+    if (st != TC_OK) return st;
+    return create_stream(ctx, out, nullptr);
+}
+
+tc_status_t tc_stream_wrap(tc_context *ctx, void *hip_stream, tc_stream **out) {
+    if (!ctx || !out) return TC_ERR_INVALID_ARGUMENT;
+    tc_status_t st = bind_device(ctx);
+    if (st != TC_OK) return st;
+    tc_stream *s = new (std::nothrow) tc_stream();
+    if (!s) return TC_ERR_OUT_OF_MEMORY;
+    s->ctx = ctx;
+    s->stream = static_cast<hipStream_t>(hip_stream);   // NULL: the default stream
+    s->owned = false;
+    *out = s;
+    return TC_OK;
+}
+
+tc_status_t tc_stream_sync(tc_stream *s) {
+    if (!s) return TC_ERR_INVALID_ARGUMENT;
+    hipError_t e = hipStreamSynchronize(s->stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        if (s->ctx) s->ctx->last_error = std::string("hipStreamSynchronize: ") + hipGetErrorString(e);
+        return TC_ERR_DEVICE;
+    }
+    return TC_OK;
+}
+
+void tc_stream_destroy(tc_stream *s) {
+    if (!s) return;
+    if (s->ws) {
+        (void)hipStreamSynchronize(s->stream);
+        (void)hipFree(s->ws);
+    }
+    if (s->owned && s->stream) (void)hipStreamDestroy(s->stream);
+    delete s;
+}
+
+tc_status_t tc_gemm(tc_context *ctx, const tc_gemm_desc *d, const void *A, const void *B, void *C) {
+    if (!d) {
+        if (ctx) ctx->last_error = "descriptor is NULL";
+        return TC_ERR_INVALID_ARGUMENT;
+    }
+    tc_gemm_batched_desc bd = single(d);
+    return run(ctx, &bd, A, B, C, nullptr, true);
+}
+
+tc_status_t tc_gemm_async(tc_context *ctx, const tc_gemm_desc *d, const void *A, const void *B,
+                          void *C, tc_stream *s) {
+    if (!d || !s) {
+        if (ctx) ctx->last_error = !d ? "descriptor is NULL" : "stream is NULL";
+        return TC_ERR_INVALID_ARGUMENT;
+    }
+    tc_gemm_batched_desc bd = single(d);
+    return run(ctx, &bd, A, B, C, s, false);
+}
+
+tc_status_t tc_gemm_batched(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A,
+                            const void *B, void *C) {
+    return run(ctx, bd, A, B, C, nullptr, true);
+}
+
+tc_status_t tc_gemm_batched_async(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A,
+                                  const void *B, void *C, tc_stream *s) {
+    if (!s) {
+        if (ctx) ctx->last_error = "stream is NULL";
+        return TC_ERR_INVALID_ARGUMENT;
+    }
+    return run(ctx, bd, A, B, C, s, false);
+}
+
+tc_status_t tc_gemm_plan(tc_context *ctx, const tc_gemm_batched_desc *bd, tc_plan_info *info) {
+    std::string *err = ctx ? &ctx->last_error : &g_plan_error;
+    err->clear();
+    Problem p;
+    tc_status_t st = validate(bd, &p, err);
+    if (st != TC_OK) return st;
+    Plan pl;
+    make_plan(p, &pl);
+    fill_info(p, pl, info);
+    return TC_OK;
+}
+
+const char *tc_last_kernel(const tc_context *ctx) { return ctx ? ctx->last_kernel.c_str() : ""; }
+
+uint64_t tc_dispatch_count(const tc_context *ctx) { return ctx ? ctx->dispatches : 0; }
+
+const char *tc_status_string(tc_status_t status) {
+    switch (status) {
+    case TC_OK: return "TC_OK";
+    case TC_ERR_INVALID_ARGUMENT: return "TC_ERR_INVALID_ARGUMENT";
+    case TC_ERR_UNSUPPORTED: return "TC_ERR_UNSUPPORTED";
+    case TC_ERR_OVERFLOW: return "TC_ERR_OVERFLOW";
+    case TC_ERR_ALIASING: return "TC_ERR_ALIASING";
+    case TC_ERR_OUT_OF_MEMORY: return "TC_ERR_OUT_OF_MEMORY";
+    case TC_ERR_DEVICE: return "TC_ERR_DEVICE";
+    default: return "TC_ERR_UNKNOWN";
+    }
+}
+
+const char *tc_last_error(const tc_context *ctx) {
+    return ctx ? ctx->last_error.c_str() : g_plan_error.c_str();
+}
+
+tc_status_t tc_tile_of_workgroup(int32_t tiles_m, int32_t tiles_n, int32_t groups, int32_t band,
+                                 int64_t wg, int32_t *tm, int32_t *tn, int32_t *g) {
+    if (tiles_m < 1 || tiles_n < 1 || groups < 1 || !tm || !tn || !g) return TC_ERR_INVALID_ARGUMENT;
+    const int64_t n_wg = (int64_t)tiles_m * tiles_n * groups;
+    if (wg < 0 || wg >= n_wg) return TC_ERR_INVALID_ARGUMENT;
+    tile_of_workgroup(tiles_m, tiles_n, band, wg, n_wg, tm, tn, g);
+    return TC_OK;
+}
+
+const char *tc_version(void) { return "tcgemm 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,183 @@
+/*
+ * tcgemm.h -- C ABI of the MI355X (gfx950) dense GEMM library libtcgemm.so.
+ *
+ * Operation (tensorcore "GEMM", section "Surface"): in BLAS row-major layout,
+ *
+ *     C[M,N] = alpha * op(A)[M,K] @ op(B)[K,N] + beta * C[M,N]
+ *
+ * where op(A) = A stored [M,K] (lda >= K) or, with transpose_a, A stored
+ * [K,M] (lda >= M); op(B) = B stored [K,N] (ldb >= N) or, with transpose_b,
+ * B stored [N,K] (ldb >= K).  A transposed operand is the same storage read
+ * with swapped strides; no transpose pass runs (tensorcore "GEMM", section
+ * "Transposes").  The NT form is a linear layer's x @ W^T (Phobos "Matrix
+ * products", matmul_t).  Leading dims of 0 mean contiguous.  All sizes and
+ * leading dims count ELEMENTS.
+ *
+ * Types (a_dtype == b_dtype; accum_dtype as listed):
+ *     f32  x f32  -> f32            accum f32
+ *     f16  x f16  -> f16 or f32     accum f32 (always; tensorcore "GEMM",
+ *     bf16 x bf16 -> bf16 or f32     section "The 64x64 tile")
+ *     i8   x i8   -> i32            accum i32, exact (tessl "Architecture",
+ *                                    section "Integer GEMM"); alpha must be 1,
+ *                                    beta 0 and K <= 131071 so no sum can wrap.
+ * The accumulator stays in registers for the whole K loop and C is written
+ * once (tessl "Architecture", section "Two Accumulation Models"); C is read
+ * only when beta != 0 (same page, section "Fused Epilogue").  Float results
+ * are rounded to c_dtype round-to-nearest-even.  alpha == 0 gives C = beta*C
+ * without reading A or B (BLAS convention).
+ *
+ * Pointers: A, B, C are device pointers owned by the caller (for example the
+ * storage of torch tensors).  The library never allocates, frees or retains
+ * them.  C must not overlap A or B; A may alias B.
+ *
+ * Errors (tessl "Architecture", section "The Kernel Library and the nn
+ * Boundary"): every argument is validated, with checked 64-bit arithmetic,
+ * before anything is enqueued.  A call that returns an error has launched
+ * nothing and tc_dispatch_count() is unchanged; tc_last_error() describes the
+ * failure.  The library refuses rather than silently falling back.
+ *
+ * Streams (tensorcore "GEMM", section "Async, batched, and streams"): the
+ * _async calls enqueue on a tc_stream and return; tc_stream_sync waits.  The
+ * synchronous calls run on the context's own stream and return after the
+ * result is in C.  A tc_context is not thread-safe; use one per host thread.
+ */
+#ifndef TCGEMM_H
+#define TCGEMM_H
+
+#include <stdbool.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TC_F32 = 0,
+    TC_F16 = 1,
+    TC_BF16 = 2,
+    TC_I8 = 3,
+    TC_I32 = 4
+} tc_dtype_t;
+
+typedef enum {
+    TC_OK = 0,
+    TC_ERR_INVALID_ARGUMENT = 1, /* null pointer, dim < 1, ld too small, non-finite scalar */
+    TC_ERR_UNSUPPORTED = 2,      /* dtype combination or int8 alpha/beta outside the contract */
+    TC_ERR_OVERFLOW = 3,         /* an extent, index or integer sum would not fit */
+    TC_ERR_ALIASING = 4,         /* C overlaps A or B, or batch outputs overlap */
+    TC_ERR_OUT_OF_MEMORY = 5,    /* split-K workspace could not be allocated */
+    TC_ERR_DEVICE = 6            /* HIP reported an error (message in tc_last_error) */
+} tc_status_t;
+
+/* The GEMM descriptor: fields as listed by tensorcore "GEMM", "Surface". */
+typedef struct {
+    int32_t M, N, K;
+    tc_dtype_t a_dtype, b_dtype, c_dtype, accum_dtype;
+    bool transpose_a, transpose_b;
+    float alpha, beta;
+    int32_t lda, ldb, ldc;        /* elements; 0 = contiguous */
+} tc_gemm_desc;
+
+/* Batched same-shape GEMM (tensorcore "GEMM", "Async, batched, and
+ * streams"): problem z uses A + z*stride_a, B + z*stride_b, C + z*stride_c
+ * (strides in elements).  stride_a or stride_b may be 0 (operand shared by
+ * every problem); the C ranges of different problems must not overlap. */
+typedef struct {
+    tc_gemm_desc base;
+    int32_t batch;
+    int64_t stride_a, stride_b, stride_c;
+} tc_gemm_batched_desc;
+
+typedef struct tc_context tc_context;
+typedef struct tc_stream tc_stream;
+
+/* What the planner chose for a descriptor (introspection, no GPU needed). */
+typedef struct {
+    char kernel[96];              /* kernel instantiation name */
+    int32_t tile_m, tile_n, tile_k;
+    int32_t threads;
+    int32_t tiles_m, tiles_n;
+    int32_t splits;               /* split-K factor S (1 = no split) */
+    int32_t k_per_split;
+    int64_t grid;                 /* workgroups of the main launch */
+    int64_t workspace_bytes;      /* split-K partials, 0 when S = 1 */
+    int32_t launches;             /* kernels one call enqueues (1 or 2) */
+    int32_t band;                 /* tile-order band height */
+} tc_plan_info;
+
+/* Context: host-side state only; creating one touches no GPU.  The HIP
+ * device current at the first launching call (or tc_stream_create/wrap) is
+ * bound to the context from then on.  The context owns an internal stream
+ * (created at the first synchronous call) for tc_gemm / tc_gemm_batched. */
+tc_status_t tc_context_create(tc_context **out);
+void tc_context_destroy(tc_context *ctx);
+
+/* Streams.  tc_stream_create owns a new hipStream_t; tc_stream_wrap borrows
+ * an existing one (for example torch's current stream) and never destroys
+ * it.  Each tc_stream owns the split-K workspace of the calls enqueued on it
+ * (grown on demand, freed by tc_stream_destroy), so two streams never share
+ * scratch memory. */
+tc_status_t tc_stream_create(tc_context *ctx, tc_stream **out);
+tc_status_t tc_stream_wrap(tc_context *ctx, void *hip_stream, tc_stream **out);
+tc_status_t tc_stream_sync(tc_stream *s);
+void tc_stream_destroy(tc_stream *s);
+
+/* One GEMM, synchronous: returns when C holds the result. */
+tc_status_t tc_gemm(tc_context *ctx, const tc_gemm_desc *d,
+                    const void *A, const void *B, void *C);
+
+/* One GEMM enqueued on stream s; returns after enqueue. */
+tc_status_t tc_gemm_async(tc_context *ctx, const tc_gemm_desc *d,
+                          const void *A, const void *B, void *C, tc_stream *s);
+
+/* batch same-shape GEMMs in one launch (split-K: two launches), synchronous. */
+tc_status_t tc_gemm_batched(tc_context *ctx, const tc_gemm_batched_desc *bd,
+                            const void *A, const void *B, void *C);
+
+/* Batched, enqueued on stream s. */
+tc_status_t tc_gemm_batched_async(tc_context *ctx, const tc_gemm_batched_desc *bd,
+                                  const void *A, const void *B, void *C,
+                                  tc_stream *s);
+
+/* Validate and plan without touching the GPU or any pointer.  Fills *info
+ * (if non-NULL) with the kernel, tile, grid and split-K choice; returns the
+ * status the descriptor alone earns.  ctx may be NULL; when non-NULL the
+ * error text goes to tc_last_error(ctx). */
+tc_status_t tc_gemm_plan(tc_context *ctx, const tc_gemm_batched_desc *bd,
+                         tc_plan_info *info);
+
+/* Name of the kernel instantiation the last successful call launched
+ * (the analog of tensorcore's tc_last_backend()). "" before any call. */
+const char *tc_last_kernel(const tc_context *ctx);
+
+/* Number of kernels this context has launched so far. */
+uint64_t tc_dispatch_count(const tc_context *ctx);
+
+/* Static text for a status code; never NULL. */
+const char *tc_status_string(tc_status_t status);
+
+/* Text of the last error on this context ("" if none); NULL ctx gives the
+ * last error of tc_gemm_plan calls made without a context. */
+const char *tc_last_error(const tc_context *ctx);
+
+/* The workgroup -> output tile order every GEMM launch uses, evaluated on the
+ * host: workgroup wg of a launch of n_wg = tiles_m*tiles_n*groups workgroups
+ * gets tile (*tm, *tn) of group *g (group = batch element x split slice).
+ * Workgroups are first regrouped so that each of the 8 XCDs of the chip runs
+ * a contiguous range of logical ids; inside a group tiles follow the
+ * column-panel band order of tessl "Architecture", "Column-Panel Grid
+ * Swizzling", with band height `band` (band <= 0 selects plain row-major).
+ * Returns TC_ERR_INVALID_ARGUMENT for wg outside [0, n_wg). */
+tc_status_t tc_tile_of_workgroup(int32_t tiles_m, int32_t tiles_n, int32_t groups,
+                                 int32_t band, int64_t wg,
+                                 int32_t *tm, int32_t *tn, int32_t *g);
+
+/* Library version string. */
+const char *tc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TCGEMM_H */

@@ -1,0 +1,284 @@
+"""GPU parity of the HIP path against the CPU oracle (needs an MI355X).
+
+Every case runs the library through its C ABI (dense_gemm_tiled_amd.gemm ->
+tc_gemm_batched_async) on seeded inputs from workloads.py and compares with
+oracle/ on the same bits: int8 -> int32 bit-exact; float results within the
+relative Frobenius error 1e-3 (fp16/bf16 inputs) or 1e-5 (fp32 inputs) of the
+oracle rounded to the output type.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import compare, env, from_dev, oracle_full, run_library, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+P = workloads.Problem
+
+# (input, output) type pairs the library supports
+PAIRS = [("f32", "f32"), ("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"),
+         ("bf16", "f32"), ("i8", "i32")]
+LAYOUTS = [(False, False), (False, True), (True, False), (True, True)]
+
+
+def lay(ta, tb):
+    return ("T" if ta else "N") + ("T" if tb else "N")
+
+
+def problem(a, c, M, N, K, ta=False, tb=False, **kw):
+    dist = "int8" if a == "i8" else kw.pop("dist", "normal")
+    float_ok = a != "i8"
+    alpha = kw.pop("alpha", 0.5 if float_ok else 1.0)
+    beta = kw.pop("beta", 1.0 if float_ok else 0.0)
+    c_dist = kw.pop("c_dist", "normal" if beta != 0.0 else "nan")
+    seed = kw.pop("seed", hash((a, c, M, N, K, ta, tb)) % 2 ** 31)
+    return P("case", M, N, K, a, c, transpose_a=ta, transpose_b=tb, alpha=alpha, beta=beta,
+             dist=dist, c_dist=c_dist, seed=seed, **kw)
+
+
+def check(p, label, **envs):
+    A, B, C = workloads.make_inputs(p)
+    say("GPU case:", label, p.M, p.N, p.K, p.a_dtype, p.c_dtype, p.layout, envs)
+    with env(**envs):
+        got = run_library(p, A, B, C)
+    ref = oracle_full(p, A, B, C)
+    return compare(p, got, ref, C_in=C, label=label)
+
+
+# ---------------------------------------------------------------- all kernels, ragged
+@pytest.mark.parametrize("tile", [256, 128, 64])
+@pytest.mark.parametrize("ta,tb", LAYOUTS, ids=[lay(*l) for l in LAYOUTS])
+@pytest.mark.parametrize("a,c", PAIRS, ids=["%s-%s" % pc for pc in PAIRS])
+def test_every_kernel_ragged(a, c, ta, tb, tile):
+    """M, N, K all ragged (K leaves a partial 16-byte chunk for every type),
+    several tiles in M and N, alpha = 0.5 and beta = 1 for floats."""
+    check(problem(a, c, 300, 270, 197, ta, tb), "ragged tile%d" % tile, TCGEMM_TILE=tile)
+
+
+@pytest.mark.parametrize("tile", [256, 128, 64])
+@pytest.mark.parametrize("a,c", PAIRS, ids=["%s-%s" % pc for pc in PAIRS])
+def test_aligned_vector_epilogue_beta0_nan_c(a, c, tile):
+    """N and ldc multiples of 4 (vector stores), beta = 0 with a NaN-filled C:
+    C must not be read."""
+    p = problem(a, c, 264, 520, 256, alpha=1.0, beta=0.0, c_dist="nan")
+    check(p, "vec tile%d" % tile, TCGEMM_TILE=tile)
+
+
+@pytest.mark.parametrize("splits", [2, 5])
+@pytest.mark.parametrize("a,c,ta,tb", [("bf16", "f32", True, False), ("bf16", "bf16", False, False),
+                                       ("f16", "f16", False, True), ("f32", "f32", False, False),
+                                       ("i8", "i32", False, False), ("i8", "i32", True, True)])
+def test_split_k_forced(a, c, ta, tb, splits):
+    p = problem(a, c, 130, 200, 1100, ta, tb, batch=2)
+    check(p, "splitk%d" % splits, TCGEMM_SPLITS=splits)
+
+
+@pytest.mark.parametrize("a,c", [("bf16", "bf16"), ("f32", "f32"), ("i8", "i32")])
+def test_padded_leading_dims(a, c):
+    p = problem(a, c, 150, 130, 90, True, False, lda=150 + 9, ldb=130 + 3, ldc=130 + 5)
+    check(p, "padded")
+    p = problem(a, c, 150, 130, 90, False, True, lda=90 + 16, ldb=90 + 1, ldc=130 + 12)
+    check(p, "padded2")
+
+
+# ---------------------------------------------------------------- exact regime
+@pytest.mark.parametrize("a,c", [("bf16", "f32"), ("bf16", "bf16"), ("f16", "f16"), ("f32", "f32")])
+def test_exact_regime_bitwise(a, c):
+    """Integer-valued inputs in [-4, 4] keep every fp32 partial sum below 2^24,
+    so accumulation is exact in any order: the GPU must equal the oracle bit for
+    bit."""
+    p = problem(a, c, 200, 190, 1000, False, False, alpha=1.0, beta=0.0, dist="small_int",
+                scale=4.0, c_dist="zeros")
+    A, B, C = workloads.make_inputs(p)
+    say("GPU case: exact", a, c)
+    got = run_library(p, A, B, C)
+    ref = oracle_full(p, A, B, C)
+    assert np.array_equal(got.view(np.uint8), ref.view(np.uint8))
+
+
+def test_ones_closed_form():
+    """A = B = ones gives C = K exactly."""
+    import torch
+    import dense_gemm_tiled_amd as tg
+    for dt, ct in ((torch.bfloat16, torch.float32), (torch.float16, torch.float16)):
+        a = torch.ones(333, 2049, dtype=dt, device="cuda")
+        b = torch.ones(2049, 444, dtype=dt, device="cuda")
+        c = torch.empty(333, 444, dtype=ct, device="cuda")
+        say("GPU case: ones", dt, ct)
+        tg.gemm(a, b, c)
+        want = 2049.0 if ct == torch.float32 else 2048.0   # 2049 rounds to 2048 in fp16
+        assert torch.all(c.float() == want)
+
+
+def test_int8_extremes():
+    """All (-128)*(-128) gives 16384*K; 127*(-128) gives -16256*K (tessl
+    "Architecture", "Integer GEMM": operands pinned at the extremes)."""
+    import torch
+    import dense_gemm_tiled_amd as tg
+    K = 8192
+    a = torch.full((130, K), -128, dtype=torch.int8, device="cuda")
+    b = torch.full((K, 70), -128, dtype=torch.int8, device="cuda")
+    c = torch.empty(130, 70, dtype=torch.int32, device="cuda")
+    say("GPU case: int8 extremes")
+    tg.gemm(a, b, c)
+    assert torch.all(c == 16384 * K)
+    a.fill_(127)
+    tg.gemm(a, b, c)
+    assert torch.all(c == -16256 * K)
+
+
+# ---------------------------------------------------------------- edge cases
+EDGE = [(1, 1, 1), (1, 300, 5), (300, 1, 77), (5, 7, 1), (17, 33, 3), (64, 64, 64),
+        (65, 63, 129), (256, 256, 8)]
+
+
+@pytest.mark.parametrize("M,N,K", EDGE)
+@pytest.mark.parametrize("a,c,ta,tb", [("bf16", "bf16", False, False), ("f16", "f32", True, False),
+                                       ("f32", "f32", False, True), ("i8", "i32", True, True)])
+def test_edge_shapes(a, c, ta, tb, M, N, K):
+    check(problem(a, c, M, N, K, ta, tb), "edge")
+
+
+@pytest.mark.parametrize("a,c", [("bf16", "bf16"), ("f32", "f32"), ("f16", "f16")])
+def test_alpha_zero(a, c):
+    """alpha = 0 is C = beta * C without reading A or B (BLAS convention)."""
+    p = problem(a, c, 70, 90, 40, alpha=0.0, beta=2.0)
+    check(p, "alpha0")
+    p = problem(a, c, 70, 90, 40, alpha=0.0, beta=0.0, c_dist="nan")
+    check(p, "alpha0beta0")
+
+
+def test_batched_matches_per_problem_and_broadcast():
+    import torch
+    import dense_gemm_tiled_amd as tg
+    p = problem("bf16", "f32", 96, 80, 300, True, False, batch=3, alpha=1.0, beta=0.0,
+                c_dist="zeros")
+    check(p, "batched")
+    A, B, C = workloads.make_inputs(p)
+    a, b = to_dev(A, "bf16"), to_dev(B, "bf16")
+    c = torch.zeros(3, 96, 80, dtype=torch.float32, device="cuda")
+    say("GPU case: batched vs singles")
+    tg.gemm(a, b, c, transpose_a=True)
+    for z in range(3):
+        cz = torch.zeros(96, 80, dtype=torch.float32, device="cuda")
+        tg.gemm(a[z], b[z], cz, transpose_a=True)
+        assert torch.equal(cz, c[z])
+    # a 2-D operand is shared by every problem (stride 0)
+    c2 = torch.zeros(3, 96, 80, dtype=torch.float32, device="cuda")
+    tg.gemm(a[1], b, c2, transpose_a=True)
+    for z in range(3):
+        cz = torch.zeros(96, 80, dtype=torch.float32, device="cuda")
+        tg.gemm(a[1], b[z], cz, transpose_a=True)
+        assert torch.equal(cz, c2[z])
+
+
+def test_deterministic_runs():
+    import torch
+    import dense_gemm_tiled_amd as tg
+    for splits in (None, 4):
+        p = problem("bf16", "f32", 128, 384, 4096, True, False, batch=2, alpha=1.0, beta=0.0,
+                    c_dist="zeros", dist="uniform")
+        A, B, C = workloads.make_inputs(p)
+        say("GPU case: determinism", splits)
+        with env(TCGEMM_SPLITS=splits):
+            r1 = run_library(p, A, B, C)
+            r2 = run_library(p, A, B, C)
+        assert np.array_equal(r1, r2)
+
+
+def test_sync_entry_point_matches_async():
+    import torch
+    import dense_gemm_tiled_amd as tg
+    p = problem("f16", "f16", 200, 300, 150, False, True)
+    A, B, C = workloads.make_inputs(p)
+    a, b = to_dev(A, "f16"), to_dev(B, "f16")
+    c1, c2 = to_dev(C, "f16"), to_dev(C, "f16")
+    say("GPU case: sync vs async")
+    tg.gemm(a, b, c1, alpha=p.alpha, beta=p.beta, transpose_b=True)
+    tg.gemm_sync(a, b, c2, alpha=p.alpha, beta=p.beta, transpose_b=True)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
+    assert tg.last_kernel().startswith("gemm_f16_nt_")
+
+
+# ---------------------------------------------------------------- refusals on a GPU
+def test_refusals_launch_nothing():
+    import ctypes
+    import torch
+    import dense_gemm_tiled_amd as tg
+    a = torch.zeros(64, 64, dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros(64, 64, dtype=torch.bfloat16, device="cuda")
+    c = torch.zeros(64, 64, dtype=torch.bfloat16, device="cuda")
+    tg.gemm(a, b, c)
+    torch.cuda.synchronize()
+    n0 = tg.dispatch_count()
+    with pytest.raises(tg.TcGemmError) as e:            # shape mismatch, caught in the binding
+        tg.gemm(a, b[:, :32], c)
+    with pytest.raises(tg.TcGemmError) as e:            # C overlaps A
+        tg.gemm(a, b, a)
+    assert e.value.status == 4
+    big = torch.zeros(4096, dtype=torch.bfloat16, device="cuda")
+    d = tg.make_desc(a, b, c)
+    d.base.M = 1 << 20                                   # A would reach far past its allocation
+    d.base.ldc = 64
+    lib = tg.load_library()
+    ctx, s = tg._torch_stream(0)
+    cbig = torch.zeros((1 << 20) * 64 + 64, dtype=torch.bfloat16, device="cuda")
+    st = lib.tc_gemm_batched_async(ctx, ctypes.byref(d), ctypes.c_void_p(big.data_ptr()),
+                                   ctypes.c_void_p(b.data_ptr()), ctypes.c_void_p(cbig.data_ptr()), s)
+    assert st == 1 and b"allocation" in lib.tc_last_error(ctx)
+    with pytest.raises(tg.TcGemmError):                 # int8 K past the wrap bound
+        ai = torch.zeros(2, 131072, dtype=torch.int8, device="cuda")
+        bi = torch.zeros(131072, 2, dtype=torch.int8, device="cuda")
+        tg.gemm(ai, bi, torch.zeros(2, 2, dtype=torch.int32, device="cuda"))
+    assert tg.dispatch_count() == n0
+
+
+# ---------------------------------------------------------------- the five workloads, full size
+def full_case(name, **over):
+    p = workloads.get(name)
+    if over:
+        p = p.with_(**over)
+    A, B, C = workloads.make_inputs(p)
+    say("GPU case: workload", name, over)
+    got = run_library(p, A, B, C)
+    return p, A, B, C, got
+
+
+def test_workload_sgemm_nn_256():
+    p, A, B, C, got = full_case("sgemm_nn_256")
+    compare(p, got, oracle_full(p, A, B, C), label=p.name)
+
+
+def test_workload_bf16_nn_4096():
+    p, A, B, C, got = full_case("bf16_nn_4096")
+    compare(p, got, oracle_full(p, A, B, C), label=p.name)
+
+
+@pytest.mark.parametrize("name", ["f16_tn_4096", "f16_nt_4096"])
+def test_workload_f16_backward_pair(name):
+    """Both layouts with alpha = 0.5, beta = 1; the product term is small
+    against beta*C, so a beta = 0 companion run on the same A and B pins it."""
+    for beta in (1.0, 0.0):
+        over = {} if beta == 1.0 else dict(beta=0.0, c_dist="zeros")
+        p, A, B, C, got = full_case(name, **over)
+        if p.transpose_b:   # oracle on the materialized B^T: the NN form of the same sums
+            q = p.with_(transpose_b=False)
+            ref = oracle_full(q, A, np.ascontiguousarray(B.T), C)
+        else:
+            ref = oracle_full(p, A, B, C)
+        compare(p, got, ref, label="%s beta=%g" % (name, beta))
+
+
+def test_workload_bf16_tn_splitk_b8():
+    import dense_gemm_tiled_amd as tg
+    p, A, B, C, got = full_case("bf16_tn_splitk_b8")
+    assert tg.last_kernel().endswith("+splitk_reduce")
+    compare(p, got, oracle_full(p, A, B, C), label=p.name)
+
+
+def test_workload_i8_nn_ragged_bit_exact():
+    p, A, B, C, got = full_case("i8_nn_ragged")
+    compare(p, got, oracle_full(p, A, B, C), label=p.name)

@@ -1,0 +1,251 @@
+"""Host-side tests of libtcgemm.so that need no GPU.
+
+* the library loads and exports every function include/tcgemm.h declares;
+* every invalid descriptor is refused with the documented status before any
+  launch (the dispatch count stays 0), as tessl "Architecture" requires of its
+  boundary ("The Kernel Library and the nn Boundary");
+* the planner's choices for the measured shapes;
+* the workgroup -> tile order is a bijection and keeps each XCD's tiles in a
+  compact block (tessl "Architecture", "Column-Panel Grid Swizzling").
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import dense_gemm_tiled_amd as tg
+import workloads
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "tcgemm.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tg.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tc_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree(lib):
+    names = declared_functions()
+    assert len(names) >= 17
+    assert set(names) == set(tg._SIGNATURES), set(names) ^ set(tg._SIGNATURES)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.tc_version().startswith(b"tcgemm")
+    for code, name in tg._STATUS.items():
+        assert lib.tc_status_string(code).decode() == name
+    assert lib.tc_status_string(99) == b"TC_ERR_UNKNOWN"
+
+
+def desc(M=64, N=64, K=64, a=tg.BF16, c=tg.BF16, acc=tg.F32, ta=False, tb=False, alpha=1.0,
+         beta=0.0, lda=0, ldb=0, ldc=0, batch=1, sa=0, sb=0, sc=0):
+    d = tg.BatchedDescT()
+    b = d.base
+    b.M, b.N, b.K = M, N, K
+    b.a_dtype, b.b_dtype, b.c_dtype, b.accum_dtype = a, a, c, acc
+    b.transpose_a, b.transpose_b = ta, tb
+    b.alpha, b.beta = alpha, beta
+    b.lda, b.ldb, b.ldc = lda, ldb, ldc
+    d.batch, d.stride_a, d.stride_b, d.stride_c = batch, sa, sb, sc
+    return d
+
+
+@pytest.fixture()
+def ctx(lib):
+    out = ctypes.c_void_p()
+    assert lib.tc_context_create(ctypes.byref(out)) == 0
+    yield out.value
+    lib.tc_context_destroy(out.value)
+
+
+# fake, distinct, non-overlapping "device" addresses: validation must refuse
+# before it ever looks at them
+A_PTR, B_PTR, C_PTR = 0x10000000000, 0x20000000000, 0x30000000000
+
+BAD = [
+    ("M=0", dict(M=0), 1),
+    ("N<0", dict(N=-3), 1),
+    ("K=0", dict(K=0), 1),
+    ("batch=0", dict(batch=0), 1),
+    ("lda<K", dict(lda=63), 1),
+    ("lda<M (TN)", dict(ta=True, M=100, lda=99), 1),
+    ("ldb<N", dict(ldb=10), 1),
+    ("ldb<K (NT)", dict(tb=True, K=70, ldb=69), 1),
+    ("ldc<N", dict(ldc=63), 1),
+    ("alpha=nan", dict(alpha=float("nan")), 1),
+    ("beta=inf", dict(beta=float("inf")), 1),
+    ("a/c dtype", dict(a=tg.BF16, c=tg.F16), 2),
+    ("f32->bf16", dict(a=tg.F32, c=tg.BF16), 2),
+    ("accum f16", dict(a=tg.F16, c=tg.F16, acc=tg.F16), 2),
+    ("i8->f32", dict(a=tg.I8, c=tg.F32, acc=tg.I32), 2),
+    ("i8 alpha", dict(a=tg.I8, c=tg.I32, acc=tg.I32, alpha=2.0), 2),
+    ("i8 beta", dict(a=tg.I8, c=tg.I32, acc=tg.I32, beta=1.0), 2),
+    ("i8 K wrap", dict(a=tg.I8, c=tg.I32, acc=tg.I32, K=131072), 3),
+    ("A extent", dict(M=70000, K=40000), 3),
+    ("C extent", dict(M=50000, N=50000, K=8), 3),
+    ("ld 8MiB", dict(lda=5_000_000, M=4), 3),
+    ("stride<0", dict(batch=2, sa=-1, sc=4096), 1),
+    ("batch C overlap", dict(batch=2, sc=64 * 63), 4),
+    ("batch C stride 0", dict(batch=2, sa=4096, sb=4096, sc=0), 4),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", BAD, ids=[b[0] for b in BAD])
+def test_invalid_descriptor_refused_before_launch(lib, ctx, name, kw, status):
+    d = desc(**kw)
+    st = lib.tc_gemm_batched(ctx, ctypes.byref(d), A_PTR, B_PTR, C_PTR)
+    assert st == status, (tg.status_name(st), lib.tc_last_error(ctx))
+    assert lib.tc_last_error(ctx) != b""
+    assert lib.tc_dispatch_count(ctx) == 0
+    assert lib.tc_gemm_plan(None, ctypes.byref(d), None) == status
+
+
+def test_null_arguments(lib, ctx):
+    d = desc()
+    assert lib.tc_gemm_batched(ctx, ctypes.byref(d), None, B_PTR, C_PTR) == 1
+    assert lib.tc_gemm_batched(ctx, ctypes.byref(d), A_PTR, B_PTR, None) == 1
+    assert lib.tc_gemm_batched(ctx, None, A_PTR, B_PTR, C_PTR) == 1
+    assert lib.tc_gemm_batched(None, ctypes.byref(d), A_PTR, B_PTR, C_PTR) == 1
+    assert lib.tc_gemm(ctx, None, A_PTR, B_PTR, C_PTR) == 1
+    assert lib.tc_gemm_async(ctx, ctypes.byref(d.base), A_PTR, B_PTR, C_PTR, None) == 1
+    assert lib.tc_dispatch_count(ctx) == 0
+
+
+def test_overlap_refused(lib, ctx):
+    d = desc(M=64, N=64, K=64)                  # bf16: A spans 8192 bytes
+    assert lib.tc_gemm_batched(ctx, ctypes.byref(d), A_PTR, B_PTR, A_PTR + 4096) == 4
+    assert lib.tc_gemm_batched(ctx, ctypes.byref(d), A_PTR, B_PTR, B_PTR - 100) == 4
+    assert lib.tc_dispatch_count(ctx) == 0
+
+
+def test_int8_k_bound_accepted_at_131071(lib):
+    d = desc(a=tg.I8, c=tg.I32, acc=tg.I32, K=131071, M=16, N=16)
+    assert lib.tc_gemm_plan(None, ctypes.byref(d), None) == 0
+
+
+def test_valid_call_without_gpu_fails_cleanly(lib, ctx):
+    """With a valid descriptor but no usable device the call reports an error
+    instead of launching (on a GPU host the fake pointers are refused)."""
+    d = desc()
+    st = lib.tc_gemm_batched(ctx, ctypes.byref(d), A_PTR, B_PTR, C_PTR)
+    assert st in (1, 6)
+    assert lib.tc_dispatch_count(ctx) == 0
+
+
+# ------------------------------------------------------------------ planner
+def plan_of(p: workloads.Problem):
+    code = {"f32": tg.F32, "f16": tg.F16, "bf16": tg.BF16, "i8": tg.I8, "i32": tg.I32}
+    d = desc(M=p.M, N=p.N, K=p.K, a=code[p.a_dtype], c=code[p.c_dtype],
+             acc=tg.I32 if p.a_dtype == "i8" else tg.F32, ta=p.transpose_a, tb=p.transpose_b,
+             alpha=p.alpha, beta=p.beta, lda=p.lda, ldb=p.ldb, ldc=p.ldc, batch=p.batch,
+             sa=p.stride_a, sb=p.stride_b, sc=p.stride_c)
+    return tg.plan(d)
+
+
+def test_plan_headline_uses_one_256_tile_per_cu():
+    pl = plan_of(workloads.get("bf16_nn_4096"))
+    assert pl["kernel"] == "gemm_bf16_nn_256x256"
+    assert (pl["tiles_m"], pl["tiles_n"], pl["grid"], pl["splits"]) == (16, 16, 256, 1)
+    assert pl["launches"] == 1 and pl["workspace_bytes"] == 0
+
+
+def test_plan_splitk_shape():
+    p = workloads.get("bf16_tn_splitk_b8")
+    pl = plan_of(p)
+    assert pl["kernel"].startswith("gemm_bf16_tn_") and pl["kernel"].endswith("+splitk_reduce")
+    assert pl["splits"] > 1 and pl["launches"] == 2
+    assert pl["k_per_split"] % pl["tile_k"] == 0
+    assert pl["splits"] * pl["k_per_split"] >= p.K > (pl["splits"] - 1) * pl["k_per_split"]
+    assert pl["workspace_bytes"] == pl["splits"] * p.batch * p.M * p.N * 4
+    assert pl["grid"] >= 256
+
+
+def test_plan_other_workloads():
+    assert plan_of(workloads.get("i8_nn_ragged"))["kernel"] == "gemm_i8_nn_256x256"
+    assert plan_of(workloads.get("f16_tn_4096"))["kernel"] == "gemm_f16_tn_256x256"
+    assert plan_of(workloads.get("f16_nt_4096"))["kernel"] == "gemm_f16_nt_256x256"
+    pl = plan_of(workloads.get("sgemm_nn_256"))
+    assert pl["kernel"].startswith("gemm_f32_nn_64x64")
+    z = plan_of(workloads.get("bf16_nn_4096").with_(alpha=0.0, beta=2.0))
+    assert z["kernel"] == "scale_c" and z["launches"] == 1
+
+
+# ------------------------------------------------------------------ tile order
+def tile_map(lib, tm_, tn_, groups, band):
+    n = tm_ * tn_ * groups
+    out = []
+    a, b, g = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    for wg in range(n):
+        assert lib.tc_tile_of_workgroup(tm_, tn_, groups, band, wg, ctypes.byref(a),
+                                        ctypes.byref(b), ctypes.byref(g)) == 0
+        out.append((a.value, b.value, g.value))
+    return out
+
+
+@pytest.mark.parametrize("tm_,tn_,groups,band", [
+    (16, 16, 1, 8), (17, 33, 1, 8), (3, 5, 7, 8), (1, 1, 1, 8), (13, 4, 2, 8),
+    (16, 16, 1, 0), (9, 9, 3, 4), (2, 6, 24, 8), (100, 3, 1, 8)])
+def test_tile_order_is_a_bijection(lib, tm_, tn_, groups, band):
+    m = tile_map(lib, tm_, tn_, groups, band)
+    assert sorted(m) == [(i, j, g) for i in range(tm_) for j in range(tn_) for g in range(groups)]
+
+
+def test_tile_order_out_of_range(lib):
+    a, b, g = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    assert lib.tc_tile_of_workgroup(4, 4, 1, 8, 16, ctypes.byref(a), ctypes.byref(b),
+                                    ctypes.byref(g)) == 1
+    assert lib.tc_tile_of_workgroup(4, 4, 1, 8, -1, ctypes.byref(a), ctypes.byref(b),
+                                    ctypes.byref(g)) == 1
+
+
+def test_band_order_matches_the_pages_formula(lib):
+    """Inside one group, logical ids follow the column-panel band order: with
+    the XCD regrouping undone, id t maps to tile (band*PH + rem % h, rem / h)."""
+    tm_, tn_, PH = 19, 7, 8                     # last band holds only 3 rows
+    n = tm_ * tn_
+    m = tile_map(lib, tm_, tn_, 1, PH)
+    q, r = divmod(n, 8)
+    for wg in range(n):
+        xcd, j = wg % 8, wg // 8
+        t = (xcd * (q + 1) if xcd < r else r * (q + 1) + (xcd - r) * q) + j
+        band = t // (PH * tn_)
+        rem = t - band * PH * tn_
+        h = min(PH, tm_ - band * PH)
+        assert m[wg][:2] == (band * PH + rem % h, rem // h)
+
+
+def test_each_xcd_gets_a_compact_block(lib):
+    """16x16 tiles (the 4096^3 headline with 256x256 tiles): every XCD's 32
+    workgroups touch at most 8 A row panels + 4 B column panels, against 2 + 16
+    for plain row-major order."""
+    m = tile_map(lib, 16, 16, 1, 8)
+    for xcd in range(8):
+        tiles = [m[wg] for wg in range(256) if wg % 8 == xcd]
+        rows = {t[0] for t in tiles}
+        cols = {t[1] for t in tiles}
+        assert len(tiles) == 32 and len(rows) + len(cols) <= 12
+    raster = tile_map(lib, 16, 16, 1, 0)
+    tiles = [raster[wg] for wg in range(256) if wg % 8 == 0]
+    assert len({t[0] for t in tiles}) + len({t[1] for t in tiles}) == 18
+
+
+def test_lds_budget_of_the_tile_classes():
+    """The pages size their 64x64 tile against a 32 KB threadgroup budget
+    (tensorcore "GEMM", "Why 64x64?": 4 KB + 4 KB + 16 KB = 24 KB).  Here each
+    class double-buffers (BM + BN) rows of 128 bytes; the largest needs
+    128 KiB of the 160 KiB LDS of a gfx950 CU."""
+    assert 64 * 32 * 2 + 32 * 64 * 2 + 64 * 64 * 4 == 24 * 1024
+    for bm, bn in ((256, 256), (128, 128), (64, 64)):
+        assert 2 * (bm + bn) * 128 <= 160 * 1024
+    assert 2 * (256 + 256) * 128 == 128 * 1024
