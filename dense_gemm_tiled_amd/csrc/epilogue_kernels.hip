@@ -45,12 +45,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const EpilogueArgs a
         if (wvec && nvalid >= 4) {
             u32x4 w = ld128(rw, off);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) s4[e] += __builtin_bit_cast(float, w[e]);
+            for (int e = 0; e < 4; ++e) s4[e] += as_f32(w[e]);
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 if (e < nvalid)
-                    s4[e] += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, off + 4 * e, 0, 0));
+                    s4[e] += as_f32(__builtin_amdgcn_raw_buffer_load_b32(rw, off + 4 * e, 0, 0));
         }
     }
     switch (a.c_dtype) {

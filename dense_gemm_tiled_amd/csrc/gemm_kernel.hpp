@@ -48,6 +48,14 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
+// Scalar reinterpretation through a by-value parameter.  With this clang,
+// __builtin_bit_cast applied directly to an element of an ext_vector_type
+// value reads element 0 whatever the index; copying the element into a
+// parameter first gives the element that was asked for.
+__device__ inline float as_f32(u32 x) { return __builtin_bit_cast(float, x); }
+__device__ inline u32 as_u32(float x) { return __builtin_bit_cast(u32, x); }
+__device__ inline int as_i32(float x) { return __builtin_bit_cast(int, x); }
+
 // Word 3 of a gfx9-family buffer resource: raw (untyped) 32-bit data.
 constexpr int kRsrcWord3 = 0x00020000;
 
@@ -279,8 +287,7 @@ struct Mma<DT_F32> {
     __device__ static inline void run(Acc &acc, u32x4 b, u32x4 a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, b[e]),
-                                                       __builtin_bit_cast(float, a[e]), acc,
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(b[e]), as_f32(a[e]), acc,
                                                        0, 0, 0);
     }
 };
@@ -294,7 +301,7 @@ __device__ inline u32 to_bf16_bits(float x) {
 __device__ inline u32 to_f16_bits(float x) {
     return (u32)__builtin_bit_cast(unsigned short, static_cast<_Float16>(x));
 }
-__device__ inline float from_bf16_bits(u32 h) { return __builtin_bit_cast(float, h << 16); }
+__device__ inline float from_bf16_bits(u32 h) { return as_f32(h << 16); }
 __device__ inline float from_f16_bits(u32 h) {
     return (float)__builtin_bit_cast(_Float16, (unsigned short)h);
 }
@@ -307,12 +314,11 @@ __device__ inline void load_c4(__amdgpu_buffer_rsrc_t r, int off, int nvalid, bo
         if (vec && nvalid >= 4) {
             u32x4 w = ld128(r, off);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = __builtin_bit_cast(float, w[e]);
+            for (int e = 0; e < 4; ++e) o[e] = as_f32(w[e]);
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                o[e] = e < nvalid ? __builtin_bit_cast(
-                                        float, __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * e, 0, 0))
+                o[e] = e < nvalid ? as_f32(__builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * e, 0, 0))
                                   : 0.f;
         }
     } else {
@@ -338,14 +344,13 @@ __device__ inline void store_c4(__amdgpu_buffer_rsrc_t r, int off, int nvalid, b
                                 const float (&v)[4]) {
     if constexpr (CDT == DT_F32) {
         if (vec && nvalid >= 4) {
-            u32x4 w = {__builtin_bit_cast(u32, v[0]), __builtin_bit_cast(u32, v[1]),
-                       __builtin_bit_cast(u32, v[2]), __builtin_bit_cast(u32, v[3])};
+            u32x4 w = {as_u32(v[0]), as_u32(v[1]), as_u32(v[2]), as_u32(v[3])};
             __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 0);
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 if (e < nvalid)
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(u32, v[e]), r,
+                    __builtin_amdgcn_raw_buffer_store_b32(as_u32(v[e]), r,
                                                           off + 4 * e, 0, 0);
         }
     } else {
@@ -523,7 +528,10 @@ __global__ __launch_bounds__(256, Occupancy<CLS>::value) void gemm_kernel(const 
                 if (nvalid <= 0) continue;
                 int v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = __builtin_bit_cast(int, acc[i][j][e]);
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (DT == DT_I8) v[e] = acc[i][j][e];
+                    else v[e] = as_i32(acc[i][j][e]);
+                }
                 store_i4(rw, (ml * N + nl) * 4, nvalid, vec, v);
             }
         }
