@@ -1,0 +1,406 @@
+// gemm_dma_kernel.hpp -- the 256x256 GEMM kernel for gfx950 whose operand
+// tiles go from HBM straight into LDS (buffer loads with the LDS flag), for
+// 16-bit and int8 inputs whose rows start on 16-byte boundaries.
+//
+// Same computation and epilogue as gemm_kernel (C = alpha*op(A)op(B) +
+// beta*C, accumulator in registers for the whole K loop, C written once;
+// tessl "Architecture", "Cooperative Destination Accumulation"), with a
+// schedule built for one workgroup per CU:
+//
+//   * 256 threads = 4 wave64s in a 2 x 2 grid, each wave owns 128 x 128 of C
+//     as 8 x 8 blocks of 16 x 16 MFMA accumulators (256 fp32/int32 AGPRs per
+//     lane);
+//   * per K-tile (128 bytes of K: 64 bf16/f16 or 128 int8) every wave issues
+//     16 direct-to-LDS loads of 1 KiB; two LDS stages of 64 KiB hold tile t
+//     and tile t+1;
+//   * the MFMAs of a K-tile run in two sub-steps of 64.  While one sub-step
+//     runs, the fragments of the next are read from LDS into a second
+//     register set, one read between every few MFMAs;
+//   * one barrier per K-tile, between the sub-steps: after it, tile t+1 is
+//     visible to every wave and the stage of tile t is free, so the loads of
+//     tile t+2 are issued into it during the second sub-step;
+//   * K-contiguous operands are read with ds_read_b128; M/N-contiguous ones
+//     with the gfx950 transposing LDS reads (ds_read_b64_tr_b16 / _b8),
+//     which hand every lane the K-run of one column -- no transpose pass and
+//     no register shuffles (tensorcore "GEMM", "Transposes": a transpose is a
+//     choice of strides).
+//
+// The MFMAs, the LDS-bound loads and the barrier are inline assembly.  The
+// accumulators are pinned to AGPRs (operand constraint "+a", destination =
+// source C), the loads are invisible to the compiler (so it cannot order the
+// LDS reads of one stage behind the loads into the other), and every
+// assembly statement is volatile, so the interleave below is the issue order.
+// The waits the compiler cannot see are written out: vmcnt(0) before each
+// barrier and at the end of the loop, and wait states between the last MFMA
+// and the first read of the accumulators.
+//
+// LDS layouts (bytes; both chosen so that the reads below hit every bank once
+// per 256 bytes and the DMA writes stay contiguous):
+//   K-contiguous tile: 256 rows x 128 B; 16-byte chunk c of row r at
+//     position c ^ ((r & 7) ^ ((r >> 3) & 1)).
+//   M/N-contiguous tile, 16-bit: 64 k-rows x 512 B; 32-byte segment s (16
+//     columns) of row k at position s ^ ((k & 3) | ((k >> 3) & 1) << 2).
+//   M/N-contiguous tile, int8: 128 k-rows x 256 B; 16-byte segment s of row
+//     k at position s ^ ((k & 7) | ((k >> 4) & 1) << 3).
+//
+// Ragged edges (tessl "Architecture", "Edge-Slice Support"): rows past M or
+// N only feed outputs that are never stored, and buffer range checks return
+// zero past the operand; k past K is zeroed per 16-byte chunk (the planner
+// sends this kernel only shapes whose K is a whole number of chunks).
+
+#pragma once
+
+#include "gemm_kernel.hpp"
+
+namespace tcg {
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+#define TCG_LDS __attribute__((address_space(3)))
+
+constexpr int kDmaTile = 256;                          // BM = BN
+constexpr int kDmaOpBytes = kDmaTile * kLdsRowBytes;   // 32 KiB per operand tile
+constexpr int kDmaStageBytes = 2 * kDmaOpBytes;        // [A tile | B tile]
+// An offset past every buffer range (ranges are < 2^31 bytes; the offset plus
+// the 16-byte access does not wrap 32 bits): such a load reads zeros.
+constexpr int kOobOffset = INT32_MIN;
+
+__device__ inline int swz_kc(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <int ES>
+__device__ inline int swz_mc(int k) {
+    if constexpr (ES == 2) return (k & 3) | (((k >> 3) & 1) << 2);
+    else return (k & 7) | (((k >> 4) & 1) << 3);
+}
+
+// Raw buffer resource as four SGPRs (same fields as make_rsrc).
+__device__ inline i32x4 rsrc4(const void *base, int64_t bytes) {
+    const int32_t n = bytes <= 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int32_t)bytes);
+    const uint64_t a = (uint64_t)base;
+    return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xFFFF), n, kRsrcWord3};
+}
+
+// 16 bytes per lane from buffer offset `voff` to LDS byte address
+// lds + 16 * lane.  M0 holds the LDS address; a load with the LDS flag needs
+// one wait state after an SALU write of M0.  (M0 is listed as clobbered; the
+// compiler reserves it and sets it itself wherever it needs it.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ inline void dma16(i32x4 rsrc, uint32_t lds, int voff) {
+    asm volatile("s_mov_b32 m0, %0\n\t"
+                 "s_nop 0\n\t"
+                 "buffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait for this wave's loads and LDS reads, then for the other waves.
+__device__ inline void wait_all_barrier() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int DT>
+struct MmaAsm;
+
+template <>
+struct MmaAsm<DT_BF16> {
+    using Acc = f32x4;
+    __device__ static inline void run(Acc &acc, const u32x4 &b, const u32x4 &a) {
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+    }
+};
+
+template <>
+struct MmaAsm<DT_F16> {
+    using Acc = f32x4;
+    __device__ static inline void run(Acc &acc, const u32x4 &b, const u32x4 &a) {
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+    }
+};
+
+template <>
+struct MmaAsm<DT_I8> {
+    using Acc = i32x4;
+    __device__ static inline void run(Acc &acc, const u32x4 &b, const u32x4 &a) {
+        asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+    }
+};
+
+// One operand's share of the DMA of a tile: 8 loads of 1 KiB per wave.
+// MC: the operand is M/N-contiguous in memory (global row = one k).
+// Load u of wave w fills tile rows (8w + u) * RPI + lane / LPR.  A lane's byte
+// offset is a lane part, which depends on u only through the swizzle (u & 1
+// and u >> 2), plus u * RPI rows, which is wave-uniform.
+template <int ES, bool MC>
+struct DmaLoader {
+    static constexpr int RB = MC ? kDmaTile * ES : kLdsRowBytes;   // LDS row bytes
+    static constexpr int LPR = RB / 16;                            // lanes per row
+    static constexpr int RPI = 64 / LPR;                           // rows per load
+    int lane_off[4];  // [(u & 1) | (u >> 2) << 1]: lane part of the byte offset
+    int row0;         // MC: tile row (k) of this lane for u = 0
+    int kfirst[2];    // KC: first k (elements) of this lane's chunk, [u & 1]
+    int ld_bytes;
+
+    __device__ static inline int row_of(int wave, int lane, int u) {
+        return (wave * 8 + u) * RPI + lane / LPR;
+    }
+    __device__ static inline int col_of(int r, int q) {
+        if constexpr (MC) {
+            if constexpr (ES == 2) return (((q >> 1) ^ swz_mc<2>(r)) << 5) + ((q & 1) << 4);
+            else return (q ^ swz_mc<1>(r)) << 4;
+        } else {
+            return (q ^ swz_kc(r)) << 4;
+        }
+    }
+
+    __device__ inline void init(int wave, int lane, int ldb) {
+        ld_bytes = ldb;
+        row0 = row_of(wave, lane, 0);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int u = (s & 1) | ((s >> 1) << 2);
+            lane_off[s] = row0 * ldb + col_of(row_of(wave, lane, u), lane % LPR);
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            kfirst[s] = (col_of(row_of(wave, lane, s), lane % LPR) >> 4) * (16 / ES);
+    }
+
+    // Byte offset of load u for a tile with k_valid valid k (<= tile depth);
+    // chunks past K get an offset outside the buffer, which loads zeros.
+    __device__ inline int offset(int u, int k_valid) const {
+        const int off = lane_off[(u & 1) | ((u >> 2) << 1)] + u * RPI * ld_bytes;
+        const bool in = MC ? (row0 < k_valid - u * RPI) : (kfirst[u & 1] < k_valid);
+        return in ? off : kOobOffset;
+    }
+};
+
+// LDS fragment reads.  KC: ds_read_b128 of a K-contiguous tile; MC: two
+// transposing reads of an M/N-contiguous tile.  Both give lane l the K-run
+// {8*(l/16) .. +7} (16-bit) or {16*(l/16) .. +15} (int8) of sub-step ks for
+// row/column (l % 16) of 16-block i -- the operand layout of the
+// 16x16x32 (16-bit) and 16x16x64 (int8) MFMAs.
+template <int ES, bool MC>
+struct FragReader {
+    int base[MC ? 8 : 2];   // lane byte offsets inside an operand tile
+
+    __device__ inline void init(int lane, int blk0) {
+        const int l16 = lane & 15, g = lane >> 4;
+        if constexpr (MC) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int seg = blk0 / 16 + j;
+                if constexpr (ES == 2) {
+                    const int k = 8 * g + (l16 >> 2);
+                    base[j] = k * 512 + ((seg ^ swz_mc<2>(k)) << 5) + ((lane & 3) << 3);
+                } else {
+                    const int k = 16 * g + (l16 >> 1);
+                    base[j] = k * 256 + ((seg ^ swz_mc<1>(k)) << 4) + ((lane & 1) << 3);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                base[ks] = (blk0 + l16) * kLdsRowBytes + (((ks * 4 + g) ^ swz_kc(l16)) << 4);
+        }
+    }
+
+    // tile: LDS byte address of the operand tile.
+    __device__ inline void read(uint32_t tile, int ks, int i, u32x4 &out) const {
+        if constexpr (MC) {
+            // rows advance by 32 (16-bit) / 64 (int8) per sub-step, by 4 / 8
+            // for the second half of the K-run
+            constexpr int RB = kDmaTile * ES;
+            constexpr int KS_ROWS = ES == 2 ? 32 : 64, H_ROWS = ES == 2 ? 4 : 8;
+            const uint32_t p = tile + base[i] + ks * KS_ROWS * RB;
+            i32x2 lo, hi;
+            if constexpr (ES == 2) {
+                lo = __builtin_bit_cast(
+                    i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((TCG_LDS s16x4 *)(size_t)p));
+                hi = __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                   (TCG_LDS s16x4 *)(size_t)(p + H_ROWS * RB)));
+            } else {
+                lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((TCG_LDS i32x2 *)(size_t)p);
+                hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (TCG_LDS i32x2 *)(size_t)(p + H_ROWS * RB));
+            }
+            out = u32x4{(u32)lo[0], (u32)lo[1], (u32)hi[0], (u32)hi[1]};
+        } else {
+            out = *(const TCG_LDS u32x4 *)(size_t)(tile + base[ks] + i * 16 * kLdsRowBytes);
+        }
+    }
+};
+
+template <int DT, bool TA, bool TB, int OUT>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void gemm_dma_kernel(const GemmArgs args) {
+    constexpr int ES = dt_size(DT);
+    static_assert(ES == 2 || ES == 1, "direct-to-LDS kernel: 16-bit and int8 inputs");
+    constexpr int BK = kLdsRowBytes / ES;
+    constexpr bool A_MC = TA, B_MC = !TB;
+    using Mma = MmaAsm<DT>;
+    using Acc = typename Mma::Acc;
+
+    __shared__ __attribute__((aligned(1024))) char smem[2 * kDmaStageBytes];
+    const uint32_t lds = (uint32_t)(size_t)(TCG_LDS char *)smem;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int wm = wave >> 1, wn = wave & 1;
+
+    int32_t tm, tn, g;
+    tile_of_workgroup(args.tiles_m, args.tiles_n, args.band, blockIdx.x, gridDim.x, &tm, &tn, &g);
+    const int z = g / args.splits, sidx = g % args.splits;
+    const int M = args.M, N = args.N, K = args.K;
+    const int m0 = tm * kDmaTile, n0 = tn * kDmaTile;
+    const int k_lo = sidx * args.k_per_split;
+    const int k_hi = min(K, k_lo + args.k_per_split);
+    const int nkt = (k_hi - k_lo + BK - 1) / BK;
+
+    const char *Ab = static_cast<const char *>(args.A) + z * args.stride_a * ES;
+    const char *Bb = static_cast<const char *>(args.B) + z * args.stride_b * ES;
+
+    DmaLoader<ES, A_MC> la;
+    DmaLoader<ES, B_MC> lb;
+    la.init(wave, lane, args.lda * ES);
+    lb.init(wave, lane, args.ldb * ES);
+    FragReader<ES, A_MC> fa;
+    FragReader<ES, B_MC> fb;
+    fa.init(lane, wm * 128);
+    fb.init(lane, wn * 128);
+
+    // Buffer resources of tile kt, based at its origin; a tile past the end
+    // gets empty ranges (its loads read zeros).
+    struct TileSrc {
+        i32x4 ra, rb;
+        int kv;
+    };
+    auto tile_src = [&](int kt) {
+        TileSrc s;
+        const int k0 = k_lo + kt * BK;
+        const int64_t a_org = A_MC ? ((int64_t)k0 * args.lda + m0) * ES
+                                   : ((int64_t)m0 * args.lda + k0) * ES;
+        const int64_t b_org = B_MC ? ((int64_t)k0 * args.ldb + n0) * ES
+                                   : ((int64_t)n0 * args.ldb + k0) * ES;
+        s.ra = rsrc4(Ab + a_org, args.a_extent - a_org);
+        s.rb = rsrc4(Bb + b_org, args.b_extent - b_org);
+        s.kv = min(BK, k_hi - k0);
+        return s;
+    };
+    // DMA load number d (0..15) of a tile: 0..7 A, 8..15 B.
+    auto dma = [&](const TileSrc &s, uint32_t stage, int d) {
+        const int u = d & 7;
+        const uint32_t dst = stage + (d >= 8 ? kDmaOpBytes : 0) + (wave * 8 + u) * 1024;
+        if (d < 8) dma16(s.ra, dst, la.offset(u, s.kv));
+        else dma16(s.rb, dst, lb.offset(u, s.kv));
+    };
+
+    Acc acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+
+    u32x4 a0[8], b0[8], a1[8], b1[8];
+
+    // fragment read number r (0..15) of sub-step ks: 0..7 B blocks, then A
+    auto read = [&](uint32_t stage, int ks, int r, u32x4 (&af)[8], u32x4 (&bf)[8]) {
+        if (r < 8) fb.read(stage + kDmaOpBytes, ks, r, bf[r]);
+        else fa.read(stage, ks, r - 8, af[r - 8]);
+    };
+
+    // Sub-step 0 of the tile in `cur`: MFMAs on (a0, b0); one fragment read
+    // of sub-step 1 after every 4th MFMA.
+    auto sub0 = [&](uint32_t cur) {
+#pragma unroll
+        for (int q = 0; q < 64; ++q) {
+            Mma::run(acc[q >> 3][q & 7], b0[q & 7], a0[q >> 3]);
+            if ((q & 3) == 0) read(cur, 1, q >> 2, a1, b1);
+        }
+    };
+    // Sub-step 1: MFMAs on (a1, b1); after every 2nd MFMA one of: a DMA load
+    // of tile kt+2 into `cur`, a fragment read of the next tile.  Past the
+    // last tile the loads are empty (zero-fill a stage nobody reads) and the
+    // reads return stale data nobody uses, so the loop body has no branch.
+    auto sub1 = [&](uint32_t cur, uint32_t nxt, const TileSrc &s) {
+#pragma unroll
+        for (int q = 0; q < 64; ++q) {
+            Mma::run(acc[q >> 3][q & 7], b1[q & 7], a1[q >> 3]);
+            if ((q & 1) == 0) {
+                const int r = q >> 1;
+                if ((r & 1) == 0) dma(s, cur, r >> 1);
+                else read(nxt, 0, r >> 1, a0, b0);
+            }
+        }
+    };
+
+    if (nkt > 0) {
+        {
+            const TileSrc s0 = tile_src(0);
+            const TileSrc s1 = tile_src(1);
+#pragma unroll
+            for (int d = 0; d < 16; ++d) dma(s0, lds, d);
+#pragma unroll
+            for (int d = 0; d < 16; ++d) dma(s1, lds + kDmaStageBytes, d);
+        }
+        wait_all_barrier();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) read(lds, 0, r, a0, b0);
+        for (int kt = 0; kt < nkt; ++kt) {
+            const uint32_t cur = lds + (kt & 1) * kDmaStageBytes;
+            const uint32_t nxt = lds + ((kt + 1) & 1) * kDmaStageBytes;
+            sub0(cur);
+            wait_all_barrier();   // tile kt+1 landed for every wave; `cur` is free
+            sub1(cur, nxt, tile_src(kt + 2));
+        }
+        // no load may still be writing LDS when the workgroup ends, and the
+        // last MFMA results need wait states before the accumulators are read
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" :::
+                         "memory");
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
+
+    // ---- epilogue: lane holds C[m][n .. n+3] of each 16x16 block
+    const int ml0 = wm * 128 + (lane & 15);
+    const int nl0 = wn * 128 + 4 * (lane >> 4);
+    constexpr int CES = dt_size(OUT);
+    const int64_t c_org = ((int64_t)m0 * args.ldc + n0) * CES;
+    char *Cb = static_cast<char *>(args.C) + z * args.stride_c * CES + c_org;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cb, args.c_extent - c_org);
+    const bool vec = args.c_vec_ok != 0;
+    const int ldc = args.ldc;
+    const float alpha = args.alpha, beta = args.beta;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int ml = ml0 + i * 16;
+        if (m0 + ml >= M) continue;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int nl = nl0 + j * 16;
+            const int nvalid = N - (n0 + nl);
+            if (nvalid <= 0) continue;
+            const int off = (ml * ldc + nl) * CES;
+            if constexpr (OUT == DT_I32) {
+                int v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e];
+                store_i4(rc, off, nvalid, vec, v);
+            } else {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e];
+                finish4<OUT>(rc, off, nvalid, vec, alpha, beta, v);
+            }
+        }
+    }
+}
+
+}  // namespace
+}  // namespace tcg

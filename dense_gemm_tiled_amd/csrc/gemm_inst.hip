@@ -2,7 +2,7 @@
 // layout and exports that object's launcher.  The build compiles this file
 // once per (TCG_DT, TCG_TA, TCG_TB) with TCG_LAUNCHER naming the launcher,
 // so the 16 objects compile in parallel.
-#include "gemm_kernel.hpp"
+#include "gemm_dma_kernel.hpp"
 
 #if !defined(TCG_DT) || !defined(TCG_TA) || !defined(TCG_TB) || !defined(TCG_LAUNCHER)
 #error "the build defines TCG_DT, TCG_TA, TCG_TB and TCG_LAUNCHER"
@@ -13,8 +13,10 @@ namespace {
 
 // Output types that exist for this input type (include/tcgemm.h lists the
 // supported tuples); split-K partials only for the 64x64 class, the only
-// class the planner splits.
+// class the planner splits; the direct-to-LDS class only for 16-bit and int8
+// inputs.
 constexpr bool out_ok(int cls, int out) {
+    if (cls == TILE_256_DMA && (TCG_DT == DT_F32 || out == OUT_PARTIAL)) return false;
     if (out == OUT_PARTIAL) return cls == TILE_64;
     if (TCG_DT == DT_I8) return out == DT_I32;
     if (TCG_DT == DT_F32) return out == DT_F32;
@@ -23,7 +25,11 @@ constexpr bool out_ok(int cls, int out) {
 
 template <int CLS, int OUT>
 hipError_t launch_one(const GemmArgs &args, int64_t grid, hipStream_t stream) {
-    if constexpr (out_ok(CLS, OUT)) {
+    if constexpr (CLS == TILE_256_DMA && out_ok(CLS, OUT)) {
+        hipLaunchKernelGGL((gemm_dma_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, OUT>),
+                           dim3((unsigned)grid), dim3(256), 0, stream, args);
+        return hipGetLastError();
+    } else if constexpr (CLS != TILE_256_DMA && out_ok(CLS, OUT)) {
         hipLaunchKernelGGL((gemm_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, CLS, OUT>),
                            dim3((unsigned)grid), dim3(256), 0, stream, args);
         return hipGetLastError();
@@ -54,6 +60,7 @@ hipError_t TCG_LAUNCHER(int cls, int out, const tcg::GemmArgs &args, int64_t gri
     case TILE_256: return launch_cls<TILE_256>(out, args, grid, stream);
     case TILE_128: return launch_cls<TILE_128>(out, args, grid, stream);
     case TILE_64: return launch_cls<TILE_64>(out, args, grid, stream);
+    case TILE_256_DMA: return launch_cls<TILE_256_DMA>(out, args, grid, stream);
     default: return hipErrorInvalidValue;
     }
 }

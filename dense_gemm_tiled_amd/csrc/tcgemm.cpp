@@ -192,16 +192,31 @@ tc_status_t validate(const tc_gemm_batched_desc *bd, Problem *p, std::string *er
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// The direct-to-LDS kernel moves 16-byte chunks: 16-bit or int8 inputs whose
+// rows and batch strides are whole chunks, and a K that is a whole number of
+// chunks (k past K is zeroed per chunk).  A and B must also start on 16 bytes
+// (checked at launch, where the pointers are known).
+bool dma_ok(const Problem &p) {
+    if (p.dt != TC_F16 && p.dt != TC_BF16 && p.dt != TC_I8) return false;
+    const int es = dt_size(p.dt);
+    return (p.lda * es) % 16 == 0 && (p.ldb * es) % 16 == 0 && (p.stride_a * es) % 16 == 0 &&
+           (p.stride_b * es) % 16 == 0 && (p.K * es) % 16 == 0;
+}
+
 // Tile class and split-K choice.  MI355X has 256 CUs; a launch wants at least
 // about one workgroup per CU.  The big tile is used when it alone fills the
 // chip; otherwise the smaller classes, then split-K for tall-K outputs with
 // few tiles (the case tessl "Architecture" routes to split-K: K >= 2048 with
 // small M and N).
 //
+// The 256x256 class runs as the direct-to-LDS kernel when the operands allow
+// it (dma_ok; the base pointers' alignment is checked at launch time).
+//
 // Tuning overrides (environment, read at every call; unset in normal use):
-// TCGEMM_TILE=256|128|64 forces a tile class, TCGEMM_SPLITS=S forces split-K
-// with S slices (on the 64x64 class, the one with a partial-sum output),
-// TCGEMM_BAND=h sets the band height of the tile order (0: row-major).
+// TCGEMM_TILE=dma|256|128|64 forces a tile class (dma only where allowed),
+// TCGEMM_SPLITS=S forces split-K with S slices (on the 64x64 class, the one
+// with a partial-sum output), TCGEMM_BAND=h sets the band height of the tile
+// order (0: row-major).
 void make_plan(const Problem &p, Plan *pl) {
     const int es = dt_size(p.dt);
     const int bk = kLdsRowBytes / es;
@@ -211,10 +226,12 @@ void make_plan(const Problem &p, Plan *pl) {
         const int64_t tiles = ceil_div(p.M, ts.bm) * ceil_div(p.N, ts.bn) * p.batch;
         if (tiles >= 192 || c == TILE_64) { cls = c; break; }
     }
+    if (cls == TILE_256 && dma_ok(p)) cls = TILE_256_DMA;
     int64_t forced_splits = 0;
     if (const char *env = getenv("TCGEMM_TILE")) {
         const int v = atoi(env);
-        cls = v == 256 ? TILE_256 : v == 128 ? TILE_128 : v == 64 ? TILE_64 : cls;
+        if (strcmp(env, "dma") == 0) cls = dma_ok(p) ? TILE_256_DMA : cls;
+        else cls = v == 256 ? TILE_256 : v == 128 ? TILE_128 : v == 64 ? TILE_64 : cls;
     }
     if (const char *env = getenv("TCGEMM_SPLITS")) {
         forced_splits = atoi(env);
@@ -363,6 +380,8 @@ tc_status_t run(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A, 
         return fail(err, TC_ERR_ALIASING, "C overlaps A or B");
     Plan pl;
     make_plan(p, &pl);
+    if (pl.cls == TILE_256_DMA && ((uintptr_t)A % 16 != 0 || (uintptr_t)B % 16 != 0))
+        pl.cls = TILE_256;   // same tile, register-staged loads
 
     st = bind_device(ctx);
     if (st != TC_OK) return st;

@@ -155,7 +155,7 @@ def plan_of(p: workloads.Problem):
 
 def test_plan_headline_uses_one_256_tile_per_cu():
     pl = plan_of(workloads.get("bf16_nn_4096"))
-    assert pl["kernel"] == "gemm_bf16_nn_256x256"
+    assert pl["kernel"] == "gemm_bf16_nn_256x256_dma"
     assert (pl["tiles_m"], pl["tiles_n"], pl["grid"], pl["splits"]) == (16, 16, 256, 1)
     assert pl["launches"] == 1 and pl["workspace_bytes"] == 0
 
@@ -172,13 +172,28 @@ def test_plan_splitk_shape():
 
 
 def test_plan_other_workloads():
+    # ldb = 4099 bytes: rows not 16-byte aligned, so the register-staged loads
     assert plan_of(workloads.get("i8_nn_ragged"))["kernel"] == "gemm_i8_nn_256x256"
-    assert plan_of(workloads.get("f16_tn_4096"))["kernel"] == "gemm_f16_tn_256x256"
-    assert plan_of(workloads.get("f16_nt_4096"))["kernel"] == "gemm_f16_nt_256x256"
+    assert plan_of(workloads.get("f16_tn_4096"))["kernel"] == "gemm_f16_tn_256x256_dma"
+    assert plan_of(workloads.get("f16_nt_4096"))["kernel"] == "gemm_f16_nt_256x256_dma"
     pl = plan_of(workloads.get("sgemm_nn_256"))
     assert pl["kernel"].startswith("gemm_f32_nn_64x64")
     z = plan_of(workloads.get("bf16_nn_4096").with_(alpha=0.0, beta=2.0))
     assert z["kernel"] == "scale_c" and z["launches"] == 1
+
+
+def test_plan_dma_eligibility():
+    """The direct-to-LDS class needs 16-bit or int8 inputs, 16-byte row pitches
+    and batch strides, and K in whole 16-byte chunks; otherwise the same tile
+    runs with register-staged loads."""
+    base = workloads.get("bf16_nn_4096")
+    assert plan_of(base.with_(K=4096 - 8))["kernel"].endswith("_dma")
+    assert not plan_of(base.with_(K=4096 - 4))["kernel"].endswith("_dma")     # partial chunk
+    assert not plan_of(base.with_(lda=4096 + 4))["kernel"].endswith("_dma")   # 8-byte pitch
+    assert plan_of(base.with_(lda=4096 + 8))["kernel"].endswith("_dma")
+    assert not plan_of(base.with_(a_dtype="f32", c_dtype="f32"))["kernel"].endswith("_dma")
+    i8 = workloads.get("i8_nn_ragged")
+    assert plan_of(i8.with_(N=4096 + 16))["kernel"] == "gemm_i8_nn_256x256_dma"
 
 
 # ------------------------------------------------------------------ tile order
