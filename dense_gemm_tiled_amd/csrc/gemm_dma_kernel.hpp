@@ -92,7 +92,7 @@ __device__ inline void dma16(i32x4 rsrc, uint32_t lds, int voff) {
                  "s_nop 0\n\t"
                  "buffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
-                 : "s"(lds), "v"(voff), "s"(rsrc)
+                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc)
                  : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -100,6 +100,13 @@ __device__ inline void dma16(i32x4 rsrc, uint32_t lds, int voff) {
 // Wait for this wave's loads and LDS reads, then for the other waves.
 __device__ inline void wait_all_barrier() {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Same, but leaving the newest VM loads of this wave in flight.
+template <int VM>
+__device__ inline void wait_barrier_vm() {
+    static_assert(VM >= 0 && VM <= 63, "vmcnt is a 6-bit count");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
 }
 
 template <int DT>
@@ -129,23 +136,25 @@ struct MmaAsm<DT_I8> {
     }
 };
 
-// One operand's share of the DMA of a tile: 8 loads of 1 KiB per wave.
-// MC: the operand is M/N-contiguous in memory (global row = one k).
-// Load u of wave w fills tile rows (8w + u) * RPI + lane / LPR.  A lane's byte
-// offset is a lane part, which depends on u only through the swizzle (u & 1
-// and u >> 2), plus u * RPI rows, which is wave-uniform.
-template <int ES, bool MC>
+// One operand's share of the DMA of a tile: LPW = 32 / NW loads of 1 KiB per
+// wave (NW loading waves).  MC: the operand is M/N-contiguous in memory
+// (global row = one k).  Load u of wave w fills tile rows (LPW w + u) * RPI +
+// lane / LPR.  A lane's byte offset is a lane part, which depends on u only
+// through the swizzle (u & 1 and u >> 2), plus u * RPI rows, which is
+// wave-uniform.
+template <int ES, bool MC, int NW>
 struct DmaLoader {
     static constexpr int RB = MC ? kDmaTile * ES : kLdsRowBytes;   // LDS row bytes
     static constexpr int LPR = RB / 16;                            // lanes per row
     static constexpr int RPI = 64 / LPR;                           // rows per load
+    static constexpr int LPW = 32 / NW;                            // loads per wave
     int lane_off[4];  // [(u & 1) | (u >> 2) << 1]: lane part of the byte offset
     int row0;         // MC: tile row (k) of this lane for u = 0
     int kfirst[2];    // KC: first k (elements) of this lane's chunk, [u & 1]
     int ld_bytes;
 
     __device__ static inline int row_of(int wave, int lane, int u) {
-        return (wave * 8 + u) * RPI + lane / LPR;
+        return (wave * LPW + u) * RPI + lane / LPR;
     }
     __device__ static inline int col_of(int r, int q) {
         if constexpr (MC) {
@@ -182,16 +191,16 @@ struct DmaLoader {
 // transposing reads of an M/N-contiguous tile.  Both give lane l the K-run
 // {8*(l/16) .. +7} (16-bit) or {16*(l/16) .. +15} (int8) of sub-step ks for
 // row/column (l % 16) of 16-block i -- the operand layout of the
-// 16x16x32 (16-bit) and 16x16x64 (int8) MFMAs.
-template <int ES, bool MC>
+// 16x16x32 (16-bit) and 16x16x64 (int8) MFMAs.  NB: 16-blocks per wave.
+template <int ES, bool MC, int NB>
 struct FragReader {
-    int base[MC ? 8 : 2];   // lane byte offsets inside an operand tile
+    int base[MC ? NB : 2];   // lane byte offsets inside an operand tile
 
     __device__ inline void init(int lane, int blk0) {
         const int l16 = lane & 15, g = lane >> 4;
         if constexpr (MC) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < NB; ++j) {
                 const int seg = blk0 / 16 + j;
                 if constexpr (ES == 2) {
                     const int k = 8 * g + (l16 >> 2);
@@ -234,13 +243,33 @@ struct FragReader {
     }
 };
 
-template <int DT, bool TA, bool TB, int OUT>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+// The static interleave of a sub-step: QN MFMAs; in sub-step 0 the NR
+// fragment reads of sub-step 1, in sub-step 1 the ND loads of tile t+2 and
+// the NR fragment reads of tile t+1 alternating (load first).  Operation o of
+// n goes after MFMA (o * QN) / n, so MFMA q is followed by operations
+// op_begin(q) .. op_begin(q + 1) - 1.
+constexpr int op_begin(int q, int n, int qn) { return (q * n + qn - 1) / qn; }
+
+template <int DT, bool TA, bool TB, int OUT, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
+                          amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void gemm_dma_kernel(const GemmArgs args) {
     constexpr int ES = dt_size(DT);
     static_assert(ES == 2 || ES == 1, "direct-to-LDS kernel: 16-bit and int8 inputs");
+    static_assert(NW == 4 || NW == 8, "4 or 8 waves");
     constexpr int BK = kLdsRowBytes / ES;
     constexpr bool A_MC = TA, B_MC = !TB;
+    // waves: 2 along M, NW/2 along N; each owns 128 x WTN of C
+    constexpr int WNW = NW / 2, WTN = kDmaTile / WNW;
+    constexpr int FM = 8, FN = WTN / 16;
+    constexpr int QN = FM * FN;         // MFMAs per wave and sub-step
+    constexpr int NR = FM + FN;         // fragment reads per sub-step
+    // The loads are issued by 4 waves: all of them with 4 waves; with 8, the
+    // second four only, so that while a loading wave waits to issue a load
+    // the other wave on its SIMD keeps the matrix core busy.
+    constexpr int NDW = 4;
+    constexpr int LPW = 32 / NDW;       // loads per loading wave and operand
+    constexpr int ND = 2 * LPW;         // loads per loading wave and tile
     using Mma = MmaAsm<DT>;
     using Acc = typename Mma::Acc;
 
@@ -250,7 +279,7 @@ void gemm_dma_kernel(const GemmArgs args) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WNW, wn = wave % WNW;
 
     int32_t tm, tn, g;
     tile_of_workgroup(args.tiles_m, args.tiles_n, args.band, blockIdx.x, gridDim.x, &tm, &tn, &g);
@@ -264,14 +293,16 @@ void gemm_dma_kernel(const GemmArgs args) {
     const char *Ab = static_cast<const char *>(args.A) + z * args.stride_a * ES;
     const char *Bb = static_cast<const char *>(args.B) + z * args.stride_b * ES;
 
-    DmaLoader<ES, A_MC> la;
-    DmaLoader<ES, B_MC> lb;
-    la.init(wave, lane, args.lda * ES);
-    lb.init(wave, lane, args.ldb * ES);
-    FragReader<ES, A_MC> fa;
-    FragReader<ES, B_MC> fb;
+    const int dwave = wave % NDW;                 // index among the loading waves
+    const bool loads = wave >= NW - NDW;          // wave-uniform
+    DmaLoader<ES, A_MC, NDW> la;
+    DmaLoader<ES, B_MC, NDW> lb;
+    la.init(dwave, lane, args.lda * ES);
+    lb.init(dwave, lane, args.ldb * ES);
+    FragReader<ES, A_MC, FM> fa;
+    FragReader<ES, B_MC, FN> fb;
     fa.init(lane, wm * 128);
-    fb.init(lane, wn * 128);
+    fb.init(lane, wn * WTN);
 
     // Buffer resources of tile kt, based at its origin; a tile past the end
     // gets empty ranges (its loads read zeros).
@@ -291,49 +322,60 @@ void gemm_dma_kernel(const GemmArgs args) {
         s.kv = min(BK, k_hi - k0);
         return s;
     };
-    // DMA load number d (0..15) of a tile: 0..7 A, 8..15 B.
+    // DMA load number d (0 .. ND-1) of a tile: A first, then B.
     auto dma = [&](const TileSrc &s, uint32_t stage, int d) {
-        const int u = d & 7;
-        const uint32_t dst = stage + (d >= 8 ? kDmaOpBytes : 0) + (wave * 8 + u) * 1024;
-        if (d < 8) dma16(s.ra, dst, la.offset(u, s.kv));
+        if (!loads) return;
+        const int u = d % LPW;
+        const uint32_t dst = stage + (d >= LPW ? kDmaOpBytes : 0) + (dwave * LPW + u) * 1024;
+        if (d < LPW) dma16(s.ra, dst, la.offset(u, s.kv));
         else dma16(s.rb, dst, lb.offset(u, s.kv));
     };
 
-    Acc acc[8][8];
+    Acc acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+        for (int j = 0; j < FN; ++j) acc[i][j] = Acc{0, 0, 0, 0};
 
-    u32x4 a0[8], b0[8], a1[8], b1[8];
+    u32x4 a0[FM], b0[FN], a1[FM], b1[FN];
 
-    // fragment read number r (0..15) of sub-step ks: 0..7 B blocks, then A
-    auto read = [&](uint32_t stage, int ks, int r, u32x4 (&af)[8], u32x4 (&bf)[8]) {
-        if (r < 8) fb.read(stage + kDmaOpBytes, ks, r, bf[r]);
-        else fa.read(stage, ks, r - 8, af[r - 8]);
+    // fragment read number r (0 .. NR-1) of sub-step ks: B blocks, then A
+    auto read = [&](uint32_t stage, int ks, int r, u32x4 (&af)[FM], u32x4 (&bf)[FN]) {
+        if (r < FN) fb.read(stage + kDmaOpBytes, ks, r, bf[r]);
+        else fa.read(stage, ks, r - FN, af[r - FN]);
     };
 
-    // Sub-step 0 of the tile in `cur`: MFMAs on (a0, b0); one fragment read
-    // of sub-step 1 after every 4th MFMA.
+    // Sub-step 0 of the tile in `cur`: MFMAs on (a0, b0) and the reads of
+    // sub-step 1.
     auto sub0 = [&](uint32_t cur) {
 #pragma unroll
-        for (int q = 0; q < 64; ++q) {
-            Mma::run(acc[q >> 3][q & 7], b0[q & 7], a0[q >> 3]);
-            if ((q & 3) == 0) read(cur, 1, q >> 2, a1, b1);
+        for (int q = 0; q < QN; ++q) {
+            Mma::run(acc[q / FN][q % FN], b0[q % FN], a0[q / FN]);
+#pragma unroll
+            for (int r = op_begin(q, NR, QN); r < op_begin(q + 1, NR, QN); ++r)
+                read(cur, 1, r, a1, b1);
         }
     };
-    // Sub-step 1: MFMAs on (a1, b1); after every 2nd MFMA one of: a DMA load
-    // of tile kt+2 into `cur`, a fragment read of the next tile.  Past the
-    // last tile the loads are empty (zero-fill a stage nobody reads) and the
-    // reads return stale data nobody uses, so the loop body has no branch.
+    // Sub-step 1: MFMAs on (a1, b1); the loads of tile kt+2 into `cur` and
+    // the reads of the next tile's sub-step 0, alternating.  Past the last
+    // tile the loads are empty (zero-fill a stage nobody reads) and the reads
+    // return stale data nobody uses, so the loop body has no branch.
     auto sub1 = [&](uint32_t cur, uint32_t nxt, const TileSrc &s) {
 #pragma unroll
-        for (int q = 0; q < 64; ++q) {
-            Mma::run(acc[q >> 3][q & 7], b1[q & 7], a1[q >> 3]);
-            if ((q & 1) == 0) {
-                const int r = q >> 1;
-                if ((r & 1) == 0) dma(s, cur, r >> 1);
-                else read(nxt, 0, r >> 1, a0, b0);
+        for (int q = 0; q < QN; ++q) {
+            Mma::run(acc[q / FN][q % FN], b1[q % FN], a1[q / FN]);
+#pragma unroll
+            for (int o = op_begin(q, ND + NR, QN); o < op_begin(q + 1, ND + NR, QN); ++o) {
+                // o -> (load or read, index): alternate while both remain
+                const int pair = 2 * (ND < NR ? ND : NR);
+                if (o < pair) {
+                    if ((o & 1) == 0) dma(s, cur, o >> 1);
+                    else read(nxt, 0, o >> 1, a0, b0);
+                } else if (ND > NR) {
+                    dma(s, cur, o - pair + NR);
+                } else {
+                    read(nxt, 0, o - pair + ND, a0, b0);
+                }
             }
         }
     };
@@ -343,13 +385,15 @@ void gemm_dma_kernel(const GemmArgs args) {
             const TileSrc s0 = tile_src(0);
             const TileSrc s1 = tile_src(1);
 #pragma unroll
-            for (int d = 0; d < 16; ++d) dma(s0, lds, d);
+            for (int d = 0; d < ND; ++d) dma(s0, lds, d);
 #pragma unroll
-            for (int d = 0; d < 16; ++d) dma(s1, lds + kDmaStageBytes, d);
+            for (int d = 0; d < ND; ++d) dma(s1, lds + kDmaStageBytes, d);
         }
-        wait_all_barrier();
+        // tile 0 landed (tile 1 may still be in flight: the first loop
+        // barrier waits for it); the waves without loads have none in flight
+        wait_barrier_vm<ND>();
 #pragma unroll
-        for (int r = 0; r < 16; ++r) read(lds, 0, r, a0, b0);
+        for (int r = 0; r < NR; ++r) read(lds, 0, r, a0, b0);
         for (int kt = 0; kt < nkt; ++kt) {
             const uint32_t cur = lds + (kt & 1) * kDmaStageBytes;
             const uint32_t nxt = lds + ((kt + 1) & 1) * kDmaStageBytes;
@@ -363,13 +407,13 @@ void gemm_dma_kernel(const GemmArgs args) {
                          "memory");
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
+        for (int j = 0; j < FN; ++j) asm volatile("" : "+a"(acc[i][j]));
 
     // ---- epilogue: lane holds C[m][n .. n+3] of each 16x16 block
     const int ml0 = wm * 128 + (lane & 15);
-    const int nl0 = wn * 128 + 4 * (lane >> 4);
+    const int nl0 = wn * WTN + 4 * (lane >> 4);
     constexpr int CES = dt_size(OUT);
     const int64_t c_org = ((int64_t)m0 * args.ldc + n0) * CES;
     char *Cb = static_cast<char *>(args.C) + z * args.stride_c * CES + c_org;
@@ -378,11 +422,11 @@ void gemm_dma_kernel(const GemmArgs args) {
     const int ldc = args.ldc;
     const float alpha = args.alpha, beta = args.beta;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < FM; ++i) {
         const int ml = ml0 + i * 16;
         if (m0 + ml >= M) continue;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < FN; ++j) {
             const int nl = nl0 + j * 16;
             const int nvalid = N - (n0 + nl);
             if (nvalid <= 0) continue;

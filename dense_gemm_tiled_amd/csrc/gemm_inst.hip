@@ -16,7 +16,8 @@ namespace {
 // class the planner splits; the direct-to-LDS class only for 16-bit and int8
 // inputs.
 constexpr bool out_ok(int cls, int out) {
-    if (cls == TILE_256_DMA && (TCG_DT == DT_F32 || out == OUT_PARTIAL)) return false;
+    if ((cls == TILE_256_DMA || cls == TILE_256_DMA8) && (TCG_DT == DT_F32 || out == OUT_PARTIAL))
+        return false;
     if (out == OUT_PARTIAL) return cls == TILE_64;
     if (TCG_DT == DT_I8) return out == DT_I32;
     if (TCG_DT == DT_F32) return out == DT_F32;
@@ -25,11 +26,12 @@ constexpr bool out_ok(int cls, int out) {
 
 template <int CLS, int OUT>
 hipError_t launch_one(const GemmArgs &args, int64_t grid, hipStream_t stream) {
-    if constexpr (CLS == TILE_256_DMA && out_ok(CLS, OUT)) {
-        hipLaunchKernelGGL((gemm_dma_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, OUT>),
-                           dim3((unsigned)grid), dim3(256), 0, stream, args);
+    if constexpr ((CLS == TILE_256_DMA || CLS == TILE_256_DMA8) && out_ok(CLS, OUT)) {
+        constexpr int NW = CLS == TILE_256_DMA8 ? 8 : 4;
+        hipLaunchKernelGGL((gemm_dma_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, OUT, NW>),
+                           dim3((unsigned)grid), dim3(NW * 64), 0, stream, args);
         return hipGetLastError();
-    } else if constexpr (CLS != TILE_256_DMA && out_ok(CLS, OUT)) {
+    } else if constexpr (CLS != TILE_256_DMA && CLS != TILE_256_DMA8 && out_ok(CLS, OUT)) {
         hipLaunchKernelGGL((gemm_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, CLS, OUT>),
                            dim3((unsigned)grid), dim3(256), 0, stream, args);
         return hipGetLastError();
@@ -61,6 +63,7 @@ hipError_t TCG_LAUNCHER(int cls, int out, const tcg::GemmArgs &args, int64_t gri
     case TILE_128: return launch_cls<TILE_128>(out, args, grid, stream);
     case TILE_64: return launch_cls<TILE_64>(out, args, grid, stream);
     case TILE_256_DMA: return launch_cls<TILE_256_DMA>(out, args, grid, stream);
+    case TILE_256_DMA8: return launch_cls<TILE_256_DMA8>(out, args, grid, stream);
     default: return hipErrorInvalidValue;
     }
 }

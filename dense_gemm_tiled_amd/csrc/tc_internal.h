@@ -18,21 +18,25 @@ __host__ __device__ constexpr int dt_size(int dt) {
 // bytes of K (64 bf16/f16, 128 int8, 32 f32), so the swizzle and the MFMA
 // fragment reads are the same for every element type.  TILE_256_DMA is the
 // 256x256 tile of gemm_dma_kernel (direct-to-LDS loads; 16-bit and int8
-// inputs with 16-byte aligned rows).
+// inputs with 16-byte aligned rows) with 4 waves of 128x128, TILE_256_DMA8
+// the same with 8 waves of 128x64 (two per SIMD).
 enum TileClass : int {
     TILE_256 = 0,
     TILE_128 = 1,
     TILE_64 = 2,
     TILE_256_DMA = 3,
-    NUM_TILE_CLASSES = 4
+    TILE_256_DMA8 = 4,
+    NUM_TILE_CLASSES = 5
 };
+
+__host__ __device__ constexpr int tile_threads(int cls) { return cls == TILE_256_DMA8 ? 512 : 256; }
 
 struct TileShape {
     int bm, bn, wm, wn;   // tile rows/cols, waves along m/n (4 waves = 256 threads)
 };
 
 __host__ __device__ constexpr TileShape tile_shape(int cls) {
-    return (cls == TILE_256 || cls == TILE_256_DMA) ? TileShape{256, 256, 2, 2}
+    return (cls == TILE_256 || cls == TILE_256_DMA || cls == TILE_256_DMA8) ? TileShape{256, 256, 2, 2}
          : cls == TILE_128                          ? TileShape{128, 128, 2, 2}
                                                     : TileShape{64, 64, 2, 2};
 }

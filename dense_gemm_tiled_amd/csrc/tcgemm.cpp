@@ -213,7 +213,7 @@ bool dma_ok(const Problem &p) {
 // it (dma_ok; the base pointers' alignment is checked at launch time).
 //
 // Tuning overrides (environment, read at every call; unset in normal use):
-// TCGEMM_TILE=dma|256|128|64 forces a tile class (dma only where allowed),
+// TCGEMM_TILE=dma|dma8|256|128|64 forces a tile class (dma only where allowed),
 // TCGEMM_SPLITS=S forces split-K with S slices (on the 64x64 class, the one
 // with a partial-sum output), TCGEMM_BAND=h sets the band height of the tile
 // order (0: row-major).
@@ -231,6 +231,7 @@ void make_plan(const Problem &p, Plan *pl) {
     if (const char *env = getenv("TCGEMM_TILE")) {
         const int v = atoi(env);
         if (strcmp(env, "dma") == 0) cls = dma_ok(p) ? TILE_256_DMA : cls;
+        else if (strcmp(env, "dma8") == 0) cls = dma_ok(p) ? TILE_256_DMA8 : cls;
         else cls = v == 256 ? TILE_256 : v == 128 ? TILE_128 : v == 64 ? TILE_64 : cls;
     }
     if (const char *env = getenv("TCGEMM_SPLITS")) {
@@ -279,7 +280,7 @@ void fill_info(const Problem &p, const Plan &pl, tc_plan_info *info) {
              pl.splits > 1 ? "+splitk_reduce" : "");
     if (p.alpha == 0.0f) snprintf(info->kernel, sizeof info->kernel, "scale_c");
     info->tile_m = pl.bm; info->tile_n = pl.bn; info->tile_k = pl.bk;
-    info->threads = 256;
+    info->threads = tile_threads(pl.cls);
     info->tiles_m = pl.tiles_m; info->tiles_n = pl.tiles_n;
     info->splits = pl.splits; info->k_per_split = pl.k_per_split;
     info->grid = p.alpha == 0.0f ? 0 : pl.grid;
@@ -380,7 +381,8 @@ tc_status_t run(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A, 
         return fail(err, TC_ERR_ALIASING, "C overlaps A or B");
     Plan pl;
     make_plan(p, &pl);
-    if (pl.cls == TILE_256_DMA && ((uintptr_t)A % 16 != 0 || (uintptr_t)B % 16 != 0))
+    if ((pl.cls == TILE_256_DMA || pl.cls == TILE_256_DMA8) &&
+        ((uintptr_t)A % 16 != 0 || (uintptr_t)B % 16 != 0))
         pl.cls = TILE_256;   // same tile, register-staged loads
 
     st = bind_device(ctx);

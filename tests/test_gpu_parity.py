@@ -87,18 +87,22 @@ def test_padded_leading_dims(a, c):
 DMA_PAIRS = [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32"), ("i8", "i32")]
 
 
-def dma_check(p, label):
-    """Run p with the direct-to-LDS 256x256 kernel forced and check that it
-    is the kernel that ran."""
+DMA_TILES = ["dma", "dma8"]
+
+
+def dma_check(p, label, tile):
+    """Run p with a direct-to-LDS 256x256 kernel (4 or 8 waves) forced and
+    check that it is the kernel that ran."""
     import dense_gemm_tiled_amd as tg
-    res = check(p, label, TCGEMM_TILE="dma")
-    assert tg.last_kernel().endswith("_256x256_dma"), tg.last_kernel()
+    res = check(p, label, TCGEMM_TILE=tile)
+    assert tg.last_kernel().endswith("_256x256_" + tile), tg.last_kernel()
     return res
 
 
+@pytest.mark.parametrize("tile", DMA_TILES)
 @pytest.mark.parametrize("ta,tb", LAYOUTS, ids=[lay(*l) for l in LAYOUTS])
 @pytest.mark.parametrize("a,c", DMA_PAIRS, ids=["%s-%s" % pc for pc in DMA_PAIRS])
-def test_dma_kernel_ragged(a, c, ta, tb):
+def test_dma_kernel_ragged(a, c, ta, tb, tile):
     """2 x 2 tiles ragged in M and N, a K tail shorter than the 128-byte tile
     (whole 16-byte chunks), alpha = 0.5 and beta = 1 for floats.  M and N are
     multiples of 16 bytes so that M/N-contiguous rows stay aligned."""
@@ -106,23 +110,25 @@ def test_dma_kernel_ragged(a, c, ta, tb):
         p = problem(a, c, 304, 272, 208, ta, tb)
     else:
         p = problem(a, c, 296, 264, 200, ta, tb)
-    dma_check(p, "dma ragged")
+    dma_check(p, "dma ragged", tile)
 
 
+@pytest.mark.parametrize("tile", DMA_TILES)
 @pytest.mark.parametrize("a,c", DMA_PAIRS, ids=["%s-%s" % pc for pc in DMA_PAIRS])
-def test_dma_kernel_short_k_and_nan_c(a, c):
+def test_dma_kernel_short_k_and_nan_c(a, c, tile):
     """K below one tile (one partial tile plus an empty prefetch), and beta = 0
     with a NaN-filled C: C must not be read."""
     k = 16 if a == "i8" else 8
     p = problem(a, c, 272, 528, k, False, False, alpha=1.0, beta=0.0, c_dist="nan")
-    dma_check(p, "dma shortK")
+    dma_check(p, "dma shortK", tile)
     p = problem(a, c, 512, 256, 3 * k, True, False, alpha=1.0, beta=0.0, c_dist="nan")
-    dma_check(p, "dma shortK TN")
+    dma_check(p, "dma shortK TN", tile)
 
 
+@pytest.mark.parametrize("tile", DMA_TILES)
 @pytest.mark.parametrize("a,c,ta,tb", [("bf16", "f32", True, False), ("f16", "f16", False, True),
                                        ("i8", "i32", False, False)])
-def test_dma_kernel_batched_padded(a, c, ta, tb):
+def test_dma_kernel_batched_padded(a, c, ta, tb, tile):
     """Batched problems with padded leading dims (kept 16-byte multiples)."""
     es = 1 if a == "i8" else 2
     pad = 16 // es
@@ -130,20 +136,21 @@ def test_dma_kernel_batched_padded(a, c, ta, tb):
     lda = (M + 4 if ta else K) + pad
     ldb = (K if tb else N) + 2 * pad
     p = problem(a, c, M, N, K, ta, tb, batch=3, lda=lda, ldb=ldb, ldc=N + 3)
-    dma_check(p, "dma batched")
+    dma_check(p, "dma batched", tile)
 
 
+@pytest.mark.parametrize("tile", DMA_TILES)
 @pytest.mark.parametrize("a,c", [("bf16", "f32"), ("f16", "f16")])
-def test_dma_kernel_exact_regime_bitwise(a, c):
+def test_dma_kernel_exact_regime_bitwise(a, c, tile):
     """Integer inputs in [-4, 4]: exact accumulation, bit-equal to the oracle."""
     p = problem(a, c, 512, 512, 1024, False, False, alpha=1.0, beta=0.0, dist="small_int",
                 scale=4.0, c_dist="zeros")
     A, B, C = workloads.make_inputs(p)
     say("GPU case: dma exact", a, c)
-    with env(TCGEMM_TILE="dma"):
+    with env(TCGEMM_TILE=tile):
         got = run_library(p, A, B, C)
     import dense_gemm_tiled_amd as tg
-    assert tg.last_kernel().endswith("_dma")
+    assert tg.last_kernel().endswith("_" + tile)
     ref = oracle_full(p, A, B, C)
     assert np.array_equal(got.view(np.uint8), ref.view(np.uint8))
 
