@@ -178,10 +178,14 @@ struct DmaLoader {
             kfirst[s] = (col_of(row_of(wave, lane, s), lane % LPR) >> 4) * (16 / ES);
     }
 
-    // Byte offset of load u for a tile with k_valid valid k (<= tile depth);
-    // chunks past K get an offset outside the buffer, which loads zeros.
+    // Byte offset of load u for a tile with k_valid valid k (<= tile depth).
+    // KMASK: chunks past K get an offset outside the buffer, which loads
+    // zeros; without it (K a whole number of tiles) every tile the loop reads
+    // is full, and a tile past the end has an empty buffer range anyway.
+    template <bool KMASK>
     __device__ inline int offset(int u, int k_valid) const {
         const int off = lane_off[(u & 1) | ((u >> 2) << 1)] + u * RPI * ld_bytes;
+        if constexpr (!KMASK) return off;
         const bool in = MC ? (row0 < k_valid - u * RPI) : (kfirst[u & 1] < k_valid);
         return in ? off : kOobOffset;
     }
@@ -250,7 +254,7 @@ struct FragReader {
 // op_begin(q) .. op_begin(q + 1) - 1.
 constexpr int op_begin(int q, int n, int qn) { return (q * n + qn - 1) / qn; }
 
-template <int DT, bool TA, bool TB, int OUT, int NW>
+template <int DT, bool TA, bool TB, int OUT, int NW, bool KMASK>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void gemm_dma_kernel(const GemmArgs args) {
@@ -327,8 +331,8 @@ void gemm_dma_kernel(const GemmArgs args) {
         if (!loads) return;
         const int u = d % LPW;
         const uint32_t dst = stage + (d >= LPW ? kDmaOpBytes : 0) + (dwave * LPW + u) * 1024;
-        if (d < LPW) dma16(s.ra, dst, la.offset(u, s.kv));
-        else dma16(s.rb, dst, lb.offset(u, s.kv));
+        if (d < LPW) dma16(s.ra, dst, la.template offset<KMASK>(u, s.kv));
+        else dma16(s.rb, dst, lb.template offset<KMASK>(u, s.kv));
     };
 
     Acc acc[FM][FN];

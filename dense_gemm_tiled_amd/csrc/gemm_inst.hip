@@ -27,9 +27,16 @@ constexpr bool out_ok(int cls, int out) {
 template <int CLS, int OUT>
 hipError_t launch_one(const GemmArgs &args, int64_t grid, hipStream_t stream) {
     if constexpr ((CLS == TILE_256_DMA || CLS == TILE_256_DMA8) && out_ok(CLS, OUT)) {
+        // the K tail needs per-chunk masks only when K is not a whole number
+        // of 128-byte tiles (split-K slices are whole tiles)
         constexpr int NW = CLS == TILE_256_DMA8 ? 8 : 4;
-        hipLaunchKernelGGL((gemm_dma_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, OUT, NW>),
-                           dim3((unsigned)grid), dim3(NW * 64), 0, stream, args);
+        constexpr int BK = kLdsRowBytes / dt_size(TCG_DT);
+        if (args.K % BK != 0)
+            hipLaunchKernelGGL((gemm_dma_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, OUT, NW, true>),
+                               dim3((unsigned)grid), dim3(NW * 64), 0, stream, args);
+        else
+            hipLaunchKernelGGL((gemm_dma_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, OUT, NW, false>),
+                               dim3((unsigned)grid), dim3(NW * 64), 0, stream, args);
         return hipGetLastError();
     } else if constexpr (CLS != TILE_256_DMA && CLS != TILE_256_DMA8 && out_ok(CLS, OUT)) {
         hipLaunchKernelGGL((gemm_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, CLS, OUT>),
