@@ -70,7 +70,7 @@ class BatchedDescT(ctypes.Structure):
 
 class PlanInfoT(ctypes.Structure):
     """tc_plan_info"""
-    _fields_ = [("kernel", ctypes.c_char * 96),
+    _fields_ = [("kernel", ctypes.c_char * 128),
                 ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
                 ("tile_k", ctypes.c_int32), ("threads", ctypes.c_int32),
                 ("tiles_m", ctypes.c_int32), ("tiles_n", ctypes.c_int32),

@@ -40,7 +40,23 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const EpilogueArgs a
         return;
     }
     float s4[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < a.splits; ++s) {
+    int s = 0;
+    if (wvec && nvalid >= 4) {
+        // groups of 8 slices: the 8 loads are in flight together, the adds
+        // still run in ascending s
+        const int plane_b = (int)(plane * 4);
+        const int off0 = (int)(((int64_t)m * a.N + n) * 4);
+        for (; s + 8 <= a.splits; s += 8) {
+            u32x4 w[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) w[u] = ld128(rw, off0 + (s + u) * plane_b);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s4[e] += as_f32(w[u][e]);
+        }
+    }
+    for (; s < a.splits; ++s) {
         const int off = (int)((s * plane + (int64_t)m * a.N + n) * 4);
         if (wvec && nvalid >= 4) {
             u32x4 w = ld128(rw, off);
@@ -88,6 +104,30 @@ __global__ __launch_bounds__(256) void scale_c_kernel(const EpilogueArgs a) {
     }
 }
 
+// Operand repacking into 16-byte row pitches, so that an operand whose rows
+// do not start on 16-byte boundaries (or whose rows end inside a 16-byte
+// chunk) can feed the direct-to-LDS GEMM kernel.  One wave per row (the
+// buffer resource of the source row is then wave-uniform), four rows per
+// workgroup; each lane moves 16 bytes at a time.  The source may sit at any
+// byte address: buffer loads of 16 bytes take unaligned offsets, and the
+// last partial chunk of a row is read byte by byte, the rest of it zero.
+__global__ __launch_bounds__(256) void pack_rows_kernel(const PackArgs a) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (row >= (int64_t)a.batch * a.rows) return;
+    const int z = (int)(row / a.rows), r = (int)(row % a.rows);
+    const char *src = static_cast<const char *>(a.src) + z * a.src_stride + r * a.src_pitch;
+    char *dst = static_cast<char *>(a.dst) + z * a.dst_stride + r * a.dst_pitch;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, a.row_bytes);
+    const int chunks = (int)(a.dst_pitch / 16);
+    for (int c = threadIdx.x & 63; c < chunks; c += 64) {
+        const int nb = a.row_bytes - 16 * c;
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (nb >= 16) v = ld128(rs, 16 * c);
+        else if (nb > 0) v = ld_partial<1>(rs, 16 * c, nb);
+        *reinterpret_cast<u32x4 *>(dst + 16 * c) = v;
+    }
+}
+
 using Launcher = hipError_t (*)(int, int, const GemmArgs &, int64_t, hipStream_t);
 
 // [input type][transpose_a * 2 + transpose_b]
@@ -100,7 +140,7 @@ const Launcher kLaunchers[4][4] = {
 const char *const kDtName[4] = {"f32", "f16", "bf16", "i8"};
 const char *const kLayoutName[2][2] = {{"nn", "nt"}, {"tn", "tt"}};
 const char *const kTileName[NUM_TILE_CLASSES] = {"256x256", "128x128", "64x64",
-                                                   "256x256_dma", "256x256_dma8"};
+                                                   "256x256_dma", "256x256_dma8", "128x128_dma"};
 
 char g_names[4][2][2][NUM_TILE_CLASSES][64];
 bool g_names_ready = false;
@@ -115,6 +155,15 @@ hipError_t tcg_launch_gemm(int dt, bool ta, bool tb, int cls, int out, const Gem
     if (dt < 0 || dt > 3 || cls < 0 || cls >= NUM_TILE_CLASSES || grid <= 0 || grid > 0x7FFFFFFF)
         return hipErrorInvalidValue;
     return kLaunchers[dt][(ta ? 2 : 0) + (tb ? 1 : 0)](cls, out, args, grid, stream);
+}
+
+hipError_t tcg_launch_pack_rows(const PackArgs &args, hipStream_t stream) {
+    const int64_t blocks = ((int64_t)args.batch * args.rows + 3) / 4;
+    if (blocks <= 0 || blocks > 0x7FFFFFFF || args.dst_pitch % 16 != 0 ||
+        args.dst_pitch < args.row_bytes)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, args);
+    return hipGetLastError();
 }
 
 hipError_t tcg_launch_splitk_reduce(const EpilogueArgs &args, hipStream_t stream) {

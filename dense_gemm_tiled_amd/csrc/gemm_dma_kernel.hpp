@@ -1,21 +1,23 @@
-// gemm_dma_kernel.hpp -- the 256x256 GEMM kernel for gfx950 whose operand
-// tiles go from HBM straight into LDS (buffer loads with the LDS flag), for
-// 16-bit and int8 inputs whose rows start on 16-byte boundaries.
+// gemm_dma_kernel.hpp -- the GEMM kernel for gfx950 whose operand tiles go
+// from HBM straight into LDS (buffer loads with the LDS flag), for 16-bit and
+// int8 inputs whose rows start on 16-byte boundaries.
 //
 // Same computation and epilogue as gemm_kernel (C = alpha*op(A)op(B) +
-// beta*C, accumulator in registers for the whole K loop, C written once;
-// tessl "Architecture", "Cooperative Destination Accumulation"), with a
-// schedule built for one workgroup per CU:
+// beta*C, accumulator in registers for the whole K loop of a slice, C or the
+// slice's partial sums written once; tessl "Architecture", "Cooperative
+// Destination Accumulation"), with a static schedule.  Tile shapes:
 //
-//   * 256 threads = 4 wave64s in a 2 x 2 grid, each wave owns 128 x 128 of C
-//     as 8 x 8 blocks of 16 x 16 MFMA accumulators (256 fp32/int32 AGPRs per
-//     lane);
-//   * per K-tile (128 bytes of K: 64 bf16/f16 or 128 int8) every wave issues
-//     16 direct-to-LDS loads of 1 KiB; two LDS stages of 64 KiB hold tile t
-//     and tile t+1;
-//   * the MFMAs of a K-tile run in two sub-steps of 64.  While one sub-step
-//     runs, the fragments of the next are read from LDS into a second
-//     register set, one read between every few MFMAs;
+//   256 x 256, 4 waves of 128 x 128 (256 AGPRs per lane), one workgroup per
+//     CU; or 8 waves of 128 x 64, two per SIMD;
+//   128 x 128, 4 waves of 64 x 64, two workgroups per CU (mid-size outputs
+//     and split-K).
+//
+//   * per K-tile (128 bytes of K: 64 bf16/f16 or 128 int8) the operand tiles
+//     arrive as direct-to-LDS loads of 1 KiB, issued by 4 waves; two LDS
+//     stages hold tile t and tile t+1;
+//   * the MFMAs of a K-tile run in two sub-steps.  While one sub-step runs,
+//     the fragments of the next are read from LDS into a second register
+//     set, one read between every few MFMAs;
 //   * one barrier per K-tile, between the sub-steps: after it, tile t+1 is
 //     visible to every wave and the stage of tile t is free, so the loads of
 //     tile t+2 are issued into it during the second sub-step;
@@ -34,14 +36,17 @@
 // barrier and at the end of the loop, and wait states between the last MFMA
 // and the first read of the accumulators.
 //
-// LDS layouts (bytes; both chosen so that the reads below hit every bank once
-// per 256 bytes and the DMA writes stay contiguous):
-//   K-contiguous tile: 256 rows x 128 B; 16-byte chunk c of row r at
-//     position c ^ ((r & 7) ^ ((r >> 3) & 1)).
-//   M/N-contiguous tile, 16-bit: 64 k-rows x 512 B; 32-byte segment s (16
+// LDS layouts (bytes; chosen so that the reads below hit every bank once per
+// 256 bytes and the DMA writes stay contiguous).  R is the tile extent along
+// M (A) or N (B):
+//   K-contiguous tile: R rows x 128 B; 16-byte chunk c of row r at position
+//     c ^ ((r & 7) ^ ((r >> 3) & 1)).
+//   M/N-contiguous tile, 16-bit: 64 k-rows x 2R B; 32-byte segment s (16
 //     columns) of row k at position s ^ ((k & 3) | ((k >> 3) & 1) << 2).
-//   M/N-contiguous tile, int8: 128 k-rows x 256 B; 16-byte segment s of row
-//     k at position s ^ ((k & 7) | ((k >> 4) & 1) << 3).
+//   M/N-contiguous tile, int8, R = 256: 128 k-rows x 256 B; 16-byte segment s
+//     of row k at position s ^ ((k & 7) | ((k >> 4) & 1) << 3); R = 128:
+//     128 k-rows x 128 B, segment s at s ^ (((k >> 1) & 3) | ((k >> 4) & 1) << 2)
+//     (two rows share 256 bytes of banks, so the row parity picks the half).
 //
 // Ragged edges (tessl "Architecture", "Edge-Slice Support"): rows past M or
 // N only feed outputs that are never stored, and buffer range checks return
@@ -59,19 +64,44 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 #define TCG_LDS __attribute__((address_space(3)))
 
-constexpr int kDmaTile = 256;                          // BM = BN
-constexpr int kDmaOpBytes = kDmaTile * kLdsRowBytes;   // 32 KiB per operand tile
-constexpr int kDmaStageBytes = 2 * kDmaOpBytes;        // [A tile | B tile]
 // An offset past every buffer range (ranges are < 2^31 bytes; the offset plus
 // the 16-byte access does not wrap 32 bits): such a load reads zeros.
 constexpr int kOobOffset = INT32_MIN;
 
 __device__ inline int swz_kc(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-template <int ES>
+// M/N-contiguous swizzle for LDS rows of RB bytes (16-bit: 32-byte segments;
+// int8: 16-byte segments).
+template <int ES, int RB>
 __device__ inline int swz_mc(int k) {
     if constexpr (ES == 2) return (k & 3) | (((k >> 3) & 1) << 2);
-    else return (k & 7) | (((k >> 4) & 1) << 3);
+    else if constexpr (RB == 256) return (k & 7) | (((k >> 4) & 1) << 3);
+    else return ((k >> 1) & 3) | (((k >> 4) & 1) << 2);
+}
+
+// The row bits each swizzle reads.
+template <int ES, bool MC, int RB>
+constexpr int swz_bits() {
+    if constexpr (!MC) return 0xF;
+    else if constexpr (ES == 2) return 0xB;
+    else if constexpr (RB == 256) return 0x17;
+    else return 0x16;
+}
+
+constexpr int bit_count(int v) { return v == 0 ? 0 : (v & 1) + bit_count(v >> 1); }
+
+// The bits of u selected by mask, packed to the bottom (and the reverse).
+constexpr int bits_extract(int u, int mask) {
+    int r = 0, o = 0;
+    for (int b = 0; b < 8; ++b)
+        if ((mask >> b) & 1) r |= ((u >> b) & 1) << o++;
+    return r;
+}
+constexpr int bits_deposit(int c, int mask) {
+    int r = 0, o = 0;
+    for (int b = 0; b < 8; ++b)
+        if ((mask >> b) & 1) r |= ((c >> o++) & 1) << b;
+    return r;
 }
 
 // Raw buffer resource as four SGPRs (same fields as make_rsrc).
@@ -136,21 +166,25 @@ struct MmaAsm<DT_I8> {
     }
 };
 
-// One operand's share of the DMA of a tile: LPW = 32 / NW loads of 1 KiB per
-// wave (NW loading waves).  MC: the operand is M/N-contiguous in memory
-// (global row = one k).  Load u of wave w fills tile rows (LPW w + u) * RPI +
-// lane / LPR.  A lane's byte offset is a lane part, which depends on u only
-// through the swizzle (u & 1 and u >> 2), plus u * RPI rows, which is
+// One operand's share of the DMA of a tile of R rows (M or N indices) x 128
+// bytes of K: R / 8 loads of 1 KiB, LPW = R / (8 NDW) per loading wave (NDW
+// loading waves).  MC: the operand is M/N-contiguous in memory (global row =
+// one k).  Load u of wave w fills tile rows (LPW w + u) * RPI + lane / LPR.
+// A lane's byte offset is a lane part, which depends on u only through the
+// swizzle (the u bits in UMASK: NCLS variants), plus u * RPI rows, which is
 // wave-uniform.
-template <int ES, bool MC, int NW>
+template <int ES, bool MC, int R, int NDW>
 struct DmaLoader {
-    static constexpr int RB = MC ? kDmaTile * ES : kLdsRowBytes;   // LDS row bytes
+    static constexpr int RB = MC ? R * ES : kLdsRowBytes;          // LDS row bytes
     static constexpr int LPR = RB / 16;                            // lanes per row
     static constexpr int RPI = 64 / LPR;                           // rows per load
-    static constexpr int LPW = 32 / NW;                            // loads per wave
-    int lane_off[4];  // [(u & 1) | (u >> 2) << 1]: lane part of the byte offset
-    int row0;         // MC: tile row (k) of this lane for u = 0
-    int kfirst[2];    // KC: first k (elements) of this lane's chunk, [u & 1]
+    static constexpr int LPW = R / 8 / NDW;                        // loads per wave
+    static_assert(LPW >= 2 && (LPW & (LPW - 1)) == 0, "loads per wave: a power of two");
+    static constexpr int UMASK = (swz_bits<ES, MC, RB>() / RPI) & (LPW - 1);
+    static constexpr int NCLS = 1 << bit_count(UMASK);
+    int lane_off[NCLS];  // [bits_extract(u, UMASK)]: lane part of the byte offset
+    int row0;            // MC: tile row (k) of this lane for u = 0
+    int kfirst[NCLS];    // KC: first k (elements) of this lane's chunk
     int ld_bytes;
 
     __device__ static inline int row_of(int wave, int lane, int u) {
@@ -158,8 +192,8 @@ struct DmaLoader {
     }
     __device__ static inline int col_of(int r, int q) {
         if constexpr (MC) {
-            if constexpr (ES == 2) return (((q >> 1) ^ swz_mc<2>(r)) << 5) + ((q & 1) << 4);
-            else return (q ^ swz_mc<1>(r)) << 4;
+            if constexpr (ES == 2) return (((q >> 1) ^ swz_mc<2, RB>(r)) << 5) + ((q & 1) << 4);
+            else return (q ^ swz_mc<1, RB>(r)) << 4;
         } else {
             return (q ^ swz_kc(r)) << 4;
         }
@@ -169,13 +203,11 @@ struct DmaLoader {
         ld_bytes = ldb;
         row0 = row_of(wave, lane, 0);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int u = (s & 1) | ((s >> 1) << 2);
-            lane_off[s] = row0 * ldb + col_of(row_of(wave, lane, u), lane % LPR);
+        for (int c = 0; c < NCLS; ++c) {
+            const int r = row_of(wave, lane, bits_deposit(c, UMASK));
+            lane_off[c] = row0 * ldb + col_of(r, lane % LPR);
+            kfirst[c] = (col_of(r, lane % LPR) >> 4) * (16 / ES);
         }
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-            kfirst[s] = (col_of(row_of(wave, lane, s), lane % LPR) >> 4) * (16 / ES);
     }
 
     // Byte offset of load u for a tile with k_valid valid k (<= tile depth).
@@ -184,21 +216,23 @@ struct DmaLoader {
     // is full, and a tile past the end has an empty buffer range anyway.
     template <bool KMASK>
     __device__ inline int offset(int u, int k_valid) const {
-        const int off = lane_off[(u & 1) | ((u >> 2) << 1)] + u * RPI * ld_bytes;
+        const int c = bits_extract(u, UMASK);
+        const int off = lane_off[c] + u * RPI * ld_bytes;
         if constexpr (!KMASK) return off;
-        const bool in = MC ? (row0 < k_valid - u * RPI) : (kfirst[u & 1] < k_valid);
+        const bool in = MC ? (row0 < k_valid - u * RPI) : (kfirst[c] < k_valid);
         return in ? off : kOobOffset;
     }
 };
 
 // LDS fragment reads.  KC: ds_read_b128 of a K-contiguous tile; MC: two
-// transposing reads of an M/N-contiguous tile.  Both give lane l the K-run
-// {8*(l/16) .. +7} (16-bit) or {16*(l/16) .. +15} (int8) of sub-step ks for
-// row/column (l % 16) of 16-block i -- the operand layout of the
-// 16x16x32 (16-bit) and 16x16x64 (int8) MFMAs.  NB: 16-blocks per wave.
-template <int ES, bool MC, int NB>
+// transposing reads of an M/N-contiguous tile of extent R.  Both give lane l
+// the K-run {8*(l/16) .. +7} (16-bit) or {16*(l/16) .. +15} (int8) of
+// sub-step ks for row/column (l % 16) of 16-block i -- the operand layout of
+// the 16x16x32 (16-bit) and 16x16x64 (int8) MFMAs.  NB: 16-blocks per wave.
+template <int ES, bool MC, int R, int NB>
 struct FragReader {
-    int base[MC ? NB : 2];   // lane byte offsets inside an operand tile
+    static constexpr int RB = R * ES;   // MC: LDS row bytes
+    int base[MC ? NB : 2];              // lane byte offsets inside an operand tile
 
     __device__ inline void init(int lane, int blk0) {
         const int l16 = lane & 15, g = lane >> 4;
@@ -208,10 +242,10 @@ struct FragReader {
                 const int seg = blk0 / 16 + j;
                 if constexpr (ES == 2) {
                     const int k = 8 * g + (l16 >> 2);
-                    base[j] = k * 512 + ((seg ^ swz_mc<2>(k)) << 5) + ((lane & 3) << 3);
+                    base[j] = k * RB + ((seg ^ swz_mc<2, RB>(k)) << 5) + ((lane & 3) << 3);
                 } else {
                     const int k = 16 * g + (l16 >> 1);
-                    base[j] = k * 256 + ((seg ^ swz_mc<1>(k)) << 4) + ((lane & 1) << 3);
+                    base[j] = k * RB + ((seg ^ swz_mc<1, RB>(k)) << 4) + ((lane & 1) << 3);
                 }
             }
         } else {
@@ -225,8 +259,7 @@ struct FragReader {
     __device__ inline void read(uint32_t tile, int ks, int i, u32x4 &out) const {
         if constexpr (MC) {
             // rows advance by 32 (16-bit) / 64 (int8) per sub-step, by 4 / 8
-            // for the second half of the K-run
-            constexpr int RB = kDmaTile * ES;
+            // for the second half of the K-run (the swizzles read neither bit)
             constexpr int KS_ROWS = ES == 2 ? 32 : 64, H_ROWS = ES == 2 ? 4 : 8;
             const uint32_t p = tile + base[i] + ks * KS_ROWS * RB;
             i32x2 lo, hi;
@@ -254,30 +287,35 @@ struct FragReader {
 // op_begin(q) .. op_begin(q + 1) - 1.
 constexpr int op_begin(int q, int n, int qn) { return (q * n + qn - 1) / qn; }
 
-template <int DT, bool TA, bool TB, int OUT, int NW, bool KMASK>
+// BM x BN tile, NW waves (2 along M, NW/2 along N), OCC workgroups per CU.
+template <int DT, bool TA, bool TB, int OUT, int BM, int BN, int NW, int OCC, bool KMASK>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
-                          amdgpu_waves_per_eu(NW / 4, NW / 4)))
+                          amdgpu_waves_per_eu(NW / 4 * OCC, NW / 4 * OCC)))
 void gemm_dma_kernel(const GemmArgs args) {
     constexpr int ES = dt_size(DT);
     static_assert(ES == 2 || ES == 1, "direct-to-LDS kernel: 16-bit and int8 inputs");
     static_assert(NW == 4 || NW == 8, "4 or 8 waves");
     constexpr int BK = kLdsRowBytes / ES;
     constexpr bool A_MC = TA, B_MC = !TB;
-    // waves: 2 along M, NW/2 along N; each owns 128 x WTN of C
-    constexpr int WNW = NW / 2, WTN = kDmaTile / WNW;
-    constexpr int FM = 8, FN = WTN / 16;
+    // waves: 2 along M, NW/2 along N; each owns WTM x WTN of C
+    constexpr int WNW = NW / 2, WTM = BM / 2, WTN = BN / WNW;
+    constexpr int FM = WTM / 16, FN = WTN / 16;
     constexpr int QN = FM * FN;         // MFMAs per wave and sub-step
     constexpr int NR = FM + FN;         // fragment reads per sub-step
     // The loads are issued by 4 waves: all of them with 4 waves; with 8, the
     // second four only, so that while a loading wave waits to issue a load
     // the other wave on its SIMD keeps the matrix core busy.
     constexpr int NDW = 4;
-    constexpr int LPW = 32 / NDW;       // loads per loading wave and operand
-    constexpr int ND = 2 * LPW;         // loads per loading wave and tile
+    using LoadA = DmaLoader<ES, A_MC, BM, NDW>;
+    using LoadB = DmaLoader<ES, B_MC, BN, NDW>;
+    constexpr int LPA = LoadA::LPW, LPB = LoadB::LPW;   // loads per loading wave
+    constexpr int ND = LPA + LPB;                       // ... and tile
+    constexpr int A_BYTES = BM * kLdsRowBytes;          // [A tile | B tile]
+    constexpr int STAGE = (BM + BN) * kLdsRowBytes;
     using Mma = MmaAsm<DT>;
     using Acc = typename Mma::Acc;
 
-    __shared__ __attribute__((aligned(1024))) char smem[2 * kDmaStageBytes];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
     const uint32_t lds = (uint32_t)(size_t)(TCG_LDS char *)smem;
 
     const int tid = threadIdx.x;
@@ -289,7 +327,7 @@ void gemm_dma_kernel(const GemmArgs args) {
     tile_of_workgroup(args.tiles_m, args.tiles_n, args.band, blockIdx.x, gridDim.x, &tm, &tn, &g);
     const int z = g / args.splits, sidx = g % args.splits;
     const int M = args.M, N = args.N, K = args.K;
-    const int m0 = tm * kDmaTile, n0 = tn * kDmaTile;
+    const int m0 = tm * BM, n0 = tn * BN;
     const int k_lo = sidx * args.k_per_split;
     const int k_hi = min(K, k_lo + args.k_per_split);
     const int nkt = (k_hi - k_lo + BK - 1) / BK;
@@ -299,13 +337,13 @@ void gemm_dma_kernel(const GemmArgs args) {
 
     const int dwave = wave % NDW;                 // index among the loading waves
     const bool loads = wave >= NW - NDW;          // wave-uniform
-    DmaLoader<ES, A_MC, NDW> la;
-    DmaLoader<ES, B_MC, NDW> lb;
+    LoadA la;
+    LoadB lb;
     la.init(dwave, lane, args.lda * ES);
     lb.init(dwave, lane, args.ldb * ES);
-    FragReader<ES, A_MC, FM> fa;
-    FragReader<ES, B_MC, FN> fb;
-    fa.init(lane, wm * 128);
+    FragReader<ES, A_MC, BM, FM> fa;
+    FragReader<ES, B_MC, BN, FN> fb;
+    fa.init(lane, wm * WTM);
     fb.init(lane, wn * WTN);
 
     // Buffer resources of tile kt, based at its origin; a tile past the end
@@ -329,10 +367,11 @@ void gemm_dma_kernel(const GemmArgs args) {
     // DMA load number d (0 .. ND-1) of a tile: A first, then B.
     auto dma = [&](const TileSrc &s, uint32_t stage, int d) {
         if (!loads) return;
-        const int u = d % LPW;
-        const uint32_t dst = stage + (d >= LPW ? kDmaOpBytes : 0) + (dwave * LPW + u) * 1024;
-        if (d < LPW) dma16(s.ra, dst, la.template offset<KMASK>(u, s.kv));
-        else dma16(s.rb, dst, lb.template offset<KMASK>(u, s.kv));
+        if (d < LPA)
+            dma16(s.ra, stage + (dwave * LPA + d) * 1024, la.template offset<KMASK>(d, s.kv));
+        else
+            dma16(s.rb, stage + A_BYTES + (dwave * LPB + d - LPA) * 1024,
+                  lb.template offset<KMASK>(d - LPA, s.kv));
     };
 
     Acc acc[FM][FN];
@@ -345,7 +384,7 @@ void gemm_dma_kernel(const GemmArgs args) {
 
     // fragment read number r (0 .. NR-1) of sub-step ks: B blocks, then A
     auto read = [&](uint32_t stage, int ks, int r, u32x4 (&af)[FM], u32x4 (&bf)[FN]) {
-        if (r < FN) fb.read(stage + kDmaOpBytes, ks, r, bf[r]);
+        if (r < FN) fb.read(stage + A_BYTES, ks, r, bf[r]);
         else fa.read(stage, ks, r - FN, af[r - FN]);
     };
 
@@ -391,7 +430,7 @@ void gemm_dma_kernel(const GemmArgs args) {
 #pragma unroll
             for (int d = 0; d < ND; ++d) dma(s0, lds, d);
 #pragma unroll
-            for (int d = 0; d < ND; ++d) dma(s1, lds + kDmaStageBytes, d);
+            for (int d = 0; d < ND; ++d) dma(s1, lds + STAGE, d);
         }
         // tile 0 landed (tile 1 may still be in flight: the first loop
         // barrier waits for it); the waves without loads have none in flight
@@ -399,8 +438,8 @@ void gemm_dma_kernel(const GemmArgs args) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) read(lds, 0, r, a0, b0);
         for (int kt = 0; kt < nkt; ++kt) {
-            const uint32_t cur = lds + (kt & 1) * kDmaStageBytes;
-            const uint32_t nxt = lds + ((kt + 1) & 1) * kDmaStageBytes;
+            const uint32_t cur = lds + (kt & 1) * STAGE;
+            const uint32_t nxt = lds + ((kt + 1) & 1) * STAGE;
             sub0(cur);
             wait_all_barrier();   // tile kt+1 landed for every wave; `cur` is free
             sub1(cur, nxt, tile_src(kt + 2));
@@ -416,9 +455,36 @@ void gemm_dma_kernel(const GemmArgs args) {
         for (int j = 0; j < FN; ++j) asm volatile("" : "+a"(acc[i][j]));
 
     // ---- epilogue: lane holds C[m][n .. n+3] of each 16x16 block
-    const int ml0 = wm * 128 + (lane & 15);
+    const int ml0 = wm * WTM + (lane & 15);
     const int nl0 = wn * WTN + 4 * (lane >> 4);
-    constexpr int CES = dt_size(OUT);
+    if constexpr (OUT == OUT_PARTIAL) {
+        // raw fp32 / int32 partial sums of this K slice: workspace plane g
+        char *wsb = static_cast<char *>(args.ws) +
+                    ((int64_t)g * M * N + (int64_t)m0 * N + n0) * 4;
+        const int64_t ws_ext = (int64_t)(M - m0) * N * 4 - (int64_t)n0 * 4;
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(wsb, ws_ext);
+        const bool vec = (N % 4) == 0;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int ml = ml0 + i * 16;
+            if (m0 + ml >= M) continue;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int nl = nl0 + j * 16;
+                const int nvalid = N - (n0 + nl);
+                if (nvalid <= 0) continue;
+                int v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (DT == DT_I8) v[e] = acc[i][j][e];
+                    else v[e] = as_i32(acc[i][j][e]);
+                }
+                store_i4(rw, (ml * N + nl) * 4, nvalid, vec, v);
+            }
+        }
+        return;
+    }
+    constexpr int CES = dt_size(OUT == OUT_PARTIAL ? DT_F32 : OUT);
     const int64_t c_org = ((int64_t)m0 * args.ldc + n0) * CES;
     char *Cb = static_cast<char *>(args.C) + z * args.stride_c * CES + c_org;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cb, args.c_extent - c_org);
@@ -440,7 +506,7 @@ void gemm_dma_kernel(const GemmArgs args) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e];
                 store_i4(rc, off, nvalid, vec, v);
-            } else {
+            } else if constexpr (OUT != OUT_PARTIAL) {
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e];

@@ -12,13 +12,12 @@ namespace tcg {
 namespace {
 
 // Output types that exist for this input type (include/tcgemm.h lists the
-// supported tuples); split-K partials only for the 64x64 class, the only
-// class the planner splits; the direct-to-LDS class only for 16-bit and int8
-// inputs.
+// supported tuples); split-K partials only for the classes the planner
+// splits (64x64 and the 128x128 tiles); the direct-to-LDS classes only for
+// 16-bit and int8 inputs.
 constexpr bool out_ok(int cls, int out) {
-    if ((cls == TILE_256_DMA || cls == TILE_256_DMA8) && (TCG_DT == DT_F32 || out == OUT_PARTIAL))
-        return false;
-    if (out == OUT_PARTIAL) return cls == TILE_64;
+    if (is_dma_class(cls) && TCG_DT == DT_F32) return false;
+    if (out == OUT_PARTIAL) return cls == TILE_64 || cls == TILE_128 || cls == TILE_128_DMA;
     if (TCG_DT == DT_I8) return out == DT_I32;
     if (TCG_DT == DT_F32) return out == DT_F32;
     return out == TCG_DT || out == DT_F32;
@@ -26,19 +25,23 @@ constexpr bool out_ok(int cls, int out) {
 
 template <int CLS, int OUT>
 hipError_t launch_one(const GemmArgs &args, int64_t grid, hipStream_t stream) {
-    if constexpr ((CLS == TILE_256_DMA || CLS == TILE_256_DMA8) && out_ok(CLS, OUT)) {
+    if constexpr (is_dma_class(CLS) && out_ok(CLS, OUT)) {
         // the K tail needs per-chunk masks only when K is not a whole number
         // of 128-byte tiles (split-K slices are whole tiles)
+        constexpr int T = tile_shape(CLS).bm;
         constexpr int NW = CLS == TILE_256_DMA8 ? 8 : 4;
+        constexpr int OCC = CLS == TILE_128_DMA ? 2 : 1;
         constexpr int BK = kLdsRowBytes / dt_size(TCG_DT);
         if (args.K % BK != 0)
-            hipLaunchKernelGGL((gemm_dma_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, OUT, NW, true>),
-                               dim3((unsigned)grid), dim3(NW * 64), 0, stream, args);
+            hipLaunchKernelGGL(
+                (gemm_dma_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, OUT, T, T, NW, OCC, true>),
+                dim3((unsigned)grid), dim3(NW * 64), 0, stream, args);
         else
-            hipLaunchKernelGGL((gemm_dma_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, OUT, NW, false>),
-                               dim3((unsigned)grid), dim3(NW * 64), 0, stream, args);
+            hipLaunchKernelGGL(
+                (gemm_dma_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, OUT, T, T, NW, OCC, false>),
+                dim3((unsigned)grid), dim3(NW * 64), 0, stream, args);
         return hipGetLastError();
-    } else if constexpr (CLS != TILE_256_DMA && CLS != TILE_256_DMA8 && out_ok(CLS, OUT)) {
+    } else if constexpr (!is_dma_class(CLS) && out_ok(CLS, OUT)) {
         hipLaunchKernelGGL((gemm_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, CLS, OUT>),
                            dim3((unsigned)grid), dim3(256), 0, stream, args);
         return hipGetLastError();
@@ -71,6 +74,7 @@ hipError_t TCG_LAUNCHER(int cls, int out, const tcg::GemmArgs &args, int64_t gri
     case TILE_64: return launch_cls<TILE_64>(out, args, grid, stream);
     case TILE_256_DMA: return launch_cls<TILE_256_DMA>(out, args, grid, stream);
     case TILE_256_DMA8: return launch_cls<TILE_256_DMA8>(out, args, grid, stream);
+    case TILE_128_DMA: return launch_cls<TILE_128_DMA>(out, args, grid, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -19,15 +19,21 @@ __host__ __device__ constexpr int dt_size(int dt) {
 // fragment reads are the same for every element type.  TILE_256_DMA is the
 // 256x256 tile of gemm_dma_kernel (direct-to-LDS loads; 16-bit and int8
 // inputs with 16-byte aligned rows) with 4 waves of 128x128, TILE_256_DMA8
-// the same with 8 waves of 128x64 (two per SIMD).
+// the same with 8 waves of 128x64 (two per SIMD), TILE_128_DMA its 128x128
+// tile with 4 waves of 64x64 and two workgroups per CU.
 enum TileClass : int {
     TILE_256 = 0,
     TILE_128 = 1,
     TILE_64 = 2,
     TILE_256_DMA = 3,
     TILE_256_DMA8 = 4,
-    NUM_TILE_CLASSES = 5
+    TILE_128_DMA = 5,
+    NUM_TILE_CLASSES = 6
 };
+
+__host__ __device__ constexpr bool is_dma_class(int cls) {
+    return cls == TILE_256_DMA || cls == TILE_256_DMA8 || cls == TILE_128_DMA;
+}
 
 __host__ __device__ constexpr int tile_threads(int cls) { return cls == TILE_256_DMA8 ? 512 : 256; }
 
@@ -37,7 +43,7 @@ struct TileShape {
 
 __host__ __device__ constexpr TileShape tile_shape(int cls) {
     return (cls == TILE_256 || cls == TILE_256_DMA || cls == TILE_256_DMA8) ? TileShape{256, 256, 2, 2}
-         : cls == TILE_128                          ? TileShape{128, 128, 2, 2}
+         : (cls == TILE_128 || cls == TILE_128_DMA) ? TileShape{128, 128, 2, 2}
                                                     : TileShape{64, 64, 2, 2};
 }
 
@@ -79,6 +85,17 @@ struct EpilogueArgs {
     int32_t acc_is_int;
     int32_t c_vec_ok;          // C rows allow 4-element vector access
     float alpha, beta;
+};
+
+// Operand repacking: `rows` rows of `row_bytes` bytes, read at pitch
+// src_pitch and written at pitch dst_pitch (a multiple of 16, >= row_bytes)
+// with the bytes from row_bytes to dst_pitch zeroed, for `batch` problems.
+struct PackArgs {
+    const void *src;
+    void *dst;
+    int64_t src_stride, dst_stride;   // bytes between batch problems
+    int64_t src_pitch, dst_pitch;     // bytes between rows
+    int32_t rows, row_bytes, batch;
 };
 
 // Workgroup -> (tile_m, tile_n, group).
@@ -129,6 +146,7 @@ hipError_t tcg_launch_gemm(int dt, bool ta, bool tb, int cls, int out, const tcg
                            int64_t grid, hipStream_t stream);
 hipError_t tcg_launch_splitk_reduce(const tcg::EpilogueArgs &args, hipStream_t stream);
 hipError_t tcg_launch_scale_c(const tcg::EpilogueArgs &args, hipStream_t stream);
+hipError_t tcg_launch_pack_rows(const tcg::PackArgs &args, hipStream_t stream);
 const char *tcg_kernel_name(int dt, bool ta, bool tb, int cls);
 
 // One launcher per (input type, layout) object; each dispatches on (cls, out).

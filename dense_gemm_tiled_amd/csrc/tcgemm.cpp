@@ -66,8 +66,16 @@ struct Plan {
     int32_t tiles_m, tiles_n;
     int32_t splits, k_per_split;
     int64_t grid;
-    int64_t ws_bytes;
+    int64_t ws_bytes;           // whole workspace: split-K partials, then packed operands
     int32_t band;
+    // Operand repacking for the direct-to-LDS classes ([0] = A, [1] = B):
+    // byte pitch, batch stride and workspace offset of the packed copy.
+    bool pack[2];
+    int64_t pack_pitch[2], pack_stride[2], pack_off[2];
+    // Edge split: 1 = the columns from edge_at on, 2 = the rows from edge_at
+    // on, run as a second GEMM after the whole tiles (0: no split).
+    int edge;
+    int32_t edge_at;
 };
 
 tc_status_t fail(std::string *err, tc_status_t st, const char *fmt, ...) {
@@ -192,15 +200,53 @@ tc_status_t validate(const tc_gemm_batched_desc *bd, Problem *p, std::string *er
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// The direct-to-LDS kernel moves 16-byte chunks: 16-bit or int8 inputs whose
-// rows and batch strides are whole chunks, and a K that is a whole number of
-// chunks (k past K is zeroed per chunk).  A and B must also start on 16 bytes
-// (checked at launch, where the pointers are known).
-bool dma_ok(const Problem &p) {
-    if (p.dt != TC_F16 && p.dt != TC_BF16 && p.dt != TC_I8) return false;
+// The direct-to-LDS kernel takes 16-bit and int8 inputs.  It moves 16-byte
+// chunks, so an operand feeds it as it is when its row pitch, its batch
+// stride and its rows themselves are whole chunks: the loads zero whole
+// chunks past K, and no chunk may straddle the end of the operand, where a
+// range-checked load would not return the valid part.  Any other operand is
+// first copied into a packed layout in the workspace (rows padded to 16
+// bytes with zeros; pack_rows_kernel) -- and so is one whose base pointer is
+// not 16-byte aligned, which only the launch can see.
+bool dma_types(const Problem &p) { return p.dt == TC_F16 || p.dt == TC_BF16 || p.dt == TC_I8; }
+
+// Rows and columns (elements) of operand w (0 = A, 1 = B) as stored.
+void operand_shape(const Problem &p, int w, int64_t *rows, int64_t *cols) {
+    const int64_t mn = w == 0 ? p.M : p.N;
+    const bool mc = w == 0 ? p.ta : !p.tb;   // M/N-contiguous: rows are k
+    *rows = mc ? p.K : mn;
+    *cols = mc ? mn : p.K;
+}
+
+bool operand_dma_ready(const Problem &p, int w) {
     const int es = dt_size(p.dt);
-    return (p.lda * es) % 16 == 0 && (p.ldb * es) % 16 == 0 && (p.stride_a * es) % 16 == 0 &&
-           (p.stride_b * es) % 16 == 0 && (p.K * es) % 16 == 0;
+    const int64_t ld = w == 0 ? p.lda : p.ldb, stride = w == 0 ? p.stride_a : p.stride_b;
+    int64_t rows, cols;
+    operand_shape(p, w, &rows, &cols);
+    return (ld * es) % 16 == 0 && (stride * es) % 16 == 0 && (cols * es) % 16 == 0;
+}
+
+int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+// Workspace layout of a plan: split-K partials at offset 0, then the packed
+// copies of the operands that need one (aligned: whether the operand's base
+// pointer is 16-byte aligned).
+void layout_workspace(const Problem &p, Plan *pl, const bool aligned[2]) {
+    const int es = dt_size(p.dt);
+    int64_t off = pl->splits > 1 ? align_up(pl->splits * p.batch * (int64_t)p.M * p.N * 4, 256) : 0;
+    for (int w = 0; w < 2; ++w) {
+        pl->pack[w] = is_dma_class(pl->cls) && (!operand_dma_ready(p, w) || !aligned[w]);
+        pl->pack_pitch[w] = pl->pack_stride[w] = pl->pack_off[w] = 0;
+        if (!pl->pack[w]) continue;
+        int64_t rows, cols;
+        operand_shape(p, w, &rows, &cols);
+        const int64_t stride = w == 0 ? p.stride_a : p.stride_b;
+        pl->pack_pitch[w] = align_up(cols * es, 16);
+        pl->pack_stride[w] = stride == 0 ? 0 : rows * pl->pack_pitch[w];
+        pl->pack_off[w] = off;
+        off += align_up((stride == 0 ? 1 : p.batch) * rows * pl->pack_pitch[w], 256);
+    }
+    pl->ws_bytes = off;
 }
 
 // Tile class and split-K choice.  MI355X has 256 CUs; a launch wants at least
@@ -209,83 +255,196 @@ bool dma_ok(const Problem &p) {
 // few tiles (the case tessl "Architecture" routes to split-K: K >= 2048 with
 // small M and N).
 //
-// The 256x256 class runs as the direct-to-LDS kernel when the operands allow
-// it (dma_ok; the base pointers' alignment is checked at launch time).
+// For 16-bit and int8 inputs the 256x256 and 128x128 classes run as the
+// direct-to-LDS kernel (an operand it cannot read as it is gets packed
+// first), and split-K runs on its 128x128 tile, two workgroups per CU: the
+// slices stream the operands from HBM and write fp32 partial sums that one
+// more kernel adds up in a fixed order.
 //
 // Tuning overrides (environment, read at every call; unset in normal use):
-// TCGEMM_TILE=dma|dma8|256|128|64 forces a tile class (dma only where allowed),
-// TCGEMM_SPLITS=S forces split-K with S slices (on the 64x64 class, the one
-// with a partial-sum output), TCGEMM_BAND=h sets the band height of the tile
-// order (0: row-major).
-void make_plan(const Problem &p, Plan *pl) {
+// TCGEMM_TILE=dma|dma8|dma128|256|128|64 forces a tile class (dma* only for
+// 16-bit and int8 inputs) without split-K, TCGEMM_SPLITS=S forces split-K
+// with S slices (on a class with a partial-sum output: 64x64 or 128x128,
+// else 64x64), TCGEMM_BAND=h sets the band height of the tile order (0:
+// row-major).
+void make_plan(const Problem &p, Plan *pl, bool allow_edge = true) {
     const int es = dt_size(p.dt);
     const int bk = kLdsRowBytes / es;
-    int cls = TILE_64;
-    for (int c = TILE_256; c <= TILE_64; ++c) {
+    const bool dma = dma_types(p);
+    const int64_t ktiles = ceil_div(p.K, bk);
+    auto tile_count = [&](int c) {
         const TileShape ts = tile_shape(c);
-        const int64_t tiles = ceil_div(p.M, ts.bm) * ceil_div(p.N, ts.bn) * p.batch;
-        if (tiles >= 192 || c == TILE_64) { cls = c; break; }
+        return ceil_div(p.M, ts.bm) * ceil_div(p.N, ts.bn) * p.batch;
+    };
+    int cls = TILE_64;
+    for (int c = TILE_256; c <= TILE_64; ++c)
+        if (tile_count(c) >= 192 || c == TILE_64) { cls = c; break; }
+    int64_t splits = 1;
+    // tall K and too few tiles to fill the chip: split K
+    const bool split = cls == TILE_64 && tile_count(TILE_64) < 128 && ktiles >= 16 && p.alpha != 0.0f;
+    if (split && dma) {
+        cls = TILE_128_DMA;
+        splits = ceil_div(2 * 256, tile_count(TILE_128_DMA));   // two workgroups per CU
+        if (splits > ktiles / 4) splits = ktiles / 4;          // keep >= 4 K-tiles per slice
+        if (splits > 32) splits = 32;
+    } else if (split) {
+        splits = ceil_div(256, tile_count(TILE_64));
+        if (splits > ktiles / 8) splits = ktiles / 8;          // keep >= 8 K-tiles per slice
+        if (splits > 16) splits = 16;
     }
-    if (cls == TILE_256 && dma_ok(p)) cls = TILE_256_DMA;
-    int64_t forced_splits = 0;
+    if (splits < 1) splits = 1;
+    if (dma && cls == TILE_256) cls = TILE_256_DMA;
+    if (dma && cls == TILE_128) cls = TILE_128_DMA;
     if (const char *env = getenv("TCGEMM_TILE")) {
         const int v = atoi(env);
-        if (strcmp(env, "dma") == 0) cls = dma_ok(p) ? TILE_256_DMA : cls;
-        else if (strcmp(env, "dma8") == 0) cls = dma_ok(p) ? TILE_256_DMA8 : cls;
+        if (strcmp(env, "dma") == 0) cls = dma ? TILE_256_DMA : cls;
+        else if (strcmp(env, "dma8") == 0) cls = dma ? TILE_256_DMA8 : cls;
+        else if (strcmp(env, "dma128") == 0) cls = dma ? TILE_128_DMA : cls;
         else cls = v == 256 ? TILE_256 : v == 128 ? TILE_128 : v == 64 ? TILE_64 : cls;
+        splits = 1;   // a forced class splits only when TCGEMM_SPLITS says so
     }
     if (const char *env = getenv("TCGEMM_SPLITS")) {
-        forced_splits = atoi(env);
-        if (forced_splits > 1) cls = TILE_64;
+        const int64_t forced = atoi(env);
+        if (forced > 0 && p.alpha != 0.0f) splits = forced > ktiles ? ktiles : forced;
     }
+    if (splits > 1 && cls != TILE_64 && cls != TILE_128 && cls != TILE_128_DMA) cls = TILE_64;
     const TileShape ts = tile_shape(cls);
     pl->cls = cls;
     pl->bm = ts.bm; pl->bn = ts.bn; pl->bk = bk;
     pl->tiles_m = (int32_t)ceil_div(p.M, ts.bm);
     pl->tiles_n = (int32_t)ceil_div(p.N, ts.bn);
     const int64_t tiles = (int64_t)pl->tiles_m * pl->tiles_n * p.batch;
-    const int64_t ktiles = ceil_div(p.K, bk);
 
-    int64_t splits = 1;
-    if (cls == TILE_64 && tiles < 128 && ktiles >= 16 && p.alpha != 0.0f) {
-        splits = ceil_div(256, tiles);
-        if (splits > ktiles / 8) splits = ktiles / 8;      // keep >= 8 K-tiles per slice
-        if (splits > 16) splits = 16;
-        if (splits < 1) splits = 1;
-    }
-    if (forced_splits > 0 && p.alpha != 0.0f) splits = forced_splits > ktiles ? ktiles : forced_splits;
     int64_t kps = ceil_div(ceil_div(p.K, splits), bk) * bk;
     splits = ceil_div(p.K, kps);                            // every slice non-empty
-    int64_t ws = 0;
-    if (splits > 1) {
-        ws = splits * p.batch * (int64_t)p.M * p.N * 4;
-        if ((int64_t)splits * p.M * p.N * 4 > 0x7FFFFFFF) {  // reduce-kernel offsets are 32-bit
-            splits = 1;
-            kps = ceil_div(p.K, bk) * bk;
-            ws = 0;
-        }
+    if (splits > 1 && (int64_t)splits * p.M * p.N * 4 > 0x7FFFFFFF) {  // reduce offsets are 32-bit
+        splits = 1;
+        kps = ceil_div(p.K, bk) * bk;
     }
     pl->splits = (int32_t)splits;
     pl->k_per_split = (int32_t)kps;
     pl->grid = tiles * splits;
-    pl->ws_bytes = ws;
     pl->band = 8;
     if (const char *env = getenv("TCGEMM_BAND")) pl->band = atoi(env);   // tuning knob
+    const bool aligned[2] = {true, true};
+    layout_workspace(p, pl, aligned);
+
+    // Edge split.  A 256x256 launch whose last tile column (or row) holds
+    // only a thin ragged strip can cost a whole extra round of workgroups
+    // (272 tiles on 256 CUs take two rounds).  Such a strip runs as a
+    // second, split-K GEMM of its own when dropping it from the main launch
+    // saves a round.
+    pl->edge = 0;
+    pl->edge_at = 0;
+    const char *env_edge = getenv("TCGEMM_EDGE");   // tuning knob: 0 disables
+    if (allow_edge && p.alpha != 0.0f && (cls == TILE_256_DMA || cls == TILE_256_DMA8) && splits == 1 &&
+        !(env_edge && atoi(env_edge) == 0)) {
+        auto rounds = [](int64_t t) { return (t + 255) / 256; };
+        const int64_t rn = p.N % ts.bn, rm = p.M % ts.bm;
+        const int64_t tmn = (int64_t)pl->tiles_m * pl->tiles_n;
+        if (rn != 0 && rn <= ts.bn / 2 &&
+            rounds((tmn - pl->tiles_m) * p.batch) < rounds(tmn * p.batch)) {
+            pl->edge = 1;
+            pl->edge_at = (int32_t)(p.N - rn);
+        } else if (rm != 0 && rm <= ts.bm / 2 &&
+                   rounds((tmn - pl->tiles_n) * p.batch) < rounds(tmn * p.batch)) {
+            pl->edge = 2;
+            pl->edge_at = (int32_t)(p.M - rm);
+        }
+    }
+}
+
+// The part [lo, lo + n) of problem p along N (axis 1) or M (axis 2), and the
+// element offsets of its A, B and C origins.
+Problem sub_problem(const Problem &p, int axis, int64_t lo, int64_t n, int64_t off[3]) {
+    Problem q = p;
+    off[0] = off[1] = off[2] = 0;
+    if (axis == 1) {
+        q.N = (int32_t)n;
+        off[1] = p.tb ? lo * p.ldb : lo;
+        off[2] = lo;
+        q.b_ext = p.tb ? span(n, p.K, p.ldb) : span(p.K, n, p.ldb);
+    } else {
+        q.M = (int32_t)n;
+        off[0] = p.ta ? lo : lo * p.lda;
+        off[2] = lo * p.ldc;
+        q.a_ext = p.ta ? span(p.K, n, p.lda) : span(n, p.K, p.lda);
+    }
+    q.c_ext = span(q.M, q.N, p.ldc);
+    const int es = dt_size(p.dt), ces = dt_size(p.cdt);
+    q.a_total = total_bytes(p.batch, p.stride_a, q.a_ext, es);
+    q.b_total = total_bytes(p.batch, p.stride_b, q.b_ext, es);
+    q.c_total = total_bytes(p.batch, p.stride_c, q.c_ext, ces);
+    return q;
+}
+
+// The two parts of an edge-split problem with their plans.
+struct Parts {
+    int n;
+    Problem p[2];
+    Plan pl[2];
+    int64_t off[2][3];
+};
+
+Parts split_parts(const Problem &p, const Plan &pl) {
+    Parts r;
+    if (pl.edge == 0) {
+        r.n = 1;
+        r.p[0] = p;
+        r.pl[0] = pl;
+        r.off[0][0] = r.off[0][1] = r.off[0][2] = 0;
+        return r;
+    }
+    r.n = 2;
+    const int64_t ext = pl.edge == 1 ? p.N : p.M;
+    r.p[0] = sub_problem(p, pl.edge, 0, pl.edge_at, r.off[0]);
+    r.p[1] = sub_problem(p, pl.edge, pl.edge_at, ext - pl.edge_at, r.off[1]);
+    for (int i = 0; i < 2; ++i) make_plan(r.p[i], &r.pl[i], false);
+    return r;
+}
+
+// The kernels a plan launches, in order, joined by '+'.
+std::string kernel_chain(const Problem &p, const Plan &pl) {
+    if (p.alpha == 0.0f) return "scale_c";
+    std::string name;
+    if (pl.pack[0]) name += "pack_a+";
+    if (pl.pack[1]) name += "pack_b+";
+    name += tcg_kernel_name(p.dt, p.ta, p.tb, pl.cls);
+    if (pl.splits > 1) name += "+splitk_reduce";
+    return name;
+}
+
+int plan_launches(const Problem &p, const Plan &pl) {
+    if (p.alpha == 0.0f) return 1;
+    return 1 + (pl.splits > 1) + pl.pack[0] + pl.pack[1];
+}
+
+// Kernel chains of the parts, joined by '|'.
+std::string parts_chain(const Parts &r) {
+    std::string name = kernel_chain(r.p[0], r.pl[0]);
+    for (int i = 1; i < r.n; ++i) name += "|" + kernel_chain(r.p[i], r.pl[i]);
+    return name;
 }
 
 void fill_info(const Problem &p, const Plan &pl, tc_plan_info *info) {
     if (!info) return;
     memset(info, 0, sizeof *info);
-    snprintf(info->kernel, sizeof info->kernel, "%s%s", tcg_kernel_name(p.dt, p.ta, p.tb, pl.cls),
-             pl.splits > 1 ? "+splitk_reduce" : "");
-    if (p.alpha == 0.0f) snprintf(info->kernel, sizeof info->kernel, "scale_c");
-    info->tile_m = pl.bm; info->tile_n = pl.bn; info->tile_k = pl.bk;
-    info->threads = tile_threads(pl.cls);
-    info->tiles_m = pl.tiles_m; info->tiles_n = pl.tiles_n;
-    info->splits = pl.splits; info->k_per_split = pl.k_per_split;
-    info->grid = p.alpha == 0.0f ? 0 : pl.grid;
-    info->workspace_bytes = p.alpha == 0.0f ? 0 : pl.ws_bytes;
-    info->launches = p.alpha == 0.0f ? 1 : (pl.splits > 1 ? 2 : 1);
+    const Parts parts = split_parts(p, pl);
+    snprintf(info->kernel, sizeof info->kernel, "%s", parts_chain(parts).c_str());
+    const Plan &m = parts.pl[0];   // tile fields: the main (whole-tile) part
+    info->tile_m = m.bm; info->tile_n = m.bn; info->tile_k = m.bk;
+    info->threads = tile_threads(m.cls);
+    info->tiles_m = m.tiles_m; info->tiles_n = m.tiles_n;
+    info->splits = m.splits; info->k_per_split = m.k_per_split;
+    info->grid = 0;
+    info->workspace_bytes = 0;
+    info->launches = 0;
+    for (int i = 0; i < parts.n; ++i) {
+        if (p.alpha != 0.0f) info->grid += parts.pl[i].grid;
+        if (p.alpha != 0.0f && parts.pl[i].ws_bytes > info->workspace_bytes)
+            info->workspace_bytes = parts.pl[i].ws_bytes;
+        info->launches += plan_launches(parts.p[i], parts.pl[i]);
+    }
     info->band = pl.band;
 }
 
@@ -367,36 +526,18 @@ tc_status_t create_stream(tc_context *ctx, tc_stream **out, hipStream_t existing
     return TC_OK;
 }
 
-// Validate, plan and enqueue one (batched) GEMM on stream s.
-tc_status_t run(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A, const void *B,
-                void *C, tc_stream *s, bool sync) {
-    if (!ctx) return TC_ERR_INVALID_ARGUMENT;
-    ctx->last_error.clear();
-    std::string *err = &ctx->last_error;
-    if (!A || !B || !C) return fail(err, TC_ERR_INVALID_ARGUMENT, "A, B and C must be non-NULL");
-    Problem p;
-    tc_status_t st = validate(bd, &p, err);
-    if (st != TC_OK) return st;
-    if (ranges_overlap(C, p.c_total, A, p.a_total) || ranges_overlap(C, p.c_total, B, p.b_total))
-        return fail(err, TC_ERR_ALIASING, "C overlaps A or B");
-    Plan pl;
-    make_plan(p, &pl);
-    if ((pl.cls == TILE_256_DMA || pl.cls == TILE_256_DMA8) &&
-        ((uintptr_t)A % 16 != 0 || (uintptr_t)B % 16 != 0))
-        pl.cls = TILE_256;   // same tile, register-staged loads
-
-    st = bind_device(ctx);
-    if (st != TC_OK) return st;
-    if ((st = check_allocation("A", A, p.a_total, err)) != TC_OK) return st;
-    if ((st = check_allocation("B", B, p.b_total, err)) != TC_OK) return st;
-    if ((st = check_allocation("C", C, p.c_total, err)) != TC_OK) return st;
-
-    if (!s) {
-        if (!ctx->internal && (st = create_stream(ctx, &ctx->internal, nullptr)) != TC_OK) return st;
-        s = ctx->internal;
-    }
+// Enqueue the launches of one planned problem (packs, GEMM, reduction) on
+// stream s; their names are appended to *names.
+tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan &plan,
+                    const void *A, const void *B, void *C, std::string *names, std::string *err) {
+    Plan pl = plan;
+    const bool aligned[2] = {(uintptr_t)A % 16 == 0, (uintptr_t)B % 16 == 0};
+    layout_workspace(p, &pl, aligned);   // a misaligned base pointer is packed too
+    *names += kernel_chain(p, pl);
+    tc_status_t st;
     const bool use_splitk = p.alpha != 0.0f && pl.splits > 1;
-    if (use_splitk && (st = ensure_workspace(s, pl.ws_bytes, err)) != TC_OK) return st;
+    const bool use_ws = p.alpha != 0.0f && pl.ws_bytes > 0;
+    if (use_ws && (st = ensure_workspace(s, pl.ws_bytes, err)) != TC_OK) return st;
 
     const int ces = dt_size(p.cdt);
     const bool c_vec_ok = (p.ldc % 4 == 0) && (p.stride_c % 4 == 0) && ((uintptr_t)C % 16 == 0);
@@ -412,23 +553,49 @@ tc_status_t run(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A, 
     ea.alpha = p.alpha; ea.beta = p.beta;
     ea.c_vec_ok = c_vec_ok;
 
-    hipError_t e;
-    std::string name;
+    hipError_t e = hipSuccess;
     if (p.alpha == 0.0f) {
         e = tcg_launch_scale_c(ea, s->stream);
-        name = "scale_c";
         if (e == hipSuccess) ctx->dispatches += 1;
     } else {
+        const int es = dt_size(p.dt);
+        const void *src[2] = {A, B};
+        int64_t ld[2] = {p.lda, p.ldb}, stride[2] = {p.stride_a, p.stride_b};
+        int64_t extent[2] = {p.a_ext * es, p.b_ext * es};
+        for (int w = 0; w < 2 && e == hipSuccess; ++w) {
+            if (!pl.pack[w]) continue;
+            int64_t rows, cols;
+            operand_shape(p, w, &rows, &cols);
+            PackArgs pa;
+            memset(&pa, 0, sizeof pa);
+            pa.src = src[w];
+            pa.dst = static_cast<char *>(s->ws) + pl.pack_off[w];
+            pa.src_stride = stride[w] * es;
+            pa.dst_stride = pl.pack_stride[w];
+            pa.src_pitch = ld[w] * es;
+            pa.dst_pitch = pl.pack_pitch[w];
+            pa.rows = (int32_t)rows;
+            pa.row_bytes = (int32_t)(cols * es);
+            pa.batch = stride[w] == 0 ? 1 : p.batch;
+            e = tcg_launch_pack_rows(pa, s->stream);
+            if (e != hipSuccess) break;
+            ctx->dispatches += 1;
+            // the GEMM reads the packed copy
+            src[w] = pa.dst;
+            ld[w] = pl.pack_pitch[w] / es;
+            stride[w] = pl.pack_stride[w] / es;
+            extent[w] = rows * pl.pack_pitch[w];   // whole padded rows
+        }
         GemmArgs ga;
         memset(&ga, 0, sizeof ga);
-        ga.A = A; ga.B = B; ga.C = C;
+        ga.A = src[0]; ga.B = src[1]; ga.C = C;
         ga.ws = use_splitk ? s->ws : nullptr;
-        ga.stride_a = p.stride_a; ga.stride_b = p.stride_b; ga.stride_c = p.stride_c;
-        ga.a_extent = p.a_ext * dt_size(p.dt);
-        ga.b_extent = p.b_ext * dt_size(p.dt);
+        ga.stride_a = stride[0]; ga.stride_b = stride[1]; ga.stride_c = p.stride_c;
+        ga.a_extent = extent[0];
+        ga.b_extent = extent[1];
         ga.c_extent = p.c_ext * ces;
         ga.M = p.M; ga.N = p.N; ga.K = p.K;
-        ga.lda = (int32_t)p.lda; ga.ldb = (int32_t)p.ldb; ga.ldc = (int32_t)p.ldc;
+        ga.lda = (int32_t)ld[0]; ga.ldb = (int32_t)ld[1]; ga.ldc = (int32_t)p.ldc;
         ga.c_dtype = p.cdt;
         ga.alpha = p.alpha; ga.beta = p.beta;
         ga.tiles_m = pl.tiles_m; ga.tiles_n = pl.tiles_n;
@@ -436,16 +603,15 @@ tc_status_t run(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A, 
         ga.groups = p.batch * pl.splits;
         ga.band = pl.band;
         ga.c_vec_ok = c_vec_ok;
-        e = tcg_launch_gemm(p.dt, p.ta, p.tb, pl.cls, use_splitk ? OUT_PARTIAL : p.cdt, ga,
-                            pl.grid, s->stream);
-        name = tcg_kernel_name(p.dt, p.ta, p.tb, pl.cls);
+        if (e == hipSuccess)
+            e = tcg_launch_gemm(p.dt, p.ta, p.tb, pl.cls, use_splitk ? OUT_PARTIAL : p.cdt, ga,
+                                pl.grid, s->stream);
         if (e == hipSuccess) {
             ctx->dispatches += 1;
             if (use_splitk) {
                 ea.ws = s->ws;
                 ea.splits = pl.splits;
                 e = tcg_launch_splitk_reduce(ea, s->stream);
-                name += "+splitk_reduce";
                 if (e == hipSuccess) ctx->dispatches += 1;
             }
         }
@@ -454,9 +620,49 @@ tc_status_t run(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A, 
         (void)hipGetLastError();
         return fail(err, TC_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
     }
+    return TC_OK;
+}
+
+// Validate, plan and enqueue one (batched) GEMM on stream s.
+tc_status_t run(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A, const void *B,
+                void *C, tc_stream *s, bool sync) {
+    if (!ctx) return TC_ERR_INVALID_ARGUMENT;
+    ctx->last_error.clear();
+    std::string *err = &ctx->last_error;
+    if (!A || !B || !C) return fail(err, TC_ERR_INVALID_ARGUMENT, "A, B and C must be non-NULL");
+    Problem p;
+    tc_status_t st = validate(bd, &p, err);
+    if (st != TC_OK) return st;
+    if (ranges_overlap(C, p.c_total, A, p.a_total) || ranges_overlap(C, p.c_total, B, p.b_total))
+        return fail(err, TC_ERR_ALIASING, "C overlaps A or B");
+    Plan pl;
+    make_plan(p, &pl);
+
+    st = bind_device(ctx);
+    if (st != TC_OK) return st;
+    if ((st = check_allocation("A", A, p.a_total, err)) != TC_OK) return st;
+    if ((st = check_allocation("B", B, p.b_total, err)) != TC_OK) return st;
+    if ((st = check_allocation("C", C, p.c_total, err)) != TC_OK) return st;
+
+    if (!s) {
+        if (!ctx->internal && (st = create_stream(ctx, &ctx->internal, nullptr)) != TC_OK) return st;
+        s = ctx->internal;
+    }
+    // the whole tiles, then the edge strip if the plan splits one off
+    const Parts parts = split_parts(p, pl);
+    std::string name;
+    for (int i = 0; i < parts.n; ++i) {
+        const int es = dt_size(p.dt), ces = dt_size(p.cdt);
+        const void *Ai = static_cast<const char *>(A) + parts.off[i][0] * es;
+        const void *Bi = static_cast<const char *>(B) + parts.off[i][1] * es;
+        void *Ci = static_cast<char *>(C) + parts.off[i][2] * ces;
+        if (i) name += "|";
+        if ((st = enqueue(ctx, s, parts.p[i], parts.pl[i], Ai, Bi, Ci, &name, err)) != TC_OK)
+            return st;
+    }
     ctx->last_kernel = name;
     if (sync) {
-        e = hipStreamSynchronize(s->stream);
+        const hipError_t e = hipStreamSynchronize(s->stream);
         if (e != hipSuccess) {
             (void)hipGetLastError();
             return fail(err, TC_ERR_DEVICE, "hipStreamSynchronize: %s", hipGetErrorString(e));

@@ -92,17 +92,23 @@ typedef struct {
 typedef struct tc_context tc_context;
 typedef struct tc_stream tc_stream;
 
-/* What the planner chose for a descriptor (introspection, no GPU needed). */
+/* What the planner chose for a descriptor (introspection, no GPU needed).
+ * A call runs one part, or two when a thin ragged strip of the output is
+ * split off the whole tiles (the strip runs after them as a GEMM of its
+ * own).  Each part launches, in order: pack_a / pack_b when an operand must
+ * first be copied into 16-byte row pitches, the GEMM kernel, and the split-K
+ * reduction when K is split. */
 typedef struct {
-    char kernel[96];              /* kernel instantiation name */
-    int32_t tile_m, tile_n, tile_k;
+    char kernel[128];             /* the launches: names joined by '+', parts by '|' */
+    int32_t tile_m, tile_n, tile_k;   /* tile fields: the first (main) part */
     int32_t threads;
     int32_t tiles_m, tiles_n;
     int32_t splits;               /* split-K factor S (1 = no split) */
     int32_t k_per_split;
-    int64_t grid;                 /* workgroups of the main launch */
-    int64_t workspace_bytes;      /* split-K partials, 0 when S = 1 */
-    int32_t launches;             /* kernels one call enqueues (1 or 2) */
+    int64_t grid;                 /* workgroups of the GEMM launches, all parts */
+    int64_t workspace_bytes;      /* split-K partials plus packed operands, the
+                                     larger part (parts run one after the other) */
+    int32_t launches;             /* kernels one call enqueues (1 to 8) */
     int32_t band;                 /* tile-order band height */
 } tc_plan_info;
 
@@ -115,9 +121,9 @@ void tc_context_destroy(tc_context *ctx);
 
 /* Streams.  tc_stream_create owns a new hipStream_t; tc_stream_wrap borrows
  * an existing one (for example torch's current stream) and never destroys
- * it.  Each tc_stream owns the split-K workspace of the calls enqueued on it
- * (grown on demand, freed by tc_stream_destroy), so two streams never share
- * scratch memory. */
+ * it.  Each tc_stream owns the workspace of the calls enqueued on it
+ * (split-K partials and packed operand copies; grown on demand, freed by
+ * tc_stream_destroy), so two streams never share scratch memory. */
 tc_status_t tc_stream_create(tc_context *ctx, tc_stream **out);
 tc_status_t tc_stream_wrap(tc_context *ctx, void *hip_stream, tc_stream **out);
 tc_status_t tc_stream_sync(tc_stream *s);
@@ -131,7 +137,7 @@ tc_status_t tc_gemm(tc_context *ctx, const tc_gemm_desc *d,
 tc_status_t tc_gemm_async(tc_context *ctx, const tc_gemm_desc *d,
                           const void *A, const void *B, void *C, tc_stream *s);
 
-/* batch same-shape GEMMs in one launch (split-K: two launches), synchronous. */
+/* batch same-shape GEMMs in one GEMM launch per part, synchronous. */
 tc_status_t tc_gemm_batched(tc_context *ctx, const tc_gemm_batched_desc *bd,
                             const void *A, const void *B, void *C);
 

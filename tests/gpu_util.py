@@ -44,12 +44,25 @@ def logical_views(p: workloads.Problem, a_full, b_full, c_full):
     return a_full[..., :a_cols], b_full[..., :b_cols], c_full[..., :p.N]
 
 
-def run_library(p: workloads.Problem, A, B, C, *, sync=True):
+def shifted(t):
+    """A copy of t whose storage starts one element past a 16-byte boundary."""
+    import torch
+    flat = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+    assert flat.data_ptr() % 16 == 0
+    view = flat[1:].view(t.shape)
+    view.copy_(t)
+    return view
+
+
+def run_library(p: workloads.Problem, A, B, C, *, sync=True, misalign=False):
     """Run the HIP path on the stored inputs; returns the whole C buffer
-    (padding included) as stored values."""
+    (padding included) as stored values.  misalign: A and B start one element
+    past a 16-byte boundary."""
     import torch
     import dense_gemm_tiled_amd as tg
     a_full, b_full, c_full = to_dev(A, p.a_dtype), to_dev(B, p.a_dtype), to_dev(C, p.c_dtype)
+    if misalign:
+        a_full, b_full = shifted(a_full), shifted(b_full)
     a, b, c = logical_views(p, a_full, b_full, c_full)
     tg.gemm(a, b, c, alpha=p.alpha, beta=p.beta, transpose_a=p.transpose_a,
             transpose_b=p.transpose_b)

@@ -163,7 +163,7 @@ def test_plan_headline_uses_one_256_tile_per_cu():
 def test_plan_splitk_shape():
     p = workloads.get("bf16_tn_splitk_b8")
     pl = plan_of(p)
-    assert pl["kernel"].startswith("gemm_bf16_tn_") and pl["kernel"].endswith("+splitk_reduce")
+    assert pl["kernel"] == "gemm_bf16_tn_128x128_dma+splitk_reduce"
     assert pl["splits"] > 1 and pl["launches"] == 2
     assert pl["k_per_split"] % pl["tile_k"] == 0
     assert pl["splits"] * pl["k_per_split"] >= p.K > (pl["splits"] - 1) * pl["k_per_split"]
@@ -172,8 +172,15 @@ def test_plan_splitk_shape():
 
 
 def test_plan_other_workloads():
-    # ldb = 4099 bytes: rows not 16-byte aligned, so the register-staged loads
-    assert plan_of(workloads.get("i8_nn_ragged"))["kernel"] == "gemm_i8_nn_256x256"
+    # ldb = 4099 bytes: B rows do not start on 16-byte boundaries, so B is
+    # packed into the workspace first
+    # packed into the workspace first; N = 4099 leaves a 3-column strip past
+    # 16 tile columns, which runs as a split-K GEMM of its own
+    pl = plan_of(workloads.get("i8_nn_ragged"))
+    assert pl["kernel"] == ("pack_b+gemm_i8_nn_256x256_dma|"
+                            "pack_b+gemm_i8_nn_128x128_dma+splitk_reduce"), pl["kernel"]
+    assert pl["launches"] == 5
+    assert pl["workspace_bytes"] == 4096 * 4096   # the larger part: main B packed
     assert plan_of(workloads.get("f16_tn_4096"))["kernel"] == "gemm_f16_tn_256x256_dma"
     assert plan_of(workloads.get("f16_nt_4096"))["kernel"] == "gemm_f16_nt_256x256_dma"
     pl = plan_of(workloads.get("sgemm_nn_256"))
@@ -183,17 +190,76 @@ def test_plan_other_workloads():
 
 
 def test_plan_dma_eligibility():
-    """The direct-to-LDS class needs 16-bit or int8 inputs, 16-byte row pitches
-    and batch strides, and K in whole 16-byte chunks; otherwise the same tile
-    runs with register-staged loads."""
+    """The direct-to-LDS classes take 16-bit and int8 inputs.  An operand whose
+    row pitch, batch stride or row length (K for K-contiguous operands, M or N
+    for M/N-contiguous ones) is not a whole number of 16-byte chunks is packed
+    into the workspace first; f32 inputs take the register-staged kernel."""
     base = workloads.get("bf16_nn_4096")
-    assert plan_of(base.with_(K=4096 - 8))["kernel"].endswith("_dma")
-    assert not plan_of(base.with_(K=4096 - 4))["kernel"].endswith("_dma")     # partial chunk
-    assert not plan_of(base.with_(lda=4096 + 4))["kernel"].endswith("_dma")   # 8-byte pitch
-    assert plan_of(base.with_(lda=4096 + 8))["kernel"].endswith("_dma")
-    assert not plan_of(base.with_(a_dtype="f32", c_dtype="f32"))["kernel"].endswith("_dma")
+    assert plan_of(base.with_(K=4096 - 8))["kernel"] == "gemm_bf16_nn_256x256_dma"
+    # K = 4092: A rows (K-contiguous) end inside a chunk; B (N-contiguous) is fine
+    pl = plan_of(base.with_(K=4096 - 4))
+    assert pl["kernel"] == "pack_a+gemm_bf16_nn_256x256_dma"
+    assert pl["workspace_bytes"] == 4096 * 8192 and pl["launches"] == 2
+    assert plan_of(base.with_(lda=4096 + 4))["kernel"] == "pack_a+gemm_bf16_nn_256x256_dma"
+    assert plan_of(base.with_(lda=4096 + 8))["kernel"] == "gemm_bf16_nn_256x256_dma"
+    # N = 4100: the last B row would end inside a chunk
+    assert plan_of(base.with_(M=3072, N=4100, ldb=4104))["kernel"] == "pack_b+gemm_bf16_nn_256x256_dma"
+    # TN: both operands M/N-contiguous, so any K is fine
+    assert plan_of(base.with_(transpose_a=True, K=4093))["kernel"] == "gemm_bf16_tn_256x256_dma"
+    assert plan_of(base.with_(a_dtype="f32", c_dtype="f32"))["kernel"] == "gemm_f32_nn_256x256"
     i8 = workloads.get("i8_nn_ragged")
-    assert plan_of(i8.with_(N=4096 + 16))["kernel"] == "gemm_i8_nn_256x256_dma"
+    assert plan_of(i8.with_(N=4096 + 16))["kernel"].startswith("gemm_i8_nn_256x256_dma|")
+    assert plan_of(i8.with_(N=4096))["kernel"] == "gemm_i8_nn_256x256_dma"
+
+
+def test_plan_edge_split():
+    """A thin ragged last tile column (or row) that would cost a second round
+    of 256x256 workgroups runs as a second GEMM; a strip that saves no round,
+    a thick one, or TCGEMM_EDGE=0 keeps one launch."""
+    base = workloads.get("bf16_nn_4096")
+    main = "gemm_bf16_nn_256x256_dma"
+    assert plan_of(base.with_(N=4104))["kernel"] == main + "|gemm_bf16_nn_128x128_dma+splitk_reduce"
+    assert plan_of(base.with_(M=4100))["kernel"] == main + "|gemm_bf16_nn_128x128_dma+splitk_reduce"
+    assert plan_of(base.with_(N=4096 + 128))["kernel"].startswith(main + "|")
+    assert plan_of(base.with_(N=4096 + 136))["kernel"] == main            # strip > half a tile
+    assert plan_of(base.with_(M=3072, N=4104))["kernel"] == main          # 204 tiles: one round
+    pl = plan_of(base.with_(N=4104))
+    assert pl["tiles_m"] == 16 and pl["tiles_n"] == 16 and pl["grid"] > 256
+    os.environ["TCGEMM_EDGE"] = "0"
+    try:
+        assert plan_of(base.with_(N=4104))["kernel"] == main
+    finally:
+        del os.environ["TCGEMM_EDGE"]
+
+
+def test_plan_packed_batch_strides():
+    """A shared operand (batch stride 0) is packed once; a batched one per
+    problem, the packed copies placed after the split-K partials."""
+    common = dict(M=256, N=256, K=8190, a=tg.BF16, c=tg.F32, batch=3, sb=8190 * 256, sc=256 * 256)
+    pl = tg.plan(desc(sa=0, **common))
+    assert pl["kernel"] == "pack_a+gemm_bf16_nn_128x128_dma+splitk_reduce", pl["kernel"]
+    part = pl["splits"] * 3 * 256 * 256 * 4
+    assert part % 256 == 0
+    assert pl["workspace_bytes"] == part + 256 * 16384
+    pl = tg.plan(desc(sa=256 * 8190, **common))
+    assert pl["workspace_bytes"] == part + 3 * 256 * 16384 and pl["launches"] == 3
+
+
+def test_plan_mid_size_and_split_k_classes():
+    """Outputs too small for 192 tiles of 256 x 256 take the 128 x 128 tile,
+    direct-to-LDS for 16-bit and int8 inputs; tall K with few tiles splits K
+    on that tile (on the 64 x 64 tile for f32)."""
+    mid = workloads.Problem("mid", 1536, 2048, 1024, "bf16", "bf16")
+    assert plan_of(mid)["kernel"] == "gemm_bf16_nn_128x128_dma"
+    assert plan_of(mid.with_(a_dtype="f32", c_dtype="f32"))["kernel"] == "gemm_f32_nn_128x128"
+    tall = workloads.Problem("tall", 256, 256, 8192, "f16", "f32")
+    pl = plan_of(tall)
+    assert pl["kernel"] == "gemm_f16_nn_128x128_dma+splitk_reduce" and pl["splits"] > 1
+    assert pl["grid"] == 4 * pl["splits"]
+    pl = plan_of(tall.with_(K=8192 - 2))   # A rows (K-contiguous) not in whole chunks
+    assert pl["kernel"] == "pack_a+gemm_f16_nn_128x128_dma+splitk_reduce"
+    pl = plan_of(tall.with_(a_dtype="f32"))
+    assert pl["kernel"] == "gemm_f32_nn_64x64+splitk_reduce"
 
 
 # ------------------------------------------------------------------ tile order
