@@ -70,7 +70,7 @@ struct GemmArgs {
     int32_t splits, k_per_split;   // k_per_split is a multiple of the tile K
     int32_t groups;                // batch * splits
     int32_t band;                  // tile-order band height (<= 0: row-major)
-    int32_t c_vec_ok;              // C rows allow 4-element vector access
+    int32_t c_vec_ok;              // 4 complete C values go as one vector access
 };
 
 // Arguments of the split-K reduction and of the alpha == 0 scaling kernel.
@@ -83,7 +83,7 @@ struct EpilogueArgs {
     int32_t batch, splits;
     int32_t c_dtype;
     int32_t acc_is_int;
-    int32_t c_vec_ok;          // C rows allow 4-element vector access
+    int32_t c_vec_ok;          // 4 complete C values go as one vector access
     float alpha, beta;
 };
 

@@ -540,7 +540,11 @@ tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan 
     if (use_ws && (st = ensure_workspace(s, pl.ws_bytes, err)) != TC_OK) return st;
 
     const int ces = dt_size(p.cdt);
-    const bool c_vec_ok = (p.ldc % 4 == 0) && (p.stride_c % 4 == 0) && ((uintptr_t)C % 16 == 0);
+    // Four complete C values of a row go as one vector access (16 bytes for
+    // 32-bit types, 8 for 16-bit) at any alignment: the GPU runs with
+    // unaligned memory access enabled, and one unaligned vector access costs
+    // less than four element accesses (odd ldc included).
+    const bool c_vec_ok = true;
     EpilogueArgs ea;
     memset(&ea, 0, sizeof ea);
     ea.C = C;
