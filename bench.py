@@ -10,9 +10,10 @@ total) are used in rotation so that successive steps do not find their
 operands in the 256 MB last-level cache.
 
 Prints one JSON line: whole-job TFLOP/s (or GB/s for the HBM-bound split-K
-workload), the roofline position of the dominant kernel (its average duration
-measured with HIP events recorded on the launch stream around every timed
-step), and the CPU oracle timed on a bounded sample of the same workload.
+workload), the roofline position of the dominant kernel (the step's main
+GEMM kernel; its average duration comes from HIP events that the library
+records on the launch stream right around it in every eighth timed step),
+and the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -33,14 +34,17 @@ import workloads  # noqa: E402
 # MI355X published peaks
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "i8": 5033.2}
 PEAK_HBM_GBS = 8000.0
+KEV_EVERY = 8   # timed steps per sampled kernel duration
 ROCPROF_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # the default warm-up (about a quarter of a second of GEMMs) brings the
+    # GPU clocks to their steady state before the timed steps
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default=workloads.HEADLINE, choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--sets", type=int, default=0, help="input sets in rotation (0: >= 512 MiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -135,18 +139,28 @@ def main():
     kernel = tg.last_kernel()
 
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # Every KEV_EVERY-th timed step, the library records a pair of HIP events
+    # on the launch stream right around the step's main GEMM kernel.  Each
+    # timestamp costs the stream a few microseconds, so only a sample of the
+    # steps carries them.
+    kev_steps = list(range(0, args.steps, KEV_EVERY))
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in kev_steps]
+    for a_ev, b_ev in kev:   # create the HIP events before handing them over
+        a_ev.record(stream)
+        b_ev.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    j = 0
     for i in range(args.steps):
-        ev[i][0].record(stream)
+        if i % KEV_EVERY == 0:
+            tg.time_next_gemm(kev[j][0], kev[j][1])
+            j += 1
         step(i)
-        ev[i][1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
-    durs = np.array([s.elapsed_time(e) for s, e in ev]) * 1e-3   # seconds per step (events)
+    kdurs = np.array([s.elapsed_time(e) for s, e in kev]) * 1e-3   # seconds per main kernel
     ms_per_step = wall / args.steps * 1e3
 
     flops = float(p.flops)
@@ -161,17 +175,30 @@ def main():
         metric = ("GEMM TFLOP/s and % of MI355X MFMA peak, bf16 4096^3 NN (1 GPU)"
                   if p.name == workloads.HEADLINE else "GEMM throughput, %s (1 GPU)" % p.name)
 
-    kern_s = float(np.mean(durs))
+    # The dominant kernel is the main GEMM kernel of a step; its algorithmic
+    # work: 2*M*N*K over the output part it computes (the whole output unless
+    # a thin edge strip is split off), or for the HBM-bound split-K workload
+    # the bytes of A and B it reads once (partial sums are overhead).
+    info = tg.plan(tg.make_desc(*sets[0][:3], alpha=p.alpha, beta=p.beta,
+                                transpose_a=p.transpose_a, transpose_b=p.transpose_b))
+    mm = min(p.M, info["tiles_m"] * info["tile_m"])
+    nm = min(p.N, info["tiles_n"] * info["tile_n"])
+    kern_s = float(np.mean(kdurs))
+    es = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}[p.a_dtype]
     if hbm_bound:
-        roof = {"bound": "hbm", "achieved": alg_bytes / kern_s / 1e9, "peak": PEAK_HBM_GBS,
+        kbytes = float((p.M * p.K + p.K * p.N) * es * p.batch)
+        roof = {"bound": "hbm", "achieved": kbytes / kern_s / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": flops / kern_s / 1e12,
+        kflops = 2.0 * mm * nm * p.K * p.batch
+        roof = {"bound": "mfma", "achieved": kflops / kern_s / 1e12,
                 "peak": PEAK_TFLOPS[p.a_dtype], "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["kernel"] = kernel
+    roof["main_part"] = [mm, nm, p.K]
     roof["kernel_us_mean"] = kern_s * 1e6
-    roof["kernel_us_median"] = float(np.median(durs)) * 1e6
+    roof["kernel_us_median"] = float(np.median(kdurs)) * 1e6
+    roof["kernel_samples"] = len(kdurs)
     roof["traffic"] = None
     if os.path.exists(ROCPROF_TRAFFIC_FILE):
         with open(ROCPROF_TRAFFIC_FILE) as f:
@@ -203,12 +230,14 @@ def main():
 
 
 def tg_source_hash() -> str:
-    """Hash of the kernel sources, to tell whether stored counters still
-    describe the kernel that runs."""
+    """Hash of the device sources (every csrc file but the host planner), to
+    tell whether stored counters still describe the kernels that run."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dense_gemm_tiled_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if name == "tcgemm.cpp":
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())

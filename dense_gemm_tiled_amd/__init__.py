@@ -20,7 +20,7 @@ import os
 from typing import Dict, Optional, Tuple
 
 __all__ = [
-    "gemm", "plan", "TcGemmError", "last_kernel", "dispatch_count", "library_path",
+    "gemm", "plan", "TcGemmError", "last_kernel", "dispatch_count", "time_next_gemm", "library_path",
     "load_library", "F32", "F16", "BF16", "I8", "I32", "status_name", "DescT",
     "BatchedDescT", "PlanInfoT",
 ]
@@ -97,6 +97,7 @@ _SIGNATURES = {
                                     ctypes.POINTER(PlanInfoT)]),
     "tc_last_kernel": (ctypes.c_char_p, [_VP]),
     "tc_dispatch_count": (ctypes.c_uint64, [_VP]),
+    "tc_time_next_gemm": (ctypes.c_int, [_VP, _VP, _VP]),
     "tc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "tc_last_error": (ctypes.c_char_p, [_VP]),
     "tc_tile_of_workgroup": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -179,6 +180,14 @@ def last_kernel(device: int = 0) -> str:
 
 def dispatch_count(device: int = 0) -> int:
     return int(load_library().tc_dispatch_count(_context(device)))
+
+
+def time_next_gemm(start, end, device: int = 0) -> None:
+    """Have the next GEMM call record torch.cuda.Event `start` and `end` on
+    its stream right around its main GEMM kernel (see tc_time_next_gemm).
+    The events must already exist on the device (recorded once)."""
+    ctx = _context(device)
+    _check(load_library().tc_time_next_gemm(ctx, _VP(start.cuda_event), _VP(end.cuda_event)), ctx)
 
 
 # ------------------------------------------------------------------ descriptors

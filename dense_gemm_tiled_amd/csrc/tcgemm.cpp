@@ -37,6 +37,7 @@ struct tc_context {
     uint64_t dispatches = 0;
     std::string last_kernel;
     std::string last_error;
+    hipEvent_t time_ev[2] = {nullptr, nullptr};   // armed by tc_time_next_gemm
 };
 
 namespace {
@@ -529,7 +530,8 @@ tc_status_t create_stream(tc_context *ctx, tc_stream **out, hipStream_t existing
 // Enqueue the launches of one planned problem (packs, GEMM, reduction) on
 // stream s; their names are appended to *names.
 tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan &plan,
-                    const void *A, const void *B, void *C, std::string *names, std::string *err) {
+                    const void *A, const void *B, void *C, bool main_part, std::string *names,
+                    std::string *err) {
     Plan pl = plan;
     const bool aligned[2] = {(uintptr_t)A % 16 == 0, (uintptr_t)B % 16 == 0};
     layout_workspace(p, &pl, aligned);   // a misaligned base pointer is packed too
@@ -607,9 +609,18 @@ tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan 
         ga.groups = p.batch * pl.splits;
         ga.band = pl.band;
         ga.c_vec_ok = c_vec_ok;
+        // an armed measurement brackets the GEMM kernel alone (one call only)
+        hipEvent_t ev_start = nullptr, ev_end = nullptr;
+        if (main_part) {
+            ev_start = ctx->time_ev[0];
+            ev_end = ctx->time_ev[1];
+            ctx->time_ev[0] = ctx->time_ev[1] = nullptr;
+        }
+        if (ev_start && e == hipSuccess) e = hipEventRecord(ev_start, s->stream);
         if (e == hipSuccess)
             e = tcg_launch_gemm(p.dt, p.ta, p.tb, pl.cls, use_splitk ? OUT_PARTIAL : p.cdt, ga,
                                 pl.grid, s->stream);
+        if (ev_end && e == hipSuccess) e = hipEventRecord(ev_end, s->stream);
         if (e == hipSuccess) {
             ctx->dispatches += 1;
             if (use_splitk) {
@@ -661,7 +672,7 @@ tc_status_t run(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A, 
         const void *Bi = static_cast<const char *>(B) + parts.off[i][1] * es;
         void *Ci = static_cast<char *>(C) + parts.off[i][2] * ces;
         if (i) name += "|";
-        if ((st = enqueue(ctx, s, parts.p[i], parts.pl[i], Ai, Bi, Ci, &name, err)) != TC_OK)
+        if ((st = enqueue(ctx, s, parts.p[i], parts.pl[i], Ai, Bi, Ci, i == 0, &name, err)) != TC_OK)
             return st;
     }
     ctx->last_kernel = name;
@@ -788,6 +799,13 @@ tc_status_t tc_gemm_plan(tc_context *ctx, const tc_gemm_batched_desc *bd, tc_pla
 const char *tc_last_kernel(const tc_context *ctx) { return ctx ? ctx->last_kernel.c_str() : ""; }
 
 uint64_t tc_dispatch_count(const tc_context *ctx) { return ctx ? ctx->dispatches : 0; }
+
+tc_status_t tc_time_next_gemm(tc_context *ctx, void *start_event, void *end_event) {
+    if (!ctx || (!start_event) != (!end_event)) return TC_ERR_INVALID_ARGUMENT;
+    ctx->time_ev[0] = static_cast<hipEvent_t>(start_event);
+    ctx->time_ev[1] = static_cast<hipEvent_t>(end_event);
+    return TC_OK;
+}
 
 const char *tc_status_string(tc_status_t status) {
     switch (status) {

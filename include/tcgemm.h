@@ -160,6 +160,17 @@ const char *tc_last_kernel(const tc_context *ctx);
 /* Number of kernels this context has launched so far. */
 uint64_t tc_dispatch_count(const tc_context *ctx);
 
+/* Measurement hook.  start_event and end_event are hipEvent_t handles the
+ * caller created (for example the handles behind two torch.cuda.Event
+ * objects).  The next GEMM call on this context that launches a GEMM kernel
+ * records start_event on its stream immediately before its main GEMM kernel
+ * (the first part's, when the call runs two parts) and end_event right
+ * after it, so hipEventElapsedTime gives that kernel's own duration.  One
+ * arming serves one call; two NULLs disarm.  Returns TC_ERR_INVALID_ARGUMENT
+ * for a NULL ctx or exactly one NULL event.  A failed hipEventRecord makes
+ * that GEMM call return TC_ERR_DEVICE. */
+tc_status_t tc_time_next_gemm(tc_context *ctx, void *start_event, void *end_event);
+
 /* Static text for a status code; never NULL. */
 const char *tc_status_string(tc_status_t status);
 

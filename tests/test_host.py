@@ -27,6 +27,9 @@ def lib():
     return tg.load_library()
 
 
+_VP = ctypes.c_void_p
+
+
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -39,6 +42,15 @@ def test_header_and_binding_agree(lib):
     assert set(names) == set(tg._SIGNATURES), set(names) ^ set(tg._SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_time_next_gemm_arguments(lib, ctx):
+    """The measurement hook only stores the two handles: both or neither."""
+    assert lib.tc_time_next_gemm(None, _VP(16), _VP(32)) == 1
+    assert lib.tc_time_next_gemm(ctx, _VP(16), None) == 1
+    assert lib.tc_time_next_gemm(ctx, None, _VP(32)) == 1
+    assert lib.tc_time_next_gemm(ctx, _VP(16), _VP(32)) == 0
+    assert lib.tc_time_next_gemm(ctx, None, None) == 0   # disarm
 
 
 def test_version_and_status_strings(lib):
