@@ -287,8 +287,10 @@ struct FragReader {
 // op_begin(q) .. op_begin(q + 1) - 1.
 constexpr int op_begin(int q, int n, int qn) { return (q * n + qn - 1) / qn; }
 
-// BM x BN tile, NW waves (2 along M, NW/2 along N), OCC workgroups per CU.
-template <int DT, bool TA, bool TB, int OUT, int BM, int BN, int NW, int OCC, bool KMASK>
+// BM x BN tile, NW waves (2 along M, NW/2 along N), OCC workgroups per CU;
+// BETA: beta != 0 (the epilogue reads C).
+template <int DT, bool TA, bool TB, int OUT, int BM, int BN, int NW, int OCC, bool KMASK,
+          bool BETA>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(NW / 4 * OCC, NW / 4 * OCC)))
 void gemm_dma_kernel(const GemmArgs args) {
@@ -490,7 +492,36 @@ void gemm_dma_kernel(const GemmArgs args) {
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cb, args.c_extent - c_org);
     const bool vec = args.c_vec_ok != 0;
     const int ldc = args.ldc;
-    const float alpha = args.alpha, beta = args.beta;
+    const float alpha = args.alpha, beta = BETA ? args.beta : 0.f;
+
+    // beta != 0 with a 16-bit C tile that lies wholly inside C and whose
+    // rows are whole 16-byte chunks: the tile (BM x BN x 2 bytes, the size of
+    // the two operand stages) comes into LDS with direct-to-LDS loads, all of
+    // it in flight at once, instead of one round trip per 16x16 block from
+    // the registers' side.  Row r of the LDS image holds 16-byte chunk q at
+    // position q ^ ((r & 15) * CSW), so the epilogue's reads of 16 rows at
+    // one column hit distinct banks.
+    constexpr int CRB = BN * 2;                    // C tile row bytes (16-bit)
+    constexpr int CSW = CRB >= 512 ? 2 : 1;
+    static_assert(BM * CRB <= 2 * STAGE, "the C tile fits the operand stages");
+    bool c_lds = false;
+    if constexpr (BETA && (OUT == DT_F16 || OUT == DT_BF16)) {
+        c_lds = beta != 0.f && args.c_dma_ok != 0 && m0 + BM <= M && n0 + BN <= N;
+        if (c_lds) {
+            // every wave is done with the operand stages
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            const i32x4 rcc = rsrc4(Cb, args.c_extent - c_org);
+            constexpr int LOADS = BM * CRB / 1024 / NW;   // per wave
+            constexpr int LPR_C = CRB / 16, RPI_C = 64 / LPR_C;
+#pragma unroll
+            for (int u = 0; u < LOADS; ++u) {
+                const int r = (wave * LOADS + u) * RPI_C + lane / LPR_C;
+                const int q = (lane % LPR_C) ^ ((r & 15) * CSW);
+                dma16(rcc, lds + (wave * LOADS + u) * 1024, r * ldc * CES + q * 16);
+            }
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         const int ml = ml0 + i * 16;
@@ -510,6 +541,23 @@ void gemm_dma_kernel(const GemmArgs args) {
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e];
+                if constexpr (BETA && (OUT == DT_F16 || OUT == DT_BF16)) {
+                    if (c_lds) {
+                        // C_old from the LDS image (8 bytes: 4 values)
+                        const int q = (nl * 2) / 16;
+                        const uint32_t a = lds + ml * CRB + ((q ^ ((ml & 15) * CSW)) << 4) +
+                                           ((nl * 2) & 15);
+                        const u32x2 w = *(const TCG_LDS u32x2 *)(size_t)a;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const u32 h = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                            const float old = OUT == DT_BF16 ? from_bf16_bits(h) : from_f16_bits(h);
+                            v[e] = __builtin_fmaf(beta, old, v[e] * alpha);
+                        }
+                        store_c4<OUT>(rc, off, 4, true, v);
+                        continue;
+                    }
+                }
                 finish4<OUT>(rc, off, nvalid, vec, alpha, beta, v);
             }
         }

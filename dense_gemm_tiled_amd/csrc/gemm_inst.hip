@@ -31,15 +31,24 @@ hipError_t launch_one(const GemmArgs &args, int64_t grid, hipStream_t stream) {
         constexpr int T = tile_shape(CLS).bm;
         constexpr int NW = CLS == TILE_256_DMA8 ? 8 : 4;
         constexpr int OCC = CLS == TILE_128_DMA ? 2 : 1;
+        // and the epilogue reads C only when beta != 0 (float outputs)
         constexpr int BK = kLdsRowBytes / dt_size(TCG_DT);
-        if (args.K % BK != 0)
-            hipLaunchKernelGGL(
-                (gemm_dma_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, OUT, T, T, NW, OCC, true>),
-                dim3((unsigned)grid), dim3(NW * 64), 0, stream, args);
-        else
-            hipLaunchKernelGGL(
-                (gemm_dma_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, OUT, T, T, NW, OCC, false>),
-                dim3((unsigned)grid), dim3(NW * 64), 0, stream, args);
+        constexpr bool FLOAT_OUT = OUT == DT_F32 || OUT == DT_F16 || OUT == DT_BF16;
+        const bool kmask = args.K % BK != 0, beta = FLOAT_OUT && args.beta != 0.f;
+        const dim3 g((unsigned)grid), b(NW * 64);
+#define TCG_DMA(KM, BE) \
+    hipLaunchKernelGGL((gemm_dma_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, OUT, T, T, NW, OCC, KM, BE>), \
+                       g, b, 0, stream, args)
+        if constexpr (FLOAT_OUT) {
+            if (kmask && beta) TCG_DMA(true, true);
+            else if (kmask) TCG_DMA(true, false);
+            else if (beta) TCG_DMA(false, true);
+            else TCG_DMA(false, false);
+        } else {
+            if (kmask) TCG_DMA(true, false);
+            else TCG_DMA(false, false);
+        }
+#undef TCG_DMA
         return hipGetLastError();
     } else if constexpr (!is_dma_class(CLS) && out_ok(CLS, OUT)) {
         hipLaunchKernelGGL((gemm_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, CLS, OUT>),

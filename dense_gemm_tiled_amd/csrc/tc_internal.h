@@ -71,6 +71,7 @@ struct GemmArgs {
     int32_t groups;                // batch * splits
     int32_t band;                  // tile-order band height (<= 0: row-major)
     int32_t c_vec_ok;              // 4 complete C values go as one vector access
+    int32_t c_dma_ok;              // C rows, batch stride and base are whole 16-byte chunks
 };
 
 // Arguments of the split-K reduction and of the alpha == 0 scaling kernel.

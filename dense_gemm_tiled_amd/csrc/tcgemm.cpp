@@ -609,6 +609,8 @@ tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan 
         ga.groups = p.batch * pl.splits;
         ga.band = pl.band;
         ga.c_vec_ok = c_vec_ok;
+        ga.c_dma_ok = (p.ldc * ces) % 16 == 0 && (p.stride_c * ces) % 16 == 0 &&
+                      (uintptr_t)C % 16 == 0;
         // an armed measurement brackets the GEMM kernel alone (one call only)
         hipEvent_t ev_start = nullptr, ev_end = nullptr;
         if (main_part) {
