@@ -284,8 +284,16 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true) {
     // tall K and too few tiles to fill the chip: split K
     const bool split = cls == TILE_64 && tile_count(TILE_64) < 128 && ktiles >= 16 && p.alpha != 0.0f;
     if (split && dma) {
+        // about 1.5 workgroups per CU (measured best on the batched 128 x 384
+        // x 16384 shape: enough slices to keep HBM busy, few enough partial
+        // sums), preferring a slice count that divides the K-tiles evenly
         cls = TILE_128_DMA;
-        splits = ceil_div(2 * 256, tile_count(TILE_128_DMA));   // two workgroups per CU
+        const int64_t want = ceil_div(384, tile_count(TILE_128_DMA));
+        splits = want;
+        for (int64_t d = 0; d <= want / 4; ++d) {
+            if (want - d >= 2 && ktiles % (want - d) == 0) { splits = want - d; break; }
+            if (ktiles % (want + d) == 0) { splits = want + d; break; }
+        }
         if (splits > ktiles / 4) splits = ktiles / 4;          // keep >= 4 K-tiles per slice
         if (splits > 32) splits = 32;
     } else if (split) {
