@@ -26,7 +26,8 @@ ARCH = "gfx950"
 # (object name, source, extra defines): the host library, the reduction and
 # dispatch object, and one GEMM object per input type and layout.
 _DT = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3}
-SOURCES = [("tcgemm", "tcgemm.cpp", []), ("epilogue_kernels", "epilogue_kernels.hip", [])]
+SOURCES = [("tcgemm", "tcgemm.cpp", []), ("epilogue_kernels", "epilogue_kernels.hip", []),
+           ("thin_kernel", "thin_kernel.hip", [])]
 for _name, _code in _DT.items():
     for _ta in (0, 1):
         for _tb in (0, 1):

@@ -119,12 +119,20 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const PackArgs a) {
     char *dst = static_cast<char *>(a.dst) + z * a.dst_stride + r * a.dst_pitch;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, a.row_bytes);
     const int chunks = (int)(a.dst_pitch / 16);
-    for (int c = threadIdx.x & 63; c < chunks; c += 64) {
-        const int nb = a.row_bytes - 16 * c;
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (nb >= 16) v = ld128(rs, 16 * c);
-        else if (nb > 0) v = ld_partial<1>(rs, 16 * c, nb);
-        *reinterpret_cast<u32x4 *>(dst + 16 * c) = v;
+    // four chunks per lane in flight before their stores
+    for (int c0 = threadIdx.x & 63; c0 < chunks; c0 += 256) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = c0 + 64 * u;
+            const int nb = a.row_bytes - 16 * c;
+            v[u] = u32x4{0u, 0u, 0u, 0u};
+            if (nb >= 16) v[u] = ld128(rs, 16 * c);
+            else if (nb > 0) v[u] = ld_partial<1>(rs, 16 * c, nb);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (c0 + 64 * u < chunks) *reinterpret_cast<u32x4 *>(dst + 16 * (c0 + 64 * u)) = v[u];
     }
 }
 
@@ -140,7 +148,8 @@ const Launcher kLaunchers[4][4] = {
 const char *const kDtName[4] = {"f32", "f16", "bf16", "i8"};
 const char *const kLayoutName[2][2] = {{"nn", "nt"}, {"tn", "tt"}};
 const char *const kTileName[NUM_TILE_CLASSES] = {"256x256", "128x128", "64x64",
-                                                   "256x256_dma", "256x256_dma8", "128x128_dma"};
+                                                   "256x256_dma", "256x256_dma8", "128x128_dma",
+                                                   "thin"};
 
 char g_names[4][2][2][NUM_TILE_CLASSES][64];
 bool g_names_ready = false;

@@ -28,8 +28,11 @@ enum TileClass : int {
     TILE_256_DMA = 3,
     TILE_256_DMA8 = 4,
     TILE_128_DMA = 5,
-    NUM_TILE_CLASSES = 6
+    TILE_THIN = 6,          // thin_kernel: N <= 16, A K-contiguous; kThinRows rows per workgroup
+    NUM_TILE_CLASSES = 7
 };
+
+constexpr int kThinRows = 8;    // output rows per thin_kernel workgroup (2 waves)
 
 __host__ __device__ constexpr bool is_dma_class(int cls) {
     return cls == TILE_256_DMA || cls == TILE_256_DMA8 || cls == TILE_128_DMA;
@@ -44,6 +47,7 @@ struct TileShape {
 __host__ __device__ constexpr TileShape tile_shape(int cls) {
     return (cls == TILE_256 || cls == TILE_256_DMA || cls == TILE_256_DMA8) ? TileShape{256, 256, 2, 2}
          : (cls == TILE_128 || cls == TILE_128_DMA) ? TileShape{128, 128, 2, 2}
+         : cls == TILE_THIN                         ? TileShape{kThinRows, 16, kThinRows / 4, 1}
                                                     : TileShape{64, 64, 2, 2};
 }
 
@@ -148,6 +152,11 @@ hipError_t tcg_launch_gemm(int dt, bool ta, bool tb, int cls, int out, const tcg
 hipError_t tcg_launch_splitk_reduce(const tcg::EpilogueArgs &args, hipStream_t stream);
 hipError_t tcg_launch_scale_c(const tcg::EpilogueArgs &args, hipStream_t stream);
 hipError_t tcg_launch_pack_rows(const tcg::PackArgs &args, hipStream_t stream);
+// B stored [N, K] (K-contiguous rows)
+hipError_t tcg_launch_thin(int dt, int out, const tcg::GemmArgs &args, int64_t grid, hipStream_t stream);
+// rows = K, row_bytes = N * es of a B stored [K, N]; writes Bt[n][k] rows of
+// dst_pitch bytes
+hipError_t tcg_launch_thin_pack_bt(const tcg::PackArgs &args, int es, hipStream_t stream);
 const char *tcg_kernel_name(int dt, bool ta, bool tb, int cls);
 
 // One launcher per (input type, layout) object; each dispatches on (cls, out).

@@ -229,6 +229,12 @@ bool operand_dma_ready(const Problem &p, int w) {
 
 int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
+// The thin kernel reads B as N rows of K values: a B stored [K, N] (not
+// transposed) is gathered into a transposed copy first, once, rather than
+// by every workgroup (read from a wide matrix, each row of B is a cache
+// line of its own).
+bool thin_transposes_b(const Problem &p, const Plan &pl) { return pl.cls == TILE_THIN && !p.tb; }
+
 // Workspace layout of a plan: split-K partials at offset 0, then the packed
 // copies of the operands that need one (aligned: whether the operand's base
 // pointer is 16-byte aligned).
@@ -238,6 +244,16 @@ void layout_workspace(const Problem &p, Plan *pl, const bool aligned[2]) {
     for (int w = 0; w < 2; ++w) {
         pl->pack[w] = is_dma_class(pl->cls) && (!operand_dma_ready(p, w) || !aligned[w]);
         pl->pack_pitch[w] = pl->pack_stride[w] = pl->pack_off[w] = 0;
+        if (w == 1 && thin_transposes_b(p, *pl)) {
+            // thin kernel: B^T, N rows of K values
+            const int64_t stride = p.stride_b;
+            pl->pack[1] = true;
+            pl->pack_pitch[1] = align_up((int64_t)p.K * es, 16);
+            pl->pack_stride[1] = stride == 0 ? 0 : p.N * pl->pack_pitch[1];
+            pl->pack_off[1] = off;
+            off += align_up((stride == 0 ? 1 : p.batch) * p.N * pl->pack_pitch[1], 256);
+            continue;
+        }
         if (!pl->pack[w]) continue;
         int64_t rows, cols;
         operand_shape(p, w, &rows, &cols);
@@ -263,8 +279,9 @@ void layout_workspace(const Problem &p, Plan *pl, const bool aligned[2]) {
 // more kernel adds up in a fixed order.
 //
 // Tuning overrides (environment, read at every call; unset in normal use):
-// TCGEMM_TILE=dma|dma8|dma128|256|128|64 forces a tile class (dma* only for
-// 16-bit and int8 inputs) without split-K, TCGEMM_SPLITS=S forces split-K
+// TCGEMM_TILE=dma|dma8|dma128|thin|256|128|64 forces a tile class (dma* only
+// for 16-bit and int8 inputs, thin only for N <= 16 with A not transposed)
+// without split-K, TCGEMM_SPLITS=S forces split-K
 // with S slices (on a class with a partial-sum output: 64x64 or 128x128,
 // else 64x64), TCGEMM_BAND=h sets the band height of the tile order (0:
 // row-major).
@@ -302,6 +319,15 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true) {
         if (splits > 16) splits = 16;
     }
     if (splits < 1) splits = 1;
+    // at most 16 output columns and K-contiguous A rows: the vector-ALU
+    // dot-product kernel, when its 8-row workgroups give every CU at least
+    // one (a matrix-core tile would be at least 16 / N padding, and the
+    // work is bound by reading A once)
+    const bool thin_ok = p.N <= 16 && !p.ta && p.alpha != 0.0f;
+    if (thin_ok && ceil_div(p.M, kThinRows) * p.batch >= 256) {
+        cls = TILE_THIN;
+        splits = 1;
+    }
     if (dma && cls == TILE_256) cls = TILE_256_DMA;
     if (dma && cls == TILE_128) cls = TILE_128_DMA;
     if (const char *env = getenv("TCGEMM_TILE")) {
@@ -309,6 +335,7 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true) {
         if (strcmp(env, "dma") == 0) cls = dma ? TILE_256_DMA : cls;
         else if (strcmp(env, "dma8") == 0) cls = dma ? TILE_256_DMA8 : cls;
         else if (strcmp(env, "dma128") == 0) cls = dma ? TILE_128_DMA : cls;
+        else if (strcmp(env, "thin") == 0) cls = thin_ok ? TILE_THIN : cls;
         else cls = v == 256 ? TILE_256 : v == 128 ? TILE_128 : v == 64 ? TILE_64 : cls;
         splits = 1;   // a forced class splits only when TCGEMM_SPLITS says so
     }
@@ -317,6 +344,7 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true) {
         if (forced > 0 && p.alpha != 0.0f) splits = forced > ktiles ? ktiles : forced;
     }
     if (splits > 1 && cls != TILE_64 && cls != TILE_128 && cls != TILE_128_DMA) cls = TILE_64;
+    if (cls == TILE_THIN) splits = 1;
     const TileShape ts = tile_shape(cls);
     pl->cls = cls;
     pl->bm = ts.bm; pl->bn = ts.bn; pl->bk = bk;
@@ -417,7 +445,7 @@ std::string kernel_chain(const Problem &p, const Plan &pl) {
     if (p.alpha == 0.0f) return "scale_c";
     std::string name;
     if (pl.pack[0]) name += "pack_a+";
-    if (pl.pack[1]) name += "pack_b+";
+    if (pl.pack[1]) name += thin_transposes_b(p, pl) ? "transpose_b+" : "pack_b+";
     name += tcg_kernel_name(p.dt, p.ta, p.tb, pl.cls);
     if (pl.splits > 1) name += "+splitk_reduce";
     return name;
@@ -576,8 +604,32 @@ tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan 
         const void *src[2] = {A, B};
         int64_t ld[2] = {p.lda, p.ldb}, stride[2] = {p.stride_a, p.stride_b};
         int64_t extent[2] = {p.a_ext * es, p.b_ext * es};
+        bool tb = p.tb;
         for (int w = 0; w < 2 && e == hipSuccess; ++w) {
             if (!pl.pack[w]) continue;
+            if (w == 1 && thin_transposes_b(p, pl)) {
+                PackArgs pa;
+                memset(&pa, 0, sizeof pa);
+                pa.src = src[1];
+                pa.dst = static_cast<char *>(s->ws) + pl.pack_off[1];
+                pa.src_stride = stride[1] * es;
+                pa.dst_stride = pl.pack_stride[1];
+                pa.src_pitch = ld[1] * es;
+                pa.dst_pitch = pl.pack_pitch[1];
+                pa.rows = p.K;
+                pa.row_bytes = p.N * es;
+                pa.batch = stride[1] == 0 ? 1 : p.batch;
+                e = tcg_launch_thin_pack_bt(pa, es, s->stream);
+                if (e != hipSuccess) break;
+                ctx->dispatches += 1;
+                // the thin kernel reads B^T: N rows of K values
+                src[1] = pa.dst;
+                ld[1] = pl.pack_pitch[1] / es;
+                stride[1] = pl.pack_stride[1] / es;
+                extent[1] = (int64_t)p.N * pl.pack_pitch[1];
+                tb = true;
+                continue;
+            }
             int64_t rows, cols;
             operand_shape(p, w, &rows, &cols);
             PackArgs pa;
@@ -627,7 +679,9 @@ tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan 
             ctx->time_ev[0] = ctx->time_ev[1] = nullptr;
         }
         if (ev_start && e == hipSuccess) e = hipEventRecord(ev_start, s->stream);
-        if (e == hipSuccess)
+        if (e == hipSuccess && pl.cls == TILE_THIN)
+            e = tb ? tcg_launch_thin(p.dt, p.cdt, ga, pl.grid, s->stream) : hipErrorInvalidValue;
+        else if (e == hipSuccess)
             e = tcg_launch_gemm(p.dt, p.ta, p.tb, pl.cls, use_splitk ? OUT_PARTIAL : p.cdt, ga,
                                 pl.grid, s->stream);
         if (ev_end && e == hipSuccess) e = hipEventRecord(ev_end, s->stream);

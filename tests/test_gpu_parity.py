@@ -230,12 +230,14 @@ def test_dma128_split_k_packed_shared_operand():
 
 
 @pytest.mark.parametrize("a,c,M,N,K,batch,ta,tb,strip", [
-    # column strip, split-K on the 128x128 tile
-    ("bf16", "bf16", 4096, 4104, 1024, 1, False, False, "|gemm_bf16_nn_128x128_dma+splitk_reduce"),
+    # column strip of 8 on the thin-output kernel
+    ("bf16", "bf16", 4096, 4104, 1024, 1, False, False, "|transpose_b+gemm_bf16_nn_thin"),
     # row strip; the main part packs A (M-contiguous rows of 4100 halves)
     ("f16", "f32", 4100, 4096, 192, 1, True, True, "_dma|gemm_f16_tt_64x64"),
     # batched column strip; the main part packs B (rows of 2051 bytes)
-    ("i8", "i32", 2048, 2051, 256, 4, False, False, "_dma|gemm_i8_nn_64x64"),
+    ("i8", "i32", 2048, 2051, 256, 4, False, False, "_dma|transpose_b+gemm_i8_nn_thin"),
+    # strip of 40 columns: split-K on the 128x128 tile
+    ("bf16", "f32", 4096, 4136, 1024, 1, False, False, "|gemm_bf16_nn_128x128_dma+splitk_reduce"),
 ])
 def test_edge_split(a, c, M, N, K, batch, ta, tb, strip):
     """A thin ragged strip past the whole 256x256 tiles runs as a second GEMM
@@ -244,6 +246,60 @@ def test_edge_split(a, c, M, N, K, batch, ta, tb, strip):
     p = problem(a, c, M, N, K, ta, tb, batch=batch)
     check(p, "edge split")
     assert tg.last_kernel().endswith(strip), tg.last_kernel()
+
+
+# ---------------------------------------------------------------- thin outputs
+THIN_N = [1, 3, 8, 13, 16]
+
+
+@pytest.mark.parametrize("n", THIN_N)
+@pytest.mark.parametrize("tb,ldb", [(False, 0), (False, 70), (True, 0)], ids=["nn", "nn-wide", "nt"])
+@pytest.mark.parametrize("a,c", PAIRS, ids=["%s-%s" % pc for pc in PAIRS])
+def test_thin_kernel(a, c, tb, ldb, n):
+    """The vector-ALU kernel for N <= 16: 300 rows (a ragged last block of 16),
+    K = 5000 (whole 4 KiB chunks of K then a ragged one, for every type),
+    batch 2, alpha = 0.5 and beta = 1 for floats; then K = 77 (one partial
+    chunk) with beta = 0 and a NaN-filled C.  A B stored [K, N] (rows N or 70
+    elements apart) is gathered into B^T first."""
+    import dense_gemm_tiled_amd as tg
+    name = "%sgemm_%s_%s_thin" % ("" if tb else "transpose_b+", a, "nt" if tb else "nn")
+    p = problem(a, c, 300, n, 5000, False, tb, batch=2, ldb=ldb)
+    check(p, "thin", TCGEMM_TILE="thin")
+    assert tg.last_kernel() == name, tg.last_kernel()
+    p = problem(a, c, 35, n, 77, False, tb, alpha=1.0, beta=0.0, c_dist="nan", ldb=ldb)
+    check(p, "thin short K", TCGEMM_TILE="thin")
+    assert tg.last_kernel() == name, tg.last_kernel()
+
+
+@pytest.mark.parametrize("a,c", PAIRS, ids=["%s-%s" % pc for pc in PAIRS])
+def test_thin_kernel_odd_leading_dims(a, c):
+    """Odd lda, ldb and ldc (rows start off 16-byte boundaries), both B
+    layouts; chosen by the planner (4096 rows: 256 workgroups)."""
+    import dense_gemm_tiled_amd as tg
+    p = problem(a, c, 4096, 5, 1030, False, False, lda=1030 + 3, ldb=5 + 2, ldc=5 + 1)
+    check(p, "thin odd ld")
+    assert tg.last_kernel().endswith("_thin"), tg.last_kernel()
+    p = problem(a, c, 4096, 11, 1030, False, True, lda=1030 + 1, ldb=1030 + 5, ldc=11 + 3)
+    check(p, "thin odd ld nt")
+    assert tg.last_kernel().endswith("_thin"), tg.last_kernel()
+
+
+def test_thin_kernel_int8_extremes():
+    """All (-128)*(-128) over K = 131071 (the int8 K limit) sums to
+    16384 * K < 2^31 exactly; 127 * (-128) to -16256 * K."""
+    import torch
+    import dense_gemm_tiled_amd as tg
+    K = 131071
+    a = torch.full((2048, K), -128, dtype=torch.int8, device="cuda")
+    b = torch.full((K, 3), -128, dtype=torch.int8, device="cuda")
+    c = torch.empty(2048, 3, dtype=torch.int32, device="cuda")
+    say("GPU case: thin int8 extremes")
+    tg.gemm(a, b, c)
+    assert tg.last_kernel() == "transpose_b+gemm_i8_nn_thin", tg.last_kernel()
+    assert torch.all(c == 16384 * K)
+    a.fill_(127)
+    tg.gemm(a, b, c)
+    assert torch.all(c == -16256 * K)
 
 
 # ---------------------------------------------------------------- exact regime
@@ -448,5 +504,5 @@ def test_workload_i8_nn_ragged_bit_exact():
     import dense_gemm_tiled_amd as tg
     p, A, B, C, got = full_case("i8_nn_ragged")
     assert tg.last_kernel() == ("pack_b+gemm_i8_nn_256x256_dma|"
-                                "pack_b+gemm_i8_nn_128x128_dma+splitk_reduce"), tg.last_kernel()
+                                "transpose_b+gemm_i8_nn_thin"), tg.last_kernel()
     compare(p, got, oracle_full(p, A, B, C), label=p.name)

@@ -185,13 +185,12 @@ def test_plan_splitk_shape():
 
 def test_plan_other_workloads():
     # ldb = 4099 bytes: B rows do not start on 16-byte boundaries, so B is
-    # packed into the workspace first
     # packed into the workspace first; N = 4099 leaves a 3-column strip past
-    # 16 tile columns, which runs as a split-K GEMM of its own
+    # 16 tile columns, which runs on the thin-output kernel of its own (its
+    # B columns gathered into B^T first)
     pl = plan_of(workloads.get("i8_nn_ragged"))
-    assert pl["kernel"] == ("pack_b+gemm_i8_nn_256x256_dma|"
-                            "pack_b+gemm_i8_nn_128x128_dma+splitk_reduce"), pl["kernel"]
-    assert pl["launches"] == 5
+    assert pl["kernel"] == "pack_b+gemm_i8_nn_256x256_dma|transpose_b+gemm_i8_nn_thin", pl["kernel"]
+    assert pl["launches"] == 4
     assert pl["workspace_bytes"] == 4096 * 4096   # the larger part: main B packed
     assert plan_of(workloads.get("f16_tn_4096"))["kernel"] == "gemm_f16_tn_256x256_dma"
     assert plan_of(workloads.get("f16_nt_4096"))["kernel"] == "gemm_f16_nt_256x256_dma"
@@ -230,7 +229,7 @@ def test_plan_edge_split():
     a thick one, or TCGEMM_EDGE=0 keeps one launch."""
     base = workloads.get("bf16_nn_4096")
     main = "gemm_bf16_nn_256x256_dma"
-    assert plan_of(base.with_(N=4104))["kernel"] == main + "|gemm_bf16_nn_128x128_dma+splitk_reduce"
+    assert plan_of(base.with_(N=4104))["kernel"] == main + "|transpose_b+gemm_bf16_nn_thin"
     assert plan_of(base.with_(M=4100))["kernel"] == main + "|gemm_bf16_nn_128x128_dma+splitk_reduce"
     assert plan_of(base.with_(N=4096 + 128))["kernel"].startswith(main + "|")
     assert plan_of(base.with_(N=4096 + 136))["kernel"] == main            # strip > half a tile
@@ -242,6 +241,37 @@ def test_plan_edge_split():
         assert plan_of(base.with_(N=4104))["kernel"] == main
     finally:
         del os.environ["TCGEMM_EDGE"]
+
+
+def test_plan_thin_outputs():
+    """At most 16 output columns with K-contiguous A rows take the vector-ALU
+    thin kernel (8 rows per workgroup) once there is a workgroup per CU; a B
+    stored [K, N] is gathered into B^T first.  Transposed A, too few rows or
+    alpha = 0 keep the other paths."""
+    p = workloads.Problem("thin", 4096, 8, 1000, "bf16", "f32")
+    pl = plan_of(p)
+    assert pl["kernel"] == "transpose_b+gemm_bf16_nn_thin"
+    assert (pl["tile_m"], pl["grid"], pl["splits"], pl["launches"]) == (8, 512, 1, 2)
+    assert pl["workspace_bytes"] == 16128          # 8 rows of 2000 bytes, 256-byte aligned
+    assert plan_of(p.with_(batch=3))["workspace_bytes"] == 3 * 16000 + 128
+    assert plan_of(p.with_(ldb=1000))["workspace_bytes"] == 16128
+    for n in (1, 3, 16):
+        pl = plan_of(p.with_(N=n, transpose_b=True))
+        assert pl["kernel"] == "gemm_bf16_nt_thin" and pl["workspace_bytes"] == 0
+    assert "thin" not in plan_of(p.with_(N=17))["kernel"]
+    assert "thin" not in plan_of(p.with_(transpose_a=True))["kernel"]
+    assert "thin" not in plan_of(p.with_(M=512))["kernel"]             # 64 workgroups
+    assert plan_of(p.with_(M=512, batch=4))["grid"] == 256
+    assert "thin" not in plan_of(p.with_(M=2040))["kernel"]            # 255 workgroups
+    assert plan_of(p.with_(a_dtype="i8", c_dtype="i32", alpha=1.0, beta=0.0, K=4093,
+                           ldb=11))["kernel"] == "transpose_b+gemm_i8_nn_thin"
+    assert plan_of(p.with_(alpha=0.0))["kernel"] == "scale_c"
+    os.environ["TCGEMM_TILE"] = "thin"
+    try:
+        assert plan_of(p.with_(M=40))["kernel"] == "transpose_b+gemm_bf16_nn_thin"
+        assert "thin" not in plan_of(p.with_(M=40, N=20))["kernel"]
+    finally:
+        del os.environ["TCGEMM_TILE"]
 
 
 def test_plan_packed_batch_strides():
