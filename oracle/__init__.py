@@ -9,7 +9,8 @@ with gcc and marshals numpy arrays.
 The definition it evaluates comes from tensorcore "GEMM" (sections "Surface",
 "Transposes", "Numerical guarantees"), Phobos "Matrix products" (sgemm/hgemm
 epilogue, matmul_t) and tessl "Architecture" ("Integer GEMM", "Fused
-Epilogue"); the C file's header states it in full.
+Epilogue"); the C file's header states it in full.  The fused epilogue
+(bias and activation after alpha/beta) is plain numpy in fp64 below.
 
 Every function of this oracle is pinned by tests/test_oracle.py against facts
 the pages and the mathematics fix (exhaustive codec round trips, ties-to-even,
@@ -19,6 +20,7 @@ extremes); none is "parity unpinned".
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 from typing import Optional, Sequence, Tuple
@@ -208,6 +210,74 @@ def gemm_points(A: np.ndarray, B: np.ndarray, C_in: Optional[np.ndarray],
     if rc != 0:
         raise ValueError("oracle_gemm_points rejected its arguments (code %d)" % rc)
     return rounded, value
+
+
+# ---------------------------------------------------------------- fused epilogue
+# tessl "Architecture", section "Fused Epilogue": the fused form computes
+#   C = activation(alpha * A@B + beta * C_prev + bias)
+# with bias per output column (a row-stride-0 view: every row of C gets the
+# same N values) and the activations none, ReLU and GELU with tanh.  Readings
+# where the page is silent: bias is stored in C's element type (the view is
+# C-shaped); GELU-tanh is 0.5*y*(1 + tanh(sqrt(2/pi)*(y + 0.044715*y^3))),
+# the usual tanh form of GELU, whose clamp on the page only guards an
+# exp-based tanh against overflow and does not change the value; ReLU is
+# max(y, 0).  Evaluated in fp64 on the unrounded value, then rounded once to
+# c_dtype (ties to even) like the plain product.
+ACTIVATIONS = ("none", "relu", "gelu_tanh")
+
+
+def activation(y: np.ndarray, act: str) -> np.ndarray:
+    """The activation, elementwise in fp64."""
+    y = np.asarray(y, dtype=np.float64)
+    if act == "none":
+        return y.copy()
+    if act == "relu":
+        return np.where(y > 0.0, y, 0.0)
+    if act == "gelu_tanh":
+        u = math.sqrt(2.0 / math.pi) * (y + 0.044715 * y * y * y)
+        return 0.5 * y * (1.0 + np.tanh(u))
+    raise ValueError("unknown activation %r" % (act,))
+
+
+def epilogue_values(value: np.ndarray, bias: Optional[np.ndarray], c_dtype: str,
+                    act: str, bias_stride: int = 0) -> np.ndarray:
+    """act(value + bias[z, j]) for value [batch, M, N] (the unrounded
+    alpha*S + beta*C_in); bias holds stored c_dtype values, problem z's N
+    values starting at z*bias_stride (0: one vector for every problem)."""
+    value = np.asarray(value, dtype=np.float64)
+    batch, M, N = value.shape
+    y = value.copy()
+    if bias is not None:
+        b = decode(np.ascontiguousarray(bias).ravel(), c_dtype)
+        for z in range(batch):
+            y[z] += b[z * bias_stride: z * bias_stride + N][None, :]
+    return activation(y, act)
+
+
+def gemm_epilogue(A: np.ndarray, B: np.ndarray, C_in: Optional[np.ndarray], *,
+                  bias: Optional[np.ndarray] = None, bias_stride: int = 0,
+                  act: str = "none", **kw) -> Tuple[np.ndarray, np.ndarray]:
+    """The fused form: gemm()'s arguments plus bias / bias_stride / act.
+    Returns (C_out, value) like gemm(), value being the fp64 result after the
+    epilogue (before rounding to c_dtype)."""
+    if kw.get("a_dtype") == "i8":
+        raise ValueError("the fused epilogue takes float inputs (int8 sums are exact integers)")
+    if act not in ACTIVATIONS:
+        raise ValueError("unknown activation %r" % (act,))
+    kw = dict(kw)
+    kw["want_value"] = True
+    C_out, value = gemm(A, B, C_in, **kw)
+    y = epilogue_values(value, bias, kw["c_dtype"], act, bias_stride)
+    M, N, batch = kw["M"], kw["N"], kw.get("batch", 1)
+    ldc = kw.get("ldc", 0) or N
+    stride_c = kw.get("stride_c", 0)
+    enc = encode(y, kw["c_dtype"])
+    flat = C_out.ravel()
+    for z in range(batch):
+        for i in range(M):
+            o = z * stride_c + i * ldc
+            flat[o:o + N] = enc[z, i]
+    return flat.reshape(C_out.shape), y
 
 
 def rel_frobenius(got: np.ndarray, ref: np.ndarray) -> float:

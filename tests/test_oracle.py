@@ -430,3 +430,107 @@ def test_rel_frobenius():
     assert oracle.rel_frobenius(np.zeros(3), np.zeros(3)) == 0.0
     assert oracle.rel_frobenius(np.ones(3), np.zeros(3)) == math.inf
     assert oracle.rel_frobenius(np.array([3.0, 4.0]), np.array([3.0, 0.0])) == pytest.approx(4 / 3)
+
+
+# ----------------------------------------------------------------- fused epilogue
+def encode_lib(x, dtype):
+    """Encode exactly representable values with a library (not the oracle)."""
+    x = np.asarray(x, dtype=np.float64)
+    if dtype == "f32":
+        return x.astype(np.float32)
+    if dtype == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    t = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def gelu_erf(x):
+    """GELU by its definition x * Phi(x), with the error function."""
+    return np.array([0.5 * v * (1.0 + math.erf(v / math.sqrt(2.0))) for v in np.ravel(x)])
+
+
+def test_gelu_tanh_is_within_the_approximation_bound_of_erf_gelu():
+    """The tanh form stays within 5e-4 of x*Phi(x) everywhere (its known
+    worst case is about 4.7e-4, near |x| = 2.7); a dropped cubic term, a
+    wrong constant or a sign error misses by far more."""
+    x = np.linspace(-8.0, 8.0, 40001)
+    g = oracle.activation(x, "gelu_tanh")
+    d = np.abs(g - gelu_erf(x))
+    assert d.max() < 5e-4
+    assert d.max() > 1e-4          # it is the approximation, not erf itself
+    no_cubic = 0.5 * x * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * x))
+    assert np.abs(no_cubic - gelu_erf(x)).max() > 1e-2
+
+
+def test_gelu_tanh_identities():
+    """gelu(x) - gelu(-x) = x for the tanh form (tanh is odd); gelu(0) = 0;
+    gelu(x) = x once tanh has saturated to 1 in fp64; gelu(-x) -> 0."""
+    x = np.linspace(-6.0, 6.0, 1201)
+    g, gm = oracle.activation(x, "gelu_tanh"), oracle.activation(-x, "gelu_tanh")
+    assert np.allclose(g - gm, x, rtol=0, atol=1e-12)
+    assert oracle.activation(np.array([0.0]), "gelu_tanh")[0] == 0.0
+    big = np.array([20.0, 50.0, 1000.0])
+    assert np.array_equal(oracle.activation(big, "gelu_tanh"), big)
+    assert np.all(np.abs(oracle.activation(-big, "gelu_tanh")) < 1e-30)
+
+
+def test_relu_and_none():
+    x = np.array([-3.5, -0.0, 0.0, 1e-30, 2.25])
+    assert oracle.activation(x, "relu").tolist() == [0.0, 0.0, 0.0, 1e-30, 2.25]
+    assert oracle.activation(x, "none").tolist() == x.tolist()
+    with pytest.raises(ValueError):
+        oracle.activation(x, "tanh")
+
+
+@pytest.mark.parametrize("dtype", FLOAT_TYPES)
+def test_epilogue_closed_form_bias_per_column(dtype):
+    """A = B = ones gives S = K in every entry; with alpha, beta, C_in = c0
+    and bias[j] = j - 5 the pre-activation value is exactly
+    alpha*K + beta*c0 + j - 5, the same in every row (bias is per column)."""
+    M, N, K = 7, 11, 6
+    alpha, beta, c0 = 0.5, 2.0, 0.25
+    A = encode_lib(np.ones((M, K)), dtype)
+    B = encode_lib(np.ones((K, N)), dtype)
+    C = encode_lib(np.full((M, N), c0), dtype)
+    bias = encode_lib(np.arange(N) - 5.0, dtype)
+    kw = dict(M=M, N=N, K=K, a_dtype=dtype, c_dtype=dtype, alpha=alpha, beta=beta)
+    pre = alpha * K + beta * c0 + (np.arange(N) - 5.0)          # exact, per column
+    for act, want in (("none", pre), ("relu", np.maximum(pre, 0.0))):
+        out, val = oracle.gemm_epilogue(A, B, C, bias=bias, act=act, **kw)
+        assert np.array_equal(val[0], np.broadcast_to(want, (M, N)))
+        assert np.array_equal(lib_decode(out, dtype).reshape(M, N), np.broadcast_to(want, (M, N)))
+    out, val = oracle.gemm_epilogue(A, B, C, bias=bias, act="gelu_tanh", **kw)
+    assert np.allclose(val[0], np.broadcast_to(gelu_erf(pre), (M, N)), rtol=0, atol=5e-4)
+    # no bias and no activation is the plain product, bit for bit
+    o1, v1 = oracle.gemm_epilogue(A, B, C, **kw)
+    o2, v2 = oracle.gemm(A, B, C, **kw)
+    assert np.array_equal(o1, o2) and np.array_equal(v1, v2)
+
+
+def test_epilogue_batched_bias_stride_and_unread_c():
+    """Problem z adds its own bias vector (bias_stride = N); with stride 0
+    every problem adds the first.  beta = 0 leaves a NaN C_in unread."""
+    rng = np.random.default_rng(21)
+    b, M, N, K = 3, 4, 5, 8
+    A = draw(rng, "bf16", (b, M, K))
+    B = draw(rng, "bf16", (b, K, N))
+    bias = encode_lib(np.arange(b * N, dtype=np.float64) - 7.0, "f32")
+    kw = dict(M=M, N=N, K=K, a_dtype="bf16", c_dtype="f32", batch=b,
+              stride_a=M * K, stride_b=K * N, stride_c=M * N)
+    Cnan = np.full(b * M * N, np.nan, dtype=np.float32)
+    _, v0 = oracle.gemm(A, B, None, **kw)
+    out, v = oracle.gemm_epilogue(A, B, Cnan, bias=bias, bias_stride=N, act="relu", **kw)
+    want = np.maximum(v0 + (np.arange(b * N) - 7.0).reshape(b, 1, N), 0.0)
+    assert np.array_equal(v, want)
+    assert not np.isnan(out).any()
+    _, v_shared = oracle.gemm_epilogue(A, B, None, bias=bias, bias_stride=0, **kw)
+    assert np.array_equal(v_shared, v0 + (np.arange(N) - 7.0)[None, None, :])
+
+
+def test_epilogue_rejects_int8_and_unknown_activation():
+    A = np.zeros(4, dtype=np.int8)
+    with pytest.raises(ValueError):
+        oracle.gemm_epilogue(A, A, None, M=2, N=2, K=2, a_dtype="i8", c_dtype="i32", act="relu")
+    B = np.zeros(4, dtype=np.float32)
+    with pytest.raises(ValueError):
+        oracle.gemm_epilogue(B, B, None, M=2, N=2, K=2, a_dtype="f32", c_dtype="f32", act="gelu")
