@@ -128,10 +128,18 @@ def main():
     # beta != 0 reads C: every step restores nothing, so C drifts; that does
     # not change the work done.
 
+    # fused-epilogue workloads: one bias vector (C's type) and an activation
+    act = p.extra.get("act")
+    bias = to_dev(workloads.make_bias(p), p.c_dtype)[0] if p.extra.get("bias") else None
+
     def step(i):
         a, b, c, _ = sets[i % n_sets]
-        tg.gemm(a, b, c, alpha=p.alpha, beta=p.beta, transpose_a=p.transpose_a,
-                transpose_b=p.transpose_b)
+        if act is None and bias is None:
+            tg.gemm(a, b, c, alpha=p.alpha, beta=p.beta, transpose_a=p.transpose_a,
+                    transpose_b=p.transpose_b)
+        else:
+            tg.gemm(a, b, c, alpha=p.alpha, beta=p.beta, transpose_a=p.transpose_a,
+                    transpose_b=p.transpose_b, bias=bias, activation=act)
 
     for i in range(args.warmup):
         step(i)
@@ -213,7 +221,8 @@ def main():
         "config": {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "batch": p.batch,
                    "layout": p.layout, "a_dtype": p.a_dtype, "c_dtype": p.c_dtype,
                    "alpha": p.alpha, "beta": p.beta, "input_sets": n_sets,
-                   "parallelism": "none (1 GPU)"},
+                   "parallelism": "none (1 GPU)",
+                   **({"epilogue": dict(p.extra)} if p.extra else {})},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

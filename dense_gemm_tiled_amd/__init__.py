@@ -68,6 +68,16 @@ class BatchedDescT(ctypes.Structure):
                 ("stride_c", ctypes.c_int64)]
 
 
+class EpilogueT(ctypes.Structure):
+    """tc_epilogue"""
+    _fields_ = [("bias", ctypes.c_void_p), ("bias_stride", ctypes.c_int64),
+                ("activation", ctypes.c_int)]
+
+
+# tc_activation_t
+ACTIVATIONS = {"none": 0, "relu": 1, "gelu_tanh": 2}
+
+
 class PlanInfoT(ctypes.Structure):
     """tc_plan_info"""
     _fields_ = [("kernel", ctypes.c_char * 128),
@@ -93,6 +103,10 @@ _SIGNATURES = {
     "tc_gemm_batched": (ctypes.c_int, [_VP, ctypes.POINTER(BatchedDescT), _VP, _VP, _VP]),
     "tc_gemm_batched_async": (ctypes.c_int,
                               [_VP, ctypes.POINTER(BatchedDescT), _VP, _VP, _VP, _VP]),
+    "tc_gemm_epilogue": (ctypes.c_int, [_VP, ctypes.POINTER(BatchedDescT),
+                                        ctypes.POINTER(EpilogueT), _VP, _VP, _VP]),
+    "tc_gemm_epilogue_async": (ctypes.c_int, [_VP, ctypes.POINTER(BatchedDescT),
+                                              ctypes.POINTER(EpilogueT), _VP, _VP, _VP, _VP]),
     "tc_gemm_plan": (ctypes.c_int, [_VP, ctypes.POINTER(BatchedDescT),
                                     ctypes.POINTER(PlanInfoT)]),
     "tc_last_kernel": (ctypes.c_char_p, [_VP]),
@@ -242,18 +256,53 @@ def make_desc(a, b, c, alpha: float = 1.0, beta: float = 0.0,
 
 
 # ------------------------------------------------------------------ API
+def make_epilogue(c, bias=None, activation: Optional[str] = None) -> EpilogueT:
+    """tc_epilogue for output c: bias is a GPU tensor of c's dtype holding N
+    values per problem ([N], shared by a batch, or [batch, N] with contiguous
+    rows); activation is None, "none", "relu" or "gelu_tanh"."""
+    ep = EpilogueT()
+    act = "none" if activation is None else activation
+    if act not in ACTIVATIONS:
+        raise TcGemmError(1, "unknown activation %r" % (activation,))
+    ep.activation = ACTIVATIONS[act]
+    ep.bias, ep.bias_stride = None, 0
+    if bias is not None:
+        N = int(c.size(-1))
+        if not bias.is_cuda or bias.dtype != c.dtype:
+            raise TcGemmError(1, "bias must be a GPU tensor of c's dtype")
+        if int(bias.size(-1)) != N or (bias.size(-1) > 1 and bias.stride(-1) != 1):
+            raise TcGemmError(1, "bias must hold N contiguous values per problem")
+        if bias.dim() == 2:
+            batch = int(c.size(0)) if c.dim() == 3 else 1
+            if int(bias.size(0)) != batch:
+                raise TcGemmError(1, "bias has %d rows for %d problems" % (bias.size(0), batch))
+            ep.bias_stride = int(bias.stride(0))
+        elif bias.dim() != 1:
+            raise TcGemmError(1, "bias must be 1-D or 2-D")
+        ep.bias = bias.data_ptr()
+    return ep
+
+
 def gemm(a, b, c, *, alpha: float = 1.0, beta: float = 0.0, transpose_a: bool = False,
-         transpose_b: bool = False, stream=None):
-    """c = alpha * op(a) @ op(b) + beta * c on c's device, enqueued on torch's
-    current stream (or `stream`).  Returns c."""
+         transpose_b: bool = False, stream=None, bias=None, activation: Optional[str] = None):
+    """c = activation(alpha * op(a) @ op(b) + beta * c + bias) on c's device,
+    enqueued on torch's current stream (or `stream`).  Without bias and
+    activation this is the plain product (tc_gemm_batched_async), with them the
+    fused epilogue (tc_gemm_epilogue_async).  Returns c."""
     if not (a.is_cuda and b.is_cuda and c.is_cuda):
         raise TcGemmError(1, "a, b and c must be GPU tensors")
     device = c.device.index if c.device.index is not None else 0
     desc = make_desc(a, b, c, alpha, beta, transpose_a, transpose_b)
     lib = load_library()
     ctx, s = _torch_stream(device, stream)
-    st = lib.tc_gemm_batched_async(ctx, ctypes.byref(desc), _VP(a.data_ptr()),
-                                   _VP(b.data_ptr()), _VP(c.data_ptr()), s)
+    if bias is None and activation is None:
+        st = lib.tc_gemm_batched_async(ctx, ctypes.byref(desc), _VP(a.data_ptr()),
+                                       _VP(b.data_ptr()), _VP(c.data_ptr()), s)
+    else:
+        ep = make_epilogue(c, bias, activation)
+        st = lib.tc_gemm_epilogue_async(ctx, ctypes.byref(desc), ctypes.byref(ep),
+                                        _VP(a.data_ptr()), _VP(b.data_ptr()),
+                                        _VP(c.data_ptr()), s)
     _check(st, ctx)
     return c
 

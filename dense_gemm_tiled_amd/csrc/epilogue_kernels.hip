@@ -5,9 +5,15 @@
 namespace tcg {
 namespace {
 
+template <int CDT>
+__device__ inline EpiState epi_of(const EpilogueArgs &a, int z) {
+    return make_epi<CDT>(a.bias, a.bias_stride, a.act, a.epi, z, a.N);
+}
+
 // ---------------------------------------------------------------------------
 // Split-K reduction: C = round(alpha * sum_s partial[s] + beta * C_old), the
-// slices summed in ascending s so the result is the same on every run.
+// slices summed in ascending s so the result is the same on every run; the
+// fused epilogue, when one is on, runs here (the partials have none).
 // One thread per 4 consecutive outputs of a row.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const EpilogueArgs a) {
@@ -70,13 +76,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const EpilogueArgs a
         }
     }
     switch (a.c_dtype) {
-    case DT_F32: finish4<DT_F32>(rc, coff, nvalid, cvec, a.alpha, a.beta, s4); break;
-    case DT_BF16: finish4<DT_BF16>(rc, coff, nvalid, cvec, a.alpha, a.beta, s4); break;
-    default: finish4<DT_F16>(rc, coff, nvalid, cvec, a.alpha, a.beta, s4); break;
+    case DT_F32: finish4<DT_F32>(rc, coff, nvalid, cvec, a.alpha, a.beta, s4, epi_of<DT_F32>(a, z), n); break;
+    case DT_BF16: finish4<DT_BF16>(rc, coff, nvalid, cvec, a.alpha, a.beta, s4, epi_of<DT_BF16>(a, z), n); break;
+    default: finish4<DT_F16>(rc, coff, nvalid, cvec, a.alpha, a.beta, s4, epi_of<DT_F16>(a, z), n); break;
     }
 }
 
-// alpha == 0: C = beta * C (beta == 0 writes zeros without reading C).
+// alpha == 0: C = beta * C (beta == 0 writes zeros without reading C), then
+// the fused epilogue when one is on.
 __global__ __launch_bounds__(256) void scale_c_kernel(const EpilogueArgs a) {
     const int nq = (a.N + 3) / 4;
     const int64_t total = (int64_t)a.batch * a.M * nq;
@@ -94,9 +101,9 @@ __global__ __launch_bounds__(256) void scale_c_kernel(const EpilogueArgs a) {
     float v[4] = {0.f, 0.f, 0.f, 0.f};
     // alpha = 1 on zeros keeps them zero; finish4 then adds beta * C_old.
     switch (a.c_dtype) {
-    case DT_F32: finish4<DT_F32>(rc, coff, nvalid, cvec, 1.f, a.beta, v); break;
-    case DT_BF16: finish4<DT_BF16>(rc, coff, nvalid, cvec, 1.f, a.beta, v); break;
-    case DT_F16: finish4<DT_F16>(rc, coff, nvalid, cvec, 1.f, a.beta, v); break;
+    case DT_F32: finish4<DT_F32>(rc, coff, nvalid, cvec, 1.f, a.beta, v, epi_of<DT_F32>(a, z), n); break;
+    case DT_BF16: finish4<DT_BF16>(rc, coff, nvalid, cvec, 1.f, a.beta, v, epi_of<DT_BF16>(a, z), n); break;
+    case DT_F16: finish4<DT_F16>(rc, coff, nvalid, cvec, 1.f, a.beta, v, epi_of<DT_F16>(a, z), n); break;
     default: {
         int iv[4] = {0, 0, 0, 0};
         store_i4(rc, coff, nvalid, cvec, iv);

@@ -287,10 +287,16 @@ struct FragReader {
 // op_begin(q) .. op_begin(q + 1) - 1.
 constexpr int op_begin(int q, int n, int qn) { return (q * n + qn - 1) / qn; }
 
+// Epilogue variants of the kernel: beta == 0 and no fused epilogue; beta != 0
+// (16-bit C tiles staged through LDS); the fused epilogue (bias and
+// activation, any beta, C_old read per block).  The last one is a separate
+// instantiation so that its code does not weigh on the other two.
+constexpr int EPI_PLAIN = 0, EPI_BETA = 1, EPI_FUSED = 2;
+
 // BM x BN tile, NW waves (2 along M, NW/2 along N), OCC workgroups per CU;
-// BETA: beta != 0 (the epilogue reads C).
+// EPI: one of the epilogue variants above.
 template <int DT, bool TA, bool TB, int OUT, int BM, int BN, int NW, int OCC, bool KMASK,
-          bool BETA>
+          int EPI>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(NW / 4 * OCC, NW / 4 * OCC)))
 void gemm_dma_kernel(const GemmArgs args) {
@@ -492,7 +498,7 @@ void gemm_dma_kernel(const GemmArgs args) {
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cb, args.c_extent - c_org);
     const bool vec = args.c_vec_ok != 0;
     const int ldc = args.ldc;
-    const float alpha = args.alpha, beta = BETA ? args.beta : 0.f;
+    const float alpha = args.alpha, beta = EPI != EPI_PLAIN ? args.beta : 0.f;
 
     // beta != 0 with a 16-bit C tile that lies wholly inside C and whose
     // rows are whole 16-byte chunks: the tile (BM x BN x 2 bytes, the size of
@@ -505,7 +511,7 @@ void gemm_dma_kernel(const GemmArgs args) {
     constexpr int CSW = CRB >= 512 ? 2 : 1;
     static_assert(BM * CRB <= 2 * STAGE, "the C tile fits the operand stages");
     bool c_lds = false;
-    if constexpr (BETA && (OUT == DT_F16 || OUT == DT_BF16)) {
+    if constexpr (EPI == EPI_BETA && (OUT == DT_F16 || OUT == DT_BF16)) {
         c_lds = beta != 0.f && args.c_dma_ok != 0 && m0 + BM <= M && n0 + BN <= N;
         if (c_lds) {
             // every wave is done with the operand stages
@@ -521,6 +527,16 @@ void gemm_dma_kernel(const GemmArgs args) {
             }
             asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
         }
+    }
+    [[maybe_unused]] const EpiState ep = make_epi<OUT == DT_I32 ? DT_F32 : OUT>(
+        args.bias, args.bias_stride, args.act, args.epi, z, N);
+    // fused epilogue: the tile's bias into the operand stages, once every
+    // wave is done with them
+    [[maybe_unused]] float *lds_bias = reinterpret_cast<float *>(smem);
+    if constexpr (EPI == EPI_FUSED) {
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        stage_bias<OUT>(ep, n0, N, BN, lds_bias, tid, NW * 64);
+        __syncthreads();
     }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -541,7 +557,7 @@ void gemm_dma_kernel(const GemmArgs args) {
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e];
-                if constexpr (BETA && (OUT == DT_F16 || OUT == DT_BF16)) {
+                if constexpr (EPI == EPI_BETA && (OUT == DT_F16 || OUT == DT_BF16)) {
                     if (c_lds) {
                         // C_old from the LDS image (8 bytes: 4 values)
                         const int q = (nl * 2) / 16;
@@ -558,7 +574,12 @@ void gemm_dma_kernel(const GemmArgs args) {
                         continue;
                     }
                 }
-                finish4<OUT>(rc, off, nvalid, vec, alpha, beta, v);
+                if constexpr (EPI == EPI_FUSED) {
+                    float b[4];
+                    read_bias4(lds_bias, nl, b);
+                    finish4<OUT>(rc, off, nvalid, vec, alpha, beta, v, ep, b);
+                }
+                else finish4<OUT>(rc, off, nvalid, vec, alpha, beta, v);
             }
         }
     }

@@ -31,22 +31,31 @@ hipError_t launch_one(const GemmArgs &args, int64_t grid, hipStream_t stream) {
         constexpr int T = tile_shape(CLS).bm;
         constexpr int NW = CLS == TILE_256_DMA8 ? 8 : 4;
         constexpr int OCC = CLS == TILE_128_DMA ? 2 : 1;
-        // and the epilogue reads C only when beta != 0 (float outputs)
+        // and the epilogue variant: C read only when beta != 0, the fused
+        // epilogue only when one is asked for (float outputs)
         constexpr int BK = kLdsRowBytes / dt_size(TCG_DT);
         constexpr bool FLOAT_OUT = OUT == DT_F32 || OUT == DT_F16 || OUT == DT_BF16;
-        const bool kmask = args.K % BK != 0, beta = FLOAT_OUT && args.beta != 0.f;
+        const bool kmask = args.K % BK != 0;
+        const int epi = !FLOAT_OUT ? EPI_PLAIN
+                      : args.epi   ? EPI_FUSED
+                      : args.beta != 0.f ? EPI_BETA : EPI_PLAIN;
         const dim3 g((unsigned)grid), b(NW * 64);
-#define TCG_DMA(KM, BE) \
-    hipLaunchKernelGGL((gemm_dma_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, OUT, T, T, NW, OCC, KM, BE>), \
+#define TCG_DMA(KM, EP) \
+    hipLaunchKernelGGL((gemm_dma_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, OUT, T, T, NW, OCC, KM, EP>), \
                        g, b, 0, stream, args)
         if constexpr (FLOAT_OUT) {
-            if (kmask && beta) TCG_DMA(true, true);
-            else if (kmask) TCG_DMA(true, false);
-            else if (beta) TCG_DMA(false, true);
-            else TCG_DMA(false, false);
+            if (kmask) {
+                if (epi == EPI_FUSED) TCG_DMA(true, EPI_FUSED);
+                else if (epi == EPI_BETA) TCG_DMA(true, EPI_BETA);
+                else TCG_DMA(true, EPI_PLAIN);
+            } else {
+                if (epi == EPI_FUSED) TCG_DMA(false, EPI_FUSED);
+                else if (epi == EPI_BETA) TCG_DMA(false, EPI_BETA);
+                else TCG_DMA(false, EPI_PLAIN);
+            }
         } else {
-            if (kmask) TCG_DMA(true, false);
-            else TCG_DMA(false, false);
+            if (kmask) TCG_DMA(true, EPI_PLAIN);
+            else TCG_DMA(false, EPI_PLAIN);
         }
 #undef TCG_DMA
         return hipGetLastError();

@@ -382,10 +382,104 @@ __device__ inline void store_i4(__amdgpu_buffer_rsrc_t r, int off, int nvalid, b
     }
 }
 
+// Fused epilogue of one problem (tessl "Architecture", "Fused Epilogue"):
+// after alpha * acc + beta * C_old, add the column's bias (stored in C's
+// element type, one vector per problem) and apply the activation, still in
+// fp32 registers, before the single rounding to the output type.
+struct EpiState {
+    __amdgpu_buffer_rsrc_t rb;   // this problem's bias vector (empty range without one)
+    int act;
+    bool bias;
+    bool on;
+};
+
+template <int CDT>
+__device__ inline EpiState make_epi(const void *bias, int64_t bias_stride, int act, int epi, int z,
+                                    int N) {
+    constexpr int CES = dt_size(CDT);
+    EpiState e;
+    e.on = epi != 0;
+    e.act = act;
+    e.bias = bias != nullptr;
+    const char *b = e.bias ? static_cast<const char *>(bias) + z * bias_stride * CES : nullptr;
+    e.rb = make_rsrc(b, e.bias ? (int64_t)N * CES : 0);
+    return e;
+}
+
+// GELU, tanh form: 0.5 y (1 + tanh(u)) with u = sqrt(2/pi) (y + 0.044715 y^3).
+// Since 1 + tanh(u) = 2 / (1 + exp(-2u)), this is y / (1 + exp(-2u)): one
+// hardware exp2 (exp(-2u) = 2^(-2u log2 e)) and one reciprocal.  Large
+// negative u gives exp = inf and the value 0 (-0 for y < 0); large positive
+// u gives y.
+__device__ inline float gelu_tanh(float y) {
+    const float u = 0.7978845608028654f * __builtin_fmaf(0.044715f * y, y * y, y);
+    const float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * u);
+    return y * __builtin_amdgcn_rcpf(1.f + e);
+}
+
+// The bias of columns n .. n + nvalid - 1 (zero past them or without a bias).
+template <int CDT>
+__device__ inline void load_bias4(const EpiState &e, int n, int nvalid, float (&b)[4]) {
+    if (e.bias) {
+        load_c4<CDT>(e.rb, n * dt_size(CDT), nvalid, true, b);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) b[q] = 0.f;
+    }
+}
+
+// The BN bias values of the tile starting at column n0, as fp32 in LDS (zero
+// past N or without a bias): staged once per workgroup, so the epilogue reads
+// each lane's four columns from LDS instead of from memory behind its own C
+// stores.  The caller makes the LDS free before and synchronizes after.
+template <int CDT>
+__device__ inline void stage_bias(const EpiState &e, int n0, int N, int bn, float *lds_bias, int tid,
+                                  int nthreads) {
+    constexpr int CES = dt_size(CDT);
+    for (int t = tid; t < bn; t += nthreads) {
+        float b = 0.f;
+        if (e.bias && n0 + t < N) {
+            const int off = (n0 + t) * CES;
+            if constexpr (CDT == DT_F32) b = as_f32(__builtin_amdgcn_raw_buffer_load_b32(e.rb, off, 0, 0));
+            else if constexpr (CDT == DT_BF16) b = from_bf16_bits(__builtin_amdgcn_raw_buffer_load_b16(e.rb, off, 0, 0));
+            else b = from_f16_bits(__builtin_amdgcn_raw_buffer_load_b16(e.rb, off, 0, 0));
+        }
+        lds_bias[t] = b;
+    }
+}
+
+// Four staged bias values from tile column nl (a multiple of 4).
+__device__ inline void read_bias4(const float *lds_bias, int nl, float (&b)[4]) {
+    const f32x4 w = *reinterpret_cast<const f32x4 *>(lds_bias + nl);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) b[q] = w[q];
+}
+
+// v + b, then the activation.
+__device__ inline void act4(const EpiState &e, const float (&b)[4], float (&v)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] += b[q];
+    if (e.act == ACT_RELU) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = v[q] > 0.f ? v[q] : 0.f;
+    } else if (e.act == ACT_GELU_TANH) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = gelu_tanh(v[q]);
+    }
+}
+
+// Bias of columns n .. n + nvalid - 1, then the activation.
+template <int CDT>
+__device__ inline void apply_epi(const EpiState &e, int n, int nvalid, float (&v)[4]) {
+    float b[4];
+    load_bias4<CDT>(e, n, nvalid, b);
+    act4(e, b, v);
+}
+
 // alpha * acc + beta * C_old for 4 values, C_old read only when beta != 0.
 template <int CDT>
-__device__ inline void finish4(__amdgpu_buffer_rsrc_t rc, int off, int nvalid, bool vec,
-                               float alpha, float beta, float (&v)[4]) {
+__device__ inline void scale4(__amdgpu_buffer_rsrc_t rc, int off, int nvalid, bool vec, float alpha,
+                              float beta, float (&v)[4]) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] *= alpha;
     if (beta != 0.f) {
@@ -394,6 +488,32 @@ __device__ inline void finish4(__amdgpu_buffer_rsrc_t rc, int off, int nvalid, b
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(beta, old[e], v[e]);
     }
+}
+
+// scale4, then the store.
+template <int CDT>
+__device__ inline void finish4(__amdgpu_buffer_rsrc_t rc, int off, int nvalid, bool vec,
+                               float alpha, float beta, float (&v)[4]) {
+    scale4<CDT>(rc, off, nvalid, vec, alpha, beta, v);
+    store_c4<CDT>(rc, off, nvalid, vec, v);
+}
+
+// scale4, the fused epilogue when one is on (n: column of v[0]), the store.
+template <int CDT>
+__device__ inline void finish4(__amdgpu_buffer_rsrc_t rc, int off, int nvalid, bool vec,
+                               float alpha, float beta, float (&v)[4], const EpiState &ep, int n) {
+    scale4<CDT>(rc, off, nvalid, vec, alpha, beta, v);
+    if (ep.on) apply_epi<CDT>(ep, n, nvalid, v);
+    store_c4<CDT>(rc, off, nvalid, vec, v);
+}
+
+// The same with the bias of the four columns already loaded.
+template <int CDT>
+__device__ inline void finish4(__amdgpu_buffer_rsrc_t rc, int off, int nvalid, bool vec,
+                               float alpha, float beta, float (&v)[4], const EpiState &ep,
+                               const float (&b)[4]) {
+    scale4<CDT>(rc, off, nvalid, vec, alpha, beta, v);
+    act4(ep, b, v);
     store_c4<CDT>(rc, off, nvalid, vec, v);
 }
 
@@ -543,6 +663,16 @@ __global__ __launch_bounds__(256, Occupancy<CLS>::value) void gemm_kernel(const 
         const bool vec = args.c_vec_ok != 0;
         const int ldc = args.ldc;
         const float alpha = args.alpha, beta = args.beta;
+        const EpiState ep = make_epi<OUT == DT_I32 ? DT_F32 : OUT>(args.bias, args.bias_stride,
+                                                                   args.act, args.epi, z, N);
+        // fused epilogue: the tile's bias into the (free) LDS
+        float *lds_bias = reinterpret_cast<float *>(smem);
+        if constexpr (OUT != DT_I32) {
+            if (ep.on) {
+                stage_bias<OUT>(ep, n0, N, BN, lds_bias, tid, 256);
+                __syncthreads();
+            }
+        }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int ml = ml0 + i * 16;
@@ -562,7 +692,13 @@ __global__ __launch_bounds__(256, Occupancy<CLS>::value) void gemm_kernel(const 
                     float v[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e];
-                    finish4<OUT>(rc, off, nvalid, vec, alpha, beta, v);
+                    if (ep.on) {
+                        float b[4];
+                        read_bias4(lds_bias, nl, b);
+                        finish4<OUT>(rc, off, nvalid, vec, alpha, beta, v, ep, b);
+                    } else {
+                        finish4<OUT>(rc, off, nvalid, vec, alpha, beta, v);
+                    }
                 }
             }
         }

@@ -58,6 +58,9 @@ constexpr int kXcds = 8;               // MI355X: 8 XCDs x 32 CUs
 // sums of one split-K slice (fp32, or int32 for int8 inputs).
 constexpr int OUT_PARTIAL = 5;
 
+// Fused-epilogue activations (tessl "Architecture", "Fused Epilogue").
+constexpr int ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_TANH = 2;
+
 // Everything a GEMM launch needs; passed by value as the kernel argument.
 struct GemmArgs {
     const void *A;
@@ -76,6 +79,11 @@ struct GemmArgs {
     int32_t band;                  // tile-order band height (<= 0: row-major)
     int32_t c_vec_ok;              // 4 complete C values go as one vector access
     int32_t c_dma_ok;              // C rows, batch stride and base are whole 16-byte chunks
+    // fused epilogue: out = act(alpha*acc + beta*C_old + bias[n])
+    const void *bias;              // N values of c_dtype per problem, or null
+    int64_t bias_stride;           // elements between the problems' bias vectors
+    int32_t act;                   // ACT_*
+    int32_t epi;                   // bias != null || act != ACT_NONE
 };
 
 // Arguments of the split-K reduction and of the alpha == 0 scaling kernel.
@@ -90,6 +98,9 @@ struct EpilogueArgs {
     int32_t acc_is_int;
     int32_t c_vec_ok;          // 4 complete C values go as one vector access
     float alpha, beta;
+    const void *bias;          // fused epilogue, as in GemmArgs
+    int64_t bias_stride;
+    int32_t act, epi;
 };
 
 // Operand repacking: `rows` rows of `row_bytes` bytes, read at pitch

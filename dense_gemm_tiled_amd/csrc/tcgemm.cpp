@@ -49,6 +49,14 @@ constexpr int kMaxTileRows = 256;
 
 std::string g_plan_error;   // error text of tc_gemm_plan(NULL, ...)
 
+// The fused epilogue of a call (none: act == ACT_NONE and no bias).
+struct Epilogue {
+    const void *bias = nullptr;   // N values of c_dtype per problem
+    int64_t bias_stride = 0;      // elements between problems' vectors
+    int act = ACT_NONE;
+    bool on() const { return bias != nullptr || act != ACT_NONE; }
+};
+
 // Everything validation derives from a descriptor.
 struct Problem {
     int32_t M, N, K, batch;
@@ -566,8 +574,8 @@ tc_status_t create_stream(tc_context *ctx, tc_stream **out, hipStream_t existing
 // Enqueue the launches of one planned problem (packs, GEMM, reduction) on
 // stream s; their names are appended to *names.
 tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan &plan,
-                    const void *A, const void *B, void *C, bool main_part, std::string *names,
-                    std::string *err) {
+                    const void *A, const void *B, void *C, const Epilogue &epi, bool main_part,
+                    std::string *names, std::string *err) {
     Plan pl = plan;
     const bool aligned[2] = {(uintptr_t)A % 16 == 0, (uintptr_t)B % 16 == 0};
     layout_workspace(p, &pl, aligned);   // a misaligned base pointer is packed too
@@ -594,6 +602,10 @@ tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan 
     ea.acc_is_int = p.dt == TC_I8;
     ea.alpha = p.alpha; ea.beta = p.beta;
     ea.c_vec_ok = c_vec_ok;
+    ea.bias = epi.bias;
+    ea.bias_stride = epi.bias_stride;
+    ea.act = epi.act;
+    ea.epi = epi.on();
 
     hipError_t e = hipSuccess;
     if (p.alpha == 0.0f) {
@@ -671,6 +683,10 @@ tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan 
         ga.c_vec_ok = c_vec_ok;
         ga.c_dma_ok = (p.ldc * ces) % 16 == 0 && (p.stride_c * ces) % 16 == 0 &&
                       (uintptr_t)C % 16 == 0;
+        ga.bias = epi.bias;
+        ga.bias_stride = epi.bias_stride;
+        ga.act = epi.act;
+        ga.epi = epi.on();
         // an armed measurement brackets the GEMM kernel alone (one call only)
         hipEvent_t ev_start = nullptr, ev_end = nullptr;
         if (main_part) {
@@ -702,9 +718,44 @@ tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan 
     return TC_OK;
 }
 
+// Bytes the bias vectors of all problems span (0 without a bias).
+int64_t epilogue_bias_bytes(const Problem &p, const Epilogue &e) {
+    if (!e.bias) return 0;
+    return ((int64_t)(p.batch - 1) * e.bias_stride + p.N) * dt_size(p.cdt);
+}
+
+// The fused epilogue (tessl "Architecture", "Fused Epilogue"): it needs the
+// register accumulator of a float GEMM, so int8 (exact int32 results) is
+// refused rather than run as separate passes; the bias is read while C is
+// written, so it may not overlap C.
+tc_status_t validate_epilogue(const Problem &p, const tc_epilogue *ep, const void *C, Epilogue *out,
+                              std::string *err) {
+    if (ep->activation != TC_ACT_NONE && ep->activation != TC_ACT_RELU &&
+        ep->activation != TC_ACT_GELU_TANH)
+        return fail(err, TC_ERR_INVALID_ARGUMENT, "unknown activation %d", (int)ep->activation);
+    if (p.dt == TC_I8)
+        return fail(err, TC_ERR_UNSUPPORTED,
+                    "the fused epilogue takes float inputs; int8 results are exact int32 sums");
+    if (ep->bias_stride < 0) return fail(err, TC_ERR_INVALID_ARGUMENT, "bias_stride must be >= 0");
+    out->bias = ep->bias;
+    out->bias_stride = p.batch > 1 ? ep->bias_stride : 0;
+    out->act = ep->activation == TC_ACT_RELU ? ACT_RELU
+             : ep->activation == TC_ACT_GELU_TANH ? ACT_GELU_TANH : ACT_NONE;
+    if (out->bias) {
+        int64_t t, bytes;
+        if (__builtin_mul_overflow((int64_t)(p.batch - 1), out->bias_stride, &t) ||
+            __builtin_add_overflow(t, (int64_t)p.N, &t) ||
+            __builtin_mul_overflow(t, (int64_t)dt_size(p.cdt), &bytes))
+            return fail(err, TC_ERR_OVERFLOW, "bias extent overflows 64 bits");
+        if (ranges_overlap(C, p.c_total, out->bias, bytes))
+            return fail(err, TC_ERR_ALIASING, "the bias overlaps C");
+    }
+    return TC_OK;
+}
+
 // Validate, plan and enqueue one (batched) GEMM on stream s.
 tc_status_t run(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A, const void *B,
-                void *C, tc_stream *s, bool sync) {
+                void *C, tc_stream *s, bool sync, const tc_epilogue *ep = nullptr) {
     if (!ctx) return TC_ERR_INVALID_ARGUMENT;
     ctx->last_error.clear();
     std::string *err = &ctx->last_error;
@@ -712,6 +763,8 @@ tc_status_t run(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A, 
     Problem p;
     tc_status_t st = validate(bd, &p, err);
     if (st != TC_OK) return st;
+    Epilogue epi;
+    if (ep && (st = validate_epilogue(p, ep, C, &epi, err)) != TC_OK) return st;
     if (ranges_overlap(C, p.c_total, A, p.a_total) || ranges_overlap(C, p.c_total, B, p.b_total))
         return fail(err, TC_ERR_ALIASING, "C overlaps A or B");
     Plan pl;
@@ -722,6 +775,8 @@ tc_status_t run(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A, 
     if ((st = check_allocation("A", A, p.a_total, err)) != TC_OK) return st;
     if ((st = check_allocation("B", B, p.b_total, err)) != TC_OK) return st;
     if ((st = check_allocation("C", C, p.c_total, err)) != TC_OK) return st;
+    if (epi.bias && (st = check_allocation("bias", epi.bias, epilogue_bias_bytes(p, epi), err)) != TC_OK)
+        return st;
 
     if (!s) {
         if (!ctx->internal && (st = create_stream(ctx, &ctx->internal, nullptr)) != TC_OK) return st;
@@ -735,8 +790,13 @@ tc_status_t run(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A, 
         const void *Ai = static_cast<const char *>(A) + parts.off[i][0] * es;
         const void *Bi = static_cast<const char *>(B) + parts.off[i][1] * es;
         void *Ci = static_cast<char *>(C) + parts.off[i][2] * ces;
+        // a column strip's bias starts at its first column
+        Epilogue epi_i = epi;
+        if (epi.bias && pl.edge == 1 && i == 1)
+            epi_i.bias = static_cast<const char *>(epi.bias) + (int64_t)pl.edge_at * ces;
         if (i) name += "|";
-        if ((st = enqueue(ctx, s, parts.p[i], parts.pl[i], Ai, Bi, Ci, i == 0, &name, err)) != TC_OK)
+        if ((st = enqueue(ctx, s, parts.p[i], parts.pl[i], Ai, Bi, Ci, epi_i, i == 0, &name, err)) !=
+            TC_OK)
             return st;
     }
     ctx->last_kernel = name;
@@ -846,6 +906,25 @@ tc_status_t tc_gemm_batched_async(tc_context *ctx, const tc_gemm_batched_desc *b
         return TC_ERR_INVALID_ARGUMENT;
     }
     return run(ctx, bd, A, B, C, s, false);
+}
+
+tc_status_t tc_gemm_epilogue(tc_context *ctx, const tc_gemm_batched_desc *bd, const tc_epilogue *ep,
+                             const void *A, const void *B, void *C) {
+    if (!ep) {
+        if (ctx) ctx->last_error = "epilogue is NULL";
+        return TC_ERR_INVALID_ARGUMENT;
+    }
+    return run(ctx, bd, A, B, C, nullptr, true, ep);
+}
+
+tc_status_t tc_gemm_epilogue_async(tc_context *ctx, const tc_gemm_batched_desc *bd,
+                                   const tc_epilogue *ep, const void *A, const void *B, void *C,
+                                   tc_stream *s) {
+    if (!ep || !s) {
+        if (ctx) ctx->last_error = !ep ? "epilogue is NULL" : "stream is NULL";
+        return TC_ERR_INVALID_ARGUMENT;
+    }
+    return run(ctx, bd, A, B, C, s, false, ep);
 }
 
 tc_status_t tc_gemm_plan(tc_context *ctx, const tc_gemm_batched_desc *bd, tc_plan_info *info) {

@@ -234,6 +234,8 @@ __global__ __launch_bounds__(kThinThreads) void thin_kernel(const GemmArgs args)
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cb, args.c_extent - c_org);
     if (kl != 0 || m0 + rl >= M) return;
     const int row_off = rl * args.ldc * CES;
+    const EpiState ep = make_epi<OUT == DT_I32 ? DT_F32 : OUT>(args.bias, args.bias_stride, args.act,
+                                                               args.epi, z, N);
 #pragma unroll
     for (int n = 0; n < NS; n += 4) {
         if (n >= N) break;
@@ -243,7 +245,8 @@ __global__ __launch_bounds__(kThinThreads) void thin_kernel(const GemmArgs args)
             store_i4(rc, row_off + n * CES, nvalid, args.c_vec_ok != 0, v);
         } else {
             float v[4] = {acc[n], acc[n + 1], acc[n + 2], acc[n + 3]};
-            finish4<OUT>(rc, row_off + n * CES, nvalid, args.c_vec_ok != 0, args.alpha, args.beta, v);
+            finish4<OUT>(rc, row_off + n * CES, nvalid, args.c_vec_ok != 0, args.alpha, args.beta, v,
+                         ep, n);
         }
     }
 }

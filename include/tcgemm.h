@@ -89,6 +89,34 @@ typedef struct {
     int64_t stride_a, stride_b, stride_c;
 } tc_gemm_batched_desc;
 
+/* Fused epilogue (tessl "Architecture", section "Fused Epilogue"):
+ *
+ *     C = activation(alpha * op(A)@op(B) + beta * C + bias)
+ *
+ * computed while the accumulator is still in registers, so C is written once
+ * and read only when beta != 0 -- no separate bias or activation pass.  bias
+ * is per column: problem z adds bias[z*bias_stride + n] to every row's column
+ * n (the page's row-stride-0 view of a C-shaped tensor), stored in C's
+ * element type (c_dtype).  bias may be NULL (activation only).  Activations:
+ *     TC_ACT_NONE       identity
+ *     TC_ACT_RELU       max(y, 0)
+ *     TC_ACT_GELU_TANH  0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3)))
+ * evaluated in fp32 before the single rounding to c_dtype. */
+typedef enum {
+    TC_ACT_NONE = 0,
+    TC_ACT_RELU = 1,
+    TC_ACT_GELU_TANH = 2
+} tc_activation_t;
+
+typedef struct {
+    const void *bias;             /* device pointer, caller-owned; N values of
+                                     c_dtype per problem, or NULL */
+    int64_t bias_stride;          /* elements between the bias vectors of
+                                     consecutive batch problems; 0 = one vector
+                                     shared by all (ignored when batch == 1) */
+    tc_activation_t activation;
+} tc_epilogue;
+
 typedef struct tc_context tc_context;
 typedef struct tc_stream tc_stream;
 
@@ -145,6 +173,24 @@ tc_status_t tc_gemm_batched(tc_context *ctx, const tc_gemm_batched_desc *bd,
 tc_status_t tc_gemm_batched_async(tc_context *ctx, const tc_gemm_batched_desc *bd,
                                   const void *A, const void *B, void *C,
                                   tc_stream *s);
+
+/* Batched GEMM with the fused epilogue *ep (see tc_epilogue), synchronous.
+ * Same descriptor, pointers and errors as tc_gemm_batched, plus:
+ * TC_ERR_INVALID_ARGUMENT for a NULL ep, an unknown activation or a negative
+ * bias_stride; TC_ERR_UNSUPPORTED for int8 inputs (their result is the exact
+ * int32 sum; the page refuses the fused form where there is no float
+ * register accumulator rather than falling back to separate passes);
+ * TC_ERR_ALIASING when the bias vectors overlap C; TC_ERR_INVALID_ARGUMENT
+ * when they do not lie inside one device allocation.  An ep with no bias and
+ * TC_ACT_NONE computes exactly what tc_gemm_batched computes. */
+tc_status_t tc_gemm_epilogue(tc_context *ctx, const tc_gemm_batched_desc *bd,
+                             const tc_epilogue *ep, const void *A, const void *B,
+                             void *C);
+
+/* The same, enqueued on stream s. */
+tc_status_t tc_gemm_epilogue_async(tc_context *ctx, const tc_gemm_batched_desc *bd,
+                                   const tc_epilogue *ep, const void *A,
+                                   const void *B, void *C, tc_stream *s);
 
 /* Validate and plan without touching the GPU or any pointer.  Fills *info
  * (if non-NULL) with the kernel, tile, grid and split-K choice; returns the

@@ -71,6 +71,37 @@ def run_library(p: workloads.Problem, A, B, C, *, sync=True, misalign=False):
     return from_dev(c_full, p.c_dtype)
 
 
+def run_library_epilogue(p: workloads.Problem, A, B, C, bias, act, *, shared=True):
+    """run_library with the fused epilogue: bias [nvec, N] stored values
+    (None: no bias), act an activation name.  shared: one vector for every
+    problem (a 1-D bias tensor), else one per problem."""
+    import torch
+    import dense_gemm_tiled_amd as tg
+    a_full, b_full, c_full = to_dev(A, p.a_dtype), to_dev(B, p.a_dtype), to_dev(C, p.c_dtype)
+    a, b, c = logical_views(p, a_full, b_full, c_full)
+    bt = None
+    if bias is not None:
+        bt = to_dev(bias, p.c_dtype)
+        bt = bt[0] if shared else bt
+    tg.gemm(a, b, c, alpha=p.alpha, beta=p.beta, transpose_a=p.transpose_a,
+            transpose_b=p.transpose_b, bias=bt, activation=act)
+    torch.cuda.synchronize()
+    return from_dev(c_full, p.c_dtype)
+
+
+def oracle_epilogue(p: workloads.Problem, A, B, C, bias, act, *, shared=True):
+    """The oracle's fused form in C's padded layout."""
+    c_in = C if p.beta != 0.0 else None
+    out, _ = oracle.gemm_epilogue(A, B, c_in, bias=bias, bias_stride=0 if shared else p.N,
+                                  act=act, M=p.M, N=p.N, K=p.K, a_dtype=p.a_dtype,
+                                  c_dtype=p.c_dtype, transpose_a=p.transpose_a,
+                                  transpose_b=p.transpose_b, alpha=p.alpha, beta=p.beta,
+                                  lda=p.LDA, ldb=p.LDB, ldc=p.LDC, batch=p.batch,
+                                  stride_a=p.stride_a, stride_b=p.stride_b,
+                                  stride_c=p.stride_c, C_like=C)
+    return out.reshape(C.shape)
+
+
 def oracle_full(p: workloads.Problem, A, B, C):
     """The whole oracle result in the same padded layout as C."""
     c_in = C if p.beta != 0.0 else None

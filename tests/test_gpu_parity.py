@@ -13,7 +13,8 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import compare, env, from_dev, oracle_full, run_library, say, to_dev
+from gpu_util import (TOL, compare, env, from_dev, logical, oracle_epilogue, oracle_full,
+                      run_library, run_library_epilogue, say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -302,6 +303,93 @@ def test_thin_kernel_int8_extremes():
     assert torch.all(c == -16256 * K)
 
 
+# ---------------------------------------------------------------- fused epilogue
+ACTS = ["none", "relu", "gelu_tanh"]
+FLOAT_PAIRS = [pc for pc in PAIRS if pc[0] != "i8"]
+
+
+def epi_check(p, act, label, *, bias=True, shared=True, **envs):
+    """act(alpha*op(A)op(B) + beta*C + bias) through the C ABI against the
+    oracle's fused form."""
+    A, B, C = workloads.make_inputs(p)
+    bv = workloads.make_bias(p, 1 if shared else p.batch) if bias else None
+    say("GPU case: epilogue", label, p.M, p.N, p.K, p.a_dtype, p.c_dtype, p.layout, act,
+        "bias" if bias else "no bias", envs)
+    with env(**envs):
+        got = run_library_epilogue(p, A, B, C, bv, act, shared=shared)
+    ref = oracle_epilogue(p, A, B, C, bv, act, shared=shared)
+    return compare(p, got, ref, C_in=C, label=label)
+
+
+@pytest.mark.parametrize("act", ACTS)
+@pytest.mark.parametrize("tile", ["dma", "dma128", "dma8"])
+@pytest.mark.parametrize("a,c", [("bf16", "bf16"), ("f16", "f32"), ("f16", "f16")])
+def test_epilogue_dma_kernels(a, c, tile, act):
+    """Bias + activation on the direct-to-LDS classes, ragged M/N/K tails,
+    alpha = 0.5 and beta = 1."""
+    import dense_gemm_tiled_amd as tg
+    p = problem(a, c, 296, 264, 200, False, False)
+    epi_check(p, act, "epi %s" % tile, TCGEMM_TILE=tile)
+    assert tg.last_kernel().endswith(DMA_NAME[tile]), tg.last_kernel()
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS, ids=[lay(*l) for l in LAYOUTS])
+@pytest.mark.parametrize("tile", [256, 128, 64])
+def test_epilogue_register_staged_f32(tile, ta, tb):
+    p = problem("f32", "f32", 300, 270, 197, ta, tb)
+    epi_check(p, "gelu_tanh", "epi f32 tile%d" % tile, TCGEMM_TILE=tile)
+
+
+@pytest.mark.parametrize("act", ACTS)
+@pytest.mark.parametrize("a,c", FLOAT_PAIRS, ids=["%s-%s" % pc for pc in FLOAT_PAIRS])
+def test_epilogue_split_k_reduce(a, c, act):
+    """With split-K the reduction kernel applies the epilogue; batched, one
+    bias vector per problem."""
+    import dense_gemm_tiled_amd as tg
+    p = problem(a, c, 130, 200, 1100, True, False, batch=2)
+    epi_check(p, act, "epi splitk", shared=False, TCGEMM_SPLITS=3)
+    assert tg.last_kernel().endswith("+splitk_reduce"), tg.last_kernel()
+
+
+@pytest.mark.parametrize("tb", [False, True], ids=["nn", "nt"])
+@pytest.mark.parametrize("a,c", FLOAT_PAIRS, ids=["%s-%s" % pc for pc in FLOAT_PAIRS])
+def test_epilogue_thin_kernel(a, c, tb):
+    p = problem(a, c, 300, 13, 5000, False, tb, batch=2)
+    epi_check(p, "gelu_tanh", "epi thin", shared=False, TCGEMM_TILE="thin")
+    epi_check(p, "relu", "epi thin shared", TCGEMM_TILE="thin")
+
+
+@pytest.mark.parametrize("a,c", [("bf16", "bf16"), ("f32", "f32")])
+def test_epilogue_alpha_zero_and_beta_zero_nan_c(a, c):
+    """alpha = 0: C = act(beta*C + bias) without reading A or B; beta = 0
+    with a NaN-filled C: C is not read."""
+    p = problem(a, c, 100, 90, 64, False, False, alpha=0.0, beta=0.5)
+    epi_check(p, "relu", "epi alpha0")
+    p = problem(a, c, 264, 520, 256, False, False, alpha=1.0, beta=0.0, c_dist="nan")
+    epi_check(p, "gelu_tanh", "epi beta0 nan")
+    epi_check(p, "relu", "epi activation only", bias=False)
+
+
+def test_epilogue_edge_split_bias_offset():
+    """The column strip of an edge split adds the bias of its own columns."""
+    import dense_gemm_tiled_amd as tg
+    p = problem("bf16", "bf16", 4096, 4104, 128, False, False)
+    epi_check(p, "gelu_tanh", "epi edge split")
+    assert tg.last_kernel().endswith("|transpose_b+gemm_bf16_nn_thin"), tg.last_kernel()
+
+
+def test_epilogue_without_bias_or_activation_is_the_plain_product():
+    """An epilogue of no bias and no activation gives the plain call's bits."""
+    import torch
+    import dense_gemm_tiled_amd as tg
+    p = problem("bf16", "bf16", 300, 280, 200, False, False)
+    A, B, C = workloads.make_inputs(p)
+    plain = run_library(p, A, B, C)
+    say("GPU case: epilogue none vs plain")
+    got = run_library_epilogue(p, A, B, C, None, "none")
+    assert np.array_equal(plain.view(np.uint16), got.view(np.uint16))
+
+
 # ---------------------------------------------------------------- exact regime
 @pytest.mark.parametrize("a,c", [("bf16", "f32"), ("bf16", "bf16"), ("f16", "f16"), ("f32", "f32")])
 def test_exact_regime_bitwise(a, c):
@@ -476,6 +564,25 @@ def test_workload_bf16_nn_4096():
     p, A, B, C, got = full_case("bf16_nn_4096")
     say("kernel:", tg.last_kernel())
     compare(p, got, oracle_full(p, A, B, C), label=p.name)
+
+
+def test_workload_bf16_nn_4096_bias_gelu():
+    """The headline shape with the fused epilogue, checked at 4096 sampled
+    outputs (every row block and column block, the strip edges included)."""
+    import dense_gemm_tiled_amd as tg
+    p = workloads.get("bf16_nn_4096_bias_gelu")
+    A, B, C = workloads.make_inputs(p)
+    bias = workloads.make_bias(p)
+    say("GPU case: workload", p.name)
+    got = logical(p, run_library_epilogue(p, A, B, C, bias, "gelu_tanh"))
+    assert tg.last_kernel() == "gemm_bf16_nn_256x256_dma", tg.last_kernel()
+    pts = workloads.sample_points(p, 4096)
+    r, _ = oracle.gemm_epilogue_points(A, B, None, pts, bias=bias, act="gelu_tanh",
+                                       M=p.M, N=p.N, K=p.K, a_dtype=p.a_dtype,
+                                       c_dtype=p.c_dtype, alpha=p.alpha, beta=p.beta)
+    g = oracle.decode(got[pts[:, 0], pts[:, 1], pts[:, 2]], p.c_dtype)
+    ref = oracle.decode(r, p.c_dtype)
+    assert oracle.rel_frobenius(g, ref) <= TOL[p.a_dtype]
 
 
 @pytest.mark.parametrize("name", ["f16_tn_4096", "f16_nt_4096"])

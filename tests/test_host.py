@@ -141,6 +141,71 @@ def test_overlap_refused(lib, ctx):
     assert lib.tc_dispatch_count(ctx) == 0
 
 
+def epi(bias=None, stride=0, act=0):
+    e = tg.EpilogueT()
+    e.bias, e.bias_stride, e.activation = bias, stride, act
+    return e
+
+
+EPI_BAD = [
+    # tessl "Architecture", "Fused Epilogue": refused where there is no float
+    # register accumulator (int8 results are exact int32 sums)
+    ("int8", dict(a=tg.I8, c=tg.I32, acc=tg.I32), {}, 2),
+    ("activation 3", {}, dict(act=3), 1),
+    ("activation -1", {}, dict(act=-1), 1),
+    ("bias_stride<0", dict(batch=2, sa=4096, sb=4096, sc=4096), dict(bias=0x40000000000, stride=-1), 1),
+    ("bias overlaps C", {}, dict(bias=C_PTR + 64), 4),
+    ("batched bias overlaps C", dict(batch=3, sa=4096, sb=4096, sc=4096),
+     dict(bias=C_PTR - 200, stride=64), 4),
+    ("descriptor first", dict(M=0), dict(act=1), 1),
+]
+
+
+@pytest.mark.parametrize("name,dkw,ekw,status", EPI_BAD, ids=[b[0] for b in EPI_BAD])
+def test_invalid_epilogue_refused_before_launch(lib, ctx, name, dkw, ekw, status):
+    d = desc(**dkw)
+    e = epi(**ekw)
+    st = lib.tc_gemm_epilogue(ctx, ctypes.byref(d), ctypes.byref(e), A_PTR, B_PTR, C_PTR)
+    assert st == status, (tg.status_name(st), lib.tc_last_error(ctx))
+    assert lib.tc_last_error(ctx) != b""
+    st = lib.tc_gemm_epilogue_async(ctx, ctypes.byref(d), ctypes.byref(e), A_PTR, B_PTR, C_PTR,
+                                    _VP(0x1234))
+    assert st == status
+    assert lib.tc_dispatch_count(ctx) == 0
+
+
+def test_epilogue_null_arguments(lib, ctx):
+    d = desc()
+    e = epi(act=1)
+    assert lib.tc_gemm_epilogue(ctx, ctypes.byref(d), None, A_PTR, B_PTR, C_PTR) == 1
+    assert lib.tc_gemm_epilogue_async(ctx, ctypes.byref(d), ctypes.byref(e), A_PTR, B_PTR,
+                                      C_PTR, None) == 1
+    assert lib.tc_gemm_epilogue(ctx, ctypes.byref(d), ctypes.byref(e), None, B_PTR, C_PTR) == 1
+    assert lib.tc_dispatch_count(ctx) == 0
+
+
+def test_epilogue_valid_call_without_gpu_fails_cleanly(lib, ctx):
+    """A valid epilogue passes validation and then fails at the device (no GPU
+    here), launching nothing."""
+    d = desc()
+    e = epi(bias=0x40000000000, act=2)
+    st = lib.tc_gemm_epilogue(ctx, ctypes.byref(d), ctypes.byref(e), A_PTR, B_PTR, C_PTR)
+    assert st in (1, 6)
+    assert lib.tc_dispatch_count(ctx) == 0
+
+
+def test_python_epilogue_arguments():
+    """make_epilogue's checks run before any library call (CPU tensors)."""
+    import torch
+    c = torch.empty(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(tg.TcGemmError):
+        tg.make_epilogue(c, activation="gelu")
+    with pytest.raises(tg.TcGemmError):
+        tg.make_epilogue(c, bias=torch.zeros(8, dtype=torch.bfloat16))   # not on a GPU
+    e = tg.make_epilogue(c, activation="gelu_tanh")
+    assert e.activation == 2 and not e.bias
+
+
 def test_int8_k_bound_accepted_at_131071(lib):
     d = desc(a=tg.I8, c=tg.I32, acc=tg.I32, K=131071, M=16, N=16)
     assert lib.tc_gemm_plan(None, ctypes.byref(d), None) == 0

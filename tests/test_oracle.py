@@ -534,3 +534,20 @@ def test_epilogue_rejects_int8_and_unknown_activation():
     B = np.zeros(4, dtype=np.float32)
     with pytest.raises(ValueError):
         oracle.gemm_epilogue(B, B, None, M=2, N=2, K=2, a_dtype="f32", c_dtype="f32", act="gelu")
+
+
+def test_epilogue_points_equal_full():
+    rng = np.random.default_rng(22)
+    b, M, N, K = 2, 6, 9, 33
+    A = draw(rng, "f16", (b, M, K))
+    B = draw(rng, "f16", (b, N, K))
+    C = draw(rng, "f16", (b, M, N))
+    bias = draw(rng, "f16", (b, N))
+    kw = dict(M=M, N=N, K=K, a_dtype="f16", c_dtype="f16", transpose_b=True, alpha=0.5,
+              beta=1.0, batch=b, stride_a=M * K, stride_b=N * K, stride_c=M * N)
+    out, val = oracle.gemm_epilogue(A, B, C, bias=bias, bias_stride=N, act="gelu_tanh", **kw)
+    pts = [(z, i, j) for z in range(b) for i in range(M) for j in range(N)]
+    kw.pop("batch")
+    r, v = oracle.gemm_epilogue_points(A, B, C, pts, bias=bias, bias_stride=N, act="gelu_tanh", **kw)
+    assert np.array_equal(v.reshape(b, M, N), val)
+    assert np.array_equal(r.reshape(b, M, N), out.reshape(b, M, N))

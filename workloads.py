@@ -169,6 +169,13 @@ def make_inputs(p: Problem):
     return A, B, C
 
 
+def make_bias(p: Problem, nvec: int = 1, seed_offset: int = 77) -> np.ndarray:
+    """Fused-epilogue bias: nvec vectors of N values, N(0,1), stored in the
+    output type (shape [nvec, N]); seeded from the problem."""
+    rng = np.random.default_rng(p.seed + seed_offset)
+    return _to_storage(rng.normal(0.0, 1.0, size=(nvec, p.N)), p.c_dtype)
+
+
 # The five measured workloads.
 WORKLOADS: Dict[str, Problem] = {
     "sgemm_nn_256": Problem(
@@ -188,6 +195,11 @@ WORKLOADS: Dict[str, Problem] = {
         batch=8, dist="uniform", scale=1.0, seed=1005),
     "i8_nn_ragged": Problem(
         "i8_nn_ragged", 4093, 4099, 4096, "i8", "i32", dist="int8", seed=1006),
+    # the headline shape with the fused epilogue (a per-column bias and
+    # GELU-tanh): not one of the five, measured against the plain headline
+    "bf16_nn_4096_bias_gelu": Problem(
+        "bf16_nn_4096_bias_gelu", 4096, 4096, 4096, "bf16", "bf16", dist="normal", scale=1.0,
+        seed=1002, extra={"bias": "1", "act": "gelu_tanh"}),
 }
 
 HEADLINE = "bf16_nn_4096"
