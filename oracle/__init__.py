@@ -221,8 +221,16 @@ def gemm_points(A: np.ndarray, B: np.ndarray, C_in: Optional[np.ndarray],
 # C-shaped); GELU-tanh is 0.5*y*(1 + tanh(sqrt(2/pi)*(y + 0.044715*y^3))),
 # the usual tanh form of GELU, whose clamp on the page only guards an
 # exp-based tanh against overflow and does not change the value; ReLU is
-# max(y, 0).  Evaluated in fp64 on the unrounded value, then rounded once to
-# c_dtype (ties to even) like the plain product.
+# max(y, 0).
+#
+# Same page, section "Integer GEMM": gemm_i8_dequant takes the exact int32
+# sum of int8 x int8 and applies a per-column dequantization in the same
+# dispatch.  Reading: the dequantization is a per-column fp32 scale s[j]
+# multiplying the sum, so with the epilogue above
+#   C = activation(alpha * s[j] * S + beta * C_prev + bias)
+# (s[j] = 1 without a scale); for int8 inputs the scale is required and C is
+# fp32, fp16 or bf16.  Everything is evaluated in fp64 from the exact sums S,
+# then rounded once to c_dtype (ties to even) like the plain product.
 ACTIVATIONS = ("none", "relu", "gelu_tanh")
 
 
@@ -239,45 +247,107 @@ def activation(y: np.ndarray, act: str) -> np.ndarray:
     raise ValueError("unknown activation %r" % (act,))
 
 
-def epilogue_values(value: np.ndarray, bias: Optional[np.ndarray], c_dtype: str,
-                    act: str, bias_stride: int = 0) -> np.ndarray:
-    """act(value + bias[z, j]) for value [batch, M, N] (the unrounded
-    alpha*S + beta*C_in); bias holds stored c_dtype values, problem z's N
-    values starting at z*bias_stride (0: one vector for every problem)."""
-    value = np.asarray(value, dtype=np.float64)
-    batch, M, N = value.shape
-    y = value.copy()
-    if bias is not None:
-        b = decode(np.ascontiguousarray(bias).ravel(), c_dtype)
-        for z in range(batch):
-            y[z] += b[z * bias_stride: z * bias_stride + N][None, :]
-    return activation(y, act)
+def _epilogue_args(kw, col_scale, act):
+    a_dtype, c_dtype = kw.get("a_dtype"), kw.get("c_dtype")
+    if act not in ACTIVATIONS:
+        raise ValueError("unknown activation %r" % (act,))
+    if a_dtype == "i8":
+        if col_scale is None:
+            raise ValueError("int8 takes the fused form only with a per-column dequant scale")
+        if c_dtype not in ("f32", "f16", "bf16"):
+            raise ValueError("dequantized int8 results are f32, f16 or bf16")
+
+
+def _sum_kw(kw):
+    """gemm() arguments that give the plain sums S (alpha 1, beta 0)."""
+    skw = dict(kw)
+    skw.update(alpha=1.0, beta=0.0)
+    if kw["a_dtype"] == "i8":
+        skw["c_dtype"] = "i32"
+    skw.pop("ldc", None)
+    skw.pop("stride_c", None)
+    skw.pop("C_like", None)
+    return skw
 
 
 def gemm_epilogue(A: np.ndarray, B: np.ndarray, C_in: Optional[np.ndarray], *,
                   bias: Optional[np.ndarray] = None, bias_stride: int = 0,
+                  col_scale: Optional[np.ndarray] = None, scale_stride: int = 0,
                   act: str = "none", **kw) -> Tuple[np.ndarray, np.ndarray]:
-    """The fused form: gemm()'s arguments plus bias / bias_stride / act.
-    Returns (C_out, value) like gemm(), value being the fp64 result after the
-    epilogue (before rounding to c_dtype)."""
-    if kw.get("a_dtype") == "i8":
-        raise ValueError("the fused epilogue takes float inputs (int8 sums are exact integers)")
-    if act not in ACTIVATIONS:
-        raise ValueError("unknown activation %r" % (act,))
-    kw = dict(kw)
-    kw["want_value"] = True
-    C_out, value = gemm(A, B, C_in, **kw)
-    y = epilogue_values(value, bias, kw["c_dtype"], act, bias_stride)
+    """The fused form: gemm()'s arguments plus bias / bias_stride (stored
+    c_dtype values, problem z's N values at z*bias_stride), col_scale /
+    scale_stride (fp32 values, likewise) and act.  Returns (C_out, value) like
+    gemm(), value being the fp64 result after the epilogue (before rounding
+    to c_dtype), dense [batch, M, N]."""
+    _epilogue_args(kw, col_scale, act)
     M, N, batch = kw["M"], kw["N"], kw.get("batch", 1)
+    c_dtype, alpha, beta = kw["c_dtype"], kw.get("alpha", 1.0), kw.get("beta", 0.0)
     ldc = kw.get("ldc", 0) or N
     stride_c = kw.get("stride_c", 0)
-    enc = encode(y, kw["c_dtype"])
+    # the exact sums (alpha = 0 reads neither A nor B)
+    if alpha != 0.0:
+        _, S = gemm(A, B, None, want_value=True, stride_c=M * N, **_sum_kw(kw))
+    else:
+        S = np.zeros((batch, M, N))
+    if col_scale is not None:
+        sc = np.asarray(col_scale, dtype=np.float32).ravel().astype(np.float64)
+        for z in range(batch):
+            S[z] *= sc[z * scale_stride: z * scale_stride + N][None, :]
+    y = alpha * S
+    if beta != 0.0:
+        cin = decode(np.ascontiguousarray(C_in).ravel(), c_dtype)
+        for z in range(batch):
+            for i in range(M):
+                o = z * stride_c + i * ldc
+                y[z, i] += beta * cin[o:o + N]
+    if bias is not None:
+        b = decode(np.ascontiguousarray(bias).ravel(), c_dtype)
+        for z in range(batch):
+            y[z] += b[z * bias_stride: z * bias_stride + N][None, :]
+    y = activation(y, act)
+    if C_in is not None:
+        C_out = np.ascontiguousarray(C_in).copy()
+    else:
+        C_like = kw.get("C_like")
+        if C_like is None:
+            C_like = np.zeros((batch - 1) * stride_c + (M - 1) * ldc + N, dtype=STORAGE[c_dtype])
+        C_out = np.ascontiguousarray(C_like).copy()
+    enc = encode(y, c_dtype)
     flat = C_out.ravel()
     for z in range(batch):
         for i in range(M):
             o = z * stride_c + i * ldc
             flat[o:o + N] = enc[z, i]
     return flat.reshape(C_out.shape), y
+
+
+def gemm_epilogue_points(A: np.ndarray, B: np.ndarray, C_in: Optional[np.ndarray],
+                         points: Sequence[Tuple[int, int, int]], *,
+                         bias: Optional[np.ndarray] = None, bias_stride: int = 0,
+                         col_scale: Optional[np.ndarray] = None, scale_stride: int = 0,
+                         act: str = "none", **kw) -> Tuple[np.ndarray, np.ndarray]:
+    """The fused form at the given (z, i, j) outputs only.  Returns (rounded,
+    value) like gemm_points."""
+    _epilogue_args(kw, col_scale, act)
+    c_dtype, alpha, beta = kw["c_dtype"], kw.get("alpha", 1.0), kw.get("beta", 0.0)
+    pts = np.asarray(points, dtype=np.int64).reshape(-1, 3)
+    if alpha != 0.0:
+        _, S = gemm_points(A, B, None, pts, **_sum_kw(kw))
+    else:
+        S = np.zeros(len(pts))
+    if col_scale is not None:
+        sc = np.asarray(col_scale, dtype=np.float32).ravel().astype(np.float64)
+        S = S * sc[pts[:, 0] * scale_stride + pts[:, 2]]
+    y = alpha * S
+    if beta != 0.0:
+        ldc = kw.get("ldc", 0) or kw["N"]
+        cin = decode(np.ascontiguousarray(C_in).ravel(), c_dtype)
+        y = y + beta * cin[pts[:, 0] * kw.get("stride_c", 0) + pts[:, 1] * ldc + pts[:, 2]]
+    if bias is not None:
+        b = decode(np.ascontiguousarray(bias).ravel(), c_dtype)
+        y = y + b[pts[:, 0] * bias_stride + pts[:, 2]]
+    y = activation(y, act)
+    return encode(y, c_dtype), y
 
 
 def rel_frobenius(got: np.ndarray, ref: np.ndarray) -> float:

@@ -529,8 +529,11 @@ def test_epilogue_batched_bias_stride_and_unread_c():
 
 def test_epilogue_rejects_int8_and_unknown_activation():
     A = np.zeros(4, dtype=np.int8)
-    with pytest.raises(ValueError):
+    with pytest.raises(ValueError):      # int8 without a dequant scale
         oracle.gemm_epilogue(A, A, None, M=2, N=2, K=2, a_dtype="i8", c_dtype="i32", act="relu")
+    with pytest.raises(ValueError):      # dequantized results are float
+        oracle.gemm_epilogue(A, A, None, M=2, N=2, K=2, a_dtype="i8", c_dtype="i32",
+                             col_scale=np.ones(2, dtype=np.float32))
     B = np.zeros(4, dtype=np.float32)
     with pytest.raises(ValueError):
         oracle.gemm_epilogue(B, B, None, M=2, N=2, K=2, a_dtype="f32", c_dtype="f32", act="gelu")
@@ -549,5 +552,90 @@ def test_epilogue_points_equal_full():
     pts = [(z, i, j) for z in range(b) for i in range(M) for j in range(N)]
     kw.pop("batch")
     r, v = oracle.gemm_epilogue_points(A, B, C, pts, bias=bias, bias_stride=N, act="gelu_tanh", **kw)
+    assert np.array_equal(v.reshape(b, M, N), val)
+    assert np.array_equal(r.reshape(b, M, N), out.reshape(b, M, N))
+
+
+# ----------------------------------------------------------------- int8 dequant
+@pytest.mark.parametrize("c_dtype", FLOAT_TYPES)
+def test_i8_dequant_against_exact_integers(c_dtype):
+    """C[i][j] = round_c(s[j] * S[i][j]) with S the exact integer sum, checked
+    against Python integers and fractions on a tiny ragged problem (all four
+    layouts), per-column scales that differ in every column."""
+    rng = np.random.default_rng(31)
+    M, N, K = 5, 7, 19
+    sc = np.array([0.5, 0.03125, 3.0, -1.25, 1e-3, 7.0, 2.0 ** -20], dtype=np.float32)
+    for ta in (False, True):
+        for tb in (False, True):
+            A = rng.integers(-128, 128, size=(K, M) if ta else (M, K), dtype=np.int8)
+            B = rng.integers(-128, 128, size=(N, K) if tb else (K, N), dtype=np.int8)
+            out, val = oracle.gemm_epilogue(A, B, None, col_scale=sc, M=M, N=N, K=K,
+                                            a_dtype="i8", c_dtype=c_dtype,
+                                            transpose_a=ta, transpose_b=tb)
+            got = lib_decode(out, c_dtype).reshape(M, N)
+            table = finite_values(c_dtype) if c_dtype != "f32" else None
+            for i in range(M):
+                for j in range(N):
+                    s = 0
+                    for k in range(K):
+                        a = int(A[k, i] if ta else A[i, k])
+                        b = int(B[j, k] if tb else B[k, j])
+                        s += a * b
+                    exact = Fraction(s) * Fraction(float(sc[j]))
+                    # |S| < 2^19 here, so s*S has at most 43 significand bits: exact in fp64
+                    assert val[0, i, j] == float(exact)
+                    if c_dtype == "f32":
+                        assert got[i, j] == float(np.float32(float(exact)))
+                    else:
+                        assert got[i, j] == nearest_by_search(float(exact), c_dtype, table)
+
+
+def test_i8_dequant_extremes_and_composition():
+    """All (-128)*(-128): S = 16384 K exactly; scales 2^-e keep the result
+    exact in fp32; with beta, a bias and ReLU the closed form is
+    relu(alpha s[j] 16384 K + beta c0 + bias[j])."""
+    M, N, K = 3, 4, 131071
+    A = np.full((M, K), -128, dtype=np.int8)
+    B = np.full((K, N), -128, dtype=np.int8)
+    sc = np.array([1.0, 2.0 ** -10, 2.0 ** -20, -2.0 ** -5], dtype=np.float32)
+    out, val = oracle.gemm_epilogue(A, B, None, col_scale=sc, M=M, N=N, K=K, a_dtype="i8",
+                                    c_dtype="f32")
+    want = 16384.0 * K * sc.astype(np.float64)
+    assert np.array_equal(val[0], np.broadcast_to(want, (M, N)))
+    assert np.array_equal(out.reshape(M, N), np.broadcast_to(want.astype(np.float32), (M, N)))
+    C = np.full(M * N, 8.0, dtype=np.float32)
+    bias = np.array([-1e9, 0.5, -3.0, 100.0], dtype=np.float32)
+    _, v = oracle.gemm_epilogue(A, B, C, col_scale=sc, bias=bias, act="relu", alpha=0.5,
+                                beta=2.0, M=M, N=N, K=K, a_dtype="i8", c_dtype="f32")
+    pre = 0.5 * want + 16.0 + bias.astype(np.float64)
+    assert np.array_equal(v[0], np.broadcast_to(np.maximum(pre, 0.0), (M, N)))
+
+
+def test_float_gemm_with_column_scale():
+    """A per-column scale on a float GEMM multiplies column j of alpha*A@B
+    by s[j] (checked on A = B = ones: S = K)."""
+    M, N, K = 4, 5, 12
+    A = encode_lib(np.ones((M, K)), "bf16")
+    B = encode_lib(np.ones((K, N)), "bf16")
+    sc = np.array([1.0, 0.5, -2.0, 0.0, 4.0], dtype=np.float32)
+    _, v = oracle.gemm_epilogue(A, B, None, col_scale=sc, alpha=0.25, M=M, N=N, K=K,
+                                a_dtype="bf16", c_dtype="f32")
+    assert np.array_equal(v[0], np.broadcast_to(0.25 * K * sc.astype(np.float64), (M, N)))
+
+
+def test_i8_dequant_points_equal_full():
+    rng = np.random.default_rng(33)
+    b, M, N, K = 2, 5, 6, 40
+    A = rng.integers(-128, 128, size=(b, M, K), dtype=np.int8)
+    B = rng.integers(-128, 128, size=(b, K, N), dtype=np.int8)
+    sc = rng.normal(0, 0.01, size=b * N).astype(np.float32)
+    bias = draw(rng, "bf16", (b, N))
+    kw = dict(M=M, N=N, K=K, a_dtype="i8", c_dtype="bf16", stride_a=M * K, stride_b=K * N,
+              stride_c=M * N)
+    out, val = oracle.gemm_epilogue(A, B, None, col_scale=sc, scale_stride=N, bias=bias,
+                                    bias_stride=N, act="gelu_tanh", batch=b, **kw)
+    pts = [(z, i, j) for z in range(b) for i in range(M) for j in range(N)]
+    r, v = oracle.gemm_epilogue_points(A, B, None, pts, col_scale=sc, scale_stride=N, bias=bias,
+                                       bias_stride=N, act="gelu_tanh", **kw)
     assert np.array_equal(v.reshape(b, M, N), val)
     assert np.array_equal(r.reshape(b, M, N), out.reshape(b, M, N))
