@@ -87,10 +87,17 @@ def cpu_baseline(p: workloads.Problem, A, B, C, target_s: float):
         B0 = B[0] if p.batch > 1 else B
         C0 = (C[0] if p.batch > 1 else C)[:rows]
         t0 = time.perf_counter()
-        oracle.gemm(a_sub, B0, C0 if p.beta != 0 else None, M=rows, N=p.N, K=p.K,
-                    a_dtype=p.a_dtype, c_dtype=p.c_dtype, transpose_a=p.transpose_a,
-                    transpose_b=p.transpose_b, alpha=p.alpha, beta=p.beta, lda=lda,
-                    ldb=p.LDB, ldc=p.LDC, C_like=C0, want_value=False)
+        if p.a_dtype == "i8" and p.c_dtype != "i32":
+            # int8 dequantized: the oracle's exact sums are the work (the
+            # per-column scale is one multiply per output)
+            oracle.gemm(a_sub, B0, None, M=rows, N=p.N, K=p.K, a_dtype="i8", c_dtype="i32",
+                        transpose_a=p.transpose_a, transpose_b=p.transpose_b, lda=lda,
+                        ldb=p.LDB, want_value=False)
+        else:
+            oracle.gemm(a_sub, B0, C0 if p.beta != 0 else None, M=rows, N=p.N, K=p.K,
+                        a_dtype=p.a_dtype, c_dtype=p.c_dtype, transpose_a=p.transpose_a,
+                        transpose_b=p.transpose_b, alpha=p.alpha, beta=p.beta, lda=lda,
+                        ldb=p.LDB, ldc=p.LDC, C_like=C0, want_value=False)
         return time.perf_counter() - t0
 
     probe = min(8, p.M)
@@ -128,18 +135,21 @@ def main():
     # beta != 0 reads C: every step restores nothing, so C drifts; that does
     # not change the work done.
 
-    # fused-epilogue workloads: one bias vector (C's type) and an activation
+    # fused-epilogue workloads: one bias vector (C's type), an activation, a
+    # per-column dequantization scale
     act = p.extra.get("act")
     bias = to_dev(workloads.make_bias(p), p.c_dtype)[0] if p.extra.get("bias") else None
+    col_scale = (torch.from_numpy(workloads.make_col_scale(p)[0]).cuda()
+                 if p.extra.get("col_scale") else None)
 
     def step(i):
         a, b, c, _ = sets[i % n_sets]
-        if act is None and bias is None:
+        if act is None and bias is None and col_scale is None:
             tg.gemm(a, b, c, alpha=p.alpha, beta=p.beta, transpose_a=p.transpose_a,
                     transpose_b=p.transpose_b)
         else:
             tg.gemm(a, b, c, alpha=p.alpha, beta=p.beta, transpose_a=p.transpose_a,
-                    transpose_b=p.transpose_b, bias=bias, activation=act)
+                    transpose_b=p.transpose_b, bias=bias, activation=act, col_scale=col_scale)
 
     for i in range(args.warmup):
         step(i)
@@ -187,8 +197,13 @@ def main():
     # work: 2*M*N*K over the output part it computes (the whole output unless
     # a thin edge strip is split off), or for the HBM-bound split-K workload
     # the bytes of A and B it reads once (partial sums are overhead).
-    info = tg.plan(tg.make_desc(*sets[0][:3], alpha=p.alpha, beta=p.beta,
-                                transpose_a=p.transpose_a, transpose_b=p.transpose_b))
+    pdesc = tg.make_desc(*sets[0][:3], alpha=p.alpha, beta=p.beta,
+                         transpose_a=p.transpose_a, transpose_b=p.transpose_b)
+    if p.a_dtype == "i8" and p.c_dtype != "i32":
+        # the plan of a dequantizing call is that of its int32 form (tiles,
+        # packing and split do not depend on the output type)
+        pdesc.base.c_dtype, pdesc.base.alpha, pdesc.base.beta = tg.I32, 1.0, 0.0
+    info = tg.plan(pdesc)
     mm = min(p.M, info["tiles_m"] * info["tile_m"])
     nm = min(p.N, info["tiles_n"] * info["tile_n"])
     kern_s = float(np.mean(kdurs))

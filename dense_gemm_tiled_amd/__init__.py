@@ -71,7 +71,8 @@ class BatchedDescT(ctypes.Structure):
 class EpilogueT(ctypes.Structure):
     """tc_epilogue"""
     _fields_ = [("bias", ctypes.c_void_p), ("bias_stride", ctypes.c_int64),
-                ("activation", ctypes.c_int)]
+                ("activation", ctypes.c_int), ("col_scale", ctypes.c_void_p),
+                ("scale_stride", ctypes.c_int64)]
 
 
 # tc_activation_t
@@ -256,50 +257,63 @@ def make_desc(a, b, c, alpha: float = 1.0, beta: float = 0.0,
 
 
 # ------------------------------------------------------------------ API
-def make_epilogue(c, bias=None, activation: Optional[str] = None) -> EpilogueT:
-    """tc_epilogue for output c: bias is a GPU tensor of c's dtype holding N
-    values per problem ([N], shared by a batch, or [batch, N] with contiguous
-    rows); activation is None, "none", "relu" or "gelu_tanh"."""
+def _column_vector(c, t, name: str, dtype) -> Tuple[int, int]:
+    """(pointer, per-problem stride) of a [N] or [batch, N] GPU tensor."""
+    N = int(c.size(-1))
+    if not t.is_cuda or t.dtype != dtype:
+        raise TcGemmError(1, "%s must be a GPU tensor of dtype %s" % (name, dtype))
+    if int(t.size(-1)) != N or (t.size(-1) > 1 and t.stride(-1) != 1):
+        raise TcGemmError(1, "%s must hold N contiguous values per problem" % name)
+    stride = 0
+    if t.dim() == 2:
+        batch = int(c.size(0)) if c.dim() == 3 else 1
+        if int(t.size(0)) != batch:
+            raise TcGemmError(1, "%s has %d rows for %d problems" % (name, t.size(0), batch))
+        stride = int(t.stride(0))
+    elif t.dim() != 1:
+        raise TcGemmError(1, "%s must be 1-D or 2-D" % name)
+    return t.data_ptr(), stride
+
+
+def make_epilogue(c, bias=None, activation: Optional[str] = None, col_scale=None) -> EpilogueT:
+    """tc_epilogue for output c: bias is a GPU tensor of c's dtype and
+    col_scale a float32 GPU tensor, each holding N values per problem ([N],
+    shared by a batch, or [batch, N] with contiguous rows); activation is
+    None, "none", "relu" or "gelu_tanh"."""
+    import torch
     ep = EpilogueT()
     act = "none" if activation is None else activation
     if act not in ACTIVATIONS:
         raise TcGemmError(1, "unknown activation %r" % (activation,))
     ep.activation = ACTIVATIONS[act]
-    ep.bias, ep.bias_stride = None, 0
+    ep.bias, ep.bias_stride, ep.col_scale, ep.scale_stride = None, 0, None, 0
     if bias is not None:
-        N = int(c.size(-1))
-        if not bias.is_cuda or bias.dtype != c.dtype:
-            raise TcGemmError(1, "bias must be a GPU tensor of c's dtype")
-        if int(bias.size(-1)) != N or (bias.size(-1) > 1 and bias.stride(-1) != 1):
-            raise TcGemmError(1, "bias must hold N contiguous values per problem")
-        if bias.dim() == 2:
-            batch = int(c.size(0)) if c.dim() == 3 else 1
-            if int(bias.size(0)) != batch:
-                raise TcGemmError(1, "bias has %d rows for %d problems" % (bias.size(0), batch))
-            ep.bias_stride = int(bias.stride(0))
-        elif bias.dim() != 1:
-            raise TcGemmError(1, "bias must be 1-D or 2-D")
-        ep.bias = bias.data_ptr()
+        ep.bias, ep.bias_stride = _column_vector(c, bias, "bias", c.dtype)
+    if col_scale is not None:
+        ep.col_scale, ep.scale_stride = _column_vector(c, col_scale, "col_scale", torch.float32)
     return ep
 
 
 def gemm(a, b, c, *, alpha: float = 1.0, beta: float = 0.0, transpose_a: bool = False,
-         transpose_b: bool = False, stream=None, bias=None, activation: Optional[str] = None):
-    """c = activation(alpha * op(a) @ op(b) + beta * c + bias) on c's device,
-    enqueued on torch's current stream (or `stream`).  Without bias and
-    activation this is the plain product (tc_gemm_batched_async), with them the
-    fused epilogue (tc_gemm_epilogue_async).  Returns c."""
+         transpose_b: bool = False, stream=None, bias=None, activation: Optional[str] = None,
+         col_scale=None):
+    """c = activation(alpha * (op(a) @ op(b)) * col_scale + beta * c + bias) on
+    c's device, enqueued on torch's current stream (or `stream`).  Without
+    bias, activation and col_scale this is the plain product
+    (tc_gemm_batched_async), with any of them the fused epilogue
+    (tc_gemm_epilogue_async); int8 a and b with a float c need col_scale
+    (per-column dequantization).  Returns c."""
     if not (a.is_cuda and b.is_cuda and c.is_cuda):
         raise TcGemmError(1, "a, b and c must be GPU tensors")
     device = c.device.index if c.device.index is not None else 0
     desc = make_desc(a, b, c, alpha, beta, transpose_a, transpose_b)
     lib = load_library()
     ctx, s = _torch_stream(device, stream)
-    if bias is None and activation is None:
+    if bias is None and activation is None and col_scale is None:
         st = lib.tc_gemm_batched_async(ctx, ctypes.byref(desc), _VP(a.data_ptr()),
                                        _VP(b.data_ptr()), _VP(c.data_ptr()), s)
     else:
-        ep = make_epilogue(c, bias, activation)
+        ep = make_epilogue(c, bias, activation, col_scale)
         st = lib.tc_gemm_epilogue_async(ctx, ctypes.byref(desc), ctypes.byref(ep),
                                         _VP(a.data_ptr()), _VP(b.data_ptr()),
                                         _VP(c.data_ptr()), s)

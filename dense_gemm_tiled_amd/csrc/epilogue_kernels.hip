@@ -7,7 +7,7 @@ namespace {
 
 template <int CDT>
 __device__ inline EpiState epi_of(const EpilogueArgs &a, int z) {
-    return make_epi<CDT>(a.bias, a.bias_stride, a.act, a.epi, z, a.N);
+    return make_epi<CDT>(a, z, a.N);
 }
 
 // ---------------------------------------------------------------------------
@@ -34,45 +34,52 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const EpilogueArgs a
     const int coff = (m * a.ldc + n) * CES;
     const bool wvec = (a.N % 4) == 0;
     const bool cvec = a.c_vec_ok != 0;
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
     if (a.acc_is_int) {
-        int s4[4] = {0, 0, 0, 0};
+        // exact int32 sums; int32 out as they are, a float out (int8 with a
+        // dequantization scale) through the float epilogue below
+        int i4[4] = {0, 0, 0, 0};
         for (int s = 0; s < a.splits; ++s) {
             const int off = (int)((s * plane + (int64_t)m * a.N + n) * 4);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                if (e < nvalid) s4[e] += (int)__builtin_amdgcn_raw_buffer_load_b32(rw, off + 4 * e, 0, 0);
+                if (e < nvalid) i4[e] += (int)__builtin_amdgcn_raw_buffer_load_b32(rw, off + 4 * e, 0, 0);
         }
-        store_i4(rc, coff, nvalid, cvec, s4);
-        return;
-    }
-    float s4[4] = {0.f, 0.f, 0.f, 0.f};
-    int s = 0;
-    if (wvec && nvalid >= 4) {
-        // groups of 8 slices: the 8 loads are in flight together, the adds
-        // still run in ascending s
-        const int plane_b = (int)(plane * 4);
-        const int off0 = (int)(((int64_t)m * a.N + n) * 4);
-        for (; s + 8 <= a.splits; s += 8) {
-            u32x4 w[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) w[u] = ld128(rw, off0 + (s + u) * plane_b);
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) s4[e] += as_f32(w[u][e]);
+        if (a.c_dtype == DT_I32) {
+            store_i4(rc, coff, nvalid, cvec, i4);
+            return;
         }
-    }
-    for (; s < a.splits; ++s) {
-        const int off = (int)((s * plane + (int64_t)m * a.N + n) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s4[e] = (float)i4[e];
+    } else {
+        int s = 0;
         if (wvec && nvalid >= 4) {
-            u32x4 w = ld128(rw, off);
+            // groups of 8 slices: the 8 loads are in flight together, the adds
+            // still run in ascending s
+            const int plane_b = (int)(plane * 4);
+            const int off0 = (int)(((int64_t)m * a.N + n) * 4);
+            for (; s + 8 <= a.splits; s += 8) {
+                u32x4 w[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) s4[e] += as_f32(w[e]);
-        } else {
+                for (int u = 0; u < 8; ++u) w[u] = ld128(rw, off0 + (s + u) * plane_b);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (e < nvalid)
-                    s4[e] += as_f32(__builtin_amdgcn_raw_buffer_load_b32(rw, off + 4 * e, 0, 0));
+                for (int u = 0; u < 8; ++u)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s4[e] += as_f32(w[u][e]);
+            }
+        }
+        for (; s < a.splits; ++s) {
+            const int off = (int)((s * plane + (int64_t)m * a.N + n) * 4);
+            if (wvec && nvalid >= 4) {
+                u32x4 w = ld128(rw, off);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s4[e] += as_f32(w[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (e < nvalid)
+                        s4[e] += as_f32(__builtin_amdgcn_raw_buffer_load_b32(rw, off + 4 * e, 0, 0));
+            }
         }
     }
     switch (a.c_dtype) {

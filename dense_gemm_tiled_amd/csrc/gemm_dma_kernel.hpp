@@ -431,6 +431,16 @@ void gemm_dma_kernel(const GemmArgs args) {
         }
     };
 
+    // fused epilogue: the tile's bias and scales go into LDS of their own at
+    // the start, their loads issued ahead of the first tiles' (the epilogue
+    // then reads them with no wait; the loop's barriers publish them)
+    constexpr int EPI_LDS = EPI == EPI_FUSED && OUT != DT_I32 && OUT != OUT_PARTIAL ? 2 * BN : 1;
+    __shared__ __attribute__((aligned(16))) float epi_smem[EPI_LDS];
+    [[maybe_unused]] float epi_b = 0.f, epi_s = 1.f;
+    if constexpr (EPI_LDS > 1) {
+        if (tid < BN)
+            load_epi1<OUT>(make_epi<OUT>(args, z, N), n0 + tid, N, epi_b, epi_s);
+    }
     if (nkt > 0) {
         {
             const TileSrc s0 = tile_src(0);
@@ -443,6 +453,12 @@ void gemm_dma_kernel(const GemmArgs args) {
         // tile 0 landed (tile 1 may still be in flight: the first loop
         // barrier waits for it); the waves without loads have none in flight
         wait_barrier_vm<ND>();
+        if constexpr (EPI_LDS > 1) {
+            if (tid < BN) {
+                epi_smem[tid] = epi_b;
+                epi_smem[BN + tid] = epi_s;
+            }
+        }
 #pragma unroll
         for (int r = 0; r < NR; ++r) read(lds, 0, r, a0, b0);
         for (int kt = 0; kt < nkt; ++kt) {
@@ -528,15 +544,33 @@ void gemm_dma_kernel(const GemmArgs args) {
             asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
         }
     }
-    [[maybe_unused]] const EpiState ep = make_epi<OUT == DT_I32 ? DT_F32 : OUT>(
-        args.bias, args.bias_stride, args.act, args.epi, z, N);
-    // fused epilogue: the tile's bias into the operand stages, once every
-    // wave is done with them
-    [[maybe_unused]] float *lds_bias = reinterpret_cast<float *>(smem);
-    if constexpr (EPI == EPI_FUSED) {
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        stage_bias<OUT>(ep, n0, N, BN, lds_bias, tid, NW * 64);
-        __syncthreads();
+    [[maybe_unused]] const EpiState ep = make_epi<OUT == DT_I32 ? DT_F32 : OUT>(args, z, N);
+    // fused epilogue: the tile's bias and scales into the operand stages,
+    // once every wave is done with them
+    if constexpr (EPI_LDS > 1) {
+        const float *lds_epi = epi_smem;
+        // row blocks outside, as in the plain epilogue, so the stores of one
+        // row's column blocks follow each other and complete whole lines
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int ml = ml0 + i * 16;
+            if (m0 + ml >= M) continue;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int nl = nl0 + j * 16;
+                const int nvalid = N - (n0 + nl);
+                if (nvalid <= 0) continue;
+                float b[4], s[4], v[4];
+                read_epi4(lds_epi, BN, nl, b, s);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    s[q] *= alpha;
+                    v[q] = acc[i][j][q];
+                }
+                finish4_fused<OUT>(rc, (ml * ldc + nl) * CES, nvalid, vec, beta, v, ep, b, s);
+            }
+        }
+        return;
     }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -574,12 +608,7 @@ void gemm_dma_kernel(const GemmArgs args) {
                         continue;
                     }
                 }
-                if constexpr (EPI == EPI_FUSED) {
-                    float b[4];
-                    read_bias4(lds_bias, nl, b);
-                    finish4<OUT>(rc, off, nvalid, vec, alpha, beta, v, ep, b);
-                }
-                else finish4<OUT>(rc, off, nvalid, vec, alpha, beta, v);
+                finish4<OUT>(rc, off, nvalid, vec, alpha, beta, v);
             }
         }
     }

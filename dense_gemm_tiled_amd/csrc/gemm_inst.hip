@@ -18,7 +18,8 @@ namespace {
 constexpr bool out_ok(int cls, int out) {
     if (is_dma_class(cls) && TCG_DT == DT_F32) return false;
     if (out == OUT_PARTIAL) return cls == TILE_64 || cls == TILE_128 || cls == TILE_128_DMA;
-    if (TCG_DT == DT_I8) return out == DT_I32;
+    // int8 into a float output: the dequantizing fused epilogue only
+    if (TCG_DT == DT_I8) return out == DT_I32 || out == DT_F32 || out == DT_F16 || out == DT_BF16;
     if (TCG_DT == DT_F32) return out == DT_F32;
     return out == TCG_DT || out == DT_F32;
 }
@@ -43,7 +44,12 @@ hipError_t launch_one(const GemmArgs &args, int64_t grid, hipStream_t stream) {
 #define TCG_DMA(KM, EP) \
     hipLaunchKernelGGL((gemm_dma_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, OUT, T, T, NW, OCC, KM, EP>), \
                        g, b, 0, stream, args)
-        if constexpr (FLOAT_OUT) {
+        if constexpr (FLOAT_OUT && TCG_DT == DT_I8) {
+            // int8 sums reach a float output only through the fused epilogue
+            if (epi != EPI_FUSED) return hipErrorInvalidValue;
+            if (kmask) TCG_DMA(true, EPI_FUSED);
+            else TCG_DMA(false, EPI_FUSED);
+        } else if constexpr (FLOAT_OUT) {
             if (kmask) {
                 if (epi == EPI_FUSED) TCG_DMA(true, EPI_FUSED);
                 else if (epi == EPI_BETA) TCG_DMA(true, EPI_BETA);
@@ -60,6 +66,8 @@ hipError_t launch_one(const GemmArgs &args, int64_t grid, hipStream_t stream) {
 #undef TCG_DMA
         return hipGetLastError();
     } else if constexpr (!is_dma_class(CLS) && out_ok(CLS, OUT)) {
+        if (TCG_DT == DT_I8 && OUT != DT_I32 && OUT != OUT_PARTIAL && !args.epi)
+            return hipErrorInvalidValue;
         hipLaunchKernelGGL((gemm_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, CLS, OUT>),
                            dim3((unsigned)grid), dim3(256), 0, stream, args);
         return hipGetLastError();

@@ -382,28 +382,38 @@ __device__ inline void store_i4(__amdgpu_buffer_rsrc_t r, int off, int nvalid, b
     }
 }
 
-// Fused epilogue of one problem (tessl "Architecture", "Fused Epilogue"):
-// after alpha * acc + beta * C_old, add the column's bias (stored in C's
-// element type, one vector per problem) and apply the activation, still in
-// fp32 registers, before the single rounding to the output type.
+// Fused epilogue of one problem (tessl "Architecture", "Fused Epilogue" and
+// "Integer GEMM"): the accumulator times the column's dequantization scale
+// (fp32, one vector per problem; 1 without), then alpha * . + beta * C_old,
+// plus the column's bias (stored in C's element type) and the activation,
+// still in fp32 registers, before the single rounding to the output type.
 struct EpiState {
     __amdgpu_buffer_rsrc_t rb;   // this problem's bias vector (empty range without one)
+    __amdgpu_buffer_rsrc_t rs;   // this problem's scale vector (likewise)
     int act;
-    bool bias;
+    bool bias, scale;
     bool on;
 };
 
 template <int CDT>
-__device__ inline EpiState make_epi(const void *bias, int64_t bias_stride, int act, int epi, int z,
-                                    int N) {
+__device__ inline EpiState make_epi(const void *bias, int64_t bias_stride, const float *scale,
+                                    int64_t scale_stride, int act, int epi, int z, int N) {
     constexpr int CES = dt_size(CDT);
     EpiState e;
     e.on = epi != 0;
     e.act = act;
     e.bias = bias != nullptr;
+    e.scale = scale != nullptr;
     const char *b = e.bias ? static_cast<const char *>(bias) + z * bias_stride * CES : nullptr;
     e.rb = make_rsrc(b, e.bias ? (int64_t)N * CES : 0);
+    const float *s = e.scale ? scale + z * scale_stride : nullptr;
+    e.rs = make_rsrc(s, e.scale ? (int64_t)N * 4 : 0);
     return e;
+}
+
+template <int CDT, typename Args>
+__device__ inline EpiState make_epi(const Args &a, int z, int N) {
+    return make_epi<CDT>(a.bias, a.bias_stride, a.scale, a.scale_stride, a.act, a.epi, z, N);
 }
 
 // GELU, tanh form: 0.5 y (1 + tanh(u)) with u = sqrt(2/pi) (y + 0.044715 y^3).
@@ -417,7 +427,8 @@ __device__ inline float gelu_tanh(float y) {
     return y * __builtin_amdgcn_rcpf(1.f + e);
 }
 
-// The bias of columns n .. n + nvalid - 1 (zero past them or without a bias).
+// The bias of columns n .. n + nvalid - 1 (zero past them or without a bias)
+// and their scales (one without a scale).
 template <int CDT>
 __device__ inline void load_bias4(const EpiState &e, int n, int nvalid, float (&b)[4]) {
     if (e.bias) {
@@ -427,38 +438,65 @@ __device__ inline void load_bias4(const EpiState &e, int n, int nvalid, float (&
         for (int q = 0; q < 4; ++q) b[q] = 0.f;
     }
 }
+__device__ inline void load_scale4(const EpiState &e, int n, int nvalid, float (&s)[4]) {
+    if (e.scale) {
+        load_c4<DT_F32>(e.rs, n * 4, nvalid, true, s);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s[q] = 1.f;
+    }
+}
 
-// The BN bias values of the tile starting at column n0, as fp32 in LDS (zero
-// past N or without a bias): staged once per workgroup, so the epilogue reads
-// each lane's four columns from LDS instead of from memory behind its own C
-// stores.  The caller makes the LDS free before and synchronizes after.
+// Column n's bias (zero past N or without a bias) and scale (one without).
 template <int CDT>
-__device__ inline void stage_bias(const EpiState &e, int n0, int N, int bn, float *lds_bias, int tid,
-                                  int nthreads) {
+__device__ inline void load_epi1(const EpiState &e, int n, int N, float &b, float &s) {
     constexpr int CES = dt_size(CDT);
-    for (int t = tid; t < bn; t += nthreads) {
-        float b = 0.f;
-        if (e.bias && n0 + t < N) {
-            const int off = (n0 + t) * CES;
+    b = 0.f;
+    s = 1.f;
+    if (n < N) {
+        if (e.bias) {
+            const int off = n * CES;
             if constexpr (CDT == DT_F32) b = as_f32(__builtin_amdgcn_raw_buffer_load_b32(e.rb, off, 0, 0));
             else if constexpr (CDT == DT_BF16) b = from_bf16_bits(__builtin_amdgcn_raw_buffer_load_b16(e.rb, off, 0, 0));
             else b = from_f16_bits(__builtin_amdgcn_raw_buffer_load_b16(e.rb, off, 0, 0));
         }
-        lds_bias[t] = b;
+        if (e.scale) s = as_f32(__builtin_amdgcn_raw_buffer_load_b32(e.rs, n * 4, 0, 0));
     }
 }
 
-// Four staged bias values from tile column nl (a multiple of 4).
-__device__ inline void read_bias4(const float *lds_bias, int nl, float (&b)[4]) {
-    const f32x4 w = *reinterpret_cast<const f32x4 *>(lds_bias + nl);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) b[q] = w[q];
+// The bn bias values of the tile starting at column n0 (lds[0 .. bn), zero
+// past N or without a bias) and its scales (lds[bn .. 2 bn), one without a
+// scale), as fp32 in LDS: staged once per workgroup, so the epilogue reads
+// each lane's four columns from LDS instead of from memory behind its own C
+// stores.  The caller makes the LDS free before and synchronizes after.
+template <int CDT>
+__device__ inline void stage_epi(const EpiState &e, int n0, int N, int bn, float *lds, int tid,
+                                 int nthreads) {
+    for (int t = tid; t < bn; t += nthreads) {
+        float b, s;
+        load_epi1<CDT>(e, n0 + t, N, b, s);
+        lds[t] = b;
+        lds[bn + t] = s;
+    }
 }
 
-// v + b, then the activation.
-__device__ inline void act4(const EpiState &e, const float (&b)[4], float (&v)[4]) {
+// Four staged bias values and scales from tile column nl (a multiple of 4).
+__device__ inline void read_epi4(const float *lds, int bn, int nl, float (&b)[4], float (&s)[4]) {
+    const f32x4 wb = *reinterpret_cast<const f32x4 *>(lds + nl);
+    const f32x4 ws = *reinterpret_cast<const f32x4 *>(lds + bn + nl);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] += b[q];
+    for (int q = 0; q < 4; ++q) {
+        b[q] = wb[q];
+        s[q] = ws[q];
+    }
+}
+
+// v + b (when there is a bias), then the activation.
+__device__ inline void act4(const EpiState &e, const float (&b)[4], float (&v)[4]) {
+    if (e.bias) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] += b[q];
+    }
     if (e.act == ACT_RELU) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = v[q] > 0.f ? v[q] : 0.f;
@@ -468,13 +506,7 @@ __device__ inline void act4(const EpiState &e, const float (&b)[4], float (&v)[4
     }
 }
 
-// Bias of columns n .. n + nvalid - 1, then the activation.
-template <int CDT>
-__device__ inline void apply_epi(const EpiState &e, int n, int nvalid, float (&v)[4]) {
-    float b[4];
-    load_bias4<CDT>(e, n, nvalid, b);
-    act4(e, b, v);
-}
+
 
 // alpha * acc + beta * C_old for 4 values, C_old read only when beta != 0.
 template <int CDT>
@@ -498,23 +530,51 @@ __device__ inline void finish4(__amdgpu_buffer_rsrc_t rc, int off, int nvalid, b
     store_c4<CDT>(rc, off, nvalid, vec, v);
 }
 
-// scale4, the fused epilogue when one is on (n: column of v[0]), the store.
-template <int CDT>
-__device__ inline void finish4(__amdgpu_buffer_rsrc_t rc, int off, int nvalid, bool vec,
-                               float alpha, float beta, float (&v)[4], const EpiState &ep, int n) {
-    scale4<CDT>(rc, off, nvalid, vec, alpha, beta, v);
-    if (ep.on) apply_epi<CDT>(ep, n, nvalid, v);
-    store_c4<CDT>(rc, off, nvalid, vec, v);
-}
-
-// The same with the bias of the four columns already loaded.
+// The fused epilogue with the four columns' bias b and scale s at hand:
+// v * s, then scale4, then bias and activation, then the store.
 template <int CDT>
 __device__ inline void finish4(__amdgpu_buffer_rsrc_t rc, int off, int nvalid, bool vec,
                                float alpha, float beta, float (&v)[4], const EpiState &ep,
-                               const float (&b)[4]) {
+                               const float (&b)[4], const float (&s)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] *= s[q];
     scale4<CDT>(rc, off, nvalid, vec, alpha, beta, v);
     act4(ep, b, v);
     store_c4<CDT>(rc, off, nvalid, vec, v);
+}
+
+// The fused epilogue with sa = alpha * scale of the four columns folded:
+// v * sa + beta * C_old (C read only when beta != 0), bias, activation,
+// store.
+template <int CDT>
+__device__ inline void finish4_fused(__amdgpu_buffer_rsrc_t rc, int off, int nvalid, bool vec,
+                                     float beta, float (&v)[4], const EpiState &ep,
+                                     const float (&b)[4], const float (&sa)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] *= sa[q];
+    if (beta != 0.f) {
+        float old[4];
+        load_c4<CDT>(rc, off, nvalid, vec, old);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = __builtin_fmaf(beta, old[q], v[q]);
+    }
+    act4(ep, b, v);
+    store_c4<CDT>(rc, off, nvalid, vec, v);
+}
+
+// The same with bias and scale loaded here (n: column of v[0]); without a
+// fused epilogue the plain finish4.
+template <int CDT>
+__device__ inline void finish4(__amdgpu_buffer_rsrc_t rc, int off, int nvalid, bool vec,
+                               float alpha, float beta, float (&v)[4], const EpiState &ep, int n) {
+    if (!ep.on) {
+        finish4<CDT>(rc, off, nvalid, vec, alpha, beta, v);
+        return;
+    }
+    float b[4], s[4];
+    load_bias4<CDT>(ep, n, nvalid, b);
+    load_scale4(ep, n, nvalid, s);
+    finish4<CDT>(rc, off, nvalid, vec, alpha, beta, v, ep, b, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -663,13 +723,12 @@ __global__ __launch_bounds__(256, Occupancy<CLS>::value) void gemm_kernel(const 
         const bool vec = args.c_vec_ok != 0;
         const int ldc = args.ldc;
         const float alpha = args.alpha, beta = args.beta;
-        const EpiState ep = make_epi<OUT == DT_I32 ? DT_F32 : OUT>(args.bias, args.bias_stride,
-                                                                   args.act, args.epi, z, N);
-        // fused epilogue: the tile's bias into the (free) LDS
-        float *lds_bias = reinterpret_cast<float *>(smem);
+        const EpiState ep = make_epi<OUT == DT_I32 ? DT_F32 : OUT>(args, z, N);
+        // fused epilogue: the tile's bias and scales into the (free) LDS
+        float *lds_epi = reinterpret_cast<float *>(smem);
         if constexpr (OUT != DT_I32) {
             if (ep.on) {
-                stage_bias<OUT>(ep, n0, N, BN, lds_bias, tid, 256);
+                stage_epi<OUT>(ep, n0, N, BN, lds_epi, tid, 256);
                 __syncthreads();
             }
         }
@@ -693,9 +752,9 @@ __global__ __launch_bounds__(256, Occupancy<CLS>::value) void gemm_kernel(const 
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e];
                     if (ep.on) {
-                        float b[4];
-                        read_bias4(lds_bias, nl, b);
-                        finish4<OUT>(rc, off, nvalid, vec, alpha, beta, v, ep, b);
+                        float b[4], s[4];
+                        read_epi4(lds_epi, BN, nl, b, s);
+                        finish4<OUT>(rc, off, nvalid, vec, alpha, beta, v, ep, b, s);
                     } else {
                         finish4<OUT>(rc, off, nvalid, vec, alpha, beta, v);
                     }

@@ -79,11 +79,13 @@ struct GemmArgs {
     int32_t band;                  // tile-order band height (<= 0: row-major)
     int32_t c_vec_ok;              // 4 complete C values go as one vector access
     int32_t c_dma_ok;              // C rows, batch stride and base are whole 16-byte chunks
-    // fused epilogue: out = act(alpha*acc + beta*C_old + bias[n])
+    // fused epilogue: out = act(alpha*scale[n]*acc + beta*C_old + bias[n])
     const void *bias;              // N values of c_dtype per problem, or null
     int64_t bias_stride;           // elements between the problems' bias vectors
+    const float *scale;            // N per-column fp32 scales per problem, or null
+    int64_t scale_stride;          // elements between the problems' scale vectors
     int32_t act;                   // ACT_*
-    int32_t epi;                   // bias != null || act != ACT_NONE
+    int32_t epi;                   // bias or scale != null || act != ACT_NONE
 };
 
 // Arguments of the split-K reduction and of the alpha == 0 scaling kernel.
@@ -100,6 +102,8 @@ struct EpilogueArgs {
     float alpha, beta;
     const void *bias;          // fused epilogue, as in GemmArgs
     int64_t bias_stride;
+    const float *scale;
+    int64_t scale_stride;
     int32_t act, epi;
 };
 

@@ -53,8 +53,10 @@ std::string g_plan_error;   // error text of tc_gemm_plan(NULL, ...)
 struct Epilogue {
     const void *bias = nullptr;   // N values of c_dtype per problem
     int64_t bias_stride = 0;      // elements between problems' vectors
+    const float *scale = nullptr; // N per-column fp32 scales per problem
+    int64_t scale_stride = 0;
     int act = ACT_NONE;
-    bool on() const { return bias != nullptr || act != ACT_NONE; }
+    bool on() const { return bias != nullptr || scale != nullptr || act != ACT_NONE; }
 };
 
 // Everything validation derives from a descriptor.
@@ -127,7 +129,10 @@ const char *dt_name(int dt) {
     }
 }
 
-tc_status_t validate(const tc_gemm_batched_desc *bd, Problem *p, std::string *err) {
+// dequant: the call carries a per-column scale, so int8 inputs may have a
+// float output (tessl "Architecture", "Integer GEMM": gemm_i8_dequant).
+tc_status_t validate(const tc_gemm_batched_desc *bd, Problem *p, std::string *err,
+                     bool dequant = false) {
     if (!bd) return fail(err, TC_ERR_INVALID_ARGUMENT, "descriptor is NULL");
     const tc_gemm_desc &d = bd->base;
     if (d.M < 1 || d.N < 1 || d.K < 1)
@@ -144,7 +149,8 @@ tc_status_t validate(const tc_gemm_batched_desc *bd, Problem *p, std::string *er
     } else if (a == TC_F16 || a == TC_BF16) {
         ok = (c == a || c == TC_F32) && acc == TC_F32;
     } else if (a == TC_I8) {
-        ok = c == TC_I32 && acc == TC_I32;
+        ok = acc == TC_I32 &&
+             (c == TC_I32 || (dequant && (c == TC_F32 || c == TC_F16 || c == TC_BF16)));
     }
     if (!ok)
         return fail(err, TC_ERR_UNSUPPORTED, "unsupported dtypes a=%s b=%s c=%s accum=%s", dt_name(a),
@@ -172,7 +178,7 @@ tc_status_t validate(const tc_gemm_batched_desc *bd, Problem *p, std::string *er
         return fail(err, TC_ERR_INVALID_ARGUMENT, "alpha and beta must be finite");
 
     if (a == TC_I8) {
-        if (d.alpha != 1.0f || d.beta != 0.0f)
+        if (c == TC_I32 && (d.alpha != 1.0f || d.beta != 0.0f))
             return fail(err, TC_ERR_UNSUPPORTED, "int8 GEMM needs alpha = 1 and beta = 0");
         if (d.K > kMaxInt8K)
             return fail(err, TC_ERR_OVERFLOW, "int8 K=%d > %d: an int32 sum could wrap", d.K, kMaxInt8K);
@@ -604,6 +610,8 @@ tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan 
     ea.c_vec_ok = c_vec_ok;
     ea.bias = epi.bias;
     ea.bias_stride = epi.bias_stride;
+    ea.scale = epi.scale;
+    ea.scale_stride = epi.scale_stride;
     ea.act = epi.act;
     ea.epi = epi.on();
 
@@ -685,6 +693,8 @@ tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan 
                       (uintptr_t)C % 16 == 0;
         ga.bias = epi.bias;
         ga.bias_stride = epi.bias_stride;
+        ga.scale = epi.scale;
+        ga.scale_stride = epi.scale_stride;
         ga.act = epi.act;
         ga.epi = epi.on();
         // an armed measurement brackets the GEMM kernel alone (one call only)
@@ -718,10 +728,10 @@ tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan 
     return TC_OK;
 }
 
-// Bytes the bias vectors of all problems span (0 without a bias).
-int64_t epilogue_bias_bytes(const Problem &p, const Epilogue &e) {
-    if (!e.bias) return 0;
-    return ((int64_t)(p.batch - 1) * e.bias_stride + p.N) * dt_size(p.cdt);
+// Bytes the bias (w = 0) or scale (w = 1) vectors of all problems span.
+int64_t epilogue_vec_bytes(const Problem &p, const Epilogue &e, int w) {
+    return ((int64_t)(p.batch - 1) * (w ? e.scale_stride : e.bias_stride) + p.N) *
+           (w ? 4 : dt_size(p.cdt));
 }
 
 // The fused epilogue (tessl "Architecture", "Fused Epilogue"): it needs the
@@ -733,22 +743,30 @@ tc_status_t validate_epilogue(const Problem &p, const tc_epilogue *ep, const voi
     if (ep->activation != TC_ACT_NONE && ep->activation != TC_ACT_RELU &&
         ep->activation != TC_ACT_GELU_TANH)
         return fail(err, TC_ERR_INVALID_ARGUMENT, "unknown activation %d", (int)ep->activation);
-    if (p.dt == TC_I8)
+    if (p.dt == TC_I8 && p.cdt == TC_I32)
         return fail(err, TC_ERR_UNSUPPORTED,
-                    "the fused epilogue takes float inputs; int8 results are exact int32 sums");
-    if (ep->bias_stride < 0) return fail(err, TC_ERR_INVALID_ARGUMENT, "bias_stride must be >= 0");
+                    "the fused epilogue needs a float result; int8 into int32 is the exact sum "
+                    "(give a per-column scale and a float C to dequantize)");
+    if (ep->bias_stride < 0 || ep->scale_stride < 0)
+        return fail(err, TC_ERR_INVALID_ARGUMENT, "bias_stride and scale_stride must be >= 0");
     out->bias = ep->bias;
     out->bias_stride = p.batch > 1 ? ep->bias_stride : 0;
+    out->scale = ep->col_scale;
+    out->scale_stride = p.batch > 1 ? ep->scale_stride : 0;
     out->act = ep->activation == TC_ACT_RELU ? ACT_RELU
              : ep->activation == TC_ACT_GELU_TANH ? ACT_GELU_TANH : ACT_NONE;
-    if (out->bias) {
+    const void *vec[2] = {out->bias, out->scale};
+    const int64_t stride[2] = {out->bias_stride, out->scale_stride};
+    const int64_t es[2] = {dt_size(p.cdt), 4};
+    const char *name[2] = {"bias", "col_scale"};
+    for (int w = 0; w < 2; ++w) {
+        if (!vec[w]) continue;
         int64_t t, bytes;
-        if (__builtin_mul_overflow((int64_t)(p.batch - 1), out->bias_stride, &t) ||
-            __builtin_add_overflow(t, (int64_t)p.N, &t) ||
-            __builtin_mul_overflow(t, (int64_t)dt_size(p.cdt), &bytes))
-            return fail(err, TC_ERR_OVERFLOW, "bias extent overflows 64 bits");
-        if (ranges_overlap(C, p.c_total, out->bias, bytes))
-            return fail(err, TC_ERR_ALIASING, "the bias overlaps C");
+        if (__builtin_mul_overflow((int64_t)(p.batch - 1), stride[w], &t) ||
+            __builtin_add_overflow(t, (int64_t)p.N, &t) || __builtin_mul_overflow(t, es[w], &bytes))
+            return fail(err, TC_ERR_OVERFLOW, "%s extent overflows 64 bits", name[w]);
+        if (ranges_overlap(C, p.c_total, vec[w], bytes))
+            return fail(err, TC_ERR_ALIASING, "the %s overlaps C", name[w]);
     }
     return TC_OK;
 }
@@ -761,7 +779,7 @@ tc_status_t run(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A, 
     std::string *err = &ctx->last_error;
     if (!A || !B || !C) return fail(err, TC_ERR_INVALID_ARGUMENT, "A, B and C must be non-NULL");
     Problem p;
-    tc_status_t st = validate(bd, &p, err);
+    tc_status_t st = validate(bd, &p, err, ep && ep->col_scale);
     if (st != TC_OK) return st;
     Epilogue epi;
     if (ep && (st = validate_epilogue(p, ep, C, &epi, err)) != TC_OK) return st;
@@ -775,7 +793,10 @@ tc_status_t run(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A, 
     if ((st = check_allocation("A", A, p.a_total, err)) != TC_OK) return st;
     if ((st = check_allocation("B", B, p.b_total, err)) != TC_OK) return st;
     if ((st = check_allocation("C", C, p.c_total, err)) != TC_OK) return st;
-    if (epi.bias && (st = check_allocation("bias", epi.bias, epilogue_bias_bytes(p, epi), err)) != TC_OK)
+    if (epi.bias && (st = check_allocation("bias", epi.bias, epilogue_vec_bytes(p, epi, 0), err)) != TC_OK)
+        return st;
+    if (epi.scale &&
+        (st = check_allocation("col_scale", epi.scale, epilogue_vec_bytes(p, epi, 1), err)) != TC_OK)
         return st;
 
     if (!s) {
@@ -790,10 +811,12 @@ tc_status_t run(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A, 
         const void *Ai = static_cast<const char *>(A) + parts.off[i][0] * es;
         const void *Bi = static_cast<const char *>(B) + parts.off[i][1] * es;
         void *Ci = static_cast<char *>(C) + parts.off[i][2] * ces;
-        // a column strip's bias starts at its first column
+        // a column strip's bias and scales start at its first column
         Epilogue epi_i = epi;
-        if (epi.bias && pl.edge == 1 && i == 1)
-            epi_i.bias = static_cast<const char *>(epi.bias) + (int64_t)pl.edge_at * ces;
+        if (pl.edge == 1 && i == 1) {
+            if (epi.bias) epi_i.bias = static_cast<const char *>(epi.bias) + (int64_t)pl.edge_at * ces;
+            if (epi.scale) epi_i.scale = epi.scale + pl.edge_at;
+        }
         if (i) name += "|";
         if ((st = enqueue(ctx, s, parts.p[i], parts.pl[i], Ai, Bi, Ci, epi_i, i == 0, &name, err)) !=
             TC_OK)

@@ -234,8 +234,7 @@ __global__ __launch_bounds__(kThinThreads) void thin_kernel(const GemmArgs args)
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cb, args.c_extent - c_org);
     if (kl != 0 || m0 + rl >= M) return;
     const int row_off = rl * args.ldc * CES;
-    const EpiState ep = make_epi<OUT == DT_I32 ? DT_F32 : OUT>(args.bias, args.bias_stride, args.act,
-                                                               args.epi, z, N);
+    const EpiState ep = make_epi<OUT == DT_I32 ? DT_F32 : OUT>(args, z, N);
 #pragma unroll
     for (int n = 0; n < NS; n += 4) {
         if (n >= N) break;
@@ -244,7 +243,7 @@ __global__ __launch_bounds__(kThinThreads) void thin_kernel(const GemmArgs args)
             int v[4] = {acc[n], acc[n + 1], acc[n + 2], acc[n + 3]};
             store_i4(rc, row_off + n * CES, nvalid, args.c_vec_ok != 0, v);
         } else {
-            float v[4] = {acc[n], acc[n + 1], acc[n + 2], acc[n + 3]};
+            float v[4] = {(float)acc[n], (float)acc[n + 1], (float)acc[n + 2], (float)acc[n + 3]};
             finish4<OUT>(rc, row_off + n * CES, nvalid, args.c_vec_ok != 0, args.alpha, args.beta, v,
                          ep, n);
         }
@@ -319,6 +318,11 @@ template <int DT>
 hipError_t launch_thin_dt(int out, const GemmArgs &args, int64_t grid, hipStream_t stream) {
     if constexpr (DT == DT_I8) {
         if (out == DT_I32) return launch_thin_ns<DT, DT_I32>(args, grid, stream);
+        // float outputs: the dequantizing fused epilogue
+        if (!args.epi) return hipErrorInvalidValue;
+        if (out == DT_F32) return launch_thin_ns<DT, DT_F32>(args, grid, stream);
+        if (out == DT_F16) return launch_thin_ns<DT, DT_F16>(args, grid, stream);
+        if (out == DT_BF16) return launch_thin_ns<DT, DT_BF16>(args, grid, stream);
     } else if constexpr (DT == DT_F32) {
         if (out == DT_F32) return launch_thin_ns<DT, DT_F32>(args, grid, stream);
     } else {

@@ -101,7 +101,18 @@ typedef struct {
  *     TC_ACT_NONE       identity
  *     TC_ACT_RELU       max(y, 0)
  *     TC_ACT_GELU_TANH  0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3)))
- * evaluated in fp32 before the single rounding to c_dtype. */
+ * evaluated in fp32 before the single rounding to c_dtype.
+ *
+ * Per-column dequantization (same page, section "Integer GEMM",
+ * gemm_i8_dequant): with col_scale, column n of the product is multiplied by
+ * col_scale[z*scale_stride + n] first,
+ *
+ *     C = activation(alpha * (op(A)@op(B)) * col_scale + beta * C + bias),
+ *
+ * and int8 inputs may then write a float C (f32, f16 or bf16; accum_dtype
+ * TC_I32; alpha and beta any finite values; K <= 131071): the int32 sums are
+ * exact, converted to fp32 (rounded to nearest), scaled, and rounded once to
+ * c_dtype.  col_scale also applies to float inputs. */
 typedef enum {
     TC_ACT_NONE = 0,
     TC_ACT_RELU = 1,
@@ -115,6 +126,9 @@ typedef struct {
                                      consecutive batch problems; 0 = one vector
                                      shared by all (ignored when batch == 1) */
     tc_activation_t activation;
+    const float *col_scale;       /* device pointer, caller-owned; N fp32
+                                     per-column scales per problem, or NULL */
+    int64_t scale_stride;         /* as bias_stride, for col_scale */
 } tc_epilogue;
 
 typedef struct tc_context tc_context;
@@ -177,12 +191,13 @@ tc_status_t tc_gemm_batched_async(tc_context *ctx, const tc_gemm_batched_desc *b
 /* Batched GEMM with the fused epilogue *ep (see tc_epilogue), synchronous.
  * Same descriptor, pointers and errors as tc_gemm_batched, plus:
  * TC_ERR_INVALID_ARGUMENT for a NULL ep, an unknown activation or a negative
- * bias_stride; TC_ERR_UNSUPPORTED for int8 inputs (their result is the exact
- * int32 sum; the page refuses the fused form where there is no float
- * register accumulator rather than falling back to separate passes);
- * TC_ERR_ALIASING when the bias vectors overlap C; TC_ERR_INVALID_ARGUMENT
- * when they do not lie inside one device allocation.  An ep with no bias and
- * TC_ACT_NONE computes exactly what tc_gemm_batched computes. */
+ * bias_stride / scale_stride; TC_ERR_UNSUPPORTED for int8 inputs into an
+ * int32 C (that result is the exact sum; the page refuses the fused form
+ * where there is no float result rather than falling back to separate
+ * passes) and for int8 into a float C without col_scale; TC_ERR_ALIASING
+ * when the bias or scale vectors overlap C; TC_ERR_INVALID_ARGUMENT when
+ * they do not lie inside one device allocation.  An ep with no bias, no
+ * scale and TC_ACT_NONE computes exactly what tc_gemm_batched computes. */
 tc_status_t tc_gemm_epilogue(tc_context *ctx, const tc_gemm_batched_desc *bd,
                              const tc_epilogue *ep, const void *A, const void *B,
                              void *C);

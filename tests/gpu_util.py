@@ -71,28 +71,34 @@ def run_library(p: workloads.Problem, A, B, C, *, sync=True, misalign=False):
     return from_dev(c_full, p.c_dtype)
 
 
-def run_library_epilogue(p: workloads.Problem, A, B, C, bias, act, *, shared=True):
+def run_library_epilogue(p: workloads.Problem, A, B, C, bias, act, *, shared=True,
+                         col_scale=None):
     """run_library with the fused epilogue: bias [nvec, N] stored values
-    (None: no bias), act an activation name.  shared: one vector for every
-    problem (a 1-D bias tensor), else one per problem."""
+    (None: no bias), act an activation name, col_scale [nvec, N] fp32 (None:
+    no scale).  shared: one vector for every problem (1-D tensors), else one
+    per problem."""
     import torch
     import dense_gemm_tiled_amd as tg
     a_full, b_full, c_full = to_dev(A, p.a_dtype), to_dev(B, p.a_dtype), to_dev(C, p.c_dtype)
     a, b, c = logical_views(p, a_full, b_full, c_full)
-    bt = None
+    bt = st = None
     if bias is not None:
         bt = to_dev(bias, p.c_dtype)
         bt = bt[0] if shared else bt
+    if col_scale is not None:
+        st = torch.from_numpy(np.ascontiguousarray(col_scale)).cuda()
+        st = st[0] if shared else st
     tg.gemm(a, b, c, alpha=p.alpha, beta=p.beta, transpose_a=p.transpose_a,
-            transpose_b=p.transpose_b, bias=bt, activation=act)
+            transpose_b=p.transpose_b, bias=bt, activation=act, col_scale=st)
     torch.cuda.synchronize()
     return from_dev(c_full, p.c_dtype)
 
 
-def oracle_epilogue(p: workloads.Problem, A, B, C, bias, act, *, shared=True):
+def oracle_epilogue(p: workloads.Problem, A, B, C, bias, act, *, shared=True, col_scale=None):
     """The oracle's fused form in C's padded layout."""
     c_in = C if p.beta != 0.0 else None
     out, _ = oracle.gemm_epilogue(A, B, c_in, bias=bias, bias_stride=0 if shared else p.N,
+                                  col_scale=col_scale, scale_stride=0 if shared else p.N,
                                   act=act, M=p.M, N=p.N, K=p.K, a_dtype=p.a_dtype,
                                   c_dtype=p.c_dtype, transpose_a=p.transpose_a,
                                   transpose_b=p.transpose_b, alpha=p.alpha, beta=p.beta,
@@ -137,7 +143,9 @@ def compare(p: workloads.Problem, got_full, ref_full, C_in=None, label=""):
     r = oracle.decode(ref, p.c_dtype)
     assert np.isfinite(g).all(), "%s: non-finite outputs" % label
     err = oracle.rel_frobenius(g, r)
-    assert err <= TOL[p.a_dtype], "%s: relF %.3g > %.1g" % (label, err, TOL[p.a_dtype])
+    # keyed by the input type; int8 dequantized into floats by the output type
+    tol = TOL[p.a_dtype] if p.a_dtype in TOL else TOL[p.c_dtype]
+    assert err <= tol, "%s: relF %.3g > %.1g" % (label, err, tol)
     return err
 
 

@@ -390,6 +390,102 @@ def test_epilogue_without_bias_or_activation_is_the_plain_product():
     assert np.array_equal(plain.view(np.uint16), got.view(np.uint16))
 
 
+# ---------------------------------------------------------------- int8 dequant
+DEQ_OUT = ["f32", "f16", "bf16"]
+
+
+def deq_check(p, label, *, act="none", bias=False, shared=True, **envs):
+    """int8 x int8 -> exact int32 sums -> per-column fp32 scale (and optionally
+    alpha, beta, bias, activation) -> float C, against the oracle."""
+    A, B, C = workloads.make_inputs(p)
+    nvec = 1 if shared else p.batch
+    sc = workloads.make_col_scale(p, nvec)
+    bv = workloads.make_bias(p, nvec) if bias else None
+    say("GPU case: dequant", label, p.M, p.N, p.K, p.c_dtype, p.layout, act, envs)
+    with env(**envs):
+        got = run_library_epilogue(p, A, B, C, bv, act, shared=shared, col_scale=sc)
+    ref = oracle_epilogue(p, A, B, C, bv, act, shared=shared, col_scale=sc)
+    return compare(p, got, ref, C_in=C, label=label)
+
+
+def deq_problem(c, M, N, K, ta=False, tb=False, **kw):
+    alpha = kw.pop("alpha", 1.0)
+    beta = kw.pop("beta", 0.0)
+    c_dist = kw.pop("c_dist", "normal" if beta != 0.0 else "nan")
+    seed = zlib.crc32(repr(("deq", c, M, N, K, ta, tb)).encode()) % 2 ** 31
+    return P("case", M, N, K, "i8", c, transpose_a=ta, transpose_b=tb, alpha=alpha, beta=beta,
+             dist="int8", c_dist=c_dist, seed=seed, **kw)
+
+
+@pytest.mark.parametrize("tile", DMA_TILES)
+@pytest.mark.parametrize("ta,tb", LAYOUTS, ids=[lay(*l) for l in LAYOUTS])
+@pytest.mark.parametrize("c", DEQ_OUT)
+def test_i8_dequant_dma_kernels(c, ta, tb, tile):
+    """The direct-to-LDS classes, every layout, ragged tiles and K tail."""
+    import dense_gemm_tiled_amd as tg
+    p = deq_problem(c, 304, 272, 208, ta, tb)
+    deq_check(p, "dequant %s" % tile, TCGEMM_TILE=tile)
+    assert tg.last_kernel().endswith(DMA_NAME[tile]), tg.last_kernel()
+
+
+@pytest.mark.parametrize("tile", [256, 128, 64])
+@pytest.mark.parametrize("c", DEQ_OUT)
+def test_i8_dequant_register_staged(c, tile):
+    p = deq_problem(c, 300, 270, 197, True, False)
+    deq_check(p, "dequant tile%d" % tile, TCGEMM_TILE=tile)
+
+
+@pytest.mark.parametrize("c", DEQ_OUT)
+def test_i8_dequant_composed_split_k(c):
+    """Split-K: the reduction sums int32 slices exactly, then dequantizes and
+    applies alpha, beta, a bias and GELU; one scale and bias per problem."""
+    import dense_gemm_tiled_amd as tg
+    p = deq_problem(c, 130, 200, 1100, False, False, alpha=0.5, beta=1.0, batch=2)
+    deq_check(p, "dequant splitk", act="gelu_tanh", bias=True, shared=False, TCGEMM_SPLITS=3)
+    assert tg.last_kernel().endswith("+splitk_reduce"), tg.last_kernel()
+
+
+@pytest.mark.parametrize("tb", [False, True], ids=["nn", "nt"])
+@pytest.mark.parametrize("c", DEQ_OUT)
+def test_i8_dequant_thin(c, tb):
+    p = deq_problem(c, 300, 11, 5000, False, tb, batch=2)
+    deq_check(p, "dequant thin", act="relu", bias=True, shared=False, TCGEMM_TILE="thin")
+
+
+def test_i8_dequant_extremes_exact():
+    """All (-128)*(-128) over K = 131071 with power-of-two scales: every f32
+    result is exact, 16384*K*s[j]."""
+    import torch
+    import dense_gemm_tiled_amd as tg
+    K = 131071
+    a = torch.full((2048, K), -128, dtype=torch.int8, device="cuda")
+    b = torch.full((K, 20), -128, dtype=torch.int8, device="cuda")
+    s = torch.tensor([2.0 ** -e for e in range(20)], dtype=torch.float32, device="cuda")
+    c = torch.empty(2048, 20, dtype=torch.float32, device="cuda")
+    say("GPU case: dequant extremes")
+    tg.gemm(a, b, c, col_scale=s)
+    torch.cuda.synchronize()
+    assert torch.equal(c, (16384.0 * K * s.double()).float().expand(2048, 20))
+
+
+def test_workload_i8_nn_ragged_dequant_bf16():
+    """The int8 ragged shape (pack, 256x256 main part, thin strip) into bf16
+    through the per-column scale, checked at sampled outputs."""
+    import dense_gemm_tiled_amd as tg
+    p = workloads.get("i8_nn_ragged_dequant_bf16")
+    A, B, C = workloads.make_inputs(p)
+    sc = workloads.make_col_scale(p)
+    say("GPU case: workload", p.name)
+    got = logical(p, run_library_epilogue(p, A, B, C, None, "none", col_scale=sc))
+    assert tg.last_kernel() == ("pack_b+gemm_i8_nn_256x256_dma|"
+                                "transpose_b+gemm_i8_nn_thin"), tg.last_kernel()
+    pts = workloads.sample_points(p, 4096)
+    r, _ = oracle.gemm_epilogue_points(A, B, None, pts, col_scale=sc, M=p.M, N=p.N, K=p.K,
+                                       a_dtype="i8", c_dtype=p.c_dtype, ldb=p.LDB)
+    g = oracle.decode(got[pts[:, 0], pts[:, 1], pts[:, 2]], p.c_dtype)
+    assert oracle.rel_frobenius(g, oracle.decode(r, p.c_dtype)) <= TOL[p.c_dtype]
+
+
 # ---------------------------------------------------------------- exact regime
 @pytest.mark.parametrize("a,c", [("bf16", "f32"), ("bf16", "bf16"), ("f16", "f16"), ("f32", "f32")])
 def test_exact_regime_bitwise(a, c):

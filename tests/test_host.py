@@ -141,16 +141,27 @@ def test_overlap_refused(lib, ctx):
     assert lib.tc_dispatch_count(ctx) == 0
 
 
-def epi(bias=None, stride=0, act=0):
+def epi(bias=None, stride=0, act=0, scale=None, sstride=0):
     e = tg.EpilogueT()
     e.bias, e.bias_stride, e.activation = bias, stride, act
+    e.col_scale, e.scale_stride = scale, sstride
     return e
+
+
+S_PTR = 0x50000000000      # a fake per-column scale vector
 
 
 EPI_BAD = [
     # tessl "Architecture", "Fused Epilogue": refused where there is no float
     # register accumulator (int8 results are exact int32 sums)
     ("int8", dict(a=tg.I8, c=tg.I32, acc=tg.I32), {}, 2),
+    ("int8 int32 with scale", dict(a=tg.I8, c=tg.I32, acc=tg.I32), dict(scale=S_PTR), 2),
+    # int8 into a float C needs a per-column dequantization scale
+    ("int8->f32 no scale", dict(a=tg.I8, c=tg.F32, acc=tg.I32), dict(act=1), 2),
+    ("int8->bf16 accum f32", dict(a=tg.I8, c=tg.BF16, acc=tg.F32), dict(scale=S_PTR), 2),
+    ("int8 dequant K wrap", dict(a=tg.I8, c=tg.F32, acc=tg.I32, K=131072), dict(scale=S_PTR), 3),
+    ("scale_stride<0", dict(batch=2, sa=4096, sb=4096, sc=4096), dict(scale=S_PTR, sstride=-2), 1),
+    ("scale overlaps C", {}, dict(scale=C_PTR + 4096), 4),
     ("activation 3", {}, dict(act=3), 1),
     ("activation -1", {}, dict(act=-1), 1),
     ("bias_stride<0", dict(batch=2, sa=4096, sb=4096, sc=4096), dict(bias=0x40000000000, stride=-1), 1),
@@ -184,13 +195,19 @@ def test_epilogue_null_arguments(lib, ctx):
     assert lib.tc_dispatch_count(ctx) == 0
 
 
-def test_epilogue_valid_call_without_gpu_fails_cleanly(lib, ctx):
+@pytest.mark.parametrize("dkw,ekw", [
+    ({}, dict(bias=0x40000000000, act=2)),
+    # int8 dequantized into f32 / bf16, alpha and beta free
+    (dict(a=tg.I8, c=tg.F32, acc=tg.I32, alpha=0.5, beta=1.0), dict(scale=S_PTR)),
+    (dict(a=tg.I8, c=tg.BF16, acc=tg.I32, K=131071), dict(scale=S_PTR, act=1)),
+], ids=["bf16 bias gelu", "int8 dequant f32", "int8 dequant bf16 relu"])
+def test_epilogue_valid_call_without_gpu_fails_cleanly(lib, ctx, dkw, ekw):
     """A valid epilogue passes validation and then fails at the device (no GPU
     here), launching nothing."""
-    d = desc()
-    e = epi(bias=0x40000000000, act=2)
+    d = desc(**dkw)
+    e = epi(**ekw)
     st = lib.tc_gemm_epilogue(ctx, ctypes.byref(d), ctypes.byref(e), A_PTR, B_PTR, C_PTR)
-    assert st in (1, 6)
+    assert st in (1, 6), (tg.status_name(st), lib.tc_last_error(ctx))
     assert lib.tc_dispatch_count(ctx) == 0
 
 

@@ -176,6 +176,13 @@ def make_bias(p: Problem, nvec: int = 1, seed_offset: int = 77) -> np.ndarray:
     return _to_storage(rng.normal(0.0, 1.0, size=(nvec, p.N)), p.c_dtype)
 
 
+def make_col_scale(p: Problem, nvec: int = 1, seed_offset: int = 91) -> np.ndarray:
+    """Per-column dequantization scales: nvec vectors of N fp32 values drawn
+    from N(0, 0.01^2) (shape [nvec, N]); seeded from the problem."""
+    rng = np.random.default_rng(p.seed + seed_offset)
+    return rng.normal(0.0, 0.01, size=(nvec, p.N)).astype(np.float32)
+
+
 # The five measured workloads.
 WORKLOADS: Dict[str, Problem] = {
     "sgemm_nn_256": Problem(
@@ -195,6 +202,11 @@ WORKLOADS: Dict[str, Problem] = {
         batch=8, dist="uniform", scale=1.0, seed=1005),
     "i8_nn_ragged": Problem(
         "i8_nn_ragged", 4093, 4099, 4096, "i8", "i32", dist="int8", seed=1006),
+    # the int8 ragged shape dequantized per column into bf16 (half the C
+    # bytes of int32): not one of the five, measured against it
+    "i8_nn_ragged_dequant_bf16": Problem(
+        "i8_nn_ragged_dequant_bf16", 4093, 4099, 4096, "i8", "bf16", dist="int8", seed=1006,
+        extra={"col_scale": "1"}),
     # the headline shape with the fused epilogue (a per-column bias and
     # GELU-tanh): not one of the five, measured against the plain headline
     "bf16_nn_4096_bias_gelu": Problem(
