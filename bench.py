@@ -121,7 +121,7 @@ def main():
     import dense_gemm_tiled_amd as tg
 
     p = workloads.get(args.workload)
-    hbm_bound = p.name == "bf16_tn_splitk_b8"
+    hbm_bound = p.name == "bf16_tn_splitk_b8" or p.extra.get("bound") == "hbm"
     torch.cuda.set_device(0)
     tg.load_library()
 
@@ -186,7 +186,8 @@ def main():
     if hbm_bound:
         value = alg_bytes * args.steps / wall / 1e9
         unit = "GB/s"
-        metric = "GEMM GB/s and % of MI355X HBM bandwidth, bf16 TN split-K 128x384x16384 x8 (1 GPU)"
+        metric = ("GEMM GB/s and % of MI355X HBM bandwidth, bf16 TN split-K 128x384x16384 x8 (1 GPU)"
+                  if p.name == "bf16_tn_splitk_b8" else "GEMM GB/s, %s (1 GPU)" % p.name)
     else:
         value = flops * args.steps / wall / 1e12
         unit = "TFLOP/s" if p.a_dtype != "i8" else "TOP/s"

@@ -86,6 +86,9 @@ struct GemmArgs {
     int64_t scale_stride;          // elements between the problems' scale vectors
     int32_t act;                   // ACT_*
     int32_t epi;                   // bias or scale != null || act != ACT_NONE
+    // thin kernel only: output (r, c) of this problem is C[c * ldc + r] (the
+    // transposed product of a small-M GEMM); bias and scales then go by r
+    int32_t c_trans;
 };
 
 // Arguments of the split-K reduction and of the alpha == 0 scaling kernel.

@@ -18,6 +18,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <utility>
 
 #include "tc_internal.h"
 
@@ -69,6 +70,9 @@ struct Problem {
     int64_t stride_a, stride_b, stride_c;
     int64_t a_ext, b_ext, c_ext;          // elements spanned by one problem
     int64_t a_total, b_total, c_total;    // bytes spanned by all problems
+    // the transposed form of a small-M GEMM: this problem's output (r, c) is
+    // C[c*ldc + r] of the caller's
+    bool c_trans = false;
 };
 
 struct Plan {
@@ -87,6 +91,9 @@ struct Plan {
     // on, run as a second GEMM after the whole tiles (0: no split).
     int edge;
     int32_t edge_at;
+    // small-M GEMM run as its transposed product (the plan fields describe
+    // that product): see transposed_problem
+    bool swap;
 };
 
 tc_status_t fail(std::string *err, tc_status_t st, const char *fmt, ...) {
@@ -299,7 +306,45 @@ void layout_workspace(const Problem &p, Plan *pl, const bool aligned[2]) {
 // with S slices (on a class with a partial-sum output: 64x64 or 128x128,
 // else 64x64), TCGEMM_BAND=h sets the band height of the tile order (0:
 // row-major).
+// C = op(A) @ B^T with few rows (M <= 16, B stored [N, K]: a linear layer
+// applied to a few vectors) is the transposed product C^T = B @ op(A)^T, an
+// output of N rows and at most 16 columns with K-contiguous rows on the left:
+// the thin-output kernel's shape, reading B (the large operand) once.  The
+// returned problem is that product: A' = B, B' = A (stored [M, K], or [K, M]
+// when transposed), C written transposed.
+Problem transposed_problem(const Problem &p) {
+    Problem q = p;
+    q.M = p.N;
+    q.N = p.M;
+    q.ta = false;
+    q.tb = !p.ta;
+    q.lda = p.ldb;
+    q.ldb = p.lda;
+    q.stride_a = p.stride_b;
+    q.stride_b = p.stride_a;
+    q.a_ext = p.b_ext;
+    q.b_ext = p.a_ext;
+    q.a_total = p.b_total;
+    q.b_total = p.a_total;
+    q.c_trans = true;
+    return q;
+}
+
+bool gemv_route(const Problem &p) {
+    if (p.c_trans || p.M > 16 || !p.tb || p.alpha == 0.0f) return false;
+    if (getenv("TCGEMM_TILE")) return false;                    // a forced class
+    if (const char *env = getenv("TCGEMM_GEMV"))                // tuning knob: 0 disables
+        if (atoi(env) == 0) return false;
+    return ceil_div(p.N, kThinRows) * p.batch >= 256;
+}
+
 void make_plan(const Problem &p, Plan *pl, bool allow_edge = true) {
+    if (gemv_route(p)) {
+        make_plan(transposed_problem(p), pl, false);
+        pl->swap = true;
+        return;
+    }
+    pl->swap = false;
     const int es = dt_size(p.dt);
     const int bk = kLdsRowBytes / es;
     const bool dma = dma_types(p);
@@ -434,11 +479,21 @@ struct Parts {
     int n;
     Problem p[2];
     Plan pl[2];
-    int64_t off[2][3];
+    int64_t off[2][3];  // element offsets of the part's A, B, C origins (caller's operands)
+    bool swap[2];       // the part runs as its transposed product (A and B exchanged)
 };
 
 Parts split_parts(const Problem &p, const Plan &pl) {
     Parts r;
+    r.swap[0] = r.swap[1] = false;
+    if (pl.swap) {
+        r.n = 1;
+        r.p[0] = transposed_problem(p);
+        r.pl[0] = pl;
+        r.off[0][0] = r.off[0][1] = r.off[0][2] = 0;
+        r.swap[0] = true;
+        return r;
+    }
     if (pl.edge == 0) {
         r.n = 1;
         r.p[0] = p;
@@ -450,7 +505,14 @@ Parts split_parts(const Problem &p, const Plan &pl) {
     const int64_t ext = pl.edge == 1 ? p.N : p.M;
     r.p[0] = sub_problem(p, pl.edge, 0, pl.edge_at, r.off[0]);
     r.p[1] = sub_problem(p, pl.edge, pl.edge_at, ext - pl.edge_at, r.off[1]);
-    for (int i = 0; i < 2; ++i) make_plan(r.p[i], &r.pl[i], false);
+    for (int i = 0; i < 2; ++i) {
+        make_plan(r.p[i], &r.pl[i], false);
+        // a strip of at most 16 rows can take the small-M route itself
+        if (r.pl[i].swap) {
+            r.p[i] = transposed_problem(r.p[i]);
+            r.swap[i] = true;
+        }
+    }
     return r;
 }
 
@@ -458,6 +520,13 @@ Parts split_parts(const Problem &p, const Plan &pl) {
 std::string kernel_chain(const Problem &p, const Plan &pl) {
     if (p.alpha == 0.0f) return "scale_c";
     std::string name;
+    if (p.c_trans) {
+        // the transposed product of a small-M GEMM, named by the caller's
+        // layout: its A is the product's B (gathered when stored [K, M])
+        if (pl.pack[1]) name += "transpose_a+";
+        name += std::string("gemv_") + dt_name(p.dt) + (p.tb ? "_nt" : "_tt") + "_thin";
+        return name;
+    }
     if (pl.pack[0]) name += "pack_a+";
     if (pl.pack[1]) name += thin_transposes_b(p, pl) ? "transpose_b+" : "pack_b+";
     name += tcg_kernel_name(p.dt, p.ta, p.tb, pl.cls);
@@ -695,6 +764,7 @@ tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan 
         ga.bias_stride = epi.bias_stride;
         ga.scale = epi.scale;
         ga.scale_stride = epi.scale_stride;
+        ga.c_trans = p.c_trans;
         ga.act = epi.act;
         ga.epi = epi.on();
         // an armed measurement brackets the GEMM kernel alone (one call only)
@@ -810,6 +880,7 @@ tc_status_t run(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A, 
         const int es = dt_size(p.dt), ces = dt_size(p.cdt);
         const void *Ai = static_cast<const char *>(A) + parts.off[i][0] * es;
         const void *Bi = static_cast<const char *>(B) + parts.off[i][1] * es;
+        if (parts.swap[i]) std::swap(Ai, Bi);   // the transposed product: A' = B, B' = A
         void *Ci = static_cast<char *>(C) + parts.off[i][2] * ces;
         // a column strip's bias and scales start at its first column
         Epilogue epi_i = epi;

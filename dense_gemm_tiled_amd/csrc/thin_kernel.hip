@@ -229,6 +229,38 @@ __global__ __launch_bounds__(kThinThreads) void thin_kernel(const GemmArgs args)
         for (int w = 8; w >= 1; w >>= 1) acc[n] += __shfl_xor(acc[n], w, 16);
 
     constexpr int CES = dt_size(OUT);
+    if (args.c_trans) {
+        // the transposed product of a small-M GEMM: row r of this problem is
+        // column r of C and its columns n are rows of C (C[n * ldc + r]);
+        // the bias and scale of C's column r apply to the whole row
+        const int64_t c_org = (int64_t)m0 * CES;
+        char *Cb = static_cast<char *>(args.C) + z * args.stride_c * CES + c_org;
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cb, args.c_extent - c_org);
+        if (kl != 0 || m0 + rl >= M) return;
+        const EpiState ep = make_epi<OUT == DT_I32 ? DT_F32 : OUT>(args, z, M);
+        [[maybe_unused]] float b = 0.f, s = 1.f;
+        if constexpr (OUT != DT_I32) {
+            if (ep.on) load_epi1<OUT>(ep, m0 + rl, M, b, s);
+        }
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+            if (n >= N) break;
+            const int off = n * args.ldc * CES + rl * CES;
+            if constexpr (OUT == DT_I32) {
+                int v[4] = {acc[n], 0, 0, 0};
+                store_i4(rc, off, 1, false, v);
+            } else {
+                float v[4] = {(float)acc[n], 0.f, 0.f, 0.f};
+                if (ep.on) {
+                    const float b4[4] = {b, b, b, b}, s4[4] = {s, s, s, s};
+                    finish4<OUT>(rc, off, 1, false, args.alpha, args.beta, v, ep, b4, s4);
+                } else {
+                    finish4<OUT>(rc, off, 1, false, args.alpha, args.beta, v);
+                }
+            }
+        }
+        return;
+    }
     const int64_t c_org = (int64_t)m0 * args.ldc * CES;
     char *Cb = static_cast<char *>(args.C) + z * args.stride_c * CES + c_org;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cb, args.c_extent - c_org);

@@ -233,8 +233,11 @@ def test_dma128_split_k_packed_shared_operand():
 @pytest.mark.parametrize("a,c,M,N,K,batch,ta,tb,strip", [
     # column strip of 8 on the thin-output kernel
     ("bf16", "bf16", 4096, 4104, 1024, 1, False, False, "|transpose_b+gemm_bf16_nn_thin"),
-    # row strip; the main part packs A (M-contiguous rows of 4100 halves)
-    ("f16", "f32", 4100, 4096, 192, 1, True, True, "_dma|gemm_f16_tt_64x64"),
+    # row strip of 4 rows, run as its transposed product (the small-M route,
+    # A gathered); the main part packs A (M-contiguous rows of 4100 halves)
+    ("f16", "f32", 4100, 4096, 192, 1, True, True, "_dma|transpose_a+gemv_f16_tt_thin"),
+    # row strip of 40 rows (too many for the small-M route)
+    ("bf16", "bf16", 4136, 4096, 192, 1, True, True, "_dma|gemm_bf16_tt_64x64"),
     # batched column strip; the main part packs B (rows of 2051 bytes)
     ("i8", "i32", 2048, 2051, 256, 4, False, False, "_dma|transpose_b+gemm_i8_nn_thin"),
     # strip of 40 columns: split-K on the 128x128 tile
@@ -484,6 +487,43 @@ def test_workload_i8_nn_ragged_dequant_bf16():
                                        a_dtype="i8", c_dtype=p.c_dtype, ldb=p.LDB)
     g = oracle.decode(got[pts[:, 0], pts[:, 1], pts[:, 2]], p.c_dtype)
     assert oracle.rel_frobenius(g, oracle.decode(r, p.c_dtype)) <= TOL[p.c_dtype]
+
+
+# ---------------------------------------------------------------- small-M GEMV
+@pytest.mark.parametrize("ta", [False, True], ids=["nt", "tt"])
+@pytest.mark.parametrize("m", [1, 4, 9, 16])
+@pytest.mark.parametrize("a,c", PAIRS, ids=["%s-%s" % pc for pc in PAIRS])
+def test_gemv_small_m(a, c, m, ta):
+    """M <= 16 with B stored [N, K]: the transposed product on the thin kernel,
+    C written transposed; N = 2056 (a ragged last block of 8 rows), K = 1000,
+    alpha = 0.5 and beta = 1 for floats; batched with N = 1032."""
+    import dense_gemm_tiled_amd as tg
+    p = problem(a, c, m, 2056, 1000, ta, True)
+    check(p, "gemv")
+    assert "gemv_%s_%s_thin" % (a, "tt" if ta else "nt") in tg.last_kernel(), tg.last_kernel()
+    p = problem(a, c, m, 1032, 1000, ta, True, batch=2)
+    check(p, "gemv batched")
+    assert "gemv_" in tg.last_kernel(), tg.last_kernel()
+
+
+@pytest.mark.parametrize("a,c", FLOAT_PAIRS, ids=["%s-%s" % pc for pc in FLOAT_PAIRS])
+def test_gemv_epilogue(a, c):
+    """Bias and GELU on the transposed product: the bias of C's column n
+    applies to row n of the product."""
+    import dense_gemm_tiled_amd as tg
+    p = problem(a, c, 5, 4104, 777, False, True)
+    epi_check(p, "gelu_tanh", "gemv epilogue")
+    assert tg.last_kernel() == "gemv_%s_nt_thin" % a, tg.last_kernel()
+    p = problem(a, c, 3, 1032, 300, True, True, batch=2)
+    epi_check(p, "relu", "gemv epilogue batched", shared=False)
+
+
+@pytest.mark.parametrize("c", DEQ_OUT)
+def test_gemv_i8_dequant(c):
+    import dense_gemm_tiled_amd as tg
+    p = deq_problem(c, 4, 4104, 1000, False, True)
+    deq_check(p, "gemv dequant", act="relu", bias=True)
+    assert tg.last_kernel() == "gemv_i8_nt_thin", tg.last_kernel()
 
 
 # ---------------------------------------------------------------- exact regime

@@ -356,6 +356,33 @@ def test_plan_thin_outputs():
         del os.environ["TCGEMM_TILE"]
 
 
+def test_plan_small_m_gemv():
+    """M <= 16 with B stored [N, K] runs as the transposed product on the
+    thin kernel (rows = N, 8 per workgroup); A stored [K, M] is gathered
+    first; B stored [K, N], M > 16, too few rows, a forced class or
+    TCGEMM_GEMV=0 keep the other paths."""
+    p = workloads.Problem("gemv", 1, 4096, 4096, "bf16", "bf16", transpose_b=True)
+    pl = plan_of(p)
+    assert pl["kernel"] == "gemv_bf16_nt_thin", pl["kernel"]
+    assert (pl["tile_m"], pl["tiles_m"], pl["grid"], pl["launches"]) == (8, 512, 512, 1)
+    assert plan_of(p.with_(M=16))["kernel"] == "gemv_bf16_nt_thin"
+    pl = plan_of(p.with_(M=3, transpose_a=True))
+    assert pl["kernel"] == "transpose_a+gemv_bf16_tt_thin" and pl["launches"] == 2
+    assert plan_of(p.with_(a_dtype="i8", c_dtype="i32", M=4))["kernel"] == "gemv_i8_nt_thin"
+    assert "gemv" not in plan_of(p.with_(M=17))["kernel"]
+    assert "gemv" not in plan_of(p.with_(transpose_b=False))["kernel"]
+    assert "gemv" not in plan_of(p.with_(N=2040))["kernel"]          # 255 row blocks
+    assert plan_of(p.with_(N=1024, batch=2))["grid"] == 256
+    assert plan_of(p.with_(alpha=0.0, beta=1.0))["kernel"] == "scale_c"
+    for env in ({"TCGEMM_GEMV": "0"}, {"TCGEMM_TILE": "64"}):
+        os.environ.update(env)
+        try:
+            assert "gemv" not in plan_of(p)["kernel"]
+        finally:
+            for k in env:
+                del os.environ[k]
+
+
 def test_plan_packed_batch_strides():
     """A shared operand (batch stride 0) is packed once; a batched one per
     problem, the packed copies placed after the split-K partials."""

@@ -207,6 +207,11 @@ WORKLOADS: Dict[str, Problem] = {
     "i8_nn_ragged_dequant_bf16": Problem(
         "i8_nn_ragged_dequant_bf16", 4093, 4099, 4096, "i8", "bf16", dist="int8", seed=1006,
         extra={"col_scale": "1"}),
+    # a linear layer applied to 4 vectors (x @ W^T, W 16384 x 8192 bf16):
+    # HBM-bound on W, the small-M route
+    "bf16_gemv_nt_m4": Problem(
+        "bf16_gemv_nt_m4", 4, 16384, 8192, "bf16", "bf16", transpose_b=True, dist="normal",
+        scale=1.0, seed=1007, extra={"bound": "hbm"}),
     # the headline shape with the fused epilogue (a per-column bias and
     # GELU-tanh): not one of the five, measured against the plain headline
     "bf16_nn_4096_bias_gelu": Problem(
