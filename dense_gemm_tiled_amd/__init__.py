@@ -110,6 +110,8 @@ _SIGNATURES = {
                                               ctypes.POINTER(EpilogueT), _VP, _VP, _VP, _VP]),
     "tc_gemm_plan": (ctypes.c_int, [_VP, ctypes.POINTER(BatchedDescT),
                                     ctypes.POINTER(PlanInfoT)]),
+    "tc_set_autotune": (ctypes.c_int, [_VP, ctypes.c_int]),
+    "tc_autotune_entries": (ctypes.c_int64, [_VP]),
     "tc_last_kernel": (ctypes.c_char_p, [_VP]),
     "tc_dispatch_count": (ctypes.c_uint64, [_VP]),
     "tc_time_next_gemm": (ctypes.c_int, [_VP, _VP, _VP]),
@@ -336,6 +338,17 @@ def gemm_sync(a, b, c, *, alpha: float = 1.0, beta: float = 0.0, transpose_a: bo
                                  _VP(c.data_ptr()))
     _check(st, ctx)
     return c
+
+
+def set_autotune(enable: bool, device: int = 0) -> None:
+    """Turn first-call autotuning on or off for the device's context (see
+    tc_set_autotune)."""
+    ctx = _context(device)
+    _check(load_library().tc_set_autotune(ctx, int(bool(enable))), ctx)
+
+
+def autotune_entries(device: int = 0) -> int:
+    return int(load_library().tc_autotune_entries(_context(device)))
 
 
 def plan(desc: BatchedDescT) -> dict:

@@ -14,11 +14,13 @@
 
 #include <cmath>
 #include <cstdarg>
+#include <map>
 #include <cstdio>
 #include <cstring>
 #include <new>
 #include <string>
 #include <utility>
+#include <vector>
 
 #include "tc_internal.h"
 
@@ -32,6 +34,13 @@ struct tc_stream {
     int64_t ws_bytes = 0;
 };
 
+// A tuned (or forced) choice the planner follows instead of its own rules.
+struct Choice {
+    int cls = -1;          // tile class, -1: the planner's
+    int64_t splits = 0;    // split-K slices with a forced class (0: none)
+    int gemv = -1;         // small-M route: 0 off, 1 on where eligible, -1: the planner's
+};
+
 struct tc_context {
     int device = -1;             // bound at the first launch
     tc_stream *internal = nullptr;
@@ -39,6 +48,8 @@ struct tc_context {
     std::string last_kernel;
     std::string last_error;
     hipEvent_t time_ev[2] = {nullptr, nullptr};   // armed by tc_time_next_gemm
+    bool autotune = false;                        // tc_set_autotune
+    std::map<std::string, Choice> tuned;          // problem key -> measured best choice
 };
 
 namespace {
@@ -330,16 +341,23 @@ Problem transposed_problem(const Problem &p) {
     return q;
 }
 
-bool gemv_route(const Problem &p) {
-    if (p.c_trans || p.M > 16 || !p.tb || p.alpha == 0.0f) return false;
+bool gemv_eligible(const Problem &p) {
+    return !p.c_trans && p.M <= 16 && p.tb && p.alpha != 0.0f &&
+           ceil_div(p.N, kThinRows) * p.batch >= 256;
+}
+
+bool gemv_route(const Problem &p, const Choice *ch) {
+    if (!gemv_eligible(p)) return false;
+    if (ch && ch->gemv >= 0) return ch->gemv == 1;
+    if (ch && ch->cls >= 0) return false;                       // a chosen class
     if (getenv("TCGEMM_TILE")) return false;                    // a forced class
     if (const char *env = getenv("TCGEMM_GEMV"))                // tuning knob: 0 disables
         if (atoi(env) == 0) return false;
-    return ceil_div(p.N, kThinRows) * p.batch >= 256;
+    return true;
 }
 
-void make_plan(const Problem &p, Plan *pl, bool allow_edge = true) {
-    if (gemv_route(p)) {
+void make_plan(const Problem &p, Plan *pl, bool allow_edge = true, const Choice *ch = nullptr) {
+    if (gemv_route(p, ch)) {
         make_plan(transposed_problem(p), pl, false);
         pl->swap = true;
         return;
@@ -402,6 +420,11 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true) {
         const int64_t forced = atoi(env);
         if (forced > 0 && p.alpha != 0.0f) splits = forced > ktiles ? ktiles : forced;
     }
+    if (ch && ch->cls >= 0) {
+        // a chosen class (validated by the caller for this problem)
+        cls = ch->cls;
+        splits = ch->splits > 0 && p.alpha != 0.0f ? (ch->splits > ktiles ? ktiles : ch->splits) : 1;
+    }
     if (splits > 1 && cls != TILE_64 && cls != TILE_128 && cls != TILE_128_DMA) cls = TILE_64;
     if (cls == TILE_THIN) splits = 1;
     const TileShape ts = tile_shape(cls);
@@ -438,11 +461,12 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true) {
         auto rounds = [](int64_t t) { return (t + 255) / 256; };
         const int64_t rn = p.N % ts.bn, rm = p.M % ts.bm;
         const int64_t tmn = (int64_t)pl->tiles_m * pl->tiles_n;
-        if (rn != 0 && rn <= ts.bn / 2 &&
+        // (a strip only when whole tiles remain beside it)
+        if (rn != 0 && rn <= ts.bn / 2 && pl->tiles_n > 1 &&
             rounds((tmn - pl->tiles_m) * p.batch) < rounds(tmn * p.batch)) {
             pl->edge = 1;
             pl->edge_at = (int32_t)(p.N - rn);
-        } else if (rm != 0 && rm <= ts.bm / 2 &&
+        } else if (rm != 0 && rm <= ts.bm / 2 && pl->tiles_m > 1 &&
                    rounds((tmn - pl->tiles_n) * p.batch) < rounds(tmn * p.batch)) {
             pl->edge = 2;
             pl->edge_at = (int32_t)(p.M - rm);
@@ -842,6 +866,128 @@ tc_status_t validate_epilogue(const Problem &p, const tc_epilogue *ep, const voi
 }
 
 // Validate, plan and enqueue one (batched) GEMM on stream s.
+// Enqueue every part of a planned call (the whole tiles, then the edge strip
+// if the plan splits one off); their kernel names go to *name.
+tc_status_t enqueue_call(tc_context *ctx, tc_stream *s, const Problem &p, const Plan &pl,
+                         const void *A, const void *B, void *C, const Epilogue &epi,
+                         std::string *name, std::string *err) {
+    const Parts parts = split_parts(p, pl);
+    for (int i = 0; i < parts.n; ++i) {
+        const int es = dt_size(p.dt), ces = dt_size(p.cdt);
+        const void *Ai = static_cast<const char *>(A) + parts.off[i][0] * es;
+        const void *Bi = static_cast<const char *>(B) + parts.off[i][1] * es;
+        if (parts.swap[i]) std::swap(Ai, Bi);   // the transposed product: A' = B, B' = A
+        void *Ci = static_cast<char *>(C) + parts.off[i][2] * ces;
+        // a column strip's bias and scales start at its first column
+        Epilogue epi_i = epi;
+        if (pl.edge == 1 && i == 1) {
+            if (epi.bias) epi_i.bias = static_cast<const char *>(epi.bias) + (int64_t)pl.edge_at * ces;
+            if (epi.scale) epi_i.scale = epi.scale + pl.edge_at;
+        }
+        if (i) *name += "|";
+        tc_status_t st = enqueue(ctx, s, parts.p[i], parts.pl[i], Ai, Bi, Ci, epi_i, i == 0, name, err);
+        if (st != TC_OK) return st;
+    }
+    return TC_OK;
+}
+
+// Autotuning key: everything the plan or the kernels' speed depends on.
+std::string tune_key(const Problem &p, const Epilogue &epi, const void *A, const void *B) {
+    char k[320];
+    snprintf(k, sizeof k, "%d:%d:%d%d:%d:%d:%d:%d:%lld:%lld:%lld:%lld:%lld:%lld:%d:%d:%d",
+             p.dt, p.cdt, (int)p.ta, (int)p.tb, p.M, p.N, p.K, p.batch, (long long)p.lda,
+             (long long)p.ldb, (long long)p.ldc, (long long)p.stride_a, (long long)p.stride_b,
+             (long long)p.stride_c, (int)(p.beta != 0.0f), (int)epi.on(),
+             (int)((uintptr_t)A % 16 == 0) * 2 + (int)((uintptr_t)B % 16 == 0));
+    return k;
+}
+
+// The candidates a first call measures: the planner's own choice, every tile
+// class that fits the input type (with and without the planner's split
+// count, halved and doubled, for the classes that split), the thin kernel
+// and the small-M route where they apply.
+std::vector<Choice> tune_candidates(const Problem &p) {
+    std::vector<Choice> c;
+    c.push_back(Choice{});
+    Plan base;
+    make_plan(p, &base);
+    const int64_t s0 = base.swap ? 1 : base.splits;
+    const bool dma = dma_types(p);
+    const int classes_dma[] = {TILE_256_DMA, TILE_256_DMA8, TILE_128_DMA, TILE_64};
+    const int classes_f32[] = {TILE_256, TILE_128, TILE_64};
+    const int *cl = dma ? classes_dma : classes_f32;
+    const int ncl = dma ? 4 : 3;
+    for (int i = 0; i < ncl; ++i) {
+        c.push_back(Choice{cl[i], 1, 0});
+        const bool splits_ok = cl[i] == TILE_64 || cl[i] == TILE_128 || cl[i] == TILE_128_DMA;
+        if (splits_ok && s0 > 1)
+            for (int64_t s : {s0 / 2, s0, s0 * 2})
+                if (s > 1) c.push_back(Choice{cl[i], s, 0});
+    }
+    if (p.N <= 16 && !p.ta && p.alpha != 0.0f) c.push_back(Choice{TILE_THIN, 1, 0});
+    if (gemv_eligible(p)) c.push_back(Choice{-1, 0, 1});
+    return c;
+}
+
+// Time each candidate on this stream (C replaced by a scratch buffer and
+// beta by 0, so C is untouched; one warm-up and three timed runs each, the
+// fastest counted) and return the best.  Candidates with identical launch
+// chains are measured once.
+tc_status_t autotune(tc_context *ctx, tc_stream *s, const Problem &p, const void *A, const void *B,
+                     const Epilogue &epi, Choice *best, std::string *err) {
+    Problem q = p;
+    q.beta = 0.0f;
+    void *scratch = nullptr;
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    hipError_t e = hipMalloc(&scratch, (size_t)p.c_total);
+    if (e == hipSuccess) e = hipEventCreate(&ev[0]);
+    if (e == hipSuccess) e = hipEventCreate(&ev[1]);
+    tc_status_t st = TC_OK;
+    float best_ms = 1e30f;
+    *best = Choice{};
+    std::vector<std::string> seen;
+    for (const Choice &ch : tune_candidates(q)) {
+        if (e != hipSuccess || st != TC_OK) break;
+        Plan pl;
+        make_plan(q, &pl, true, &ch);
+        const std::string chain = parts_chain(split_parts(q, pl));
+        bool dup = false;
+        for (const std::string &x : seen) dup = dup || x == chain;
+        if (dup) continue;
+        seen.push_back(chain);
+        float ms = 1e30f;
+        for (int rep = 0; rep < 4 && st == TC_OK && e == hipSuccess; ++rep) {
+            std::string name;
+            if (rep) e = hipEventRecord(ev[0], s->stream);
+            if (e != hipSuccess) break;
+            st = enqueue_call(ctx, s, q, pl, A, B, scratch, epi, &name, err);
+            if (st != TC_OK) break;
+            if (rep) {
+                float t = 0.f;
+                if ((e = hipEventRecord(ev[1], s->stream)) != hipSuccess) break;
+                if ((e = hipEventSynchronize(ev[1])) != hipSuccess) break;
+                if ((e = hipEventElapsedTime(&t, ev[0], ev[1])) != hipSuccess) break;
+                if (t < ms) ms = t;
+            }
+        }
+        if (st == TC_OK && e == hipSuccess && ms < best_ms) {
+            best_ms = ms;
+            *best = ch;
+        }
+    }
+    if (e == hipSuccess && st == TC_OK) e = hipStreamSynchronize(s->stream);
+    for (hipEvent_t x : ev)
+        if (x) (void)hipEventDestroy(x);
+    if (scratch) (void)hipFree(scratch);
+    if (st != TC_OK) return st;
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(err, TC_ERR_DEVICE, "autotuning: %s", hipGetErrorString(e));
+    }
+    return TC_OK;
+}
+
+// Validate, plan and enqueue one (batched) GEMM on stream s.
 tc_status_t run(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A, const void *B,
                 void *C, tc_stream *s, bool sync, const tc_epilogue *ep = nullptr) {
     if (!ctx) return TC_ERR_INVALID_ARGUMENT;
@@ -855,8 +1001,6 @@ tc_status_t run(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A, 
     if (ep && (st = validate_epilogue(p, ep, C, &epi, err)) != TC_OK) return st;
     if (ranges_overlap(C, p.c_total, A, p.a_total) || ranges_overlap(C, p.c_total, B, p.b_total))
         return fail(err, TC_ERR_ALIASING, "C overlaps A or B");
-    Plan pl;
-    make_plan(p, &pl);
 
     st = bind_device(ctx);
     if (st != TC_OK) return st;
@@ -873,26 +1017,23 @@ tc_status_t run(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A, 
         if (!ctx->internal && (st = create_stream(ctx, &ctx->internal, nullptr)) != TC_OK) return st;
         s = ctx->internal;
     }
-    // the whole tiles, then the edge strip if the plan splits one off
-    const Parts parts = split_parts(p, pl);
-    std::string name;
-    for (int i = 0; i < parts.n; ++i) {
-        const int es = dt_size(p.dt), ces = dt_size(p.cdt);
-        const void *Ai = static_cast<const char *>(A) + parts.off[i][0] * es;
-        const void *Bi = static_cast<const char *>(B) + parts.off[i][1] * es;
-        if (parts.swap[i]) std::swap(Ai, Bi);   // the transposed product: A' = B, B' = A
-        void *Ci = static_cast<char *>(C) + parts.off[i][2] * ces;
-        // a column strip's bias and scales start at its first column
-        Epilogue epi_i = epi;
-        if (pl.edge == 1 && i == 1) {
-            if (epi.bias) epi_i.bias = static_cast<const char *>(epi.bias) + (int64_t)pl.edge_at * ces;
-            if (epi.scale) epi_i.scale = epi.scale + pl.edge_at;
+    Plan pl;
+    if (ctx->autotune && p.alpha != 0.0f) {
+        // first call of this problem: measure the candidates, then keep the
+        // fastest for every later call
+        const std::string key = tune_key(p, epi, A, B);
+        auto it = ctx->tuned.find(key);
+        if (it == ctx->tuned.end()) {
+            Choice best;
+            if ((st = autotune(ctx, s, p, A, B, epi, &best, err)) != TC_OK) return st;
+            it = ctx->tuned.emplace(key, best).first;
         }
-        if (i) name += "|";
-        if ((st = enqueue(ctx, s, parts.p[i], parts.pl[i], Ai, Bi, Ci, epi_i, i == 0, &name, err)) !=
-            TC_OK)
-            return st;
+        make_plan(p, &pl, true, &it->second);
+    } else {
+        make_plan(p, &pl);
     }
+    std::string name;
+    if ((st = enqueue_call(ctx, s, p, pl, A, B, C, epi, &name, err)) != TC_OK) return st;
     ctx->last_kernel = name;
     if (sync) {
         const hipError_t e = hipStreamSynchronize(s->stream);
@@ -919,7 +1060,10 @@ extern "C" {
 tc_status_t tc_context_create(tc_context **out) {
     if (!out) return TC_ERR_INVALID_ARGUMENT;
     *out = new (std::nothrow) tc_context();
-    return *out ? TC_OK : TC_ERR_OUT_OF_MEMORY;
+    if (!*out) return TC_ERR_OUT_OF_MEMORY;
+    const char *env = getenv("TCGEMM_AUTOTUNE");
+    (*out)->autotune = env && atoi(env) != 0;
+    return TC_OK;
 }
 
 void tc_context_destroy(tc_context *ctx) {
@@ -1020,6 +1164,14 @@ tc_status_t tc_gemm_epilogue_async(tc_context *ctx, const tc_gemm_batched_desc *
     }
     return run(ctx, bd, A, B, C, s, false, ep);
 }
+
+tc_status_t tc_set_autotune(tc_context *ctx, int enable) {
+    if (!ctx) return TC_ERR_INVALID_ARGUMENT;
+    ctx->autotune = enable != 0;
+    return TC_OK;
+}
+
+int64_t tc_autotune_entries(const tc_context *ctx) { return ctx ? (int64_t)ctx->tuned.size() : 0; }
 
 tc_status_t tc_gemm_plan(tc_context *ctx, const tc_gemm_batched_desc *bd, tc_plan_info *info) {
     std::string *err = ctx ? &ctx->last_error : &g_plan_error;

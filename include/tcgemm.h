@@ -207,6 +207,26 @@ tc_status_t tc_gemm_epilogue_async(tc_context *ctx, const tc_gemm_batched_desc *
                                    const tc_epilogue *ep, const void *A,
                                    const void *B, void *C, tc_stream *s);
 
+/* First-call autotuning (the tile-class choice the pages leave to a
+ * measured cache; tessl "Architecture", "GEMM Pipeline & Kernel Selection").
+ * With it on, the first call of each problem (types, layout, M, N, K, batch,
+ * leading dims, strides, beta == 0 or not, fused epilogue or not, 16-byte
+ * alignment of A and B) runs every candidate plan -- the planner's own, each
+ * tile class the input type has (with and without split-K variants), the
+ * thin-output kernel and the small-M route where they apply -- on the call's
+ * stream, one warm-up and three timed runs each, into a scratch C with beta
+ * = 0 (C itself is not touched), keeps the fastest for the context, and then
+ * runs the call.  That first call synchronizes the stream, allocates and
+ * frees the scratch C, and adds the candidates' launches to
+ * tc_dispatch_count.  Later calls with the same key launch only the chosen
+ * plan.  Off by default; the environment variable TCGEMM_AUTOTUNE=1 turns it
+ * on for contexts created afterwards.  Returns TC_ERR_INVALID_ARGUMENT for a
+ * NULL ctx. */
+tc_status_t tc_set_autotune(tc_context *ctx, int enable);
+
+/* Number of problems the context has tuned (0 for NULL). */
+int64_t tc_autotune_entries(const tc_context *ctx);
+
 /* Validate and plan without touching the GPU or any pointer.  Fills *info
  * (if non-NULL) with the kernel, tile, grid and split-K choice; returns the
  * status the descriptor alone earns.  ctx may be NULL; when non-NULL the

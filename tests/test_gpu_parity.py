@@ -526,6 +526,43 @@ def test_gemv_i8_dequant(c):
     assert tg.last_kernel() == "gemv_i8_nt_thin", tg.last_kernel()
 
 
+# ---------------------------------------------------------------- autotune
+def _launches(chain):
+    return len([k for k in chain.replace("|", "+").split("+") if k])
+
+
+@pytest.mark.parametrize("a,c,M,N,K,ta,tb", [
+    ("bf16", "bf16", 1000, 1030, 512, False, False),     # mid-size: 128 or 256 tiles
+    ("f16", "f32", 96, 200, 8192, True, False),          # split-K candidates
+    ("i8", "i32", 600, 520, 4096, False, True),
+    ("bf16", "bf16", 3, 4096, 1000, False, True),        # small-M route candidate
+    ("f32", "f32", 300, 270, 197, False, False),
+])
+def test_autotune_first_call_then_reuse(a, c, M, N, K, ta, tb):
+    """With autotuning on, the first call measures its candidates into a
+    scratch C (C itself, read with beta = 1, stays correct), the second call
+    of the same problem launches only the chosen plan, and both match the
+    oracle."""
+    import dense_gemm_tiled_amd as tg
+    p = problem(a, c, M, N, K, ta, tb)
+    tg.set_autotune(True)
+    try:
+        n_tuned = tg.autotune_entries()
+        d0 = tg.dispatch_count()
+        check(p, "autotune first")
+        first = tg.last_kernel()
+        d1 = tg.dispatch_count()
+        assert tg.autotune_entries() == n_tuned + 1
+        assert d1 - d0 > _launches(first)                  # the candidates ran too
+        check(p, "autotune reuse")
+        assert tg.last_kernel() == first
+        assert tg.dispatch_count() - d1 == _launches(first)
+        assert tg.autotune_entries() == n_tuned + 1
+        say("autotune chose", first)
+    finally:
+        tg.set_autotune(False)
+
+
 # ---------------------------------------------------------------- exact regime
 @pytest.mark.parametrize("a,c", [("bf16", "f32"), ("bf16", "bf16"), ("f16", "f16"), ("f32", "f32")])
 def test_exact_regime_bitwise(a, c):

@@ -223,6 +223,19 @@ def test_python_epilogue_arguments():
     assert e.activation == 2 and not e.bias
 
 
+def test_autotune_switch(lib, ctx):
+    assert lib.tc_set_autotune(None, 1) == 1
+    assert lib.tc_autotune_entries(None) == 0
+    assert lib.tc_autotune_entries(ctx) == 0
+    assert lib.tc_set_autotune(ctx, 1) == 0
+    assert lib.tc_set_autotune(ctx, 0) == 0
+    # a refused call tunes nothing
+    d = desc(M=0)
+    assert lib.tc_set_autotune(ctx, 1) == 0
+    assert lib.tc_gemm_batched(ctx, ctypes.byref(d), A_PTR, B_PTR, C_PTR) == 1
+    assert lib.tc_autotune_entries(ctx) == 0 and lib.tc_dispatch_count(ctx) == 0
+
+
 def test_int8_k_bound_accepted_at_131071(lib):
     d = desc(a=tg.I8, c=tg.I32, acc=tg.I32, K=131071, M=16, N=16)
     assert lib.tc_gemm_plan(None, ctypes.byref(d), None) == 0
@@ -323,6 +336,14 @@ def test_plan_edge_split():
         assert plan_of(base.with_(N=4104))["kernel"] == main
     finally:
         del os.environ["TCGEMM_EDGE"]
+    # one partial tile row or column: no strip (there are no whole tiles
+    # beside it)
+    os.environ["TCGEMM_TILE"] = "dma"
+    try:
+        for shape in (dict(M=96, N=200, K=8192), dict(M=300, N=100, K=512), dict(M=40, N=40, K=64)):
+            assert "|" not in plan_of(base.with_(**shape))["kernel"], shape
+    finally:
+        del os.environ["TCGEMM_TILE"]
 
 
 def test_plan_thin_outputs():
