@@ -431,9 +431,9 @@ void gemm_dma_kernel(const GemmArgs args) {
         }
     };
 
-    // fused epilogue: the tile's bias and scales go into LDS of their own at
-    // the start, their loads issued ahead of the first tiles' (the epilogue
-    // then reads them with no wait; the loop's barriers publish them)
+    // fused epilogue: the tile's bias and alpha * scale go into LDS of their
+    // own at the start, their loads issued ahead of the first tiles' (the
+    // epilogue then reads them with no wait; the loop's barriers publish them)
     constexpr int EPI_LDS = EPI == EPI_FUSED && OUT != DT_I32 && OUT != OUT_PARTIAL ? 2 * BN : 1;
     __shared__ __attribute__((aligned(16))) float epi_smem[EPI_LDS];
     [[maybe_unused]] float epi_b = 0.f, epi_s = 1.f;
@@ -456,7 +456,7 @@ void gemm_dma_kernel(const GemmArgs args) {
         if constexpr (EPI_LDS > 1) {
             if (tid < BN) {
                 epi_smem[tid] = epi_b;
-                epi_smem[BN + tid] = epi_s;
+                epi_smem[BN + tid] = args.alpha * epi_s;
             }
         }
 #pragma unroll
@@ -545,8 +545,67 @@ void gemm_dma_kernel(const GemmArgs args) {
         }
     }
     [[maybe_unused]] const EpiState ep = make_epi<OUT == DT_I32 ? DT_F32 : OUT>(args, z, N);
-    // fused epilogue: the tile's bias and scales into the operand stages,
-    // once every wave is done with them
+    // A tile whose columns lie inside C, with vector-aligned rows, and no
+    // C_old to read: every block is stored whole, so the store sequence is
+    // straight-line code with no per-block bounds or alignment branches
+    // (short code: the epilogue runs once per workgroup, from a cold
+    // instruction cache).  Rows past M need no test: they start at or past
+    // M * ldc >= (M - 1) * ldc + N elements, the end of the store range of
+    // `rc`, so the buffer unit drops their stores.
+    const bool interior = vec && n0 + BN <= N;
+    // fused epilogue: act(acc * (alpha * scale) + bias), with bias and
+    // alpha * scale of the lane's columns read from LDS
+    [[maybe_unused]] auto fused_interior = [&](auto act_tag) {
+        constexpr int ACT = decltype(act_tag)::value;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int ml = ml0 + i * 16;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int nl = nl0 + j * 16;
+                float b[4], sa[4], v[4];
+                read_epi4(epi_smem, BN, nl, b, sa);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    v[q] = act1<ACT>(__builtin_fmaf((float)acc[i][j][q], sa[q], b[q]));
+                store_c4<OUT>(rc, (ml * ldc + nl) * CES, 4, true, v);
+            }
+        }
+    };
+    if constexpr (EPI_LDS > 1) {
+        if (interior && beta == 0.f) {
+            if (ep.act == ACT_GELU_TANH) fused_interior(std::integral_constant<int, ACT_GELU_TANH>{});
+            else if (ep.act == ACT_RELU) fused_interior(std::integral_constant<int, ACT_RELU>{});
+            else fused_interior(std::integral_constant<int, ACT_NONE>{});
+            return;
+        }
+    }
+    if constexpr (EPI == EPI_PLAIN) {
+        if (interior) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int ml = ml0 + i * 16;
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int off = (ml * ldc + nl0 + j * 16) * CES;
+                    if constexpr (OUT == DT_I32) {
+                        int v[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e];
+                        store_i4(rc, off, 4, true, v);
+                    } else {
+                        float v[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = alpha * (float)acc[i][j][e];
+                        store_c4<OUT>(rc, off, 4, true, v);
+                    }
+                }
+            }
+            return;
+        }
+    }
+    // fused epilogue, general case: rows and columns past C skipped, C_old
+    // read per block when beta != 0
     if constexpr (EPI_LDS > 1) {
         const float *lds_epi = epi_smem;
         // row blocks outside, as in the plain epilogue, so the stores of one
@@ -560,14 +619,11 @@ void gemm_dma_kernel(const GemmArgs args) {
                 const int nl = nl0 + j * 16;
                 const int nvalid = N - (n0 + nl);
                 if (nvalid <= 0) continue;
-                float b[4], s[4], v[4];
-                read_epi4(lds_epi, BN, nl, b, s);
+                float b[4], sa[4], v[4];
+                read_epi4(lds_epi, BN, nl, b, sa);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    s[q] *= alpha;
-                    v[q] = acc[i][j][q];
-                }
-                finish4_fused<OUT>(rc, (ml * ldc + nl) * CES, nvalid, vec, beta, v, ep, b, s);
+                for (int q = 0; q < 4; ++q) v[q] = acc[i][j][q];
+                finish4_fused<OUT>(rc, (ml * ldc + nl) * CES, nvalid, vec, beta, v, ep, b, sa);
             }
         }
         return;

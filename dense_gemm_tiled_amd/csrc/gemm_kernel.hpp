@@ -301,6 +301,17 @@ __device__ inline u32 to_bf16_bits(float x) {
 __device__ inline u32 to_f16_bits(float x) {
     return (u32)__builtin_bit_cast(unsigned short, static_cast<_Float16>(x));
 }
+// Two values rounded to the 16-bit type in one packed conversion; the first
+// in the low half.
+template <int CDT>
+__device__ inline u32 pack2_16(float lo, float hi) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t x = {lo, hi};
+    if constexpr (CDT == DT_BF16) return __builtin_bit_cast(u32, __builtin_convertvector(x, bf16x2_t));
+    else return __builtin_bit_cast(u32, __builtin_convertvector(x, f16x2_t));
+}
 __device__ inline float from_bf16_bits(u32 h) { return as_f32(h << 16); }
 __device__ inline float from_f16_bits(u32 h) {
     return (float)__builtin_bit_cast(_Float16, (unsigned short)h);
@@ -354,14 +365,14 @@ __device__ inline void store_c4(__amdgpu_buffer_rsrc_t r, int off, int nvalid, b
                                                           off + 4 * e, 0, 0);
         }
     } else {
-        u32 h[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            h[e] = (CDT == DT_BF16) ? to_bf16_bits(v[e]) : to_f16_bits(v[e]);
         if (vec && nvalid >= 4) {
-            u32x2 w = {h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+            u32x2 w = {pack2_16<CDT>(v[0], v[1]), pack2_16<CDT>(v[2], v[3])};
             __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, 0);
         } else {
+            u32 h[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                h[e] = (CDT == DT_BF16) ? to_bf16_bits(v[e]) : to_f16_bits(v[e]);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 if (e < nvalid)
@@ -418,13 +429,23 @@ __device__ inline EpiState make_epi(const Args &a, int z, int N) {
 
 // GELU, tanh form: 0.5 y (1 + tanh(u)) with u = sqrt(2/pi) (y + 0.044715 y^3).
 // Since 1 + tanh(u) = 2 / (1 + exp(-2u)), this is y / (1 + exp(-2u)): one
-// hardware exp2 (exp(-2u) = 2^(-2u log2 e)) and one reciprocal.  Large
-// negative u gives exp = inf and the value 0 (-0 for y < 0); large positive
-// u gives y.
+// hardware exp2 and one reciprocal.  The exponent -2u log2(e) is
+// y (g1 + g3 y^2) with the constants folded (g1 = -2 log2(e) sqrt(2/pi),
+// g3 = 0.044715 g1): three VALU operations.  Large negative u gives exp =
+// inf and the value 0 (-0 for y < 0); large positive u gives y.
 __device__ inline float gelu_tanh(float y) {
-    const float u = 0.7978845608028654f * __builtin_fmaf(0.044715f * y, y * y, y);
-    const float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * u);
-    return y * __builtin_amdgcn_rcpf(1.f + e);
+    constexpr float g1 = -2.3022082f;      // -2 * 1.4426950409 * 0.7978845608
+    constexpr float g3 = -0.10294324f;     // g1 * 0.044715
+    const float t = y * __builtin_fmaf(g3, y * y, g1);
+    return y * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(t));
+}
+
+// The activation of one value.
+template <int ACT>
+__device__ inline float act1(float v) {
+    if constexpr (ACT == ACT_RELU) return v > 0.f ? v : 0.f;
+    else if constexpr (ACT == ACT_GELU_TANH) return gelu_tanh(v);
+    else return v;
 }
 
 // The bias of columns n .. n + nvalid - 1 (zero past them or without a bias)

@@ -336,6 +336,52 @@ def test_epilogue_dma_kernels(a, c, tile, act):
     assert tg.last_kernel().endswith(DMA_NAME[tile]), tg.last_kernel()
 
 
+# (input, output, epilogue) for rows past M: plain products and the fused forms
+ROWS_PAST_M = [("bf16", "bf16", None), ("f16", "f32", None), ("i8", "i32", None),
+               ("bf16", "bf16", "gelu_tanh"), ("f16", "f16", "relu"), ("i8", "bf16", "dequant")]
+
+
+@pytest.mark.parametrize("tile", DMA_TILES)
+@pytest.mark.parametrize("a,c,epi", ROWS_PAST_M, ids=["%s-%s-%s" % x for x in ROWS_PAST_M])
+def test_dma_epilogue_rows_past_m(a, c, epi, tile):
+    """beta = 0 with whole column tiles and M ragged (300 rows): the tiles of
+    the last tile row store all of their rows and the buffer range of C drops
+    those past M.  Two problems back to back (problem 0's rows past M are
+    problem 1's first rows), then guard rows that must keep their bits."""
+    import torch
+    import dense_gemm_tiled_amd as tg
+    p = problem(a, c, 300, 512, 208 if a == "i8" else 200, beta=0.0, batch=2)
+    A, B, C = workloads.make_inputs(p)
+    bias = workloads.make_bias(p) if epi in ("gelu_tanh", "relu") else None
+    scale = workloads.make_col_scale(p) if epi == "dequant" else None
+    act = epi if epi in ("gelu_tanh", "relu") else None
+    say("GPU case: rows past M", tile, p.M, p.N, p.K, a, c, epi)
+    rows, guard = p.batch * p.M, 64
+    guard_bits = (np.arange(guard * p.LDC) * 2654435761 % 65521).astype(np.int64)
+    guard_np = guard_bits.astype(C.dtype).reshape(guard, p.LDC)
+    a_dev, b_dev = to_dev(A, p.a_dtype), to_dev(B, p.a_dtype)
+    big = to_dev(np.concatenate([C.reshape(rows, p.LDC), guard_np]), p.c_dtype)
+    c_view = big[:rows].view(p.batch, p.M, p.LDC)[..., :p.N]
+    a_v = a_dev[..., :p.K]
+    b_v = b_dev[..., :p.N]
+    bt = to_dev(bias, p.c_dtype)[0] if bias is not None else None
+    st = torch.from_numpy(scale).cuda()[0] if scale is not None else None
+    with env(TCGEMM_TILE=tile):
+        tg.gemm(a_v, b_v, c_view, alpha=p.alpha, beta=p.beta, bias=bt, activation=act,
+                col_scale=st)
+    torch.cuda.synchronize()
+    assert tg.last_kernel().endswith(DMA_NAME[tile]), tg.last_kernel()
+    got_big = from_dev(big, p.c_dtype)
+    assert np.array_equal(got_big[rows:].view(np.uint8), guard_np.view(np.uint8)), \
+        "rows past the last problem were written"
+    got = got_big[:rows].reshape(C.shape)
+    if epi is None:
+        ref = oracle_full(p, A, B, C)
+    else:
+        ref = oracle_epilogue(p, A, B, C, bias, act or "none", col_scale=scale)
+    compare(p, got, ref, C_in=C, label="rows past M %s" % tile)
+
+
 @pytest.mark.parametrize("ta,tb", LAYOUTS, ids=[lay(*l) for l in LAYOUTS])
 @pytest.mark.parametrize("tile", [256, 128, 64])
 def test_epilogue_register_staged_f32(tile, ta, tb):
