@@ -7,8 +7,11 @@
 //     walk its K in 16-byte pieces, so a wave reads 4 rows x 256 bytes per
 //     load, coalesced; two or more workgroups share a CU, so one computes
 //     while another waits for memory;
-//   * K runs in chunks (4, 2 or 1 KiB per row for up to 4, 8 or 16 columns).
-//     op(B) is staged in LDS one chunk at a time, transposed to Bt[n][k]
+//   * K runs in chunks: 4, 2 or 1 KiB per row for up to 4, 8 or 16 columns
+//     when the grid has few workgroups (each one then needs many loads in
+//     flight), 512 bytes for any width when it has many (registers and LDS
+//     per workgroup shrink, several workgroups share a CU and hide each
+//     other's memory latency).  op(B) is staged in LDS one chunk at a time, transposed to Bt[n][k]
 //     (zero past N and past K), in two buffers; a lane's pieces of A for the
 //     next chunk are loaded into registers while the current chunk is
 //     computed, and one barrier per chunk hands the next B buffer over;
@@ -26,11 +29,12 @@ namespace {
 
 constexpr int kThinThreads = kThinRows / 4 * 64;   // 4 rows per wave
 
-// Bytes of K per row per chunk (fewer for more columns, to keep the staged
-// B and the two chunks of A in registers), and 16-byte pieces of A per lane
-// per chunk.
+// Bytes of K per row per chunk for small grids (fewer for more columns, to
+// keep the staged B and the two chunks of A in registers).  A lane holds
+// CH / 256 pieces of 16 bytes of its row per chunk.
 constexpr int thin_chunk_bytes(int ns) { return ns > 8 ? 1024 : ns > 4 ? 2048 : 4096; }
-constexpr int thin_pieces(int ns) { return thin_chunk_bytes(ns) / 256; }
+constexpr int kThinNarrowChunk = 512;    // bytes of K per row per chunk, large grids
+constexpr int kThinNarrowGrid = 1024;    // workgroups from which the narrow chunk is used
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -76,10 +80,10 @@ __device__ inline void thin_load_a(const GemmArgs &args, const char *Ab, int64_t
 // holds pieces t, t + threads, ... (16 bytes each) of the chunk's Bt rows.
 // Rows n >= N start at or past the end of B (ldb >= K), so the range-checked
 // loads return zero there.
-template <int ES, int NS>
+template <int ES, int NS, int CH>
 __device__ inline void thin_load_bt(const GemmArgs &args, const char *Bb, int kc,
-                                    u32x4 (&v)[NS * thin_chunk_bytes(NS) / 16 / kThinThreads]) {
-    constexpr int CH = thin_chunk_bytes(NS), PER_COL = CH / 16;
+                                    u32x4 (&v)[NS * CH / 16 / kThinThreads]) {
+    constexpr int PER_COL = CH / 16;
     constexpr int Q = NS * PER_COL / kThinThreads;
     const int64_t b_org = (int64_t)kc * ES;
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + b_org, args.b_extent - b_org);
@@ -91,9 +95,9 @@ __device__ inline void thin_load_bt(const GemmArgs &args, const char *Bb, int kc
     }
 }
 
-template <int NS>
-__device__ inline void thin_store_bt(char *bt, const u32x4 (&v)[NS * thin_chunk_bytes(NS) / 16 / kThinThreads]) {
-    constexpr int Q = NS * thin_chunk_bytes(NS) / 16 / kThinThreads;
+template <int NS, int CH>
+__device__ inline void thin_store_bt(char *bt, const u32x4 (&v)[NS * CH / 16 / kThinThreads]) {
+    constexpr int Q = NS * CH / 16 / kThinThreads;
 #pragma unroll
     for (int q = 0; q < Q; ++q)
         *reinterpret_cast<u32x4 *>(bt + (threadIdx.x + q * kThinThreads) * 16) = v[q];
@@ -101,9 +105,9 @@ __device__ inline void thin_store_bt(char *bt, const u32x4 (&v)[NS * thin_chunk_
 
 // B stored [N, K], the last chunk (kv < a whole chunk of k valid), one
 // piece at a time: Bt[n][k - kc], zero past kv.
-template <int ES, int NS>
+template <int ES, int NS, int CH>
 __device__ inline void thin_stage_bt_tail(const GemmArgs &args, const char *Bb, int kc, int kv, char *bt) {
-    constexpr int CH = thin_chunk_bytes(NS), PER_COL = CH / 16;
+    constexpr int PER_COL = CH / 16;
     const int64_t b_org = (int64_t)kc * ES;
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + b_org, args.b_extent - b_org);
 #pragma unroll 1
@@ -123,9 +127,8 @@ __device__ inline void thin_stage_bt_tail(const GemmArgs &args, const char *Bb, 
 // One 16-byte piece of A (piece u of the chunk) against every staged column.
 // The scheduling fence keeps the compiler from hoisting the LDS reads of
 // every piece ahead at once (their registers would not fit).
-template <int DT, int NS, typename Acc>
+template <int DT, int NS, int CH, typename Acc>
 __device__ inline void thin_piece(const char *bt, int u, u32x4 a, Acc (&acc)[NS]) {
-    constexpr int CH = thin_chunk_bytes(NS);
     u32x4 b[NS];
 #pragma unroll
     for (int n = 0; n < NS; ++n) b[n] = *reinterpret_cast<const u32x4 *>(bt + n * CH + u * 16);
@@ -134,13 +137,14 @@ __device__ inline void thin_piece(const char *bt, int u, u32x4 a, Acc (&acc)[NS]
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// NS: columns computed (>= N, a multiple of 4).  B is stored [N, K]
-// (K-contiguous rows); a B stored [K, N] is transposed first
-// (thin_pack_bt_kernel).
-template <int DT, int OUT, int NS>
+// NS: columns computed (>= N, a multiple of 4); CH: bytes of K per row per
+// chunk.  B is stored [N, K] (K-contiguous rows); a B stored [K, N] is
+// transposed first (thin_pack_bt_kernel).
+template <int DT, int OUT, int NS, int CH>
 __global__ __launch_bounds__(kThinThreads) void thin_kernel(const GemmArgs args) {
     constexpr int ES = dt_size(DT);
-    constexpr int CH = thin_chunk_bytes(NS), KCH = CH / ES, P = thin_pieces(NS);
+    constexpr int KCH = CH / ES, P = CH / 256;
+    static_assert(NS * CH % (16 * kThinThreads) == 0, "whole pieces of B per thread");
     constexpr int Q = NS * CH / 16 / kThinThreads;
     using Acc = std::conditional_t<DT == DT_I8, int, float>;
     __shared__ __attribute__((aligned(16))) char bt[2][NS * CH];
@@ -172,8 +176,8 @@ __global__ __launch_bounds__(kThinThreads) void thin_kernel(const GemmArgs args)
         thin_load_a<ES, P>(args, Ab, a_org, rl, kl, 0, a_cur);
         {
             u32x4 bv[Q];
-            thin_load_bt<ES, NS>(args, Bb, 0, bv);
-            thin_store_bt<NS>(bt[0], bv);
+            thin_load_bt<ES, NS, CH>(args, Bb, 0, bv);
+            thin_store_bt<NS, CH>(bt[0], bv);
         }
         __syncthreads();
 #pragma unroll 1
@@ -184,11 +188,11 @@ __global__ __launch_bounds__(kThinThreads) void thin_kernel(const GemmArgs args)
             u32x4 bv[Q];
             if (more) {
                 thin_load_a<ES, P>(args, Ab, a_org, rl, kl, (c + 1) * KCH, a_nxt);
-                thin_load_bt<ES, NS>(args, Bb, (c + 1) * KCH, bv);
+                thin_load_bt<ES, NS, CH>(args, Bb, (c + 1) * KCH, bv);
             }
 #pragma unroll
-            for (int i = 0; i < P; ++i) thin_piece<DT, NS>(cur, kl + 16 * i, a_cur[i], acc);
-            if (more) thin_store_bt<NS>(nxt, bv);
+            for (int i = 0; i < P; ++i) thin_piece<DT, NS, CH>(cur, kl + 16 * i, a_cur[i], acc);
+            if (more) thin_store_bt<NS, CH>(nxt, bv);
             // every wave is done with cur, and nxt is written
             __syncthreads();
 #pragma unroll
@@ -199,7 +203,7 @@ __global__ __launch_bounds__(kThinThreads) void thin_kernel(const GemmArgs args)
     // ---- the last, partial chunk (both buffers are free here)
     const int kc = nfull * KCH, kv = K - kc;
     if (kv > 0) {
-        thin_stage_bt_tail<ES, NS>(args, Bb, kc, kv, bt[0]);
+        thin_stage_bt_tail<ES, NS, CH>(args, Bb, kc, kv, bt[0]);
         __syncthreads();
         const int64_t a_chunk = a_org + (int64_t)kc * ES;
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + a_chunk, args.a_extent - a_chunk);
@@ -218,7 +222,7 @@ __global__ __launch_bounds__(kThinThreads) void thin_kernel(const GemmArgs args)
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                if (u0 + 16 * q < CH / 16) thin_piece<DT, NS>(bt[0], u0 + 16 * q, a[q], acc);
+                if (u0 + 16 * q < CH / 16) thin_piece<DT, NS, CH>(bt[0], u0 + 16 * q, a[q], acc);
         }
     }
 
@@ -335,15 +339,22 @@ hipError_t launch_pack_bt_ns(const PackArgs &args, int64_t blocks, hipStream_t s
     return hipGetLastError();
 }
 
+template <int DT, int OUT, int NS>
+hipError_t launch_thin_ch(const GemmArgs &args, int64_t grid, hipStream_t stream) {
+    if (grid >= kThinNarrowGrid)
+        hipLaunchKernelGGL((thin_kernel<DT, OUT, NS, kThinNarrowChunk>), dim3((unsigned)grid),
+                           dim3(kThinThreads), 0, stream, args);
+    else
+        hipLaunchKernelGGL((thin_kernel<DT, OUT, NS, thin_chunk_bytes(NS)>), dim3((unsigned)grid),
+                           dim3(kThinThreads), 0, stream, args);
+    return hipGetLastError();
+}
+
 template <int DT, int OUT>
 hipError_t launch_thin_ns(const GemmArgs &args, int64_t grid, hipStream_t stream) {
-    if (args.N <= 4)
-        hipLaunchKernelGGL((thin_kernel<DT, OUT, 4>), dim3((unsigned)grid), dim3(kThinThreads), 0, stream, args);
-    else if (args.N <= 8)
-        hipLaunchKernelGGL((thin_kernel<DT, OUT, 8>), dim3((unsigned)grid), dim3(kThinThreads), 0, stream, args);
-    else
-        hipLaunchKernelGGL((thin_kernel<DT, OUT, 16>), dim3((unsigned)grid), dim3(kThinThreads), 0, stream, args);
-    return hipGetLastError();
+    if (args.N <= 4) return launch_thin_ch<DT, OUT, 4>(args, grid, stream);
+    if (args.N <= 8) return launch_thin_ch<DT, OUT, 8>(args, grid, stream);
+    return launch_thin_ch<DT, OUT, 16>(args, grid, stream);
 }
 
 template <int DT>

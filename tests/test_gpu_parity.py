@@ -275,6 +275,21 @@ def test_thin_kernel(a, c, tb, ldb, n):
     assert tg.last_kernel() == name, tg.last_kernel()
 
 
+@pytest.mark.parametrize("n", THIN_N)
+@pytest.mark.parametrize("a,c", PAIRS, ids=["%s-%s" % pc for pc in PAIRS])
+def test_thin_kernel_large_grid(a, c, n):
+    """From 1024 workgroups on the thin kernel runs 512-byte chunks of K:
+    8200 rows (1025 workgroups, a ragged last block), K = 1000 (whole chunks
+    then a ragged one for every type), B stored [N, K] and [K, N], beta = 1
+    for floats."""
+    import dense_gemm_tiled_amd as tg
+    for tb in (True, False):
+        name = "%sgemm_%s_%s_thin" % ("" if tb else "transpose_b+", a, "nt" if tb else "nn")
+        p = problem(a, c, 8200, n, 1000, False, tb)
+        check(p, "thin large grid", TCGEMM_TILE="thin")
+        assert tg.last_kernel() == name, tg.last_kernel()
+
+
 @pytest.mark.parametrize("a,c", PAIRS, ids=["%s-%s" % pc for pc in PAIRS])
 def test_thin_kernel_odd_leading_dims(a, c):
     """Odd lda, ldb and ldc (rows start off 16-byte boundaries), both B
