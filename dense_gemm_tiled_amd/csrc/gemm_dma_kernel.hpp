@@ -13,14 +13,15 @@
 //     and split-K).
 //
 //   * per K-tile (128 bytes of K: 64 bf16/f16 or 128 int8) the operand tiles
-//     arrive as direct-to-LDS loads of 1 KiB, issued by 4 waves; two LDS
-//     stages hold tile t and tile t+1;
+//     arrive as direct-to-LDS loads of 1 KiB, issued by 4 waves; NST LDS
+//     stages (2, or 4 where one workgroup per CU has the LDS to spare) hold
+//     tiles t .. t+NST-1;
 //   * the MFMAs of a K-tile run in two sub-steps.  While one sub-step runs,
 //     the fragments of the next are read from LDS into a second register
 //     set, one read between every few MFMAs;
 //   * one barrier per K-tile, between the sub-steps: after it, tile t+1 is
 //     visible to every wave and the stage of tile t is free, so the loads of
-//     tile t+2 are issued into it during the second sub-step;
+//     tile t+NST are issued into it during the second sub-step;
 //   * K-contiguous operands are read with ds_read_b128; M/N-contiguous ones
 //     with the gfx950 transposing LDS reads (ds_read_b64_tr_b16 / _b8),
 //     which hand every lane the K-run of one column -- no transpose pass and
@@ -32,8 +33,9 @@
 // source C), the loads are invisible to the compiler (so it cannot order the
 // LDS reads of one stage behind the loads into the other), and every
 // assembly statement is volatile, so the interleave below is the issue order.
-// The waits the compiler cannot see are written out: vmcnt(0) before each
-// barrier and at the end of the loop, and wait states between the last MFMA
+// The waits the compiler cannot see are written out: before each barrier a
+// vmcnt that leaves only the newer tiles' loads in flight, vmcnt(0) at the
+// end of the loop, and wait states between the last MFMA
 // and the first read of the accumulators.
 //
 // LDS layouts (bytes; chosen so that the reads below hit every bank once per
@@ -281,7 +283,7 @@ struct FragReader {
 };
 
 // The static interleave of a sub-step: QN MFMAs; in sub-step 0 the NR
-// fragment reads of sub-step 1, in sub-step 1 the ND loads of tile t+2 and
+// fragment reads of sub-step 1, in sub-step 1 the ND loads of tile t+NST and
 // the NR fragment reads of tile t+1 alternating (load first).  Operation o of
 // n goes after MFMA (o * QN) / n, so MFMA q is followed by operations
 // op_begin(q) .. op_begin(q + 1) - 1.
@@ -294,9 +296,10 @@ constexpr int op_begin(int q, int n, int qn) { return (q * n + qn - 1) / qn; }
 constexpr int EPI_PLAIN = 0, EPI_BETA = 1, EPI_FUSED = 2;
 
 // BM x BN tile, NW waves (2 along M, NW/2 along N), OCC workgroups per CU;
-// EPI: one of the epilogue variants above.
+// EPI: one of the epilogue variants above; NST LDS stages (2 or 4): tiles
+// kt+1 .. kt+NST-1 are in flight while tile kt is computed.
 template <int DT, bool TA, bool TB, int OUT, int BM, int BN, int NW, int OCC, bool KMASK,
-          int EPI>
+          int EPI, int NST>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(NW / 4 * OCC, NW / 4 * OCC)))
 void gemm_dma_kernel(const GemmArgs args) {
@@ -323,7 +326,9 @@ void gemm_dma_kernel(const GemmArgs args) {
     using Mma = MmaAsm<DT>;
     using Acc = typename Mma::Acc;
 
-    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+    static_assert(NST == 2 || NST == 4, "2 or 4 stages");
+    static_assert((NST - 1) * ND <= 63, "loads in flight fit vmcnt");
+    __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
     const uint32_t lds = (uint32_t)(size_t)(TCG_LDS char *)smem;
 
     const int tid = threadIdx.x;
@@ -355,7 +360,8 @@ void gemm_dma_kernel(const GemmArgs args) {
     fb.init(lane, wn * WTN);
 
     // Buffer resources of tile kt, based at its origin; a tile past the end
-    // gets empty ranges (its loads read zeros).
+    // of the K slice gets empty ranges (its loads fetch nothing and read
+    // zeros, into a stage nobody reads).
     struct TileSrc {
         i32x4 ra, rb;
         int kv;
@@ -367,8 +373,9 @@ void gemm_dma_kernel(const GemmArgs args) {
                                    : ((int64_t)m0 * args.lda + k0) * ES;
         const int64_t b_org = B_MC ? ((int64_t)k0 * args.ldb + n0) * ES
                                    : ((int64_t)n0 * args.ldb + k0) * ES;
-        s.ra = rsrc4(Ab + a_org, args.a_extent - a_org);
-        s.rb = rsrc4(Bb + b_org, args.b_extent - b_org);
+        const bool past = k0 >= k_hi;
+        s.ra = rsrc4(Ab + a_org, past ? 0 : args.a_extent - a_org);
+        s.rb = rsrc4(Bb + b_org, past ? 0 : args.b_extent - b_org);
         s.kv = min(BK, k_hi - k0);
         return s;
     };
@@ -407,7 +414,7 @@ void gemm_dma_kernel(const GemmArgs args) {
                 read(cur, 1, r, a1, b1);
         }
     };
-    // Sub-step 1: MFMAs on (a1, b1); the loads of tile kt+2 into `cur` and
+    // Sub-step 1: MFMAs on (a1, b1); the loads of tile kt+NST into `cur` and
     // the reads of the next tile's sub-step 0, alternating.  Past the last
     // tile the loads are empty (zero-fill a stage nobody reads) and the reads
     // return stale data nobody uses, so the loop body has no branch.
@@ -442,17 +449,15 @@ void gemm_dma_kernel(const GemmArgs args) {
             load_epi1<OUT>(make_epi<OUT>(args, z, N), n0 + tid, N, epi_b, epi_s);
     }
     if (nkt > 0) {
-        {
-            const TileSrc s0 = tile_src(0);
-            const TileSrc s1 = tile_src(1);
 #pragma unroll
-            for (int d = 0; d < ND; ++d) dma(s0, lds, d);
+        for (int t = 0; t < NST; ++t) {
+            const TileSrc st = tile_src(t);
 #pragma unroll
-            for (int d = 0; d < ND; ++d) dma(s1, lds + STAGE, d);
+            for (int d = 0; d < ND; ++d) dma(st, lds + t * STAGE, d);
         }
-        // tile 0 landed (tile 1 may still be in flight: the first loop
-        // barrier waits for it); the waves without loads have none in flight
-        wait_barrier_vm<ND>();
+        // tile 0 landed (tiles 1 .. NST-1 may still be in flight: the loop
+        // barriers wait for them); the waves without loads have none in flight
+        wait_barrier_vm<(NST - 1) * ND>();
         if constexpr (EPI_LDS > 1) {
             if (tid < BN) {
                 epi_smem[tid] = epi_b;
@@ -462,11 +467,13 @@ void gemm_dma_kernel(const GemmArgs args) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) read(lds, 0, r, a0, b0);
         for (int kt = 0; kt < nkt; ++kt) {
-            const uint32_t cur = lds + (kt & 1) * STAGE;
-            const uint32_t nxt = lds + ((kt + 1) & 1) * STAGE;
+            const uint32_t cur = lds + (kt % NST) * STAGE;
+            const uint32_t nxt = lds + ((kt + 1) % NST) * STAGE;
             sub0(cur);
-            wait_all_barrier();   // tile kt+1 landed for every wave; `cur` is free
-            sub1(cur, nxt, tile_src(kt + 2));
+            // tile kt+1 landed for every wave (tiles up to kt+NST-1 may still
+            // be in flight); every wave is done with `cur`
+            wait_barrier_vm<(NST - 2) * ND>();
+            sub1(cur, nxt, tile_src(kt + NST));
         }
         // no load may still be writing LDS when the workgroup ends, and the
         // last MFMA results need wait states before the accumulators are read
@@ -525,7 +532,7 @@ void gemm_dma_kernel(const GemmArgs args) {
     // one column hit distinct banks.
     constexpr int CRB = BN * 2;                    // C tile row bytes (16-bit)
     constexpr int CSW = CRB >= 512 ? 2 : 1;
-    static_assert(BM * CRB <= 2 * STAGE, "the C tile fits the operand stages");
+    static_assert(BM * CRB <= NST * STAGE, "the C tile fits the operand stages");
     bool c_lds = false;
     if constexpr (EPI == EPI_BETA && (OUT == DT_F16 || OUT == DT_BF16)) {
         c_lds = beta != 0.f && args.c_dma_ok != 0 && m0 + BM <= M && n0 + BN <= N;

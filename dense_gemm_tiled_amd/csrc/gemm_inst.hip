@@ -17,7 +17,8 @@ namespace {
 // 16-bit and int8 inputs.
 constexpr bool out_ok(int cls, int out) {
     if (is_dma_class(cls) && TCG_DT == DT_F32) return false;
-    if (out == OUT_PARTIAL) return cls == TILE_64 || cls == TILE_128 || cls == TILE_128_DMA;
+    if (out == OUT_PARTIAL)
+        return cls == TILE_64 || cls == TILE_128 || cls == TILE_128_DMA || cls == TILE_128_DMA4;
     // int8 into a float output: the dequantizing fused epilogue only
     if (TCG_DT == DT_I8) return out == DT_I32 || out == DT_F32 || out == DT_F16 || out == DT_BF16;
     if (TCG_DT == DT_F32) return out == DT_F32;
@@ -32,6 +33,7 @@ hipError_t launch_one(const GemmArgs &args, int64_t grid, hipStream_t stream) {
         constexpr int T = tile_shape(CLS).bm;
         constexpr int NW = CLS == TILE_256_DMA8 ? 8 : 4;
         constexpr int OCC = CLS == TILE_128_DMA ? 2 : 1;
+        constexpr int NST = CLS == TILE_128_DMA4 ? 4 : 2;
         // and the epilogue variant: C read only when beta != 0, the fused
         // epilogue only when one is asked for (float outputs)
         constexpr int BK = kLdsRowBytes / dt_size(TCG_DT);
@@ -42,7 +44,7 @@ hipError_t launch_one(const GemmArgs &args, int64_t grid, hipStream_t stream) {
                       : args.beta != 0.f ? EPI_BETA : EPI_PLAIN;
         const dim3 g((unsigned)grid), b(NW * 64);
 #define TCG_DMA(KM, EP) \
-    hipLaunchKernelGGL((gemm_dma_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, OUT, T, T, NW, OCC, KM, EP>), \
+    hipLaunchKernelGGL((gemm_dma_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, OUT, T, T, NW, OCC, KM, EP, NST>), \
                        g, b, 0, stream, args)
         if constexpr (FLOAT_OUT && TCG_DT == DT_I8) {
             // int8 sums reach a float output only through the fused epilogue
@@ -101,6 +103,7 @@ hipError_t TCG_LAUNCHER(int cls, int out, const tcg::GemmArgs &args, int64_t gri
     case TILE_256_DMA: return launch_cls<TILE_256_DMA>(out, args, grid, stream);
     case TILE_256_DMA8: return launch_cls<TILE_256_DMA8>(out, args, grid, stream);
     case TILE_128_DMA: return launch_cls<TILE_128_DMA>(out, args, grid, stream);
+    case TILE_128_DMA4: return launch_cls<TILE_128_DMA4>(out, args, grid, stream);
     default: return hipErrorInvalidValue;
     }
 }

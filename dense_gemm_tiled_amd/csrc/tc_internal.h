@@ -20,7 +20,9 @@ __host__ __device__ constexpr int dt_size(int dt) {
 // 256x256 tile of gemm_dma_kernel (direct-to-LDS loads; 16-bit and int8
 // inputs with 16-byte aligned rows) with 4 waves of 128x128, TILE_256_DMA8
 // the same with 8 waves of 128x64 (two per SIMD), TILE_128_DMA its 128x128
-// tile with 4 waves of 64x64 and two workgroups per CU.
+// tile with 4 waves of 64x64 and two workgroups per CU, TILE_128_DMA4 the
+// same tile with one workgroup per CU and 4 LDS stages (three K-tiles in
+// flight: split-K slices, whose short loops are bound by load latency).
 enum TileClass : int {
     TILE_256 = 0,
     TILE_128 = 1,
@@ -29,13 +31,14 @@ enum TileClass : int {
     TILE_256_DMA8 = 4,
     TILE_128_DMA = 5,
     TILE_THIN = 6,          // thin_kernel: N <= 16, A K-contiguous; kThinRows rows per workgroup
-    NUM_TILE_CLASSES = 7
+    TILE_128_DMA4 = 7,
+    NUM_TILE_CLASSES = 8
 };
 
 constexpr int kThinRows = 8;    // output rows per thin_kernel workgroup (2 waves)
 
 __host__ __device__ constexpr bool is_dma_class(int cls) {
-    return cls == TILE_256_DMA || cls == TILE_256_DMA8 || cls == TILE_128_DMA;
+    return cls == TILE_256_DMA || cls == TILE_256_DMA8 || cls == TILE_128_DMA || cls == TILE_128_DMA4;
 }
 
 __host__ __device__ constexpr int tile_threads(int cls) { return cls == TILE_256_DMA8 ? 512 : 256; }
@@ -46,7 +49,7 @@ struct TileShape {
 
 __host__ __device__ constexpr TileShape tile_shape(int cls) {
     return (cls == TILE_256 || cls == TILE_256_DMA || cls == TILE_256_DMA8) ? TileShape{256, 256, 2, 2}
-         : (cls == TILE_128 || cls == TILE_128_DMA) ? TileShape{128, 128, 2, 2}
+         : (cls == TILE_128 || cls == TILE_128_DMA || cls == TILE_128_DMA4) ? TileShape{128, 128, 2, 2}
          : cls == TILE_THIN                         ? TileShape{kThinRows, 16, kThinRows / 4, 1}
                                                     : TileShape{64, 64, 2, 2};
 }

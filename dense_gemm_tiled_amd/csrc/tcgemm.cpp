@@ -243,6 +243,11 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // not 16-byte aligned, which only the launch can see.
 bool dma_types(const Problem &p) { return p.dt == TC_F16 || p.dt == TC_BF16 || p.dt == TC_I8; }
 
+// Tile classes whose kernel can write split-K partial sums.
+bool splits_ok(int cls) {
+    return cls == TILE_64 || cls == TILE_128 || cls == TILE_128_DMA || cls == TILE_128_DMA4;
+}
+
 // Rows and columns (elements) of operand w (0 = A, 1 = B) as stored.
 void operand_shape(const Problem &p, int w, int64_t *rows, int64_t *cols) {
     const int64_t mn = w == 0 ? p.M : p.N;
@@ -311,9 +316,9 @@ void layout_workspace(const Problem &p, Plan *pl, const bool aligned[2]) {
 // more kernel adds up in a fixed order.
 //
 // Tuning overrides (environment, read at every call; unset in normal use):
-// TCGEMM_TILE=dma|dma8|dma128|thin|256|128|64 forces a tile class (dma* only
-// for 16-bit and int8 inputs, thin only for N <= 16 with A not transposed)
-// without split-K, TCGEMM_SPLITS=S forces split-K
+// TCGEMM_TILE=dma|dma8|dma128|dma128x4|thin|256|128|64 forces a tile class
+// (dma* only for 16-bit and int8 inputs, thin only for N <= 16 with A not
+// transposed) without split-K, TCGEMM_SPLITS=S forces split-K
 // with S slices (on a class with a partial-sum output: 64x64 or 128x128,
 // else 64x64), TCGEMM_BAND=h sets the band height of the tile order (0:
 // row-major).
@@ -378,16 +383,12 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true, const Choice 
     // tall K and too few tiles to fill the chip: split K
     const bool split = cls == TILE_64 && tile_count(TILE_64) < 128 && ktiles >= 16 && p.alpha != 0.0f;
     if (split && dma) {
-        // about 1.5 workgroups per CU (measured best on the batched 128 x 384
-        // x 16384 shape: enough slices to keep HBM busy, few enough partial
-        // sums), preferring a slice count that divides the K-tiles evenly
-        cls = TILE_128_DMA;
-        const int64_t want = ceil_div(384, tile_count(TILE_128_DMA));
-        splits = want;
-        for (int64_t d = 0; d <= want / 4; ++d) {
-            if (want - d >= 2 && ktiles % (want - d) == 0) { splits = want - d; break; }
-            if (ktiles % (want + d) == 0) { splits = want + d; break; }
-        }
+        // the 4-stage 128x128 tile, one workgroup per CU: as many slices as
+        // fit one round of workgroups (a second, partial round costs more
+        // than the extra slices gain; measured on the batched 128 x 384 x
+        // 16384 shape: 10 slices, 240 workgroups)
+        cls = TILE_128_DMA4;
+        splits = 256 / tile_count(TILE_128_DMA4);
         if (splits > ktiles / 4) splits = ktiles / 4;          // keep >= 4 K-tiles per slice
         if (splits > 32) splits = 32;
     } else if (split) {
@@ -412,6 +413,7 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true, const Choice 
         if (strcmp(env, "dma") == 0) cls = dma ? TILE_256_DMA : cls;
         else if (strcmp(env, "dma8") == 0) cls = dma ? TILE_256_DMA8 : cls;
         else if (strcmp(env, "dma128") == 0) cls = dma ? TILE_128_DMA : cls;
+        else if (strcmp(env, "dma128x4") == 0) cls = dma ? TILE_128_DMA4 : cls;
         else if (strcmp(env, "thin") == 0) cls = thin_ok ? TILE_THIN : cls;
         else cls = v == 256 ? TILE_256 : v == 128 ? TILE_128 : v == 64 ? TILE_64 : cls;
         splits = 1;   // a forced class splits only when TCGEMM_SPLITS says so
@@ -425,7 +427,7 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true, const Choice 
         cls = ch->cls;
         splits = ch->splits > 0 && p.alpha != 0.0f ? (ch->splits > ktiles ? ktiles : ch->splits) : 1;
     }
-    if (splits > 1 && cls != TILE_64 && cls != TILE_128 && cls != TILE_128_DMA) cls = TILE_64;
+    if (splits > 1 && !splits_ok(cls)) cls = TILE_64;
     if (cls == TILE_THIN) splits = 1;
     const TileShape ts = tile_shape(cls);
     pl->cls = cls;
@@ -913,14 +915,13 @@ std::vector<Choice> tune_candidates(const Problem &p) {
     make_plan(p, &base);
     const int64_t s0 = base.swap ? 1 : base.splits;
     const bool dma = dma_types(p);
-    const int classes_dma[] = {TILE_256_DMA, TILE_256_DMA8, TILE_128_DMA, TILE_64};
+    const int classes_dma[] = {TILE_256_DMA, TILE_256_DMA8, TILE_128_DMA, TILE_128_DMA4, TILE_64};
     const int classes_f32[] = {TILE_256, TILE_128, TILE_64};
     const int *cl = dma ? classes_dma : classes_f32;
-    const int ncl = dma ? 4 : 3;
+    const int ncl = dma ? 5 : 3;
     for (int i = 0; i < ncl; ++i) {
         c.push_back(Choice{cl[i], 1, 0});
-        const bool splits_ok = cl[i] == TILE_64 || cl[i] == TILE_128 || cl[i] == TILE_128_DMA;
-        if (splits_ok && s0 > 1)
+        if (splits_ok(cl[i]) && s0 > 1)
             for (int64_t s : {s0 / 2, s0, s0 * 2})
                 if (s > 1) c.push_back(Choice{cl[i], s, 0});
     }

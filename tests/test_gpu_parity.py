@@ -90,8 +90,9 @@ def test_padded_leading_dims(a, c):
 DMA_PAIRS = [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32"), ("i8", "i32")]
 
 
-DMA_TILES = ["dma", "dma8", "dma128"]
-DMA_NAME = {"dma": "_256x256_dma", "dma8": "_256x256_dma8", "dma128": "_128x128_dma"}
+DMA_TILES = ["dma", "dma8", "dma128", "dma128x4"]
+DMA_NAME = {"dma": "_256x256_dma", "dma8": "_256x256_dma8", "dma128": "_128x128_dma",
+            "dma128x4": "_128x128_dma4"}
 
 
 def dma_check(p, label, tile, **envs):
@@ -160,18 +161,19 @@ def test_dma_kernel_exact_regime_bitwise(a, c, tile):
     assert np.array_equal(got.view(np.uint8), ref.view(np.uint8))
 
 
+@pytest.mark.parametrize("tile", ["dma128", "dma128x4"])
 @pytest.mark.parametrize("splits", [3, 5])
 @pytest.mark.parametrize("ta,tb", LAYOUTS, ids=[lay(*l) for l in LAYOUTS])
 @pytest.mark.parametrize("a,c", DMA_PAIRS, ids=["%s-%s" % pc for pc in DMA_PAIRS])
-def test_dma128_split_k(a, c, ta, tb, splits):
-    """Split-K on the 128x128 direct-to-LDS tile: 2 x 2 tiles ragged in M and
-    N, batch 2, a K whose last slice is shorter and ends in a partial tile;
-    alpha = 0.5 and beta = 1 for floats."""
+def test_dma128_split_k(a, c, ta, tb, splits, tile):
+    """Split-K on the 128x128 direct-to-LDS tiles (2 and 4 LDS stages): 2 x 2
+    tiles ragged in M and N, batch 2, a K whose last slice is shorter and
+    ends in a partial tile; alpha = 0.5 and beta = 1 for floats."""
     if a == "i8":
         p = problem(a, c, 144, 208, 1104, ta, tb, batch=2)
     else:
         p = problem(a, c, 136, 200, 1096, ta, tb, batch=2)
-    dma_check(p, "dma128 splitk%d" % splits, "dma128", TCGEMM_SPLITS=splits)
+    dma_check(p, "%s splitk%d" % (tile, splits), tile, TCGEMM_SPLITS=splits)
 
 
 @pytest.mark.parametrize("tile", ["dma", "dma128"])
@@ -223,7 +225,7 @@ def test_dma128_split_k_packed_shared_operand():
     with env(TCGEMM_SPLITS=4):
         tg.gemm(a, b, c)
     torch.cuda.synchronize()
-    assert tg.last_kernel() == "pack_a+gemm_bf16_nn_128x128_dma+splitk_reduce", tg.last_kernel()
+    assert tg.last_kernel() == "pack_a+gemm_bf16_nn_128x128_dma4+splitk_reduce", tg.last_kernel()
     got = from_dev(c, "f32")
     for z in range(batch):
         ref = oracle_full(p0, A, bs[z], np.zeros((M, N), np.float32))
@@ -240,8 +242,8 @@ def test_dma128_split_k_packed_shared_operand():
     ("bf16", "bf16", 4136, 4096, 192, 1, True, True, "_dma|gemm_bf16_tt_64x64"),
     # batched column strip; the main part packs B (rows of 2051 bytes)
     ("i8", "i32", 2048, 2051, 256, 4, False, False, "_dma|transpose_b+gemm_i8_nn_thin"),
-    # strip of 40 columns: split-K on the 128x128 tile
-    ("bf16", "f32", 4096, 4136, 1024, 1, False, False, "|gemm_bf16_nn_128x128_dma+splitk_reduce"),
+    # strip of 40 columns: split-K on the 4-stage 128x128 tile
+    ("bf16", "f32", 4096, 4136, 1024, 1, False, False, "|gemm_bf16_nn_128x128_dma4+splitk_reduce"),
 ])
 def test_edge_split(a, c, M, N, K, batch, ta, tb, strip):
     """A thin ragged strip past the whole 256x256 tiles runs as a second GEMM
@@ -340,7 +342,7 @@ def epi_check(p, act, label, *, bias=True, shared=True, **envs):
 
 
 @pytest.mark.parametrize("act", ACTS)
-@pytest.mark.parametrize("tile", ["dma", "dma128", "dma8"])
+@pytest.mark.parametrize("tile", DMA_TILES)
 @pytest.mark.parametrize("a,c", [("bf16", "bf16"), ("f16", "f32"), ("f16", "f16")])
 def test_epilogue_dma_kernels(a, c, tile, act):
     """Bias + activation on the direct-to-LDS classes, ragged M/N/K tails,
@@ -837,7 +839,7 @@ def test_workload_f16_backward_pair(name):
 def test_workload_bf16_tn_splitk_b8():
     import dense_gemm_tiled_amd as tg
     p, A, B, C, got = full_case("bf16_tn_splitk_b8")
-    assert tg.last_kernel().endswith("_128x128_dma+splitk_reduce"), tg.last_kernel()
+    assert tg.last_kernel().endswith("_128x128_dma4+splitk_reduce"), tg.last_kernel()
     compare(p, got, oracle_full(p, A, B, C), label=p.name)
 
 

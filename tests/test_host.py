@@ -270,12 +270,12 @@ def test_plan_headline_uses_one_256_tile_per_cu():
 def test_plan_splitk_shape():
     p = workloads.get("bf16_tn_splitk_b8")
     pl = plan_of(p)
-    assert pl["kernel"] == "gemm_bf16_tn_128x128_dma+splitk_reduce"
+    assert pl["kernel"] == "gemm_bf16_tn_128x128_dma4+splitk_reduce"
     assert pl["splits"] > 1 and pl["launches"] == 2
     assert pl["k_per_split"] % pl["tile_k"] == 0
     assert pl["splits"] * pl["k_per_split"] >= p.K > (pl["splits"] - 1) * pl["k_per_split"]
     assert pl["workspace_bytes"] == pl["splits"] * p.batch * p.M * p.N * 4
-    assert pl["grid"] >= 256
+    assert 128 < pl["grid"] <= 256          # one round of one workgroup per CU
 
 
 def test_plan_other_workloads():
@@ -325,7 +325,7 @@ def test_plan_edge_split():
     base = workloads.get("bf16_nn_4096")
     main = "gemm_bf16_nn_256x256_dma"
     assert plan_of(base.with_(N=4104))["kernel"] == main + "|transpose_b+gemm_bf16_nn_thin"
-    assert plan_of(base.with_(M=4100))["kernel"] == main + "|gemm_bf16_nn_128x128_dma+splitk_reduce"
+    assert plan_of(base.with_(M=4100))["kernel"] == main + "|gemm_bf16_nn_128x128_dma4+splitk_reduce"
     assert plan_of(base.with_(N=4096 + 128))["kernel"].startswith(main + "|")
     assert plan_of(base.with_(N=4096 + 136))["kernel"] == main            # strip > half a tile
     assert plan_of(base.with_(M=3072, N=4104))["kernel"] == main          # 204 tiles: one round
@@ -409,7 +409,7 @@ def test_plan_packed_batch_strides():
     problem, the packed copies placed after the split-K partials."""
     common = dict(M=256, N=256, K=8190, a=tg.BF16, c=tg.F32, batch=3, sb=8190 * 256, sc=256 * 256)
     pl = tg.plan(desc(sa=0, **common))
-    assert pl["kernel"] == "pack_a+gemm_bf16_nn_128x128_dma+splitk_reduce", pl["kernel"]
+    assert pl["kernel"] == "pack_a+gemm_bf16_nn_128x128_dma4+splitk_reduce", pl["kernel"]
     part = pl["splits"] * 3 * 256 * 256 * 4
     assert part % 256 == 0
     assert pl["workspace_bytes"] == part + 256 * 16384
@@ -426,10 +426,10 @@ def test_plan_mid_size_and_split_k_classes():
     assert plan_of(mid.with_(a_dtype="f32", c_dtype="f32"))["kernel"] == "gemm_f32_nn_128x128"
     tall = workloads.Problem("tall", 256, 256, 8192, "f16", "f32")
     pl = plan_of(tall)
-    assert pl["kernel"] == "gemm_f16_nn_128x128_dma+splitk_reduce" and pl["splits"] > 1
+    assert pl["kernel"] == "gemm_f16_nn_128x128_dma4+splitk_reduce" and pl["splits"] > 1
     assert pl["grid"] == 4 * pl["splits"]
     pl = plan_of(tall.with_(K=8192 - 2))   # A rows (K-contiguous) not in whole chunks
-    assert pl["kernel"] == "pack_a+gemm_f16_nn_128x128_dma+splitk_reduce"
+    assert pl["kernel"] == "pack_a+gemm_f16_nn_128x128_dma4+splitk_reduce"
     pl = plan_of(tall.with_(a_dtype="f32"))
     assert pl["kernel"] == "gemm_f32_nn_64x64+splitk_reduce"
 
