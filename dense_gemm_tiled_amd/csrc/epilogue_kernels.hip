@@ -133,11 +133,12 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const PackArgs a) {
     char *dst = static_cast<char *>(a.dst) + z * a.dst_stride + r * a.dst_pitch;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, a.row_bytes);
     const int chunks = (int)(a.dst_pitch / 16);
-    // four chunks per lane in flight before their stores
-    for (int c0 = threadIdx.x & 63; c0 < chunks; c0 += 256) {
-        u32x4 v[4];
+    // eight chunks per lane in flight before their stores: a row of up to
+    // 8 KiB costs one memory round trip
+    for (int c0 = threadIdx.x & 63; c0 < chunks; c0 += 512) {
+        u32x4 v[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 8; ++u) {
             const int c = c0 + 64 * u;
             const int nb = a.row_bytes - 16 * c;
             v[u] = u32x4{0u, 0u, 0u, 0u};
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const PackArgs a) {
             else if (nb > 0) v[u] = ld_partial<1>(rs, 16 * c, nb);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 8; ++u)
             if (c0 + 64 * u < chunks) *reinterpret_cast<u32x4 *>(dst + 16 * (c0 + 64 * u)) = v[u];
     }
 }

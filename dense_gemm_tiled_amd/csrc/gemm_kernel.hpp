@@ -647,10 +647,14 @@ __global__ __launch_bounds__(256, Occupancy<CLS>::value) void gemm_kernel(const 
 
     using LoadA = std::conditional_t<TA, ColLoader<ES, BM, THREADS>, RowLoader<ES, BM, THREADS>>;
     using LoadB = std::conditional_t<TB, RowLoader<ES, BN, THREADS>, ColLoader<ES, BN, THREADS>>;
-    LoadA la;
-    LoadB lb;
+    // The 64x64 class (small outputs, short per-tile work) stages two tiles
+    // ahead in registers: tile t+2 loads while tile t+1 waits in the other
+    // set, so two tiles' latency overlap; the larger classes stage one.
+    constexpr bool PF2 = CLS == TILE_64;
+    LoadA la, la2;
+    LoadB lb, lb2;
 
-    auto load_tile = [&](int k0) {
+    auto load_tile = [&](int k0, LoadA &la, LoadB &lb) {
         const int64_t a_org = TA ? ((int64_t)k0 * args.lda + m0) * ES
                                  : ((int64_t)m0 * args.lda + k0) * ES;
         const int64_t b_org = TB ? ((int64_t)n0 * args.ldb + k0) * ES
@@ -673,17 +677,26 @@ __global__ __launch_bounds__(256, Occupancy<CLS>::value) void gemm_kernel(const 
         for (int j = 0; j < FN; ++j) acc[i][j] = Acc{0, 0, 0, 0};
 
     if (nkt > 0) {
-        load_tile(k_lo);
+        load_tile(k_lo, la, lb);
         la.store(smem, tid);
         lb.store(smem + BM * kLdsRowBytes, tid);
+        if (PF2 && nkt > 1) load_tile(k_lo + BK, la2, lb2);
         __syncthreads();
     }
 
     const int frag_row = lane & 15, frag_chunk = lane >> 4;
-    for (int kt = 0; kt < nkt; ++kt) {
+    // K-tile kt from LDS stage kt & 1.  One set: tile kt+1 loads into it
+    // now and goes to LDS after the MFMAs.  Two sets (PF2): tile kt+1 is
+    // already in set nxt; tile kt+2 loads into set ld (stored to LDS one
+    // iteration ago), then set nxt goes to LDS after the MFMAs.
+    auto k_step = [&](int kt, LoadA &la_ld, LoadB &lb_ld, LoadA &la_nxt, LoadB &lb_nxt) {
         char *sa = smem + (kt & 1) * STAGE;
         char *sb = sa + BM * kLdsRowBytes;
-        if (kt + 1 < nkt) load_tile(k_lo + (kt + 1) * BK);
+        if constexpr (PF2) {
+            if (kt + 2 < nkt) load_tile(k_lo + (kt + 2) * BK, la_ld, lb_ld);
+        } else {
+            if (kt + 1 < nkt) load_tile(k_lo + (kt + 1) * BK, la_nxt, lb_nxt);
+        }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             u32x4 af[FM], bf[FN];
@@ -702,10 +715,19 @@ __global__ __launch_bounds__(256, Occupancy<CLS>::value) void gemm_kernel(const 
         }
         if (kt + 1 < nkt) {
             char *na = smem + ((kt + 1) & 1) * STAGE;
-            la.store(na, tid);
-            lb.store(na + BM * kLdsRowBytes, tid);
+            la_nxt.store(na, tid);
+            lb_nxt.store(na + BM * kLdsRowBytes, tid);
         }
         __syncthreads();
+    };
+    if constexpr (PF2) {
+        // tile t sits in set t & 1 (la/lb even, la2/lb2 odd)
+        for (int kt = 0; kt < nkt; kt += 2) {
+            k_step(kt, la, lb, la2, lb2);
+            if (kt + 1 < nkt) k_step(kt + 1, la2, lb2, la, lb);
+        }
+    } else {
+        for (int kt = 0; kt < nkt; ++kt) k_step(kt, la, lb, la, lb);
     }
 
     // ---- epilogue: lane holds C[m][n .. n+3] of each 16x16 block
