@@ -104,9 +104,18 @@ def cpu_baseline(p: workloads.Problem, A, B, C, target_s: float):
     t_probe = max(run(probe), 1e-4)
     rows = int(max(probe, min(p.M, probe * target_s / t_probe)))
     t = run(rows)
-    flops = 2.0 * rows * p.N * p.K
-    bytes_ = (rows * p.K + p.K * p.N) * es
-    return {"rows": rows, "seconds": t, "flops": flops, "bytes": bytes_,
+    if t < 0.5 * target_s and rows < p.M:
+        # the small probe overestimates the cost per row: size again
+        rows = int(min(p.M, rows * target_s / max(t, 1e-4)))
+        t = run(rows)
+    # a whole problem shorter than the target runs again until the target
+    reps = 1
+    while rows == p.M and t < 0.67 * target_s and reps < 100000:
+        t += run(rows)
+        reps += 1
+    flops = 2.0 * rows * p.N * p.K * reps
+    bytes_ = (rows * p.K + p.K * p.N) * es * reps
+    return {"rows": rows, "reps": reps, "seconds": t, "flops": flops, "bytes": bytes_,
             "cores": oracle.num_threads()}
 
 
@@ -249,8 +258,8 @@ def main():
             cv, cu = cb["flops"] / cb["seconds"] / 1e12, unit
         line["cpu_baseline"] = {
             "value": cv, "unit": cu, "cores": cb["cores"], "kind": "oracle",
-            "sample": "rows 0..%d of batch element 0 of the same problem (%.1f s, fp64 "
-                      "accumulation)" % (cb["rows"] - 1, cb["seconds"])}
+            "sample": "rows 0..%d of batch element 0 of the same problem, %d time(s) (%.1f s, "
+                      "fp64 accumulation)" % (cb["rows"] - 1, cb["reps"], cb["seconds"])}
     print(json.dumps(line), flush=True)
 
 
