@@ -278,6 +278,25 @@ def test_plan_splitk_shape():
     assert 128 < pl["grid"] <= 256          # one round of one workgroup per CU
 
 
+def test_plan_split_k_fits_one_round():
+    """Split-K on the 4-stage 128x128 tile (one workgroup per CU) takes as
+    many slices as fit one round of 256 workgroups, keeps at least 4 K-tiles
+    per slice, and every slice is non-empty."""
+    shapes = [(128, 384, 16384, 8, "bf16", "f32", True), (256, 256, 8192, 1, "f16", "f32", False),
+              (130, 200, 1100, 2, "bf16", "bf16", True), (512, 640, 4096, 1, "i8", "i32", False),
+              (64, 2000, 65536, 1, "bf16", "f32", False)]
+    for M, N, K, batch, a, c, ta in shapes:
+        p = workloads.Problem("s", M, N, K, a, c, transpose_a=ta, batch=batch)
+        pl = plan_of(p)
+        tiles = -(-M // 128) * -(-N // 128) * batch
+        assert pl["kernel"].endswith("_128x128_dma4+splitk_reduce"), (M, N, K, pl["kernel"])
+        assert pl["grid"] == tiles * pl["splits"] <= 256, (M, N, K, pl["grid"])
+        assert pl["splits"] >= 2 and pl["k_per_split"] >= 4 * pl["tile_k"], (M, N, K, pl)
+        assert (pl["splits"] - 1) * pl["k_per_split"] < K <= pl["splits"] * pl["k_per_split"]
+        # one more slice would not fit the round, or the slices would get too short
+        assert tiles * (pl["splits"] + 1) > 256 or -(-K // pl["tile_k"]) // (pl["splits"] + 1) < 4
+
+
 def test_plan_other_workloads():
     # ldb = 4099 bytes: B rows do not start on 16-byte boundaries, so B is
     # packed into the workspace first; N = 4099 leaves a 3-column strip past
