@@ -129,12 +129,8 @@ __device__ inline void dma16(i32x4 rsrc, uint32_t lds, int voff) {
 }
 #pragma clang diagnostic pop
 
-// Wait for this wave's loads and LDS reads, then for the other waves.
-__device__ inline void wait_all_barrier() {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Same, but leaving the newest VM loads of this wave in flight.
+// Wait for this wave's LDS reads and all but its newest VM loads, then for
+// the other waves.
 template <int VM>
 __device__ inline void wait_barrier_vm() {
     static_assert(VM >= 0 && VM <= 63, "vmcnt is a 6-bit count");

@@ -14,16 +14,18 @@
 //   * per K-tile: every thread loads its share of the A and B tiles from HBM
 //     into registers (buffer loads; transposed operands are transposed in
 //     registers), writes them to one of two LDS stages, and the waves run MFMA
-//     on the other stage -- one barrier per K-tile;
+//     on the other stage -- one barrier per K-tile; the 64x64 class keeps two
+//     tiles in flight in two register sets, the larger classes one;
 //   * LDS holds both operands K-contiguous: one 128-byte row of K per M (or
 //     N) index, its 16-byte chunks XOR-swizzled by the row so that fragment
 //     reads and transposed writes do not collide in banks;
 //   * each wave owns a (BM/2) x (BN/2) block of C as 16x16 MFMA blocks;
 //     operands enter the MFMA swapped (B block as src0, A block as src1) so
 //     each lane ends up with 4 consecutive columns of one C row;
-//   * epilogue: alpha*acc + beta*C_old (C read only when beta != 0), rounded
-//     once to the output type, masked to the M x N extent -- or, for split-K,
-//     the raw fp32/int32 partial to the workspace.
+//   * epilogue: alpha*acc + beta*C_old (C read only when beta != 0), or the
+//     fused form act(alpha*scale[n]*acc + beta*C_old + bias[n]), rounded once
+//     to the output type, masked to the M x N extent -- or, for split-K, the
+//     raw fp32/int32 partial to the workspace.
 //
 // Ragged edges (tessl "Architecture", "Edge-Slice Support"): tiles that reach
 // past M, N or K take a checked load path that zero-fills everything outside
