@@ -125,13 +125,27 @@ __global__ __launch_bounds__(256) void scale_c_kernel(const EpilogueArgs a) {
 // workgroup; each lane moves 16 bytes at a time.  The source may sit at any
 // byte address: buffer loads of 16 bytes take unaligned offsets, and the
 // last partial chunk of a row is read byte by byte, the rest of it zero.
+// With a.bt set, the few elements that follow each row's packed bytes (the
+// columns of a thin strip computed by a second GEMM) are written transposed
+// to that strip's B^T as well, so the strip needs no gather pass of its own.
 __global__ __launch_bounds__(256) void pack_rows_kernel(const PackArgs a) {
     const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (row >= (int64_t)a.batch * a.rows) return;
     const int z = (int)(row / a.rows), r = (int)(row % a.rows);
     const char *src = static_cast<const char *>(a.src) + z * a.src_stride + r * a.src_pitch;
     char *dst = static_cast<char *>(a.dst) + z * a.dst_stride + r * a.dst_pitch;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, a.row_bytes);
+    const int tail_bytes = a.bt ? a.bt_cols * a.bt_es : 0;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (int64_t)a.row_bytes + tail_bytes);
+    // the transposed tail: lane n loads element n past the packed bytes now,
+    // so its latency overlaps the row's
+    const int lane = threadIdx.x & 63;
+    u32 tail = 0;
+    if (lane < (a.bt ? a.bt_cols : 0)) {
+        const int off = a.row_bytes + lane * a.bt_es;
+        if (a.bt_es == 4) tail = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+        else if (a.bt_es == 2) tail = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
+        else tail = __builtin_amdgcn_raw_buffer_load_b8(rs, off, 0, 0);
+    }
     const int chunks = (int)(a.dst_pitch / 16);
     // eight chunks per lane in flight before their stores: a row of up to
     // 8 KiB costs one memory round trip
@@ -148,6 +162,13 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const PackArgs a) {
 #pragma unroll
         for (int u = 0; u < 8; ++u)
             if (c0 + 64 * u < chunks) *reinterpret_cast<u32x4 *>(dst + 16 * (c0 + 64 * u)) = v[u];
+    }
+    if (lane < (a.bt ? a.bt_cols : 0)) {
+        char *d = static_cast<char *>(a.bt) + z * a.bt_stride + (int64_t)lane * a.bt_pitch +
+                  (int64_t)r * a.bt_es;
+        if (a.bt_es == 4) *reinterpret_cast<u32 *>(d) = tail;
+        else if (a.bt_es == 2) *reinterpret_cast<unsigned short *>(d) = (unsigned short)tail;
+        else *reinterpret_cast<unsigned char *>(d) = (unsigned char)tail;
     }
 }
 
@@ -185,6 +206,10 @@ hipError_t tcg_launch_pack_rows(const PackArgs &args, hipStream_t stream) {
     const int64_t blocks = ((int64_t)args.batch * args.rows + 3) / 4;
     if (blocks <= 0 || blocks > 0x7FFFFFFF || args.dst_pitch % 16 != 0 ||
         args.dst_pitch < args.row_bytes)
+        return hipErrorInvalidValue;
+    if (args.bt && (args.bt_cols < 1 || args.bt_cols > 16 ||
+                    (args.bt_es != 1 && args.bt_es != 2 && args.bt_es != 4) ||
+                    args.bt_pitch < (int64_t)args.rows * args.bt_es))
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, args);
     return hipGetLastError();

@@ -122,6 +122,13 @@ struct PackArgs {
     int64_t src_stride, dst_stride;   // bytes between batch problems
     int64_t src_pitch, dst_pitch;     // bytes between rows
     int32_t rows, row_bytes, batch;
+    // row packing only, optional (bt == null: none): the bt_cols elements
+    // of bt_es bytes that follow each source row's row_bytes, transposed --
+    // element n of row r goes to bt[n * bt_pitch + r * bt_es] (the B^T of a
+    // thin column strip right after the packed columns)
+    void *bt;
+    int64_t bt_stride;                // bytes between batch problems
+    int32_t bt_pitch, bt_cols, bt_es;
 };
 
 // Workgroup -> (tile_m, tile_n, group).

@@ -311,9 +311,9 @@ void layout_workspace(const Problem &p, Plan *pl, const bool aligned[2]) {
 //
 // For 16-bit and int8 inputs the 256x256 and 128x128 classes run as the
 // direct-to-LDS kernel (an operand it cannot read as it is gets packed
-// first), and split-K runs on its 128x128 tile, two workgroups per CU: the
-// slices stream the operands from HBM and write fp32 partial sums that one
-// more kernel adds up in a fixed order.
+// first), and split-K runs on its 4-stage 128x128 tile, one workgroup per
+// CU, in one round of workgroups: the slices stream the operands from HBM and
+// write fp32 partial sums that one more kernel adds up in a fixed order.
 //
 // Tuning overrides (environment, read at every call; unset in normal use):
 // TCGEMM_TILE=dma|dma8|dma128|dma128x4|thin|256|128|64 forces a tile class
@@ -503,6 +503,7 @@ Problem sub_problem(const Problem &p, int axis, int64_t lo, int64_t n, int64_t o
 // The two parts of an edge-split problem with their plans.
 struct Parts {
     int n;
+    int axis;           // 1: the second part is a column strip, 2: a row strip
     Problem p[2];
     Plan pl[2];
     int64_t off[2][3];  // element offsets of the part's A, B, C origins (caller's operands)
@@ -512,6 +513,7 @@ struct Parts {
 Parts split_parts(const Problem &p, const Plan &pl) {
     Parts r;
     r.swap[0] = r.swap[1] = false;
+    r.axis = pl.swap ? 0 : pl.edge;
     if (pl.swap) {
         r.n = 1;
         r.p[0] = transposed_problem(p);
@@ -565,10 +567,47 @@ int plan_launches(const Problem &p, const Plan &pl) {
     return 1 + (pl.splits > 1) + pl.pack[0] + pl.pack[1];
 }
 
+// A column strip whose B^T comes out of the main part's row packing of B:
+// when the main part packs B stored [K, N] row by row and the strip runs on
+// the thin kernel (which reads B^T), the packing kernel also writes the
+// strip's columns, which follow the main part's in every row, transposed,
+// and the strip needs no gather pass.  The B^T goes after the main part's
+// workspace.  main and strip: the parts' plans as laid out for the call.
+struct StripBt {
+    bool on = false;
+    int64_t off = 0;             // workspace byte offset of the B^T
+    int64_t pitch = 0, stride = 0, bytes = 0;
+    int32_t cols = 0;            // the strip's columns
+};
+
+StripBt strip_bt(const Parts &r, const Plan &main, const Plan &strip) {
+    StripBt b;
+    if (r.n != 2 || r.axis != 1 || r.swap[0] || r.swap[1] || r.p[0].alpha == 0.0f) return b;
+    const Problem &m = r.p[0], &st = r.p[1];
+    if (!main.pack[1] || m.tb || thin_transposes_b(m, main) || !thin_transposes_b(st, strip))
+        return b;
+    b.on = true;
+    b.cols = st.N;
+    b.pitch = strip.pack_pitch[1];
+    b.stride = strip.pack_stride[1];
+    b.off = align_up(main.ws_bytes, 256);
+    b.bytes = align_up((st.stride_b == 0 ? 1 : st.batch) * st.N * b.pitch, 256);
+    return b;
+}
+
+// The strip's plan as it runs when its B^T comes from the main part.
+Plan without_bt_pass(const Plan &pl) {
+    Plan q = pl;
+    q.pack[1] = false;
+    return q;
+}
+
 // Kernel chains of the parts, joined by '|'.
 std::string parts_chain(const Parts &r) {
+    const bool fused = strip_bt(r, r.pl[0], r.pl[1]).on;
     std::string name = kernel_chain(r.p[0], r.pl[0]);
-    for (int i = 1; i < r.n; ++i) name += "|" + kernel_chain(r.p[i], r.pl[i]);
+    for (int i = 1; i < r.n; ++i)
+        name += "|" + kernel_chain(r.p[i], fused ? without_bt_pass(r.pl[i]) : r.pl[i]);
     return name;
 }
 
@@ -577,6 +616,7 @@ void fill_info(const Problem &p, const Plan &pl, tc_plan_info *info) {
     memset(info, 0, sizeof *info);
     const Parts parts = split_parts(p, pl);
     snprintf(info->kernel, sizeof info->kernel, "%s", parts_chain(parts).c_str());
+    const StripBt sb = strip_bt(parts, parts.pl[0], parts.pl[1]);
     const Plan &m = parts.pl[0];   // tile fields: the main (whole-tile) part
     info->tile_m = m.bm; info->tile_n = m.bn; info->tile_k = m.bk;
     info->threads = tile_threads(m.cls);
@@ -589,8 +629,10 @@ void fill_info(const Problem &p, const Plan &pl, tc_plan_info *info) {
         if (p.alpha != 0.0f) info->grid += parts.pl[i].grid;
         if (p.alpha != 0.0f && parts.pl[i].ws_bytes > info->workspace_bytes)
             info->workspace_bytes = parts.pl[i].ws_bytes;
-        info->launches += plan_launches(parts.p[i], parts.pl[i]);
+        info->launches += plan_launches(parts.p[i], i == 1 && sb.on ? without_bt_pass(parts.pl[i])
+                                                                     : parts.pl[i]);
     }
+    if (sb.on && sb.off + sb.bytes > info->workspace_bytes) info->workspace_bytes = sb.off + sb.bytes;
     info->band = pl.band;
 }
 
@@ -674,13 +716,18 @@ tc_status_t create_stream(tc_context *ctx, tc_stream **out, hipStream_t existing
 
 // Enqueue the launches of one planned problem (packs, GEMM, reduction) on
 // stream s; their names are appended to *names.
+// sb: a column strip's B^T made by the main part's B packing (null: none);
+// sb_writes: this part is the main part (its B packing writes the B^T), else
+// the strip (its thin kernel reads the B^T, with no gather pass).
 tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan &plan,
                     const void *A, const void *B, void *C, const Epilogue &epi, bool main_part,
-                    std::string *names, std::string *err) {
+                    std::string *names, std::string *err, const StripBt *sb = nullptr,
+                    bool sb_writes = false) {
     Plan pl = plan;
     const bool aligned[2] = {(uintptr_t)A % 16 == 0, (uintptr_t)B % 16 == 0};
     layout_workspace(p, &pl, aligned);   // a misaligned base pointer is packed too
-    *names += kernel_chain(p, pl);
+    const bool bt_ready = sb && !sb_writes;
+    *names += kernel_chain(p, bt_ready ? without_bt_pass(pl) : pl);
     tc_status_t st;
     const bool use_splitk = p.alpha != 0.0f && pl.splits > 1;
     const bool use_ws = p.alpha != 0.0f && pl.ws_bytes > 0;
@@ -722,6 +769,15 @@ tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan 
         bool tb = p.tb;
         for (int w = 0; w < 2 && e == hipSuccess; ++w) {
             if (!pl.pack[w]) continue;
+            if (w == 1 && thin_transposes_b(p, pl) && bt_ready) {
+                // the main part's B packing wrote this strip's B^T
+                src[1] = static_cast<char *>(s->ws) + sb->off;
+                ld[1] = sb->pitch / es;
+                stride[1] = sb->stride / es;
+                extent[1] = (int64_t)p.N * sb->pitch;
+                tb = true;
+                continue;
+            }
             if (w == 1 && thin_transposes_b(p, pl)) {
                 PackArgs pa;
                 memset(&pa, 0, sizeof pa);
@@ -758,6 +814,13 @@ tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan 
             pa.rows = (int32_t)rows;
             pa.row_bytes = (int32_t)(cols * es);
             pa.batch = stride[w] == 0 ? 1 : p.batch;
+            if (w == 1 && sb && sb_writes) {
+                pa.bt = static_cast<char *>(s->ws) + sb->off;
+                pa.bt_stride = sb->stride;
+                pa.bt_pitch = (int32_t)sb->pitch;
+                pa.bt_cols = sb->cols;
+                pa.bt_es = es;
+            }
             e = tcg_launch_pack_rows(pa, s->stream);
             if (e != hipSuccess) break;
             ctx->dispatches += 1;
@@ -874,11 +937,32 @@ tc_status_t enqueue_call(tc_context *ctx, tc_stream *s, const Problem &p, const 
                          const void *A, const void *B, void *C, const Epilogue &epi,
                          std::string *name, std::string *err) {
     const Parts parts = split_parts(p, pl);
+    const int es = dt_size(p.dt);
+    auto part_a = [&](int i) {
+        return parts.swap[i] ? static_cast<const char *>(B) + parts.off[i][1] * es
+                             : static_cast<const char *>(A) + parts.off[i][0] * es;
+    };
+    auto part_b = [&](int i) {
+        return parts.swap[i] ? static_cast<const char *>(A) + parts.off[i][0] * es
+                             : static_cast<const char *>(B) + parts.off[i][1] * es;
+    };
+    // the strip's B^T from the main part's packing, laid out for these
+    // pointers (a misaligned base pointer changes what is packed)
+    StripBt sb;
+    if (parts.n == 2) {
+        Plan lp[2] = {parts.pl[0], parts.pl[1]};
+        for (int i = 0; i < 2; ++i) {
+            const bool aligned[2] = {(uintptr_t)part_a(i) % 16 == 0, (uintptr_t)part_b(i) % 16 == 0};
+            layout_workspace(parts.p[i], &lp[i], aligned);
+        }
+        sb = strip_bt(parts, lp[0], lp[1]);
+        tc_status_t st;
+        if (sb.on && (st = ensure_workspace(s, sb.off + sb.bytes, err)) != TC_OK) return st;
+    }
     for (int i = 0; i < parts.n; ++i) {
-        const int es = dt_size(p.dt), ces = dt_size(p.cdt);
-        const void *Ai = static_cast<const char *>(A) + parts.off[i][0] * es;
-        const void *Bi = static_cast<const char *>(B) + parts.off[i][1] * es;
-        if (parts.swap[i]) std::swap(Ai, Bi);   // the transposed product: A' = B, B' = A
+        const int ces = dt_size(p.cdt);
+        const void *Ai = part_a(i);
+        const void *Bi = part_b(i);
         void *Ci = static_cast<char *>(C) + parts.off[i][2] * ces;
         // a column strip's bias and scales start at its first column
         Epilogue epi_i = epi;
@@ -887,7 +971,8 @@ tc_status_t enqueue_call(tc_context *ctx, tc_stream *s, const Problem &p, const 
             if (epi.scale) epi_i.scale = epi.scale + pl.edge_at;
         }
         if (i) *name += "|";
-        tc_status_t st = enqueue(ctx, s, parts.p[i], parts.pl[i], Ai, Bi, Ci, epi_i, i == 0, name, err);
+        tc_status_t st = enqueue(ctx, s, parts.p[i], parts.pl[i], Ai, Bi, Ci, epi_i, i == 0, name, err,
+                                 sb.on ? &sb : nullptr, i == 0);
         if (st != TC_OK) return st;
     }
     return TC_OK;

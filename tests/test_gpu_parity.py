@@ -240,8 +240,11 @@ def test_dma128_split_k_packed_shared_operand():
     ("f16", "f32", 4100, 4096, 192, 1, True, True, "_dma|transpose_a+gemv_f16_tt_thin"),
     # row strip of 40 rows (too many for the small-M route)
     ("bf16", "bf16", 4136, 4096, 192, 1, True, True, "_dma|gemm_bf16_tt_64x64"),
-    # batched column strip; the main part packs B (rows of 2051 bytes)
-    ("i8", "i32", 2048, 2051, 256, 4, False, False, "_dma|transpose_b+gemm_i8_nn_thin"),
+    # batched column strip; the main part packs B (rows of 2051 bytes) and
+    # writes the strip's B^T on the way
+    ("i8", "i32", 2048, 2051, 256, 4, False, False, "_dma|gemm_i8_nn_thin"),
+    # the same with 16-bit elements: rows of 4100 halves, a 4-column strip
+    ("f16", "f32", 4096, 4100, 256, 1, False, False, "pack_b+gemm_f16_nn_256x256_dma|gemm_f16_nn_thin"),
     # strip of 40 columns: split-K on the 4-stage 128x128 tile
     ("bf16", "f32", 4096, 4136, 1024, 1, False, False, "|gemm_bf16_nn_128x128_dma4+splitk_reduce"),
 ])
@@ -543,8 +546,7 @@ def test_workload_i8_nn_ragged_dequant_bf16():
     sc = workloads.make_col_scale(p)
     say("GPU case: workload", p.name)
     got = logical(p, run_library_epilogue(p, A, B, C, None, "none", col_scale=sc))
-    assert tg.last_kernel() == ("pack_b+gemm_i8_nn_256x256_dma|"
-                                "transpose_b+gemm_i8_nn_thin"), tg.last_kernel()
+    assert tg.last_kernel() == "pack_b+gemm_i8_nn_256x256_dma|gemm_i8_nn_thin", tg.last_kernel()
     pts = workloads.sample_points(p, 4096)
     r, _ = oracle.gemm_epilogue_points(A, B, None, pts, col_scale=sc, M=p.M, N=p.N, K=p.K,
                                        a_dtype="i8", c_dtype=p.c_dtype, ldb=p.LDB)
@@ -846,6 +848,5 @@ def test_workload_bf16_tn_splitk_b8():
 def test_workload_i8_nn_ragged_bit_exact():
     import dense_gemm_tiled_amd as tg
     p, A, B, C, got = full_case("i8_nn_ragged")
-    assert tg.last_kernel() == ("pack_b+gemm_i8_nn_256x256_dma|"
-                                "transpose_b+gemm_i8_nn_thin"), tg.last_kernel()
+    assert tg.last_kernel() == "pack_b+gemm_i8_nn_256x256_dma|gemm_i8_nn_thin", tg.last_kernel()
     compare(p, got, oracle_full(p, A, B, C), label=p.name)
