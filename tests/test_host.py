@@ -297,6 +297,23 @@ def test_plan_split_k_fits_one_round():
         assert tiles * (pl["splits"] + 1) > 256 or -(-K // pl["tile_k"]) // (pl["splits"] + 1) < 4
 
 
+def test_plan_strip_bt_from_row_packing():
+    """An edge split whose main part packs B row by row and whose column
+    strip runs on the thin kernel: the packing writes the strip's B^T after
+    the main part's packed B (per problem when B is batched), so the strip
+    has no gather pass; a B the main part need not pack keeps the gather."""
+    p = workloads.Problem("s", 2048, 2051, 256, "i8", "i32", batch=4)
+    pl = plan_of(p)
+    assert pl["kernel"] == "pack_b+gemm_i8_nn_256x256_dma|gemm_i8_nn_thin", pl["kernel"]
+    assert pl["launches"] == 3
+    main_b = 4 * 256 * 2048                       # 4 problems, 256 rows of 2048 packed bytes
+    strip_bt = 4 * 3 * 256                        # 4 problems, 3 rows of 256 bytes
+    assert pl["workspace_bytes"] == main_b + strip_bt
+    # a B of whole 16-byte rows is read as it is: the strip gathers its B^T
+    q = workloads.Problem("s", 4096, 4104, 1024, "bf16", "bf16")
+    assert plan_of(q)["kernel"] == "gemm_bf16_nn_256x256_dma|transpose_b+gemm_bf16_nn_thin"
+
+
 def test_plan_other_workloads():
     # ldb = 4099 bytes: B rows do not start on 16-byte boundaries, so B is
     # packed into the workspace first; N = 4099 leaves a 3-column strip past
