@@ -64,11 +64,11 @@ def _load():
     lib.oracle_gemm.restype = i32
     lib.oracle_gemm.argtypes = [i64, i64, i64, i32, i32, i32, i32, f64, f64,
                                 vp, i64, vp, i64, vp, i64, vp, vp,
-                                i64, i64, i64, i64]
+                                i64, i64, i64, i64, vp]
     lib.oracle_gemm_points.restype = i32
     lib.oracle_gemm_points.argtypes = [i64, i64, i64, i32, i32, i32, i32, f64, f64,
                                        vp, i64, vp, i64, vp, i64, i64, i64, i64,
-                                       i64, vp, vp, vp, vp, vp]
+                                       i64, vp, vp, vp, vp, vp, vp]
     for name in ("oracle_decode_bf16", "oracle_decode_f16"):
         getattr(lib, name).restype = f64
         getattr(lib, name).argtypes = [ctypes.c_uint16]
@@ -141,7 +141,7 @@ def gemm(A: np.ndarray, B: np.ndarray, C_in: Optional[np.ndarray], *,
          lda: int = 0, ldb: int = 0, ldc: int = 0,
          batch: int = 1, stride_a: int = 0, stride_b: int = 0,
          stride_c: int = 0, C_like: Optional[np.ndarray] = None,
-         want_value: bool = True) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+         want_value: bool = True, want_abs: bool = False):
     """Evaluate the whole product.
 
     A, B, C_in are flat-or-shaped numpy arrays of stored values (uint16 bit
@@ -149,6 +149,9 @@ def gemm(A: np.ndarray, B: np.ndarray, C_in: Optional[np.ndarray], *,
     (C_out, value) where C_out has C_in's layout (or C_like's when C_in is None)
     holding round_c(value) inside the M x N extent, and value is the unrounded
     fp64 result as a dense [batch, M, N] array (None unless want_value).
+    With want_abs, returns (C_out, value, T) where T, dense [batch, M, N], is
+    the sum over k of |opA(i,k) * opB(k,j)| (the magnitude that scales the
+    a-priori error bound of a length-K dot product; exact for int8).
     """
     _c_dtype_ok(a_dtype, c_dtype)
     lda = lda or (M if transpose_a else K)
@@ -165,13 +168,16 @@ def gemm(A: np.ndarray, B: np.ndarray, C_in: Optional[np.ndarray], *,
             C_like = np.zeros(size, dtype=STORAGE[c_dtype])
         C_out = np.ascontiguousarray(C_like).copy()
     value = np.empty((batch, M, N), dtype=np.float64) if want_value else None
+    mag = np.empty((batch, M, N), dtype=np.float64) if want_abs else None
     rc = _load().oracle_gemm(M, N, K, DTYPES[a_dtype], DTYPES[c_dtype],
                              int(bool(transpose_a)), int(bool(transpose_b)),
                              float(alpha), float(beta), _ptr(A), lda, _ptr(B), ldb,
                              _ptr(C_in), ldc, _ptr(C_out), _ptr(value),
-                             batch, stride_a, stride_b, stride_c)
+                             batch, stride_a, stride_b, stride_c, _ptr(mag))
     if rc != 0:
         raise ValueError("oracle_gemm rejected its arguments (code %d)" % rc)
+    if want_abs:
+        return C_out, value, mag
     return C_out, value
 
 
@@ -181,12 +187,13 @@ def gemm_points(A: np.ndarray, B: np.ndarray, C_in: Optional[np.ndarray],
                 transpose_a: bool = False, transpose_b: bool = False,
                 alpha: float = 1.0, beta: float = 0.0,
                 lda: int = 0, ldb: int = 0, ldc: int = 0,
-                stride_a: int = 0, stride_b: int = 0, stride_c: int = 0
-                ) -> Tuple[np.ndarray, np.ndarray]:
+                stride_a: int = 0, stride_b: int = 0, stride_c: int = 0,
+                want_abs: bool = False):
     """Evaluate the definition only at the given (z, i, j) outputs.
 
     Returns (rounded, value): rounded holds c_dtype stored values, value the
-    unrounded fp64 results (exact sums for int8).
+    unrounded fp64 results (exact sums for int8); with want_abs, (rounded,
+    value, T) with T the magnitude sums at those outputs (see gemm).
     """
     _c_dtype_ok(a_dtype, c_dtype)
     lda = lda or (M if transpose_a else K)
@@ -201,14 +208,17 @@ def gemm_points(A: np.ndarray, B: np.ndarray, C_in: Optional[np.ndarray],
     C_in = None if C_in is None else np.ascontiguousarray(C_in)
     value = np.empty(len(pts), dtype=np.float64)
     rounded = np.empty(len(pts), dtype=STORAGE[c_dtype])
+    mag = np.empty(len(pts), dtype=np.float64) if want_abs else None
     rc = _load().oracle_gemm_points(M, N, K, DTYPES[a_dtype], DTYPES[c_dtype],
                                     int(bool(transpose_a)), int(bool(transpose_b)),
                                     float(alpha), float(beta), _ptr(A), lda, _ptr(B),
                                     ldb, _ptr(C_in), ldc, stride_a, stride_b, stride_c,
                                     len(pts), _ptr(zs), _ptr(is_), _ptr(js),
-                                    _ptr(value), _ptr(rounded))
+                                    _ptr(value), _ptr(rounded), _ptr(mag))
     if rc != 0:
         raise ValueError("oracle_gemm_points rejected its arguments (code %d)" % rc)
+    if want_abs:
+        return rounded, value, mag
     return rounded, value
 
 
@@ -273,12 +283,13 @@ def _sum_kw(kw):
 def gemm_epilogue(A: np.ndarray, B: np.ndarray, C_in: Optional[np.ndarray], *,
                   bias: Optional[np.ndarray] = None, bias_stride: int = 0,
                   col_scale: Optional[np.ndarray] = None, scale_stride: int = 0,
-                  act: str = "none", **kw) -> Tuple[np.ndarray, np.ndarray]:
+                  act: str = "none", want_abs: bool = False, **kw):
     """The fused form: gemm()'s arguments plus bias / bias_stride (stored
     c_dtype values, problem z's N values at z*bias_stride), col_scale /
     scale_stride (fp32 values, likewise) and act.  Returns (C_out, value) like
     gemm(), value being the fp64 result after the epilogue (before rounding
-    to c_dtype), dense [batch, M, N]."""
+    to c_dtype), dense [batch, M, N]; with want_abs, (C_out, value, T) with
+    T the magnitude sums of the product (see gemm)."""
     _epilogue_args(kw, col_scale, act)
     M, N, batch = kw["M"], kw["N"], kw.get("batch", 1)
     c_dtype, alpha, beta = kw["c_dtype"], kw.get("alpha", 1.0), kw.get("beta", 0.0)
@@ -286,9 +297,11 @@ def gemm_epilogue(A: np.ndarray, B: np.ndarray, C_in: Optional[np.ndarray], *,
     stride_c = kw.get("stride_c", 0)
     # the exact sums (alpha = 0 reads neither A nor B)
     if alpha != 0.0:
-        _, S = gemm(A, B, None, want_value=True, stride_c=M * N, **_sum_kw(kw))
+        _, S, T = gemm(A, B, None, want_value=True, want_abs=True, stride_c=M * N,
+                       **_sum_kw(kw))
     else:
         S = np.zeros((batch, M, N))
+        T = np.zeros((batch, M, N))
     if col_scale is not None:
         sc = np.asarray(col_scale, dtype=np.float32).ravel().astype(np.float64)
         for z in range(batch):
@@ -318,6 +331,8 @@ def gemm_epilogue(A: np.ndarray, B: np.ndarray, C_in: Optional[np.ndarray], *,
         for i in range(M):
             o = z * stride_c + i * ldc
             flat[o:o + N] = enc[z, i]
+    if want_abs:
+        return flat.reshape(C_out.shape), y, T
     return flat.reshape(C_out.shape), y
 
 
@@ -325,16 +340,17 @@ def gemm_epilogue_points(A: np.ndarray, B: np.ndarray, C_in: Optional[np.ndarray
                          points: Sequence[Tuple[int, int, int]], *,
                          bias: Optional[np.ndarray] = None, bias_stride: int = 0,
                          col_scale: Optional[np.ndarray] = None, scale_stride: int = 0,
-                         act: str = "none", **kw) -> Tuple[np.ndarray, np.ndarray]:
+                         act: str = "none", want_abs: bool = False, **kw):
     """The fused form at the given (z, i, j) outputs only.  Returns (rounded,
-    value) like gemm_points."""
+    value) like gemm_points; with want_abs, (rounded, value, T)."""
     _epilogue_args(kw, col_scale, act)
     c_dtype, alpha, beta = kw["c_dtype"], kw.get("alpha", 1.0), kw.get("beta", 0.0)
     pts = np.asarray(points, dtype=np.int64).reshape(-1, 3)
     if alpha != 0.0:
-        _, S = gemm_points(A, B, None, pts, **_sum_kw(kw))
+        _, S, T = gemm_points(A, B, None, pts, want_abs=True, **_sum_kw(kw))
     else:
         S = np.zeros(len(pts))
+        T = np.zeros(len(pts))
     if col_scale is not None:
         sc = np.asarray(col_scale, dtype=np.float32).ravel().astype(np.float64)
         S = S * sc[pts[:, 0] * scale_stride + pts[:, 2]]
@@ -347,6 +363,8 @@ def gemm_epilogue_points(A: np.ndarray, B: np.ndarray, C_in: Optional[np.ndarray
         b = decode(np.ascontiguousarray(bias).ravel(), c_dtype)
         y = y + b[pts[:, 0] * bias_stride + pts[:, 2]]
     y = activation(y, act)
+    if want_abs:
+        return encode(y, c_dtype), y, T
     return encode(y, c_dtype), y
 
 

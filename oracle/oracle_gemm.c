@@ -13,6 +13,16 @@
  *   S(i,j)   = sum over k = 0 .. K-1, in ascending k, of opA(i,k)*opB(k,j)
  *   C(i,j)   = round_c( alpha*S(i,j) + (beta != 0 ? beta*C_in(i,j) : 0) )
  *
+ * and, on request, the magnitude sum
+ *
+ *   T(i,j)   = sum over k = 0 .. K-1, in ascending k, of |opA(i,k)*opB(k,j)|
+ *
+ * which scales the a-priori error bound of a floating-point dot product of
+ * length K (|computed - exact| <= gamma_K * T, gamma_K = K*u / (1 - K*u) for
+ * unit roundoff u; tessl "Architecture", section "Reductions and Numerical
+ * Safety", bounds its row sums the same way, by a multiple of eps * n times
+ * the term magnitudes).
+ *
  * Sources (web pages, cited by title and section):
  *  - tensorcore "GEMM", section "Surface": the descriptor, the BLAS row-major
  *    definition C = alpha*A@B + beta*C, and leading dims that default to
@@ -197,8 +207,9 @@ static int check_args(int64_t M, int64_t N, int64_t K, int a_dtype,
  * C_out (same layout as C_in, ldc) receives round_c(value) at every (i, j)
  * inside the M x N extent and is left untouched elsewhere.
  * value_out, if non-NULL, receives the unrounded fp64 value
- * alpha*S + beta*C_in, densely as [batch][M][N].  C_in may be NULL when
- * beta == 0 (it is never read then).
+ * alpha*S + beta*C_in, densely as [batch][M][N].  abs_out, if non-NULL,
+ * receives T (the sum of |products|, exact for int8), densely likewise.
+ * C_in may be NULL when beta == 0 (it is never read then).
  *
  * Returns 0 on success, a negative code on bad arguments.
  */
@@ -207,7 +218,7 @@ int oracle_gemm(int64_t M, int64_t N, int64_t K, int a_dtype, int c_dtype,
                 const void *A, int64_t lda, const void *B, int64_t ldb,
                 const void *C_in, int64_t ldc, void *C_out, double *value_out,
                 int64_t batch, int64_t stride_a, int64_t stride_b,
-                int64_t stride_c) {
+                int64_t stride_c, double *abs_out) {
     int rc = check_args(M, N, K, a_dtype, c_dtype, alpha, beta, batch);
     if (rc) return rc;
     if (beta != 0.0 && C_in == NULL) return -3;
@@ -216,7 +227,9 @@ int oracle_gemm(int64_t M, int64_t N, int64_t K, int a_dtype, int c_dtype,
 #pragma omp parallel
     {
         double *acc = (double *)malloc(sizeof(double) * (size_t)N);
+        double *tacc = (double *)malloc(sizeof(double) * (size_t)N);
         int64_t *iacc = (int64_t *)malloc(sizeof(int64_t) * (size_t)N);
+        int64_t *itacc = (int64_t *)malloc(sizeof(int64_t) * (size_t)N);
 #pragma omp for schedule(dynamic)
         for (int64_t zi = 0; zi < batch * M; ++zi) {
             int64_t z = zi / M, i = zi % M;
@@ -227,25 +240,43 @@ int oracle_gemm(int64_t M, int64_t N, int64_t K, int a_dtype, int c_dtype,
             if (is_int) {
                 const int8_t *a8 = (const int8_t *)Az + a_off;
                 const int8_t *b8 = (const int8_t *)Bz + b_off;
-                for (int64_t j = 0; j < N; ++j) iacc[j] = 0;
+                for (int64_t j = 0; j < N; ++j) iacc[j] = itacc[j] = 0;
                 for (int64_t k = 0; k < K; ++k) {
                     int64_t a = a8[opa_index(i, k, transpose_a, lda)];
-                    for (int64_t j = 0; j < N; ++j)
-                        iacc[j] += a * (int64_t)b8[opb_index(k, j, transpose_b, ldb)];
+                    if (abs_out) {
+                        for (int64_t j = 0; j < N; ++j) {
+                            int64_t t = a * (int64_t)b8[opb_index(k, j, transpose_b, ldb)];
+                            iacc[j] += t;
+                            itacc[j] += t < 0 ? -t : t;
+                        }
+                    } else {
+                        for (int64_t j = 0; j < N; ++j)
+                            iacc[j] += a * (int64_t)b8[opb_index(k, j, transpose_b, ldb)];
+                    }
                 }
                 for (int64_t j = 0; j < N; ++j) {
                     ((int32_t *)C_out)[c_off + i * ldc + j] = (int32_t)iacc[j];
                     if (value_out) value_out[(z * M + i) * N + j] = (double)iacc[j];
+                    if (abs_out) abs_out[(z * M + i) * N + j] = (double)itacc[j];
                 }
             } else {
-                for (int64_t j = 0; j < N; ++j) acc[j] = 0.0;
+                for (int64_t j = 0; j < N; ++j) acc[j] = tacc[j] = 0.0;
                 if (alpha != 0.0) {
                     for (int64_t k = 0; k < K; ++k) {
                         double a = load_float(A, a_dtype,
                                               a_off + opa_index(i, k, transpose_a, lda));
-                        for (int64_t j = 0; j < N; ++j)
-                            acc[j] += a * load_float(B, a_dtype,
-                                                     b_off + opb_index(k, j, transpose_b, ldb));
+                        if (abs_out) {
+                            for (int64_t j = 0; j < N; ++j) {
+                                double t = a * load_float(B, a_dtype,
+                                                          b_off + opb_index(k, j, transpose_b, ldb));
+                                acc[j] += t;
+                                tacc[j] += fabs(t);
+                            }
+                        } else {
+                            for (int64_t j = 0; j < N; ++j)
+                                acc[j] += a * load_float(B, a_dtype,
+                                                         b_off + opb_index(k, j, transpose_b, ldb));
+                        }
                     }
                 }
                 for (int64_t j = 0; j < N; ++j) {
@@ -254,11 +285,14 @@ int oracle_gemm(int64_t M, int64_t N, int64_t K, int a_dtype, int c_dtype,
                         v += beta * load_float(C_in, c_dtype, c_off + i * ldc + j);
                     store_rounded(C_out, c_dtype, c_off + i * ldc + j, v);
                     if (value_out) value_out[(z * M + i) * N + j] = v;
+                    if (abs_out) abs_out[(z * M + i) * N + j] = tacc[j];
                 }
             }
         }
         free(acc);
+        free(tacc);
         free(iacc);
+        free(itacc);
     }
     return 0;
 }
@@ -267,7 +301,8 @@ int oracle_gemm(int64_t M, int64_t N, int64_t K, int a_dtype, int c_dtype,
  * The same definition evaluated at npts chosen outputs (z[p], i[p], j[p]),
  * one by one, for full-size shapes where the whole product is too slow.
  * value_out[p] receives the unrounded fp64 value (the exact sum for int8);
- * rounded_out (c_dtype elements, npts of them), if non-NULL, its rounding.
+ * rounded_out (c_dtype elements, npts of them), if non-NULL, its rounding;
+ * abs_out[p], if non-NULL, the magnitude sum T at that output.
  */
 int oracle_gemm_points(int64_t M, int64_t N, int64_t K, int a_dtype,
                        int c_dtype, int transpose_a, int transpose_b,
@@ -276,7 +311,7 @@ int oracle_gemm_points(int64_t M, int64_t N, int64_t K, int a_dtype,
                        int64_t ldc, int64_t stride_a, int64_t stride_b,
                        int64_t stride_c, int64_t npts, const int64_t *zs,
                        const int64_t *is, const int64_t *js, double *value_out,
-                       void *rounded_out) {
+                       void *rounded_out, double *abs_out) {
     int rc = check_args(M, N, K, a_dtype, c_dtype, alpha, beta, 1);
     if (rc) return rc;
     if (beta != 0.0 && C_in == NULL) return -3;
@@ -287,22 +322,30 @@ int oracle_gemm_points(int64_t M, int64_t N, int64_t K, int a_dtype,
         if (a_dtype == OR_I8) {
             const int8_t *a8 = (const int8_t *)A + a_off;
             const int8_t *b8 = (const int8_t *)B + b_off;
-            int64_t s = 0;
-            for (int64_t k = 0; k < K; ++k)
-                s += (int64_t)a8[opa_index(i, k, transpose_a, lda)] *
-                     (int64_t)b8[opb_index(k, j, transpose_b, ldb)];
+            int64_t s = 0, sa = 0;
+            for (int64_t k = 0; k < K; ++k) {
+                int64_t t = (int64_t)a8[opa_index(i, k, transpose_a, lda)] *
+                            (int64_t)b8[opb_index(k, j, transpose_b, ldb)];
+                s += t;
+                sa += t < 0 ? -t : t;
+            }
             value_out[p] = (double)s;
             if (rounded_out) ((int32_t *)rounded_out)[p] = (int32_t)s;
+            if (abs_out) abs_out[p] = (double)sa;
         } else {
-            double s = 0.0;
+            double s = 0.0, sa = 0.0;
             if (alpha != 0.0)
-                for (int64_t k = 0; k < K; ++k)
-                    s += load_float(A, a_dtype, a_off + opa_index(i, k, transpose_a, lda)) *
-                         load_float(B, a_dtype, b_off + opb_index(k, j, transpose_b, ldb));
+                for (int64_t k = 0; k < K; ++k) {
+                    double t = load_float(A, a_dtype, a_off + opa_index(i, k, transpose_a, lda)) *
+                               load_float(B, a_dtype, b_off + opb_index(k, j, transpose_b, ldb));
+                    s += t;
+                    sa += fabs(t);
+                }
             double v = (alpha != 0.0) ? alpha * s : 0.0;
             if (beta != 0.0) v += beta * load_float(C_in, c_dtype, c_off + i * ldc + j);
             value_out[p] = v;
             if (rounded_out) store_rounded(rounded_out, c_dtype, p, v);
+            if (abs_out) abs_out[p] = sa;
         }
     }
     return 0;

@@ -639,3 +639,103 @@ def test_i8_dequant_points_equal_full():
                                        bias_stride=N, act="gelu_tanh", **kw)
     assert np.array_equal(v.reshape(b, M, N), val)
     assert np.array_equal(r.reshape(b, M, N), out.reshape(b, M, N))
+
+
+# ----------------------------------------------------------------- magnitude sums
+# T(i, j) = sum over k of |opA(i,k) * opB(k,j)|: the magnitude that scales the
+# a-priori error bound of a length-K dot product (tessl "Architecture",
+# "Reductions and Numerical Safety", bounds its sums by a multiple of
+# eps * n * the term magnitudes); the parity tests use it for their
+# elementwise gate.
+@pytest.mark.parametrize("dtype", FLOAT_TYPES)
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_magnitude_sum_against_exact_rationals(dtype, ta, tb):
+    """Mixed-sign inputs, padded leading dims: T within the fp64 bound of the
+    exact sum of |products| (Python fractions), and never below |S|."""
+    rng = np.random.default_rng(hash(("mag", dtype, ta, tb)) % 2**32)
+    M, N, K, pad = 7, 5, 8, 3
+    A, B, lda, ldb, ldc = _tiny_case(rng, dtype, ta, tb, M, N, K, pad, "normal")
+    Ad, Bd = lib_decode(A, dtype), lib_decode(B, dtype)
+    _, value, T = oracle.gemm(A, B, None, M=M, N=N, K=K, a_dtype=dtype, c_dtype=dtype,
+                              transpose_a=ta, transpose_b=tb, lda=lda, ldb=ldb, ldc=ldc,
+                              want_abs=True)
+    strictly = 0
+    for i in range(M):
+        for j in range(N):
+            ex = Fraction(0)
+            for k in range(K):
+                a = Ad[k * lda + i] if ta else Ad[i * lda + k]
+                b = Bd[j * ldb + k] if tb else Bd[k * ldb + j]
+                ex += abs(Fraction(float(a)) * Fraction(float(b)))
+            assert abs(Fraction(T[0, i, j]) - ex) <= Fraction(K) * Fraction(2) ** -53 * ex
+            assert T[0, i, j] >= abs(value[0, i, j])
+            strictly += T[0, i, j] > abs(value[0, i, j])
+    assert strictly > 0      # mixed signs: some sums cancel
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_magnitude_sum_int8_exact(ta, tb):
+    rng = np.random.default_rng(78)
+    M, N, K, pad = 6, 9, 13, 2
+    A, B, lda, ldb, ldc = _tiny_case(rng, "i8", ta, tb, M, N, K, pad, "")
+    _, _, T = oracle.gemm(A, B, None, M=M, N=N, K=K, a_dtype="i8", c_dtype="i32",
+                          transpose_a=ta, transpose_b=tb, lda=lda, ldb=ldb, ldc=ldc,
+                          want_abs=True)
+    for i in range(M):
+        for j in range(N):
+            s = 0
+            for k in range(K):
+                a = int(A[k * lda + i] if ta else A[i * lda + k])
+                b = int(B[j * ldb + k] if tb else B[k * ldb + j])
+                s += abs(a * b)
+            assert T[0, i, j] == s
+
+
+@pytest.mark.parametrize("dtype", FLOAT_TYPES + ("i8",))
+def test_magnitude_sum_is_the_sum_for_one_signed_terms(dtype):
+    """With every product non-negative T is the plain sum (same terms, same
+    order: bit-equal); negating A negates the sum and leaves T; negating a
+    row of A changes only that row's sums."""
+    rng = np.random.default_rng(12)
+    M, N, K = 9, 10, 300
+    c_dtype = "i32" if dtype == "i8" else dtype
+    if dtype == "i8":
+        A = np.abs(rng.integers(-127, 128, size=(M, K))).astype(np.int8)
+        B = np.abs(rng.integers(-127, 128, size=(K, N))).astype(np.int8)
+        negA = (-A.astype(np.int16)).astype(np.int8)
+    else:
+        A = encode_lib(np.abs(rng.normal(0, 1, size=(M, K))), dtype)
+        B = encode_lib(np.abs(rng.normal(0, 1, size=(K, N))), dtype)
+        negA = encode_lib(-lib_decode(A, dtype), dtype)
+    kw = dict(M=M, N=N, K=K, a_dtype=dtype, c_dtype=c_dtype, want_abs=True)
+    _, v, T = oracle.gemm(A, B, None, **kw)
+    assert np.array_equal(T, v)
+    _, vn, Tn = oracle.gemm(negA, B, None, **kw)
+    assert np.array_equal(vn, -v)
+    assert np.array_equal(Tn, T)
+    mixed = A.copy()
+    mixed[3] = negA[3]
+    _, vm, Tm = oracle.gemm(mixed, B, None, **kw)
+    assert np.array_equal(Tm, T)
+    assert np.array_equal(vm[0, 3], -v[0, 3])
+    assert np.array_equal(np.delete(vm[0], 3, axis=0), np.delete(v[0], 3, axis=0))
+
+
+def test_magnitude_sum_points_equal_full():
+    rng = np.random.default_rng(23)
+    b, M, N, K = 2, 6, 7, 45
+    for dtype in ("bf16", "i8"):
+        A = draw(rng, dtype, (b, K, M))
+        B = draw(rng, dtype, (b, N, K))
+        c_dtype = "i32" if dtype == "i8" else "f32"
+        kw = dict(M=M, N=N, K=K, a_dtype=dtype, c_dtype=c_dtype, transpose_a=True,
+                  transpose_b=True, stride_a=M * K, stride_b=N * K, stride_c=M * N)
+        _, _, T = oracle.gemm(A, B, None, batch=b, want_abs=True, **kw)
+        pts = [(z, i, j) for z in range(b) for i in range(M) for j in range(N)]
+        _, _, Tp = oracle.gemm_points(A, B, None, pts, want_abs=True, **kw)
+        assert np.array_equal(Tp.reshape(b, M, N), T)
+        _, _, Te = oracle.gemm_epilogue(A, B, None, act="relu", batch=b, want_abs=True,
+                                        col_scale=np.ones(N, np.float32)
+                                        if dtype == "i8" else None,
+                                        **dict(kw, c_dtype="f32"))
+        assert np.array_equal(Te, T)
