@@ -10,6 +10,14 @@ __device__ inline EpiState epi_of(const EpilogueArgs &a, int z) {
     return make_epi<CDT>(a, z, a.N);
 }
 
+// Row m of problem z's C as a buffer resource spanning its N values (the
+// row's byte address in 64-bit arithmetic).
+__device__ inline __amdgpu_buffer_rsrc_t c_row_rsrc(const EpilogueArgs &a, int z, int m) {
+    const int64_t ces = dt_size(a.c_dtype);
+    char *row = static_cast<char *>(a.C) + ((int64_t)z * a.stride_c + (int64_t)m * a.ldc) * ces;
+    return make_rsrc(row, (int64_t)a.N * ces);
+}
+
 // ---------------------------------------------------------------------------
 // Split-K reduction: C = round(alpha * sum_s partial[s] + beta * C_old), the
 // slices summed in ascending s so the result is the same on every run; the
@@ -28,10 +36,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const EpilogueArgs a
     const int64_t plane = (int64_t)a.M * a.N;
     const char *wsz = static_cast<const char *>(a.ws) + (int64_t)z * a.splits * plane * 4;
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(wsz, (int64_t)a.splits * plane * 4);
-    const int CES = dt_size(a.c_dtype);
-    char *Cz = static_cast<char *>(a.C) + z * a.stride_c * CES;
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cz, a.c_extent);
-    const int coff = (m * a.ldc + n) * CES;
+    // C's row m as a buffer of its N values: offsets stay small for a C of
+    // any size, and nothing past column N is written
+    const __amdgpu_buffer_rsrc_t rc = c_row_rsrc(a, z, m);
+    const int coff = n * dt_size(a.c_dtype);
     const bool wvec = (a.N % 4) == 0;
     const bool cvec = a.c_vec_ok != 0;
     float s4[4] = {0.f, 0.f, 0.f, 0.f};
@@ -100,10 +108,8 @@ __global__ __launch_bounds__(256) void scale_c_kernel(const EpilogueArgs a) {
     const int64_t rem = idx - (int64_t)z * a.M * nq;
     const int m = (int)(rem / nq), n = (int)(rem % nq) * 4;
     const int nvalid = a.N - n;
-    const int CES = dt_size(a.c_dtype);
-    char *Cz = static_cast<char *>(a.C) + z * a.stride_c * CES;
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cz, a.c_extent);
-    const int coff = (m * a.ldc + n) * CES;
+    const __amdgpu_buffer_rsrc_t rc = c_row_rsrc(a, z, m);
+    const int coff = n * dt_size(a.c_dtype);
     const bool cvec = a.c_vec_ok != 0;
     float v[4] = {0.f, 0.f, 0.f, 0.f};
     // alpha = 1 on zeros keeps them zero; finish4 then adds beta * C_old.

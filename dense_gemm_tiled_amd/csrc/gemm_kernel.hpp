@@ -2,11 +2,12 @@
 // Instantiated by gemm_inst.hip (one object per input type and layout).
 //
 // Computes C = alpha * op(A) @ op(B) + beta * C in BLAS row-major layout
-// (tensorcore "GEMM", section "Surface"), as a K-tiled loop that stages a
-// slice of each operand and accumulates their product (Phobos "Matrix
-// products", matmul / matmul_t), with the accumulator held in registers for
-// the whole K loop and C written exactly once (tessl "Architecture", section
-// "Cooperative Destination Accumulation").
+// (tensorcore "GEMM", section "Surface").  The K extent is walked in blocks:
+// each block of op(A) rows and op(B) columns is brought on chip, multiplied,
+// and added into a running sum (the loop structure of Phobos "Matrix
+// products", matmul / matmul_t).  That sum stays in registers from the first
+// K block to the last, and C is written once at the end (tessl
+// "Architecture", section "Cooperative Destination Accumulation").
 //
 // Structure of one workgroup (256 threads = 4 wave64s, 2 x 2):
 //   * tile (tm, tn, group) from tile_of_workgroup(): XCD-aware regrouping,

@@ -38,7 +38,8 @@ enum TileClass : int {
 constexpr int kThinRows = 8;    // output rows per thin_kernel workgroup (2 waves)
 
 __host__ __device__ constexpr bool is_dma_class(int cls) {
-    return cls == TILE_256_DMA || cls == TILE_256_DMA8 || cls == TILE_128_DMA || cls == TILE_128_DMA4;
+    return cls == TILE_256_DMA || cls == TILE_256_DMA8 || cls == TILE_128_DMA ||
+           cls == TILE_128_DMA4;
 }
 
 __host__ __device__ constexpr int tile_threads(int cls) { return cls == TILE_256_DMA8 ? 512 : 256; }
@@ -48,7 +49,8 @@ struct TileShape {
 };
 
 __host__ __device__ constexpr TileShape tile_shape(int cls) {
-    return (cls == TILE_256 || cls == TILE_256_DMA || cls == TILE_256_DMA8) ? TileShape{256, 256, 2, 2}
+    return (cls == TILE_256 || cls == TILE_256_DMA || cls == TILE_256_DMA8)
+               ? TileShape{256, 256, 2, 2}
          : (cls == TILE_128 || cls == TILE_128_DMA || cls == TILE_128_DMA4) ? TileShape{128, 128, 2, 2}
          : cls == TILE_THIN                         ? TileShape{kThinRows, 16, kThinRows / 4, 1}
                                                     : TileShape{64, 64, 2, 2};
@@ -143,9 +145,14 @@ struct PackArgs {
 // slice), so one XCD's range stays inside one problem where it can.
 //
 // Step 3, band order inside a group (tessl "Architecture", "Column-Panel Grid
-// Swizzling"): the tile grid is cut into bands of `band` tile rows; inside a
-// band consecutive ids walk down a column of the band before moving right, so
-// a run of ids touches few B column panels and few A row panels.
+// Swizzling"): the tile rows are grouped into horizontal bands of `band`
+// rows (the last band keeps whatever rows remain), the bands are visited top
+// to bottom, and each band is visited in column-major order -- down one tile
+// column of the band, then the next column to the right.  A run of
+// consecutive ids then touches few B column panels and few A row panels.
+// Every band above the one holding id t is full, so t's band is
+// t / (band * tiles_n) and t's position inside it the remainder; in a band of
+// h rows, position o is tile column o / h and row o % h of the band.
 __host__ __device__ inline void tile_of_workgroup(int32_t tiles_m, int32_t tiles_n,
                                                   int32_t band, int64_t wg, int64_t n_wg,
                                                   int32_t *tm, int32_t *tn, int32_t *g) {
@@ -160,6 +167,8 @@ __host__ __device__ inline void tile_of_workgroup(int32_t tiles_m, int32_t tiles
         *tn = (int32_t)(t % tiles_n);
         return;
     }
+    // (this exact arithmetic keeps the kernels' compile time low: equivalent
+    // rewrites of it made each GEMM object compile three times slower)
     int64_t per_band = (int64_t)band * tiles_n;
     int64_t b = t / per_band;
     int64_t rem = t - b * per_band;

@@ -156,8 +156,8 @@ def test_c_past_2gib_alpha_zero_and_split_k():
     a = torch.zeros(M, 8, dtype=torch.bfloat16, device="cuda")
     b = torch.zeros(8, N, dtype=torch.bfloat16, device="cuda")
     bias = torch.linspace(-1, 1, N, device="cuda").to(torch.bfloat16)
-    rows = [0, 1, 150, 255, 256, 298, 299]          # 256 * ldc * 2 bytes > 2^31
-    assert 256 * ldc * 2 > 2 ** 31
+    rows = [0, 1, 150, 256, 257, 298, 299]          # rows from 257 on start past 2 GiB
+    assert 256 * ldc * 2 < 2 ** 31 < 257 * ldc * 2
     before = _rows_of(store, rows, N + 64)
     say("GPU case: alpha = 0 on a C past 2 GiB")
     tg.gemm(a, b, c, alpha=0.0, beta=0.5, bias=bias, activation="relu")
@@ -186,8 +186,8 @@ def test_c_past_2gib_alpha_zero_and_split_k():
     tg.gemm(a, b, c)
     torch.cuda.synchronize()
     assert tg.last_kernel().endswith("+splitk_reduce"), tg.last_kernel()
-    rows = [0, 255, 256, 300, 511]
-    assert 256 * ldc * 4 > 2 ** 31
+    rows = [0, 256, 257, 300, 511]                  # rows from 257 on start past 2 GiB
+    assert 256 * ldc * 4 < 2 ** 31 < 257 * ldc * 4
     q = p.with_(M=len(rows))
     sub = np.ascontiguousarray(A[rows])
     ref = oracle_full(q, sub, B, np.zeros((len(rows), N), np.float32))
