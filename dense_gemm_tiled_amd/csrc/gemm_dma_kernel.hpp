@@ -137,11 +137,18 @@ __device__ inline void wait_barrier_vm() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
 }
 
-template <int DT>
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+// One MFMA on a 16-byte fragment of each operand per lane: MS = 16 is the
+// 16 x 16 output block (16x16x32 for 16-bit inputs, 16x16x64 for int8; 4
+// accumulators per lane), MS = 32 the 32 x 32 block (32x32x16, 32x32x32; 16
+// accumulators per lane, twice the cycles per instruction).
+template <int DT, int MS>
 struct MmaAsm;
 
 template <>
-struct MmaAsm<DT_BF16> {
+struct MmaAsm<DT_BF16, 16> {
     using Acc = f32x4;
     __device__ static inline void run(Acc &acc, const u32x4 &b, const u32x4 &a) {
         asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
@@ -149,7 +156,7 @@ struct MmaAsm<DT_BF16> {
 };
 
 template <>
-struct MmaAsm<DT_F16> {
+struct MmaAsm<DT_F16, 16> {
     using Acc = f32x4;
     __device__ static inline void run(Acc &acc, const u32x4 &b, const u32x4 &a) {
         asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
@@ -157,10 +164,34 @@ struct MmaAsm<DT_F16> {
 };
 
 template <>
-struct MmaAsm<DT_I8> {
+struct MmaAsm<DT_I8, 16> {
     using Acc = i32x4;
     __device__ static inline void run(Acc &acc, const u32x4 &b, const u32x4 &a) {
         asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+    }
+};
+
+template <>
+struct MmaAsm<DT_BF16, 32> {
+    using Acc = f32x16;
+    __device__ static inline void run(Acc &acc, const u32x4 &b, const u32x4 &a) {
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+    }
+};
+
+template <>
+struct MmaAsm<DT_F16, 32> {
+    using Acc = f32x16;
+    __device__ static inline void run(Acc &acc, const u32x4 &b, const u32x4 &a) {
+        asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+    }
+};
+
+template <>
+struct MmaAsm<DT_I8, 32> {
+    using Acc = i32x16;
+    __device__ static inline void run(Acc &acc, const u32x4 &b, const u32x4 &a) {
+        asm volatile("v_mfma_i32_32x32x32_i8 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
     }
 };
 
@@ -223,42 +254,52 @@ struct DmaLoader {
 };
 
 // LDS fragment reads.  KC: ds_read_b128 of a K-contiguous tile; MC: two
-// transposing reads of an M/N-contiguous tile of extent R.  Both give lane l
-// the K-run {8*(l/16) .. +7} (16-bit) or {16*(l/16) .. +15} (int8) of
-// sub-step ks for row/column (l % 16) of 16-block i -- the operand layout of
-// the 16x16x32 (16-bit) and 16x16x64 (int8) MFMAs.  NB: 16-blocks per wave.
-template <int ES, bool MC, int R, int NB>
+// transposing reads of an M/N-contiguous tile of extent R.  A K-tile (128
+// bytes of K) holds NKS k-steps of one MFMA each.  MS = 16: lane l gets the
+// K-run {8*(l/16) .. +7} (16-bit) or {16*(l/16) .. +15} (int8) of k-step ks
+// for row/column (l % 16) of 16-block i -- the operand layout of the
+// 16x16x32 and 16x16x64 MFMAs.  MS = 32: lane l gets the K-run
+// {8*(l/32) .. +7} / {16*(l/32) .. +15} for row/column (l % 32) of 32-block
+// i (32x32x16, 32x32x32).  NB: blocks per wave.
+template <int ES, bool MC, int R, int NB, int MS>
 struct FragReader {
     static constexpr int RB = R * ES;   // MC: LDS row bytes
-    int base[MC ? NB : 2];              // lane byte offsets inside an operand tile
+    static constexpr int NKS = MS == 16 ? 2 : 4;   // k-steps per K-tile
+    int base[MC ? NB : NKS];            // lane byte offsets inside an operand tile
 
     __device__ inline void init(int lane, int blk0) {
         const int l16 = lane & 15, g = lane >> 4;
         if constexpr (MC) {
+            // the transposing reads serve 16 lanes each: with MS = 32 lane
+            // group g covers k-half g / 2 and column half g % 2 of the block
+            const int kg = MS == 16 ? g : g >> 1;
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-                const int seg = blk0 / 16 + j;
+                const int seg = blk0 / 16 + (MS == 16 ? j : 2 * j + (g & 1));
                 if constexpr (ES == 2) {
-                    const int k = 8 * g + (l16 >> 2);
+                    const int k = 8 * kg + (l16 >> 2);
                     base[j] = k * RB + ((seg ^ swz_mc<2, RB>(k)) << 5) + ((lane & 3) << 3);
                 } else {
-                    const int k = 16 * g + (l16 >> 1);
+                    const int k = 16 * kg + (l16 >> 1);
                     base[j] = k * RB + ((seg ^ swz_mc<1, RB>(k)) << 4) + ((lane & 1) << 3);
                 }
             }
         } else {
+            const int row = MS == 16 ? l16 : (lane & 31);
+            const int part = MS == 16 ? g : lane >> 5;      // 16-byte chunk of the k-step
+            constexpr int CPS = MS == 16 ? 4 : 2;           // chunks per k-step
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                base[ks] = (blk0 + l16) * kLdsRowBytes + (((ks * 4 + g) ^ swz_kc(l16)) << 4);
+            for (int ks = 0; ks < NKS; ++ks)
+                base[ks] = (blk0 + row) * kLdsRowBytes + (((ks * CPS + part) ^ swz_kc(row)) << 4);
         }
     }
 
     // tile: LDS byte address of the operand tile.
     __device__ inline void read(uint32_t tile, int ks, int i, u32x4 &out) const {
         if constexpr (MC) {
-            // rows advance by 32 (16-bit) / 64 (int8) per sub-step, by 4 / 8
-            // for the second half of the K-run (the swizzles read neither bit)
-            constexpr int KS_ROWS = ES == 2 ? 32 : 64, H_ROWS = ES == 2 ? 4 : 8;
+            // rows advance by the k of one k-step per step, by 4 / 8 for the
+            // second half of the K-run (the swizzles read none of those bits)
+            constexpr int KS_ROWS = (ES == 2 ? 32 : 64) * 16 / MS, H_ROWS = ES == 2 ? 4 : 8;
             const uint32_t p = tile + base[i] + ks * KS_ROWS * RB;
             i32x2 lo, hi;
             if constexpr (ES == 2) {
@@ -273,7 +314,7 @@ struct FragReader {
             }
             out = u32x4{(u32)lo[0], (u32)lo[1], (u32)hi[0], (u32)hi[1]};
         } else {
-            out = *(const TCG_LDS u32x4 *)(size_t)(tile + base[ks] + i * 16 * kLdsRowBytes);
+            out = *(const TCG_LDS u32x4 *)(size_t)(tile + base[ks] + i * MS * kLdsRowBytes);
         }
     }
 };
@@ -293,9 +334,10 @@ constexpr int EPI_PLAIN = 0, EPI_BETA = 1, EPI_FUSED = 2;
 
 // BM x BN tile, NW waves (2 along M, NW/2 along N), OCC workgroups per CU;
 // EPI: one of the epilogue variants above; NST LDS stages (2 or 4): tiles
-// kt+1 .. kt+NST-1 are in flight while tile kt is computed.
+// kt+1 .. kt+NST-1 are in flight while tile kt is computed; MS: the MFMA
+// output block (16 or 32).
 template <int DT, bool TA, bool TB, int OUT, int BM, int BN, int NW, int OCC, bool KMASK,
-          int EPI, int NST>
+          int EPI, int NST, int MS>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(NW / 4 * OCC, NW / 4 * OCC)))
 void gemm_dma_kernel(const GemmArgs args) {
@@ -306,9 +348,13 @@ void gemm_dma_kernel(const GemmArgs args) {
     constexpr bool A_MC = TA, B_MC = !TB;
     // waves: 2 along M, NW/2 along N; each owns WTM x WTN of C
     constexpr int WNW = NW / 2, WTM = BM / 2, WTN = BN / WNW;
-    constexpr int FM = WTM / 16, FN = WTN / 16;
-    constexpr int QN = FM * FN;         // MFMAs per wave and sub-step
-    constexpr int NR = FM + FN;         // fragment reads per sub-step
+    static_assert(MS == 16 || MS == 32, "16x16 or 32x32 MFMA blocks");
+    constexpr int FM = WTM / MS, FN = WTN / MS;
+    static_assert(FM >= 1 && FN >= 1, "the wave tile holds whole MFMA blocks");
+    // a K-tile is two sub-steps (one barrier between them) of KSUB k-steps
+    constexpr int KSUB = MS == 16 ? 1 : 2;
+    constexpr int QN = KSUB * FM * FN;  // MFMAs per wave and sub-step
+    constexpr int NR = KSUB * (FM + FN);   // fragment reads per sub-step
     // The loads are issued by 4 waves: all of them with 4 waves; with 8, the
     // second four only, so that while a loading wave waits to issue a load
     // the other wave on its SIMD keeps the matrix core busy.
@@ -319,7 +365,7 @@ void gemm_dma_kernel(const GemmArgs args) {
     constexpr int ND = LPA + LPB;                       // ... and tile
     constexpr int A_BYTES = BM * kLdsRowBytes;          // [A tile | B tile]
     constexpr int STAGE = (BM + BN) * kLdsRowBytes;
-    using Mma = MmaAsm<DT>;
+    using Mma = MmaAsm<DT, MS>;
     using Acc = typename Mma::Acc;
 
     static_assert(NST == 2 || NST == 4, "2 or 4 stages");
@@ -350,8 +396,8 @@ void gemm_dma_kernel(const GemmArgs args) {
     LoadB lb;
     la.init(dwave, lane, args.lda * ES);
     lb.init(dwave, lane, args.ldb * ES);
-    FragReader<ES, A_MC, BM, FM> fa;
-    FragReader<ES, B_MC, BN, FN> fb;
+    FragReader<ES, A_MC, BM, FM, MS> fa;
+    FragReader<ES, B_MC, BN, FN, MS> fb;
     fa.init(lane, wm * WTM);
     fb.init(lane, wn * WTN);
 
@@ -389,14 +435,23 @@ void gemm_dma_kernel(const GemmArgs args) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+        for (int j = 0; j < FN; ++j) acc[i][j] = Acc{};
 
-    u32x4 a0[FM], b0[FN], a1[FM], b1[FN];
+    // fragments of one sub-step: [k-step of the sub-step][block]
+    u32x4 a0[KSUB][FM], b0[KSUB][FN], a1[KSUB][FM], b1[KSUB][FN];
 
-    // fragment read number r (0 .. NR-1) of sub-step ks: B blocks, then A
-    auto read = [&](uint32_t stage, int ks, int r, u32x4 (&af)[FM], u32x4 (&bf)[FN]) {
-        if (r < FN) fb.read(stage + A_BYTES, ks, r, bf[r]);
-        else fa.read(stage, ks, r - FN, af[r - FN]);
+    // fragment read number r (0 .. NR-1) of sub-step sub: per k-step, B
+    // blocks, then A
+    auto read = [&](uint32_t stage, int sub, int r, u32x4 (&af)[KSUB][FM],
+                    u32x4 (&bf)[KSUB][FN]) {
+        const int kk = r / (FM + FN), rr = r % (FM + FN), ks = sub * KSUB + kk;
+        if (rr < FN) fb.read(stage + A_BYTES, ks, rr, bf[kk][rr]);
+        else fa.read(stage, ks, rr - FN, af[kk][rr - FN]);
+    };
+    // MFMA number q (0 .. QN-1) of a sub-step: k-step major
+    auto mma = [&](int q, const u32x4 (&af)[KSUB][FM], const u32x4 (&bf)[KSUB][FN]) {
+        const int kk = q / (FM * FN), qq = q % (FM * FN);
+        Mma::run(acc[qq / FN][qq % FN], bf[kk][qq % FN], af[kk][qq / FN]);
     };
 
     // Sub-step 0 of the tile in `cur`: MFMAs on (a0, b0) and the reads of
@@ -404,7 +459,7 @@ void gemm_dma_kernel(const GemmArgs args) {
     auto sub0 = [&](uint32_t cur) {
 #pragma unroll
         for (int q = 0; q < QN; ++q) {
-            Mma::run(acc[q / FN][q % FN], b0[q % FN], a0[q / FN]);
+            mma(q, a0, b0);
 #pragma unroll
             for (int r = op_begin(q, NR, QN); r < op_begin(q + 1, NR, QN); ++r)
                 read(cur, 1, r, a1, b1);
@@ -417,7 +472,7 @@ void gemm_dma_kernel(const GemmArgs args) {
     auto sub1 = [&](uint32_t cur, uint32_t nxt, const TileSrc &s) {
 #pragma unroll
         for (int q = 0; q < QN; ++q) {
-            Mma::run(acc[q / FN][q % FN], b1[q % FN], a1[q / FN]);
+            mma(q, a1, b1);
 #pragma unroll
             for (int o = op_begin(q, ND + NR, QN); o < op_begin(q + 1, ND + NR, QN); ++o) {
                 // o -> (load or read, index): alternate while both remain
@@ -481,9 +536,15 @@ void gemm_dma_kernel(const GemmArgs args) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) asm volatile("" : "+a"(acc[i][j]));
 
-    // ---- epilogue: lane holds C[m][n .. n+3] of each 16x16 block
-    const int ml0 = wm * WTM + (lane & 15);
-    const int nl0 = wn * WTN + 4 * (lane >> 4);
+    // ---- epilogue: the lane holds NG groups of 4 consecutive columns of one
+    // C row per block (the B block is the MFMA's first operand): with MS = 16
+    // row l % 16, columns 4 (l / 16) + 0..3; with MS = 32 row l % 32,
+    // columns 8 q + 4 (l / 32) + 0..3 for group q -- accumulators 4q .. 4q+3
+    constexpr int NG = MS == 16 ? 1 : 4;
+    auto ml_of = [&](int i) { return wm * WTM + i * MS + (lane & (MS - 1)); };
+    auto nl_of = [&](int j, int q) {
+        return wn * WTN + j * MS + (MS == 16 ? 4 * (lane >> 4) : 8 * q + 4 * (lane >> 5));
+    };
     if constexpr (OUT == OUT_PARTIAL) {
         // raw fp32 / int32 partial sums of this K slice: workspace plane g
         char *wsb = static_cast<char *>(args.ws) +
@@ -493,21 +554,23 @@ void gemm_dma_kernel(const GemmArgs args) {
         const bool vec = (N % 4) == 0;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-            const int ml = ml0 + i * 16;
+            const int ml = ml_of(i);
             if (m0 + ml >= M) continue;
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int nl = nl0 + j * 16;
-                const int nvalid = N - (n0 + nl);
-                if (nvalid <= 0) continue;
-                int v[4];
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if constexpr (DT == DT_I8) v[e] = acc[i][j][e];
-                    else v[e] = as_i32(acc[i][j][e]);
+                for (int q = 0; q < NG; ++q) {
+                    const int nl = nl_of(j, q);
+                    const int nvalid = N - (n0 + nl);
+                    if (nvalid <= 0) continue;
+                    int v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if constexpr (DT == DT_I8) v[e] = acc[i][j][4 * q + e];
+                        else v[e] = as_i32(acc[i][j][4 * q + e]);
+                    }
+                    store_i4(rw, (ml * N + nl) * 4, nvalid, vec, v);
                 }
-                store_i4(rw, (ml * N + nl) * 4, nvalid, vec, v);
-            }
         }
         return;
     }
@@ -558,21 +621,36 @@ void gemm_dma_kernel(const GemmArgs args) {
     const bool interior = vec && n0 + BN <= N;
     // fused epilogue: act(acc * (alpha * scale) + bias), with bias and
     // alpha * scale of the lane's columns read from LDS
+    // (MS = 32: a lane has 16 column groups; the loops run column groups
+    // outside so that only one group's bias and scales are live)
     [[maybe_unused]] auto fused_interior = [&](auto act_tag) {
         constexpr int ACT = decltype(act_tag)::value;
+        auto one = [&](int i, int j, int q, const float (&b)[4], const float (&sa)[4]) {
+            float v[4];
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int ml = ml0 + i * 16;
+            for (int e = 0; e < 4; ++e)
+                v[e] = act1<ACT>(__builtin_fmaf((float)acc[i][j][4 * q + e], sa[e], b[e]));
+            store_c4<OUT>(rc, (ml_of(i) * ldc + nl_of(j, q)) * CES, 4, true, v);
+        };
+        if constexpr (MS == 16) {
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int nl = nl0 + j * 16;
-                float b[4], sa[4], v[4];
-                read_epi4(epi_smem, BN, nl, b, sa);
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    v[q] = act1<ACT>(__builtin_fmaf((float)acc[i][j][q], sa[q], b[q]));
-                store_c4<OUT>(rc, (ml * ldc + nl) * CES, 4, true, v);
-            }
+                for (int j = 0; j < FN; ++j) {
+                    float b[4], sa[4];
+                    read_epi4(epi_smem, BN, nl_of(j, 0), b, sa);
+                    one(i, j, 0, b, sa);
+                }
+        } else {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < NG; ++q) {
+                    float b[4], sa[4];
+                    read_epi4(epi_smem, BN, nl_of(j, q), b, sa);
+#pragma unroll
+                    for (int i = 0; i < FM; ++i) one(i, j, q, b, sa);
+                }
         }
     };
     if constexpr (EPI_LDS > 1) {
@@ -587,22 +665,24 @@ void gemm_dma_kernel(const GemmArgs args) {
         if (interior) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
-                const int ml = ml0 + i * 16;
+                const int ml = ml_of(i);
 #pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const int off = (ml * ldc + nl0 + j * 16) * CES;
-                    if constexpr (OUT == DT_I32) {
-                        int v[4];
+                for (int j = 0; j < FN; ++j)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e];
-                        store_i4(rc, off, 4, true, v);
-                    } else {
-                        float v[4];
+                    for (int q = 0; q < NG; ++q) {
+                        const int off = (ml * ldc + nl_of(j, q)) * CES;
+                        if constexpr (OUT == DT_I32) {
+                            int v[4];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] = alpha * (float)acc[i][j][e];
-                        store_c4<OUT>(rc, off, 4, true, v);
+                            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+                            store_i4(rc, off, 4, true, v);
+                        } else {
+                            float v[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) v[e] = alpha * (float)acc[i][j][4 * q + e];
+                            store_c4<OUT>(rc, off, 4, true, v);
+                        }
                     }
-                }
             }
             return;
         }
@@ -613,63 +693,78 @@ void gemm_dma_kernel(const GemmArgs args) {
         const float *lds_epi = epi_smem;
         // row blocks outside, as in the plain epilogue, so the stores of one
         // row's column blocks follow each other and complete whole lines
+        auto one = [&](int i, int j, int q, const float (&b)[4], const float (&sa)[4]) {
+            const int ml = ml_of(i), nl = nl_of(j, q);
+            const int nvalid = N - (n0 + nl);
+            if (m0 + ml >= M || nvalid <= 0) return;
+            float v[4];
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int ml = ml0 + i * 16;
-            if (m0 + ml >= M) continue;
+            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+            finish4_fused<OUT>(rc, (ml * ldc + nl) * CES, nvalid, vec, beta, v, ep, b, sa);
+        };
+        if constexpr (MS == 16) {
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int nl = nl0 + j * 16;
-                const int nvalid = N - (n0 + nl);
-                if (nvalid <= 0) continue;
-                float b[4], sa[4], v[4];
-                read_epi4(lds_epi, BN, nl, b, sa);
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) v[q] = acc[i][j][q];
-                finish4_fused<OUT>(rc, (ml * ldc + nl) * CES, nvalid, vec, beta, v, ep, b, sa);
-            }
+                for (int j = 0; j < FN; ++j) {
+                    float b[4], sa[4];
+                    read_epi4(lds_epi, BN, nl_of(j, 0), b, sa);
+                    one(i, j, 0, b, sa);
+                }
+        } else {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < NG; ++q) {
+                    float b[4], sa[4];
+                    read_epi4(lds_epi, BN, nl_of(j, q), b, sa);
+#pragma unroll
+                    for (int i = 0; i < FM; ++i) one(i, j, q, b, sa);
+                }
         }
         return;
     }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-        const int ml = ml0 + i * 16;
+        const int ml = ml_of(i);
         if (m0 + ml >= M) continue;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int nl = nl0 + j * 16;
-            const int nvalid = N - (n0 + nl);
-            if (nvalid <= 0) continue;
-            const int off = (ml * ldc + nl) * CES;
-            if constexpr (OUT == DT_I32) {
-                int v[4];
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e];
-                store_i4(rc, off, nvalid, vec, v);
-            } else if constexpr (OUT != OUT_PARTIAL) {
-                float v[4];
+            for (int q = 0; q < NG; ++q) {
+                const int nl = nl_of(j, q);
+                const int nvalid = N - (n0 + nl);
+                if (nvalid <= 0) continue;
+                const int off = (ml * ldc + nl) * CES;
+                if constexpr (OUT == DT_I32) {
+                    int v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e];
-                if constexpr (EPI == EPI_BETA && (OUT == DT_F16 || OUT == DT_BF16)) {
-                    if (c_lds) {
-                        // C_old from the LDS image (8 bytes: 4 values)
-                        const int q = (nl * 2) / 16;
-                        const uint32_t a = lds + ml * CRB + ((q ^ ((ml & 15) * CSW)) << 4) +
-                                           ((nl * 2) & 15);
-                        const u32x2 w = *(const TCG_LDS u32x2 *)(size_t)a;
+                    for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+                    store_i4(rc, off, nvalid, vec, v);
+                } else if constexpr (OUT != OUT_PARTIAL) {
+                    float v[4];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const u32 h = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                            const float old = OUT == DT_BF16 ? from_bf16_bits(h) : from_f16_bits(h);
-                            v[e] = __builtin_fmaf(beta, old, v[e] * alpha);
+                    for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+                    if constexpr (EPI == EPI_BETA && (OUT == DT_F16 || OUT == DT_BF16)) {
+                        if (c_lds) {
+                            // C_old from the LDS image (8 bytes: 4 values)
+                            const int cq = (nl * 2) / 16;
+                            const uint32_t a = lds + ml * CRB + ((cq ^ ((ml & 15) * CSW)) << 4) +
+                                               ((nl * 2) & 15);
+                            const u32x2 w = *(const TCG_LDS u32x2 *)(size_t)a;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const u32 h = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                                const float old = OUT == DT_BF16 ? from_bf16_bits(h) : from_f16_bits(h);
+                                v[e] = __builtin_fmaf(beta, old, v[e] * alpha);
+                            }
+                            store_c4<OUT>(rc, off, 4, true, v);
+                            continue;
                         }
-                        store_c4<OUT>(rc, off, 4, true, v);
-                        continue;
                     }
+                    finish4<OUT>(rc, off, nvalid, vec, alpha, beta, v);
                 }
-                finish4<OUT>(rc, off, nvalid, vec, alpha, beta, v);
             }
-        }
     }
 }
 
