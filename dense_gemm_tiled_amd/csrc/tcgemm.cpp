@@ -235,12 +235,16 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // The direct-to-LDS kernel takes 16-bit and int8 inputs.  It moves 16-byte
 // chunks, so an operand feeds it as it is when its row pitch, its batch
-// stride and its rows themselves are whole chunks: the loads zero whole
-// chunks past K, and no chunk may straddle the end of the operand, where a
-// range-checked load would not return the valid part.  Any other operand is
-// first copied into a packed layout in the workspace (rows padded to 16
-// bytes with zeros; pack_rows_kernel) -- and so is one whose base pointer is
-// not 16-byte aligned, which only the launch can see.
+// stride, its base pointer and its rows themselves are whole chunks: the
+// loads zero whole chunks past K, and no chunk may straddle the end of the
+// operand, where a range-checked load would not return the valid part.  Any
+// other operand is first copied into a packed layout in the workspace (rows
+// padded to 16 bytes with zeros; pack_rows_kernel).  The loads do take
+// unaligned addresses, so rows of whole chunks at an odd pitch or base could
+// be read in place -- but measured on the int8 ragged shape (B rows of 4096
+// bytes at a pitch of 4099) the GEMM kernel then ran 13.7 us longer than
+// the 10.5 us packing pass it saves.  Tuning knob: TCGEMM_PACK_UNALIGNED=0
+// reads such operands in place.
 bool dma_types(const Problem &p) { return p.dt == TC_F16 || p.dt == TC_BF16 || p.dt == TC_I8; }
 
 // Tile classes whose kernel can write split-K partial sums.
@@ -256,12 +260,19 @@ void operand_shape(const Problem &p, int w, int64_t *rows, int64_t *cols) {
     *cols = mc ? mn : p.K;
 }
 
-bool operand_dma_ready(const Problem &p, int w) {
+bool pack_unaligned() {
+    const char *env = getenv("TCGEMM_PACK_UNALIGNED");
+    return !env || atoi(env) != 0;
+}
+
+// aligned: the operand's base pointer is 16-byte aligned.
+bool operand_dma_ready(const Problem &p, int w, bool aligned) {
     const int es = dt_size(p.dt);
     const int64_t ld = w == 0 ? p.lda : p.ldb, stride = w == 0 ? p.stride_a : p.stride_b;
     int64_t rows, cols;
     operand_shape(p, w, &rows, &cols);
-    return (ld * es) % 16 == 0 && (stride * es) % 16 == 0 && (cols * es) % 16 == 0;
+    if ((cols * es) % 16 != 0) return false;
+    return !pack_unaligned() || ((ld * es) % 16 == 0 && (stride * es) % 16 == 0 && aligned);
 }
 
 int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
@@ -279,7 +290,7 @@ void layout_workspace(const Problem &p, Plan *pl, const bool aligned[2]) {
     const int es = dt_size(p.dt);
     int64_t off = pl->splits > 1 ? align_up(pl->splits * p.batch * (int64_t)p.M * p.N * 4, 256) : 0;
     for (int w = 0; w < 2; ++w) {
-        pl->pack[w] = is_dma_class(pl->cls) && (!operand_dma_ready(p, w) || !aligned[w]);
+        pl->pack[w] = is_dma_class(pl->cls) && !operand_dma_ready(p, w, aligned[w]);
         pl->pack_pitch[w] = pl->pack_stride[w] = pl->pack_off[w] = 0;
         if (w == 1 && thin_transposes_b(p, *pl)) {
             // thin kernel: B^T, N rows of K values

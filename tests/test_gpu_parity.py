@@ -191,10 +191,13 @@ def test_dma_kernel_packed_operands(a, c, ta, tb, tile):
     assert tg.last_kernel().startswith("pack_a+pack_b+gemm_"), tg.last_kernel()
 
 
+@pytest.mark.parametrize("pack", [True, False], ids=["packed", "in_place"])
 @pytest.mark.parametrize("a,c", [("bf16", "f32"), ("f16", "f16"), ("i8", "i32")])
-def test_dma_kernel_misaligned_base_pointers(a, c):
+def test_dma_kernel_misaligned_base_pointers(a, c, pack):
     """A and B one element past a 16-byte boundary (pitches aligned): the
-    launch packs both; the split-K variant too."""
+    direct-to-LDS loads read them in place at unaligned addresses, or, with
+    unaligned operands packed, the launch packs both; the split-K variant
+    too."""
     import dense_gemm_tiled_amd as tg
     p = problem(a, c, 512, 384, 256, True, False)
     A, B, C = workloads.make_inputs(p)
@@ -202,16 +205,21 @@ def test_dma_kernel_misaligned_base_pointers(a, c):
     for envs, want in (({"TCGEMM_TILE": "dma128"}, "_128x128_dma"),
                        ({"TCGEMM_TILE": "dma128", "TCGEMM_SPLITS": 3}, "_128x128_dma+splitk_reduce"),
                        ({"TCGEMM_TILE": "dma"}, "_256x256_dma")):
+        envs = dict(envs, TCGEMM_PACK_UNALIGNED=1 if pack else 0)
         say("GPU case: misaligned", a, c, envs)
         with env(**envs):
             got = run_library(p, A, B, C, misalign=True)
-        assert tg.last_kernel().startswith("pack_a+pack_b+") and tg.last_kernel().endswith(want)
+        assert tg.last_kernel().startswith("pack_a+pack_b+") == pack, tg.last_kernel()
+        assert pack or "pack" not in tg.last_kernel(), tg.last_kernel()
+        assert tg.last_kernel().endswith(want), tg.last_kernel()
         compare(p, got, ref, C_in=C, label="misaligned %s" % envs)
 
 
-def test_dma128_split_k_packed_shared_operand():
+@pytest.mark.parametrize("pack", [True, False], ids=["packed", "in_place"])
+def test_dma128_split_k_packed_shared_operand(pack):
     """Batched split-K with a 2-D A shared by every problem (batch stride 0)
-    and an odd lda, so the shared A is packed once."""
+    and an odd lda: with unaligned pitches packed, the shared A is packed
+    once; by default its rows (whole 16-byte chunks) are read in place."""
     import torch
     import dense_gemm_tiled_amd as tg
     M, N, K, batch = 136, 200, 2056, 3
@@ -222,39 +230,49 @@ def test_dma128_split_k_packed_shared_operand():
     a = to_dev(A, "bf16")[:, :K]
     b = torch.stack([to_dev(x, "bf16") for x in bs])
     c = torch.zeros(batch, M, N, dtype=torch.float32, device="cuda")
-    say("GPU case: shared packed A split-K")
-    with env(TCGEMM_SPLITS=4):
+    say("GPU case: shared A split-K, packed:", pack)
+    with env(TCGEMM_SPLITS=4, TCGEMM_PACK_UNALIGNED=1 if pack else 0):
         tg.gemm(a, b, c)
     torch.cuda.synchronize()
-    assert tg.last_kernel() == "pack_a+gemm_bf16_nn_128x128_dma4+splitk_reduce", tg.last_kernel()
+    assert tg.last_kernel() == ("pack_a+" if pack else "") + \
+        "gemm_bf16_nn_128x128_dma4+splitk_reduce", tg.last_kernel()
     got = from_dev(c, "f32")
     for z in range(batch):
         ref = oracle_full(p0, A, bs[z], np.zeros((M, N), np.float32))
         compare(p0, got[z], ref, label="shared A z=%d" % z)
 
 
-@pytest.mark.parametrize("a,c,M,N,K,batch,ta,tb,strip", [
+@pytest.mark.parametrize("a,c,M,N,K,batch,ta,tb,strip,pack", [
     # column strip of 8 on the thin-output kernel
-    ("bf16", "bf16", 4096, 4104, 1024, 1, False, False, "|transpose_b+gemm_bf16_nn_thin"),
+    ("bf16", "bf16", 4096, 4104, 1024, 1, False, False, "|transpose_b+gemm_bf16_nn_thin", True),
     # row strip of 4 rows, run as its transposed product (the small-M route,
-    # A gathered); the main part packs A (M-contiguous rows of 4100 halves)
-    ("f16", "f32", 4100, 4096, 192, 1, True, True, "_dma|transpose_a+gemv_f16_tt_thin"),
+    # A gathered); the main part packs A (M-contiguous rows of 4096 of 4100
+    # halves: an odd pitch)
+    ("f16", "f32", 4100, 4096, 192, 1, True, True, "_dma|transpose_a+gemv_f16_tt_thin", True),
     # row strip of 40 rows (too many for the small-M route)
-    ("bf16", "bf16", 4136, 4096, 192, 1, True, True, "_dma|gemm_bf16_tt_64x64"),
-    # batched column strip; the main part packs B (rows of 2051 bytes) and
-    # writes the strip's B^T on the way
-    ("i8", "i32", 2048, 2051, 256, 4, False, False, "_dma|gemm_i8_nn_thin"),
+    ("bf16", "bf16", 4136, 4096, 192, 1, True, True, "_dma|gemm_bf16_tt_64x64", True),
+    # batched column strip; with B (2048 of 2051 bytes per row) read in
+    # place, the strip gathers its B^T ...
+    ("i8", "i32", 2048, 2051, 256, 4, False, False, "_dma|transpose_b+gemm_i8_nn_thin", False),
+    # ... or, by default, the main part packs B and writes the strip's B^T
+    # on the way
+    ("i8", "i32", 2048, 2051, 256, 4, False, False, "pack_b+gemm_i8_nn_256x256_dma|gemm_i8_nn_thin",
+     True),
     # the same with 16-bit elements: rows of 4100 halves, a 4-column strip
-    ("f16", "f32", 4096, 4100, 256, 1, False, False, "pack_b+gemm_f16_nn_256x256_dma|gemm_f16_nn_thin"),
+    ("f16", "f32", 4096, 4100, 256, 1, False, False,
+     "gemm_f16_nn_256x256_dma|transpose_b+gemm_f16_nn_thin", False),
+    ("f16", "f32", 4096, 4100, 256, 1, False, False,
+     "pack_b+gemm_f16_nn_256x256_dma|gemm_f16_nn_thin", True),
     # strip of 40 columns: split-K on the 4-stage 128x128 tile
-    ("bf16", "f32", 4096, 4136, 1024, 1, False, False, "|gemm_bf16_nn_128x128_dma4+splitk_reduce"),
+    ("bf16", "f32", 4096, 4136, 1024, 1, False, False, "|gemm_bf16_nn_128x128_dma4+splitk_reduce",
+     True),
 ])
-def test_edge_split(a, c, M, N, K, batch, ta, tb, strip):
+def test_edge_split(a, c, M, N, K, batch, ta, tb, strip, pack):
     """A thin ragged strip past the whole 256x256 tiles runs as a second GEMM
     after them; alpha = 0.5 and beta = 1 for floats, so both parts read C."""
     import dense_gemm_tiled_amd as tg
     p = problem(a, c, M, N, K, ta, tb, batch=batch)
-    check(p, "edge split")
+    check(p, "edge split", TCGEMM_PACK_UNALIGNED=1 if pack else 0)
     assert tg.last_kernel().endswith(strip), tg.last_kernel()
 
 
@@ -858,4 +876,12 @@ def test_workload_i8_nn_ragged_bit_exact():
     import dense_gemm_tiled_amd as tg
     p, A, B, C, got = full_case("i8_nn_ragged")
     assert tg.last_kernel() == "pack_b+gemm_i8_nn_256x256_dma|gemm_i8_nn_thin", tg.last_kernel()
-    compare(p, got, oracle_full(p, A, B, C), label=p.name)
+    ref = oracle_full(p, A, B, C)
+    compare(p, got, ref, label=p.name)
+    # the same with B read in place at its 4099-byte pitch (the strip then
+    # gathers its own B^T)
+    with env(TCGEMM_PACK_UNALIGNED=0):
+        got = run_library(p, A, B, C)
+    assert tg.last_kernel() == "gemm_i8_nn_256x256_dma|transpose_b+gemm_i8_nn_thin", \
+        tg.last_kernel()
+    compare(p, got, ref, label=p.name + " in place")

@@ -301,7 +301,9 @@ def test_plan_strip_bt_from_row_packing():
     """An edge split whose main part packs B row by row and whose column
     strip runs on the thin kernel: the packing writes the strip's B^T after
     the main part's packed B (per problem when B is batched), so the strip
-    has no gather pass; a B the main part need not pack keeps the gather."""
+    has no gather pass; a B the main part need not pack keeps the gather
+    (also the B of 2048 bytes at a pitch of 2051 read in place with
+    TCGEMM_PACK_UNALIGNED=0)."""
     p = workloads.Problem("s", 2048, 2051, 256, "i8", "i32", batch=4)
     pl = plan_of(p)
     assert pl["kernel"] == "pack_b+gemm_i8_nn_256x256_dma|gemm_i8_nn_thin", pl["kernel"]
@@ -309,6 +311,14 @@ def test_plan_strip_bt_from_row_packing():
     main_b = 4 * 256 * 2048                       # 4 problems, 256 rows of 2048 packed bytes
     strip_bt = 4 * 3 * 256                        # 4 problems, 3 rows of 256 bytes
     assert pl["workspace_bytes"] == main_b + strip_bt
+    os.environ["TCGEMM_PACK_UNALIGNED"] = "0"
+    try:
+        pl = plan_of(p)
+    finally:
+        del os.environ["TCGEMM_PACK_UNALIGNED"]
+    assert pl["kernel"] == "gemm_i8_nn_256x256_dma|transpose_b+gemm_i8_nn_thin", pl["kernel"]
+    assert pl["launches"] == 3
+    assert pl["workspace_bytes"] == strip_bt
     # a B of whole 16-byte rows is read as it is: the strip gathers its B^T
     q = workloads.Problem("s", 4096, 4104, 1024, "bf16", "bf16")
     assert plan_of(q)["kernel"] == "gemm_bf16_nn_256x256_dma|transpose_b+gemm_bf16_nn_thin"
@@ -336,7 +346,8 @@ def test_plan_dma_eligibility():
     """The direct-to-LDS classes take 16-bit and int8 inputs.  An operand whose
     row pitch, batch stride or row length (K for K-contiguous operands, M or N
     for M/N-contiguous ones) is not a whole number of 16-byte chunks is packed
-    into the workspace first; f32 inputs take the register-staged kernel."""
+    into the workspace first (with TCGEMM_PACK_UNALIGNED=0 only one whose row
+    length is not); f32 inputs take the register-staged kernel."""
     base = workloads.get("bf16_nn_4096")
     assert plan_of(base.with_(K=4096 - 8))["kernel"] == "gemm_bf16_nn_256x256_dma"
     # K = 4092: A rows (K-contiguous) end inside a chunk; B (N-contiguous) is fine
@@ -345,6 +356,12 @@ def test_plan_dma_eligibility():
     assert pl["workspace_bytes"] == 4096 * 8192 and pl["launches"] == 2
     assert plan_of(base.with_(lda=4096 + 4))["kernel"] == "pack_a+gemm_bf16_nn_256x256_dma"
     assert plan_of(base.with_(lda=4096 + 8))["kernel"] == "gemm_bf16_nn_256x256_dma"
+    os.environ["TCGEMM_PACK_UNALIGNED"] = "0"
+    try:
+        assert plan_of(base.with_(lda=4096 + 4))["kernel"] == "gemm_bf16_nn_256x256_dma"
+        assert plan_of(base.with_(K=4096 - 4))["kernel"] == "pack_a+gemm_bf16_nn_256x256_dma"
+    finally:
+        del os.environ["TCGEMM_PACK_UNALIGNED"]
     # N = 4100: the last B row would end inside a chunk
     assert plan_of(base.with_(M=3072, N=4100, ldb=4104))["kernel"] == "pack_b+gemm_bf16_nn_256x256_dma"
     # TN: both operands M/N-contiguous, so any K is fine
