@@ -104,6 +104,8 @@ _SIGNATURES = {
     "tc_gemm_batched": (ctypes.c_int, [_VP, ctypes.POINTER(BatchedDescT), _VP, _VP, _VP]),
     "tc_gemm_batched_async": (ctypes.c_int,
                               [_VP, ctypes.POINTER(BatchedDescT), _VP, _VP, _VP, _VP]),
+    "tc_gemm_batched_async_noalloc": (ctypes.c_int,
+                                      [_VP, ctypes.POINTER(BatchedDescT), _VP, _VP, _VP, _VP]),
     "tc_gemm_epilogue": (ctypes.c_int, [_VP, ctypes.POINTER(BatchedDescT),
                                         ctypes.POINTER(EpilogueT), _VP, _VP, _VP]),
     "tc_gemm_epilogue_async": (ctypes.c_int, [_VP, ctypes.POINTER(BatchedDescT),

@@ -1,6 +1,16 @@
-// epilogue_kernels.hip -- the split-K reduction, the alpha == 0 kernel, and
+// epilogue_kernels.hip -- the split-K reduction, the alpha == 0 kernel, the
+// operand packing, the static scratch of the allocation-free entry point, and
 // the dispatch from (input type, layout) to the per-object launchers.
 #include "gemm_kernel.hpp"
+
+#include <mutex>
+
+// Scratch memory of the allocation-free entry point (split-K partial sums and
+// packed operand copies): one array on every GPU the library runs on, there
+// from the code object's load until the process ends.  Host code never uses
+// the array's name as an address; it asks for the device address once per
+// device (tcg_static_scratch) and passes that to kernels.
+static __device__ __align__(256) char scratch[tcg::kStaticScratchBytes];
 
 namespace tcg {
 namespace {
@@ -227,6 +237,22 @@ hipError_t tcg_launch_splitk_reduce(const EpilogueArgs &args, hipStream_t stream
     if (blocks <= 0 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, args);
     return hipGetLastError();
+}
+
+hipError_t tcg_static_scratch(int device, void **ptr) {
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    if (device < 0 || device >= kMaxDevices || !ptr) return hipErrorInvalidValue;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[device]) {
+        // the caller made `device` current: its own copy of the array
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[device] = p;
+    }
+    *ptr = addr[device];
+    return hipSuccess;
 }
 
 hipError_t tcg_launch_scale_c(const EpilogueArgs &args, hipStream_t stream) {

@@ -59,6 +59,11 @@ __host__ __device__ constexpr TileShape tile_shape(int cls) {
 constexpr int kLdsRowBytes = 128;      // bytes of K per LDS tile row
 constexpr int kXcds = 8;               // MI355X: 8 XCDs x 32 CUs
 
+// Size of the static scratch array of the allocation-free entry point, and
+// the devices whose addresses of it are cached.
+constexpr int64_t kStaticScratchBytes = 32ll << 20;
+constexpr int kMaxDevices = 64;
+
 // Output selector of the GEMM kernel beyond the element types: raw partial
 // sums of one split-K slice (fp32, or int32 for int8 inputs).
 constexpr int OUT_PARTIAL = 5;
@@ -195,6 +200,9 @@ hipError_t tcg_launch_thin(int dt, int out, const tcg::GemmArgs &args, int64_t g
 // dst_pitch bytes
 hipError_t tcg_launch_thin_pack_bt(const tcg::PackArgs &args, int es, hipStream_t stream);
 const char *tcg_kernel_name(int dt, bool ta, bool tb, int cls);
+// Device address of the static scratch array (kStaticScratchBytes) on
+// `device`, which must be the current device; looked up once per device.
+hipError_t tcg_static_scratch(int device, void **ptr);
 
 // One launcher per (input type, layout) object; each dispatches on (cls, out).
 #define TCG_DECLARE_LAUNCHER(NAME)                                                       \

@@ -730,10 +730,12 @@ tc_status_t create_stream(tc_context *ctx, tc_stream **out, hipStream_t existing
 // sb: a column strip's B^T made by the main part's B packing (null: none);
 // sb_writes: this part is the main part (its B packing writes the B^T), else
 // the strip (its thin kernel reads the B^T, with no gather pass).
+// fixed_ws: the allocation-free call's scratch (null: the stream's
+// workspace, grown here on demand); its size was checked by the caller.
 tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan &plan,
                     const void *A, const void *B, void *C, const Epilogue &epi, bool main_part,
                     std::string *names, std::string *err, const StripBt *sb = nullptr,
-                    bool sb_writes = false) {
+                    bool sb_writes = false, void *fixed_ws = nullptr) {
     Plan pl = plan;
     const bool aligned[2] = {(uintptr_t)A % 16 == 0, (uintptr_t)B % 16 == 0};
     layout_workspace(p, &pl, aligned);   // a misaligned base pointer is packed too
@@ -742,7 +744,8 @@ tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan 
     tc_status_t st;
     const bool use_splitk = p.alpha != 0.0f && pl.splits > 1;
     const bool use_ws = p.alpha != 0.0f && pl.ws_bytes > 0;
-    if (use_ws && (st = ensure_workspace(s, pl.ws_bytes, err)) != TC_OK) return st;
+    if (use_ws && !fixed_ws && (st = ensure_workspace(s, pl.ws_bytes, err)) != TC_OK) return st;
+    char *const wsb = static_cast<char *>(fixed_ws ? fixed_ws : s->ws);
 
     const int ces = dt_size(p.cdt);
     // Four complete C values of a row go as one vector access (16 bytes for
@@ -782,7 +785,7 @@ tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan 
             if (!pl.pack[w]) continue;
             if (w == 1 && thin_transposes_b(p, pl) && bt_ready) {
                 // the main part's B packing wrote this strip's B^T
-                src[1] = static_cast<char *>(s->ws) + sb->off;
+                src[1] = wsb + sb->off;
                 ld[1] = sb->pitch / es;
                 stride[1] = sb->stride / es;
                 extent[1] = (int64_t)p.N * sb->pitch;
@@ -793,7 +796,7 @@ tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan 
                 PackArgs pa;
                 memset(&pa, 0, sizeof pa);
                 pa.src = src[1];
-                pa.dst = static_cast<char *>(s->ws) + pl.pack_off[1];
+                pa.dst = wsb + pl.pack_off[1];
                 pa.src_stride = stride[1] * es;
                 pa.dst_stride = pl.pack_stride[1];
                 pa.src_pitch = ld[1] * es;
@@ -817,7 +820,7 @@ tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan 
             PackArgs pa;
             memset(&pa, 0, sizeof pa);
             pa.src = src[w];
-            pa.dst = static_cast<char *>(s->ws) + pl.pack_off[w];
+            pa.dst = wsb + pl.pack_off[w];
             pa.src_stride = stride[w] * es;
             pa.dst_stride = pl.pack_stride[w];
             pa.src_pitch = ld[w] * es;
@@ -826,7 +829,7 @@ tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan 
             pa.row_bytes = (int32_t)(cols * es);
             pa.batch = stride[w] == 0 ? 1 : p.batch;
             if (w == 1 && sb && sb_writes) {
-                pa.bt = static_cast<char *>(s->ws) + sb->off;
+                pa.bt = wsb + sb->off;
                 pa.bt_stride = sb->stride;
                 pa.bt_pitch = (int32_t)sb->pitch;
                 pa.bt_cols = sb->cols;
@@ -844,7 +847,7 @@ tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan 
         GemmArgs ga;
         memset(&ga, 0, sizeof ga);
         ga.A = src[0]; ga.B = src[1]; ga.C = C;
-        ga.ws = use_splitk ? s->ws : nullptr;
+        ga.ws = use_splitk ? wsb : nullptr;
         ga.stride_a = stride[0]; ga.stride_b = stride[1]; ga.stride_c = p.stride_c;
         ga.a_extent = extent[0];
         ga.b_extent = extent[1];
@@ -884,7 +887,7 @@ tc_status_t enqueue(tc_context *ctx, tc_stream *s, const Problem &p, const Plan 
         if (e == hipSuccess) {
             ctx->dispatches += 1;
             if (use_splitk) {
-                ea.ws = s->ws;
+                ea.ws = wsb;
                 ea.splits = pl.splits;
                 e = tcg_launch_splitk_reduce(ea, s->stream);
                 if (e == hipSuccess) ctx->dispatches += 1;
@@ -944,36 +947,54 @@ tc_status_t validate_epilogue(const Problem &p, const tc_epilogue *ep, const voi
 // Validate, plan and enqueue one (batched) GEMM on stream s.
 // Enqueue every part of a planned call (the whole tiles, then the edge strip
 // if the plan splits one off); their kernel names go to *name.
-tc_status_t enqueue_call(tc_context *ctx, tc_stream *s, const Problem &p, const Plan &pl,
-                         const void *A, const void *B, void *C, const Epilogue &epi,
-                         std::string *name, std::string *err) {
+// The operand pointers of part i of a call (the parts of an edge split,
+// or the transposed product of a small-M GEMM, which exchanges A and B).
+const void *part_operand(const Parts &parts, int i, int w, const void *A, const void *B, int es) {
+    const bool from_b = (w == 1) != parts.swap[i];
+    return static_cast<const char *>(from_b ? B : A) + parts.off[i][from_b ? 1 : 0] * es;
+}
+
+// Workspace a call uses with these operand pointers: the largest part's
+// (split-K partials and packed copies, laid out for the pointers' 16-byte
+// alignment), and the strip's B^T when the main part's packing writes it.
+// *sb receives that B^T's placement.
+int64_t call_workspace(const Problem &p, const Plan &pl, const void *A, const void *B,
+                       StripBt *sb) {
+    *sb = StripBt{};
+    if (p.alpha == 0.0f) return 0;
     const Parts parts = split_parts(p, pl);
     const int es = dt_size(p.dt);
-    auto part_a = [&](int i) {
-        return parts.swap[i] ? static_cast<const char *>(B) + parts.off[i][1] * es
-                             : static_cast<const char *>(A) + parts.off[i][0] * es;
-    };
-    auto part_b = [&](int i) {
-        return parts.swap[i] ? static_cast<const char *>(A) + parts.off[i][0] * es
-                             : static_cast<const char *>(B) + parts.off[i][1] * es;
-    };
+    Plan lp[2];
+    int64_t need = 0;
+    for (int i = 0; i < parts.n; ++i) {
+        lp[i] = parts.pl[i];
+        const bool aligned[2] = {(uintptr_t)part_operand(parts, i, 0, A, B, es) % 16 == 0,
+                                 (uintptr_t)part_operand(parts, i, 1, A, B, es) % 16 == 0};
+        layout_workspace(parts.p[i], &lp[i], aligned);
+        if (lp[i].ws_bytes > need) need = lp[i].ws_bytes;
+    }
+    if (parts.n == 2) {
+        *sb = strip_bt(parts, lp[0], lp[1]);
+        if (sb->on && sb->off + sb->bytes > need) need = sb->off + sb->bytes;
+    }
+    return need;
+}
+
+tc_status_t enqueue_call(tc_context *ctx, tc_stream *s, const Problem &p, const Plan &pl,
+                         const void *A, const void *B, void *C, const Epilogue &epi,
+                         std::string *name, std::string *err, void *fixed_ws = nullptr) {
+    const Parts parts = split_parts(p, pl);
+    const int es = dt_size(p.dt);
     // the strip's B^T from the main part's packing, laid out for these
     // pointers (a misaligned base pointer changes what is packed)
     StripBt sb;
-    if (parts.n == 2) {
-        Plan lp[2] = {parts.pl[0], parts.pl[1]};
-        for (int i = 0; i < 2; ++i) {
-            const bool aligned[2] = {(uintptr_t)part_a(i) % 16 == 0, (uintptr_t)part_b(i) % 16 == 0};
-            layout_workspace(parts.p[i], &lp[i], aligned);
-        }
-        sb = strip_bt(parts, lp[0], lp[1]);
-        tc_status_t st;
-        if (sb.on && (st = ensure_workspace(s, sb.off + sb.bytes, err)) != TC_OK) return st;
-    }
+    const int64_t need = call_workspace(p, pl, A, B, &sb);
+    tc_status_t st;
+    if (sb.on && !fixed_ws && (st = ensure_workspace(s, need, err)) != TC_OK) return st;
     for (int i = 0; i < parts.n; ++i) {
         const int ces = dt_size(p.cdt);
-        const void *Ai = part_a(i);
-        const void *Bi = part_b(i);
+        const void *Ai = part_operand(parts, i, 0, A, B, es);
+        const void *Bi = part_operand(parts, i, 1, A, B, es);
         void *Ci = static_cast<char *>(C) + parts.off[i][2] * ces;
         // a column strip's bias and scales start at its first column
         Epilogue epi_i = epi;
@@ -982,8 +1003,8 @@ tc_status_t enqueue_call(tc_context *ctx, tc_stream *s, const Problem &p, const 
             if (epi.scale) epi_i.scale = epi.scale + pl.edge_at;
         }
         if (i) *name += "|";
-        tc_status_t st = enqueue(ctx, s, parts.p[i], parts.pl[i], Ai, Bi, Ci, epi_i, i == 0, name, err,
-                                 sb.on ? &sb : nullptr, i == 0);
+        st = enqueue(ctx, s, parts.p[i], parts.pl[i], Ai, Bi, Ci, epi_i, i == 0, name, err,
+                     sb.on ? &sb : nullptr, i == 0, fixed_ws);
         if (st != TC_OK) return st;
     }
     return TC_OK;
@@ -1084,9 +1105,13 @@ tc_status_t autotune(tc_context *ctx, tc_stream *s, const Problem &p, const void
     return TC_OK;
 }
 
-// Validate, plan and enqueue one (batched) GEMM on stream s.
+// Validate, plan and enqueue one (batched) GEMM on stream s.  noalloc: the
+// allocation-free form -- the workspace is the static scratch array of the
+// current device (a plan that needs more is refused before anything is
+// enqueued), no autotuning, no allocation of any kind.
 tc_status_t run(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A, const void *B,
-                void *C, tc_stream *s, bool sync, const tc_epilogue *ep = nullptr) {
+                void *C, tc_stream *s, bool sync, const tc_epilogue *ep = nullptr,
+                bool noalloc = false) {
     if (!ctx) return TC_ERR_INVALID_ARGUMENT;
     ctx->last_error.clear();
     std::string *err = &ctx->last_error;
@@ -1115,6 +1140,30 @@ tc_status_t run(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A, 
         s = ctx->internal;
     }
     Plan pl;
+    if (noalloc) {
+        make_plan(p, &pl);
+        StripBt sb;
+        const int64_t need = call_workspace(p, pl, A, B, &sb);
+        void *fixed = nullptr;
+        if (need > 0) {
+            if (need > kStaticScratchBytes)
+                return fail(err, TC_ERR_OUT_OF_MEMORY,
+                            "this call needs %lld bytes of scratch (split-K partials and packed "
+                            "operands); the allocation-free entry point has %lld",
+                            (long long)need, (long long)kStaticScratchBytes);
+            const hipError_t e = tcg_static_scratch(ctx->device, &fixed);
+            if (e != hipSuccess) {
+                (void)hipGetLastError();
+                return fail(err, TC_ERR_DEVICE, "static scratch address: %s", hipGetErrorString(e));
+            }
+        }
+        std::string name;
+        if ((st = enqueue_call(ctx, s, p, pl, A, B, C, Epilogue{}, &name, err,
+                               need > 0 ? fixed : nullptr)) != TC_OK)
+            return st;
+        ctx->last_kernel = name;
+        return TC_OK;
+    }
     if (ctx->autotune && p.alpha != 0.0f) {
         // first call of this problem: measure the candidates, then keep the
         // fastest for every later call
@@ -1241,6 +1290,15 @@ tc_status_t tc_gemm_batched_async(tc_context *ctx, const tc_gemm_batched_desc *b
         return TC_ERR_INVALID_ARGUMENT;
     }
     return run(ctx, bd, A, B, C, s, false);
+}
+
+tc_status_t tc_gemm_batched_async_noalloc(tc_context *ctx, const tc_gemm_batched_desc *bd,
+                                          const void *A, const void *B, void *C, tc_stream *s) {
+    if (!s) {
+        if (ctx) ctx->last_error = "stream is NULL";
+        return TC_ERR_INVALID_ARGUMENT;
+    }
+    return run(ctx, bd, A, B, C, s, false, nullptr, true);
 }
 
 tc_status_t tc_gemm_epilogue(tc_context *ctx, const tc_gemm_batched_desc *bd, const tc_epilogue *ep,

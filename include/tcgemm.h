@@ -188,6 +188,26 @@ tc_status_t tc_gemm_batched_async(tc_context *ctx, const tc_gemm_batched_desc *b
                                   const void *A, const void *B, void *C,
                                   tc_stream *s);
 
+/* Allocation-free form of tc_gemm_batched_async, for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid allocation).  Same descriptor, pointers, result and
+ * errors, except:
+ *   - the scratch memory some plans use (split-K partial sums, packed copies
+ *     of operands whose rows are not whole 16-byte chunks) comes from one
+ *     static device array of 32 MiB per GPU, held from the library's load
+ *     until the process ends, instead of the stream's workspace; a call whose
+ *     plan needs more returns TC_ERR_OUT_OF_MEMORY with nothing enqueued
+ *     (tc_gemm_plan's workspace_bytes shows the need for aligned pointers);
+ *   - it never allocates or frees memory (no hipMalloc, no hipFree) and never
+ *     autotunes (the planner's own plan runs).
+ * Every call on one GPU shares that GPU's array and leaves its last contents
+ * there; no kernel relies on the array starting at zero.  Calls that overlap
+ * in time on one GPU (two streams, or two host threads) race on the array:
+ * serialize them.  s may not be NULL. */
+tc_status_t tc_gemm_batched_async_noalloc(tc_context *ctx, const tc_gemm_batched_desc *bd,
+                                          const void *A, const void *B, void *C,
+                                          tc_stream *s);
+
 /* Batched GEMM with the fused epilogue *ep (see tc_epilogue), synchronous.
  * Same descriptor, pointers and errors as tc_gemm_batched, plus:
  * TC_ERR_INVALID_ARGUMENT for a NULL ep, an unknown activation or a negative
