@@ -70,6 +70,10 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 // the 16-byte access does not wrap 32 bits): such a load reads zeros.
 constexpr int kOobOffset = INT32_MIN;
 
+// K-contiguous rows: position of chunk c of row r is c ^ swz_kc(r).  (A
+// swizzle whose 32-lane groups hit 32 distinct 16-byte slots of a 512-byte
+// window left SQ_LDS_BANK_CONFLICT exactly where it was: the counter books
+// about 4 cycles on every 64-lane ds_read_b128, whatever the addresses.)
 __device__ inline int swz_kc(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // M/N-contiguous swizzle for LDS rows of RB bytes (16-bit: 32-byte segments;
@@ -334,8 +338,19 @@ constexpr int EPI_PLAIN = 0, EPI_BETA = 1, EPI_FUSED = 2;
 
 // BM x BN tile, NW waves (2 along M, NW/2 along N), OCC workgroups per CU;
 // EPI: one of the epilogue variants above; NST LDS stages (2 or 4): tiles
-// kt+1 .. kt+NST-1 are in flight while tile kt is computed; MS: the MFMA
-// output block (16 or 32).
+// kt+1 .. kt+NST-1 are in flight while tile kt is computed -- or NST = 5:
+// a ring of five slots of one operand tile each (BM == BN; 160 KiB for the
+// 256 x 256 tile), see below; MS: the MFMA output block (16 or 32).
+//
+// The ring.  Operand tiles are items: item 2t is A of K-tile t, item 2t+1
+// its B, held in slot item % 5.  At the barrier in the middle of K-tile t
+// (after sub-step 0, whose reads fetch the rest of tile t into registers)
+// the slots of items 2t and 2t+1 are free.  Sub-step 0 of tile t loads item
+// 2t+4 (A of tile t+2, into the slot item 2t-1 left at the previous
+// barrier); sub-step 1 loads item 2t+5 (B of tile t+2, into the slot item 2t
+// just left).  So both sub-steps issue half of a tile's loads -- with two
+// stages all of them go out in sub-step 1 -- still with one barrier per
+// K-tile, and tile t+2 has from then to the middle of tile t+1 to land.
 template <int DT, bool TA, bool TB, int OUT, int BM, int BN, int NW, int OCC, bool KMASK,
           int EPI, int NST, int MS>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
@@ -368,9 +383,13 @@ void gemm_dma_kernel(const GemmArgs args) {
     using Mma = MmaAsm<DT, MS>;
     using Acc = typename Mma::Acc;
 
-    static_assert(NST == 2 || NST == 4, "2 or 4 stages");
-    static_assert((NST - 1) * ND <= 63, "loads in flight fit vmcnt");
-    __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
+    static_assert(NST == 2 || NST == 4 || NST == 5, "2 or 4 stages, or the ring of 5 slots");
+    constexpr bool RING = NST == 5;
+    static_assert(!RING || BM == BN, "the ring's slots hold either operand tile");
+    constexpr int SLOT = A_BYTES;                        // ring: one operand tile
+    constexpr int LDS_BYTES = RING ? 5 * SLOT : NST * STAGE;
+    static_assert(RING || (NST - 1) * ND <= 63, "loads in flight fit vmcnt");
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
     const uint32_t lds = (uint32_t)(size_t)(TCG_LDS char *)smem;
 
     const int tid = threadIdx.x;
@@ -421,6 +440,14 @@ void gemm_dma_kernel(const GemmArgs args) {
         s.kv = min(BK, k_hi - k0);
         return s;
     };
+    // ring: load d of an A item (0 .. LPA-1) or a B item (0 .. LPB-1) into
+    // slot address `slot`
+    [[maybe_unused]] auto dma_a = [&](const TileSrc &s, uint32_t slot, int d) {
+        if (loads) dma16(s.ra, slot + (dwave * LPA + d) * 1024, la.template offset<KMASK>(d, s.kv));
+    };
+    [[maybe_unused]] auto dma_b = [&](const TileSrc &s, uint32_t slot, int d) {
+        if (loads) dma16(s.rb, slot + (dwave * LPB + d) * 1024, lb.template offset<KMASK>(d, s.kv));
+    };
     // DMA load number d (0 .. ND-1) of a tile: A first, then B.
     auto dma = [&](const TileSrc &s, uint32_t stage, int d) {
         if (!loads) return;
@@ -442,12 +469,15 @@ void gemm_dma_kernel(const GemmArgs args) {
 
     // fragment read number r (0 .. NR-1) of sub-step sub: per k-step, B
     // blocks, then A
-    auto read = [&](uint32_t stage, int sub, int r, u32x4 (&af)[KSUB][FM],
-                    u32x4 (&bf)[KSUB][FN]) {
+    // (A tile at a_at, B tile at b_at)
+    auto read2 = [&](uint32_t a_at, uint32_t b_at, int sub, int r, u32x4 (&af)[KSUB][FM],
+                     u32x4 (&bf)[KSUB][FN]) {
         const int kk = r / (FM + FN), rr = r % (FM + FN), ks = sub * KSUB + kk;
-        if (rr < FN) fb.read(stage + A_BYTES, ks, rr, bf[kk][rr]);
-        else fa.read(stage, ks, rr - FN, af[kk][rr - FN]);
+        if (rr < FN) fb.read(b_at, ks, rr, bf[kk][rr]);
+        else fa.read(a_at, ks, rr - FN, af[kk][rr - FN]);
     };
+    auto read = [&](uint32_t stage, int sub, int r, u32x4 (&af)[KSUB][FM],
+                    u32x4 (&bf)[KSUB][FN]) { read2(stage, stage + A_BYTES, sub, r, af, bf); };
     // MFMA number q (0 .. QN-1) of a sub-step: k-step major
     auto mma = [&](int q, const u32x4 (&af)[KSUB][FM], const u32x4 (&bf)[KSUB][FN]) {
         const int kk = q / (FM * FN), qq = q % (FM * FN);
@@ -489,17 +519,105 @@ void gemm_dma_kernel(const GemmArgs args) {
         }
     };
 
+    // The ring's sub-steps: MFMAs on one register set, NR fragment reads into
+    // the other, and NL loads, the reads and loads alternating while both
+    // remain (loads first).  rd(r) and ld(d) issue read r and load d.
+    [[maybe_unused]] auto ring_sub = [&](auto nl_tag, const u32x4 (&af)[KSUB][FM],
+                                         const u32x4 (&bf)[KSUB][FN], auto &&rd, auto &&ld) {
+        constexpr int NL = decltype(nl_tag)::value;
+#pragma unroll
+        for (int q = 0; q < QN; ++q) {
+            mma(q, af, bf);
+#pragma unroll
+            for (int o = op_begin(q, NL + NR, QN); o < op_begin(q + 1, NL + NR, QN); ++o) {
+                const int pair = 2 * (NL < NR ? NL : NR);
+                if (o < pair) {
+                    if ((o & 1) == 0) ld(o >> 1);
+                    else rd(o >> 1);
+                } else if (NL > NR) {
+                    ld(o - pair + NR);
+                } else {
+                    rd(o - pair + NL);
+                }
+            }
+        }
+    };
+
     // fused epilogue: the tile's bias and alpha * scale go into LDS of their
     // own at the start, their loads issued ahead of the first tiles' (the
     // epilogue then reads them with no wait; the loop's barriers publish them)
     constexpr int EPI_LDS = EPI == EPI_FUSED && OUT != DT_I32 && OUT != OUT_PARTIAL ? 2 * BN : 1;
-    __shared__ __attribute__((aligned(16))) float epi_smem[EPI_LDS];
+    // (declared only where used: the ring takes all 160 KiB of LDS, and the
+    // fused ring kernel stages them in its first slot once the loop is done)
+    float *epi_smem = nullptr;
+    if constexpr (EPI_LDS > 1 && RING) {
+        epi_smem = reinterpret_cast<float *>(smem);
+    } else if constexpr (EPI_LDS > 1) {
+        __shared__ __attribute__((aligned(16))) float epi_buf[EPI_LDS];
+        epi_smem = epi_buf;
+    }
     [[maybe_unused]] float epi_b = 0.f, epi_s = 1.f;
     if constexpr (EPI_LDS > 1) {
         if (tid < BN)
             load_epi1<OUT>(make_epi<OUT>(args, z, N), n0 + tid, N, epi_b, epi_s);
     }
-    if (nkt > 0) {
+    if constexpr (RING) {
+      if (nkt > 0) {
+        // items 0 .. 3 (tiles 0 and 1) into slots 0 .. 3
+        const TileSrc s0 = tile_src(0), s1 = tile_src(1);
+#pragma unroll
+        for (int d = 0; d < LPA; ++d) dma_a(s0, lds, d);
+#pragma unroll
+        for (int d = 0; d < LPB; ++d) dma_b(s0, lds + SLOT, d);
+#pragma unroll
+        for (int d = 0; d < LPA; ++d) dma_a(s1, lds + 2 * SLOT, d);
+#pragma unroll
+        for (int d = 0; d < LPB; ++d) dma_b(s1, lds + 3 * SLOT, d);
+        // tile 0 landed (tile 1 may still be in flight)
+        wait_barrier_vm<LPA + LPB>();
+#pragma unroll
+        for (int r = 0; r < NR; ++r) read2(lds, lds + SLOT, 0, r, a0, b0);
+        // slot numbers of items 2kt .. 2kt+4, advanced by 2 (mod 5) per tile
+        int s_a = 0, s_b = 1, s_an = 2, s_bn = 3, s_ld = 4;
+        for (int kt = 0; kt < nkt; ++kt) {
+            const uint32_t a_at = lds + s_a * SLOT, b_at = lds + s_b * SLOT;
+            const uint32_t an_at = lds + s_an * SLOT, bn_at = lds + s_bn * SLOT;
+            const uint32_t ld_at = lds + s_ld * SLOT;
+            const TileSrc s2 = tile_src(kt + 2);
+            // sub-step 0: reads of sub-step 1 from tile kt, A of tile kt+2
+            ring_sub(std::integral_constant<int, LPA>{}, a0, b0,
+                     [&](int r) { read2(a_at, b_at, 1, r, a1, b1); },
+                     [&](int d) { dma_a(s2, ld_at, d); });
+            // tile kt+1 landed (only A of tile kt+2 may be in flight); every
+            // wave is done with the slots of tile kt
+            wait_barrier_vm<LPA>();
+            // sub-step 1: reads of tile kt+1's sub-step 0, B of tile kt+2
+            // into the slot of tile kt's A
+            ring_sub(std::integral_constant<int, LPB>{}, a1, b1,
+                     [&](int r) { read2(an_at, bn_at, 0, r, a0, b0); },
+                     [&](int d) { dma_b(s2, a_at, d); });
+            // items 2kt+2 .. 2kt+6 are in slots s_an, s_bn, s_ld, s_a, s_b
+            const int o_a = s_a, o_b = s_b;
+            s_a = s_an;
+            s_b = s_bn;
+            s_an = s_ld;
+            s_bn = o_a;
+            s_ld = o_b;
+        }
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" :::
+                         "memory");
+        if constexpr (EPI_LDS > 1) {
+            // every wave is done with the slots: the bias and alpha * scale
+            // (held in registers through the loop) go into the first one
+            asm volatile("s_barrier" ::: "memory");
+            if (tid < BN) {
+                epi_smem[tid] = epi_b;
+                epi_smem[BN + tid] = args.alpha * epi_s;
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+      }
+    } else if (nkt > 0) {
 #pragma unroll
         for (int t = 0; t < NST; ++t) {
             const TileSrc st = tile_src(t);
@@ -591,7 +709,7 @@ void gemm_dma_kernel(const GemmArgs args) {
     // one column hit distinct banks.
     constexpr int CRB = BN * 2;                    // C tile row bytes (16-bit)
     constexpr int CSW = CRB >= 512 ? 2 : 1;
-    static_assert(BM * CRB <= NST * STAGE, "the C tile fits the operand stages");
+    static_assert(BM * CRB <= LDS_BYTES, "the C tile fits the operand stages");
     bool c_lds = false;
     if constexpr (EPI == EPI_BETA && (OUT == DT_F16 || OUT == DT_BF16)) {
         c_lds = beta != 0.f && args.c_dma_ok != 0 && m0 + BM <= M && n0 + BN <= N;

@@ -23,6 +23,8 @@ __host__ __device__ constexpr int dt_size(int dt) {
 // tile with 4 waves of 64x64 and two workgroups per CU, TILE_128_DMA4 the
 // same tile with one workgroup per CU and 4 LDS stages (three K-tiles in
 // flight: split-K slices, whose short loops are bound by load latency).
+// TILE_256_DMA keeps its operand tiles in a ring of five slots (all 160 KiB
+// of LDS; half of each K-tile's loads in each of its two sub-steps).
 enum TileClass : int {
     TILE_256 = 0,
     TILE_128 = 1,
