@@ -298,6 +298,23 @@ def make_epilogue(c, bias=None, activation: Optional[str] = None, col_scale=None
     return ep
 
 
+# Descriptors of the shapes seen so far (a call rebuilds none: its fields
+# depend only on the key), bounded.
+_desc_cache: Dict[tuple, BatchedDescT] = {}
+
+
+def _desc_of(a, b, c, alpha, beta, transpose_a, transpose_b) -> BatchedDescT:
+    key = (a.dtype, b.dtype, c.dtype, tuple(a.shape), tuple(b.shape), tuple(c.shape),
+           a.stride(), b.stride(), c.stride(), float(alpha), float(beta), bool(transpose_a),
+           bool(transpose_b))
+    d = _desc_cache.get(key)
+    if d is None:
+        d = make_desc(a, b, c, alpha, beta, transpose_a, transpose_b)
+        if len(_desc_cache) < 4096:
+            _desc_cache[key] = d
+    return d
+
+
 def gemm(a, b, c, *, alpha: float = 1.0, beta: float = 0.0, transpose_a: bool = False,
          transpose_b: bool = False, stream=None, bias=None, activation: Optional[str] = None,
          col_scale=None):
@@ -310,7 +327,7 @@ def gemm(a, b, c, *, alpha: float = 1.0, beta: float = 0.0, transpose_a: bool = 
     if not (a.is_cuda and b.is_cuda and c.is_cuda):
         raise TcGemmError(1, "a, b and c must be GPU tensors")
     device = c.device.index if c.device.index is not None else 0
-    desc = make_desc(a, b, c, alpha, beta, transpose_a, transpose_b)
+    desc = _desc_of(a, b, c, alpha, beta, transpose_a, transpose_b)
     lib = load_library()
     ctx, s = _torch_stream(device, stream)
     if bias is None and activation is None and col_scale is None:

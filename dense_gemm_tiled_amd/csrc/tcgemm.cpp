@@ -406,6 +406,14 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true, const Choice 
         splits = ceil_div(256, tile_count(TILE_64));
         if (splits > ktiles / 8) splits = ktiles / 8;          // keep >= 8 K-tiles per slice
         if (splits > 16) splits = 16;
+    } else if (!dma && cls == TILE_64 && tile_count(TILE_64) < 64 && ktiles >= 4 &&
+               p.alpha != 0.0f) {
+        // fp32 with short K on a handful of tiles (256^3: 16 tiles of 8
+        // K-tiles): each K-tile of the register-staged loop waits for its
+        // loads, so a slice of one or two K-tiles per workgroup on 8x the
+        // workgroups, plus the reduction, beats the long loop on 16 CUs
+        splits = ceil_div(128, tile_count(TILE_64));
+        if (splits > ktiles) splits = ktiles;
     }
     if (splits < 1) splits = 1;
     // at most 16 output columns and K-contiguous A rows: the vector-ALU

@@ -336,8 +336,11 @@ def test_plan_other_workloads():
     assert pl["workspace_bytes"] == 4096 * 4096 + 3 * 4096
     assert plan_of(workloads.get("f16_tn_4096"))["kernel"] == "gemm_f16_tn_256x256_dma"
     assert plan_of(workloads.get("f16_nt_4096"))["kernel"] == "gemm_f16_nt_256x256_dma"
+    # fp32 256^3: 16 tiles of 64 x 64 with 8 K-tiles each, split into 8
+    # slices of one K-tile (128 workgroups) and reduced
     pl = plan_of(workloads.get("sgemm_nn_256"))
-    assert pl["kernel"].startswith("gemm_f32_nn_64x64")
+    assert pl["kernel"] == "gemm_f32_nn_64x64+splitk_reduce", pl["kernel"]
+    assert pl["splits"] == 8 and pl["grid"] == 128, pl
     z = plan_of(workloads.get("bf16_nn_4096").with_(alpha=0.0, beta=2.0))
     assert z["kernel"] == "scale_c" and z["launches"] == 1
 
