@@ -201,7 +201,8 @@ const char *const kDtName[4] = {"f32", "f16", "bf16", "i8"};
 const char *const kLayoutName[2][2] = {{"nn", "nt"}, {"tn", "tt"}};
 const char *const kTileName[NUM_TILE_CLASSES] = {"256x256", "128x128", "64x64",
                                                    "256x256_dma", "256x256_dma8", "128x128_dma",
-                                                   "thin", "128x128_dma4"};
+                                                   "thin", "128x128_dma4", "64x64_ks", "32x32_ks",
+                                                   "16x16_ks"};
 
 char g_names[4][2][2][NUM_TILE_CLASSES][64];
 bool g_names_ready = false;

@@ -19,6 +19,7 @@ constexpr bool out_ok(int cls, int out) {
     if (is_dma_class(cls) && TCG_DT == DT_F32) return false;
     if (out == OUT_PARTIAL)
         return cls == TILE_64 || cls == TILE_128 || cls == TILE_128_DMA || cls == TILE_128_DMA4;
+    if (cls == TILE_THIN) return false;
     // int8 into a float output: the dequantizing fused epilogue only
     if (TCG_DT == DT_I8) return out == DT_I32 || out == DT_F32 || out == DT_F16 || out == DT_BF16;
     if (TCG_DT == DT_F32) return out == DT_F32;
@@ -74,7 +75,12 @@ hipError_t launch_one(const GemmArgs &args, int64_t grid, hipStream_t stream) {
         }
 #undef TCG_DMA
         return hipGetLastError();
-    } else if constexpr (!is_dma_class(CLS) && out_ok(CLS, OUT)) {
+    } else if constexpr (is_ks_class(CLS) && out_ok(CLS, OUT)) {
+        if (TCG_DT == DT_I8 && OUT != DT_I32 && !args.epi) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((gemm_ks_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, OUT, tile_shape(CLS).bm>),
+                           dim3((unsigned)grid), dim3(256), 0, stream, args);
+        return hipGetLastError();
+    } else if constexpr (!is_dma_class(CLS) && !is_ks_class(CLS) && out_ok(CLS, OUT)) {
         if (TCG_DT == DT_I8 && OUT != DT_I32 && OUT != OUT_PARTIAL && !args.epi)
             return hipErrorInvalidValue;
         hipLaunchKernelGGL((gemm_kernel<TCG_DT, (bool)TCG_TA, (bool)TCG_TB, CLS, OUT>),
@@ -111,6 +117,9 @@ hipError_t TCG_LAUNCHER(int cls, int out, const tcg::GemmArgs &args, int64_t gri
     case TILE_256_DMA8: return launch_cls<TILE_256_DMA8>(out, args, grid, stream);
     case TILE_128_DMA: return launch_cls<TILE_128_DMA>(out, args, grid, stream);
     case TILE_128_DMA4: return launch_cls<TILE_128_DMA4>(out, args, grid, stream);
+    case TILE_64_KS: return launch_cls<TILE_64_KS>(out, args, grid, stream);
+    case TILE_32_KS: return launch_cls<TILE_32_KS>(out, args, grid, stream);
+    case TILE_16_KS: return launch_cls<TILE_16_KS>(out, args, grid, stream);
     default: return hipErrorInvalidValue;
     }
 }

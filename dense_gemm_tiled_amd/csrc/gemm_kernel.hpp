@@ -810,5 +810,189 @@ __global__ __launch_bounds__(256, Occupancy<CLS>::value) void gemm_kernel(const 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Small problems: a BT x BT tile (BT = 64, 32 or 16) whose 4 waves split K
+// among themselves.
+//
+// With few tiles and a short K (fp32 256^3: 16 tiles of 64 x 64 with 8
+// K-tiles each) the loop above runs on a handful of CUs and waits out one
+// memory round trip per K-tile.  Here every wave owns the whole tile and
+// takes every 4th K-tile (wave w: tiles w, w+4, ...), staging them through
+// its own two LDS stages with no workgroup barrier in the loop; the loads of
+// its next tile are in flight while it multiplies the current one, and the
+// four waves' round trips overlap.  Smaller tiles put the work on more CUs
+// (256^3 on 16 x 16 tiles: 256 workgroups).  After the loop the four partial
+// tiles meet in LDS and are added in wave order (a fixed order, so every run
+// gives the same bits), then stored once with the usual epilogue.  No
+// workspace, one launch.
+// ---------------------------------------------------------------------------
+template <int BT>
+struct KsOccupancy {
+    // LDS: 4 waves x 2 stages x 2 BT rows x 128 B = 128 / 64 / 32 KiB
+    static constexpr int value = BT == 64 ? 1 : 2;
+};
+
+template <int DT, bool TA, bool TB, int OUT, int BT>
+__global__ __launch_bounds__(256, KsOccupancy<BT>::value) void gemm_ks_kernel(const GemmArgs args) {
+    static_assert(BT == 64 || BT == 32 || BT == 16, "tile edge 64, 32 or 16");
+    constexpr int BM = BT, BN = BT, NWAVE = 4;
+    constexpr int ES = dt_size(DT);
+    constexpr int BK = kLdsRowBytes / ES;
+    constexpr int FM = BM / 16, FN = BN / 16;
+    constexpr int STAGE = (BM + BN) * kLdsRowBytes;
+    constexpr int PITCH = BN + 4;                      // partial-tile row, 32-bit words (bank offset)
+    static_assert(NWAVE * BM * PITCH * 4 <= NWAVE * 2 * STAGE, "partials fit the stages");
+    using Acc = typename Mma<DT>::Acc;
+
+    __shared__ __attribute__((aligned(16))) char smem[NWAVE * 2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    int32_t tm, tn, g;
+    tile_of_workgroup(args.tiles_m, args.tiles_n, args.band, blockIdx.x, gridDim.x, &tm, &tn, &g);
+    const int z = g;
+    const int M = args.M, N = args.N, K = args.K;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int nkt = (K + BK - 1) / BK;
+
+    const char *Ab = static_cast<const char *>(args.A) + z * args.stride_a * ES;
+    const char *Bb = static_cast<const char *>(args.B) + z * args.stride_b * ES;
+    const int lda_b = args.lda * ES, ldb_b = args.ldb * ES;
+    const bool mn_interior = (m0 + BM <= M) && (n0 + BN <= N);
+
+    // one wave loads a whole tile (64 threads)
+    using LoadA = std::conditional_t<TA, ColLoader<ES, BM, 64>, RowLoader<ES, BM, 64>>;
+    using LoadB = std::conditional_t<TB, RowLoader<ES, BN, 64>, ColLoader<ES, BN, 64>>;
+    LoadA la;
+    LoadB lb;
+    auto load_tile = [&](int k0) {
+        const int64_t a_org = TA ? ((int64_t)k0 * args.lda + m0) * ES
+                                 : ((int64_t)m0 * args.lda + k0) * ES;
+        const int64_t b_org = TB ? ((int64_t)n0 * args.ldb + k0) * ES
+                                 : ((int64_t)k0 * args.ldb + n0) * ES;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + a_org, args.a_extent - a_org);
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + b_org, args.b_extent - b_org);
+        if (mn_interior && k0 + BK <= K) {
+            la.template load<false>(ra, lane, lda_b, BM, BK);
+            lb.template load<false>(rb, lane, ldb_b, BN, BK);
+        } else {
+            la.template load<true>(ra, lane, lda_b, M - m0, K - k0);
+            lb.template load<true>(rb, lane, ldb_b, N - n0, K - k0);
+        }
+    };
+
+    Acc acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+
+    char *const wl = smem + wave * 2 * STAGE;     // this wave's two stages
+    const int frag_row = lane & 15, frag_chunk = lane >> 4;
+    if (wave < nkt) {
+        load_tile(wave * BK);
+        la.store(wl, lane);
+        lb.store(wl + BM * kLdsRowBytes, lane);
+    }
+    for (int kt = wave, j = 0; kt < nkt; kt += NWAVE, ++j) {
+        const char *sa = wl + (j & 1) * STAGE;
+        const char *sb = sa + BM * kLdsRowBytes;
+        const bool more = kt + NWAVE < nkt;
+        if (more) load_tile((kt + NWAVE) * BK);
+        // this wave's LDS writes of the tile are done before any lane reads
+        // them (a wave's LDS operations complete in order; the clobber keeps
+        // the compiler from moving the reads above the writes)
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            u32x4 af[FM], bf[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                af[i] = *reinterpret_cast<const u32x4 *>(sa + lds_off(i * 16 + frag_row, ks * 4 + frag_chunk));
+#pragma unroll
+            for (int jj = 0; jj < FN; ++jj)
+                bf[jj] = *reinterpret_cast<const u32x4 *>(sb + lds_off(jj * 16 + frag_row, ks * 4 + frag_chunk));
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int jj = 0; jj < FN; ++jj) Mma<DT>::run(acc[i][jj], bf[jj], af[i]);
+        }
+        if (more) {
+            // the other stage: its reads (the previous tile) were consumed by
+            // this wave's MFMAs above, so they are complete
+            char *na = wl + ((j + 1) & 1) * STAGE;
+            asm volatile("" ::: "memory");
+            la.store(na, lane);
+            lb.store(na + BM * kLdsRowBytes, lane);
+        }
+    }
+
+    // ---- the four partial tiles into LDS (raw 32-bit values), then summed in
+    // wave order; lane l of block (i, j) holds row i*16 + l%16, columns
+    // j*16 + 4(l/16) .. +3
+    __syncthreads();
+    u32 *part = reinterpret_cast<u32 *>(smem);
+    {
+        u32 *mine = part + wave * BM * PITCH;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < FN; ++jj) {
+                const int r = i * 16 + frag_row, c = jj * 16 + 4 * frag_chunk;
+                u32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (DT == DT_I8) w[e] = (u32)acc[i][jj][e];
+                    else w[e] = as_u32(acc[i][jj][e]);
+                }
+                *reinterpret_cast<u32x4 *>(mine + r * PITCH + c) = w;
+            }
+    }
+    __syncthreads();
+
+    constexpr int CES = dt_size(OUT == DT_I32 ? DT_I32 : OUT);
+    const int64_t c_org = ((int64_t)m0 * args.ldc + n0) * CES;
+    char *Cb = static_cast<char *>(args.C) + z * args.stride_c * CES + c_org;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cb, args.c_extent - c_org);
+    const bool vec = args.c_vec_ok != 0;
+    const int ldc = args.ldc;
+    const float alpha = args.alpha, beta = args.beta;
+    [[maybe_unused]] const EpiState ep = make_epi<OUT == DT_I32 ? DT_F32 : OUT>(args, z, N);
+    // BM rows x BN / 4 column quads, spread over the threads
+    constexpr int QPR = BN / 4;
+    for (int q = tid; q < BM * QPR; q += 256) {
+        const int r = q / QPR, c = (q % QPR) * 4;
+        const int nvalid = N - (n0 + c);
+        if (m0 + r >= M || nvalid <= 0) continue;
+        const int off = (r * ldc + c) * CES;
+        if constexpr (DT == DT_I8) {
+            int s[4] = {0, 0, 0, 0};
+#pragma unroll
+            for (int w = 0; w < NWAVE; ++w) {
+                const u32x4 p = *reinterpret_cast<const u32x4 *>(part + w * BM * PITCH + r * PITCH + c);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[e] += (int)p[e];
+            }
+            if constexpr (OUT == DT_I32) {
+                store_i4(rc, off, nvalid, vec, s);
+            } else {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (float)s[e];
+                finish4<OUT>(rc, off, nvalid, vec, alpha, beta, v, ep, n0 + c);
+            }
+        } else {
+            float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w = 0; w < NWAVE; ++w) {
+                const u32x4 p = *reinterpret_cast<const u32x4 *>(part + w * BM * PITCH + r * PITCH + c);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] += as_f32(p[e]);
+            }
+            finish4<OUT>(rc, off, nvalid, vec, alpha, beta, v, ep, n0 + c);
+        }
+    }
+}
+
 }  // namespace
 }  // namespace tcg

@@ -25,6 +25,10 @@ __host__ __device__ constexpr int dt_size(int dt) {
 // flight: split-K slices, whose short loops are bound by load latency).
 // TILE_256_DMA keeps its operand tiles in a ring of five slots (all 160 KiB
 // of LDS; half of each K-tile's loads in each of its two sub-steps).
+// TILE_64_KS, TILE_32_KS and TILE_16_KS are 64x64, 32x32 and 16x16 tiles
+// whose 4 waves split K among themselves (every wave owns the whole tile and
+// takes every 4th K-tile; the four partial tiles are added in LDS): small
+// problems with few tiles and a short K.
 enum TileClass : int {
     TILE_256 = 0,
     TILE_128 = 1,
@@ -34,8 +38,15 @@ enum TileClass : int {
     TILE_128_DMA = 5,
     TILE_THIN = 6,          // thin_kernel: N <= 16, A K-contiguous; kThinRows rows per workgroup
     TILE_128_DMA4 = 7,
-    NUM_TILE_CLASSES = 8
+    TILE_64_KS = 8,
+    TILE_32_KS = 9,
+    TILE_16_KS = 10,
+    NUM_TILE_CLASSES = 11
 };
+
+__host__ __device__ constexpr bool is_ks_class(int cls) {
+    return cls == TILE_64_KS || cls == TILE_32_KS || cls == TILE_16_KS;
+}
 
 constexpr int kThinRows = 8;    // output rows per thin_kernel workgroup (2 waves)
 
@@ -55,6 +66,9 @@ __host__ __device__ constexpr TileShape tile_shape(int cls) {
                ? TileShape{256, 256, 2, 2}
          : (cls == TILE_128 || cls == TILE_128_DMA || cls == TILE_128_DMA4) ? TileShape{128, 128, 2, 2}
          : cls == TILE_THIN                         ? TileShape{kThinRows, 16, kThinRows / 4, 1}
+         : cls == TILE_64_KS                        ? TileShape{64, 64, 1, 1}
+         : cls == TILE_32_KS                        ? TileShape{32, 32, 1, 1}
+         : cls == TILE_16_KS                        ? TileShape{16, 16, 1, 1}
                                                     : TileShape{64, 64, 2, 2};
 }
 

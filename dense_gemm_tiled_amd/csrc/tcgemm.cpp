@@ -327,7 +327,7 @@ void layout_workspace(const Problem &p, Plan *pl, const bool aligned[2]) {
 // write fp32 partial sums that one more kernel adds up in a fixed order.
 //
 // Tuning overrides (environment, read at every call; unset in normal use):
-// TCGEMM_TILE=dma|dma8|dma128|dma128x4|thin|256|128|64 forces a tile class
+// TCGEMM_TILE=dma|dma8|dma128|dma128x4|thin|256|128|64|64ks|32ks|16ks forces a tile class
 // (dma* only for 16-bit and int8 inputs, thin only for N <= 16 with A not
 // transposed) without split-K, TCGEMM_SPLITS=S forces split-K
 // with S slices (on a class with a partial-sum output: 64x64 or 128x128,
@@ -391,9 +391,27 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true, const Choice 
     for (int c = TILE_256; c <= TILE_64; ++c)
         if (tile_count(c) >= 192 || c == TILE_64) { cls = c; break; }
     int64_t splits = 1;
+    // Few tiles (under 128 of 64 x 64) and a short K: the 4 waves of a
+    // workgroup take every 4th K-tile each and add their partial tiles in
+    // LDS (each K-tile of the register-staged loop would wait out a memory
+    // round trip), on the largest tile that still gives 128 workgroups, else
+    // on 16 x 16 tiles; one launch, no workspace.  Short K: under 16 K-tiles,
+    // or for fp32 up to 32 when the tiles fill a round of workgroups (the
+    // split-K alternative there streams fp32 through the register-staged
+    // loop; 16-bit and int8 split-K streams through the direct-to-LDS tile).
+    // Measured on fp32 256^3 (16 x 16 tiles): 6.8 us per call against 9.7 us
+    // for 8 slices of split-K plus the reduction; fp32 256 x 256 x 1024:
+    // 8.6 against 10.4 us.
+    const int ks_cls = tile_count(TILE_32_KS) >= 128 ? TILE_32_KS : TILE_16_KS;
+    const bool ks = cls == TILE_64 && tile_count(TILE_64) < 128 && ktiles >= 4 &&
+                    p.alpha != 0.0f &&
+                    (ktiles < 16 || (!dma && ktiles <= 32 && tile_count(ks_cls) >= 256));
     // tall K and too few tiles to fill the chip: split K
-    const bool split = cls == TILE_64 && tile_count(TILE_64) < 128 && ktiles >= 16 && p.alpha != 0.0f;
-    if (split && dma) {
+    const bool split =
+        !ks && cls == TILE_64 && tile_count(TILE_64) < 128 && ktiles >= 16 && p.alpha != 0.0f;
+    if (ks) {
+        cls = ks_cls;
+    } else if (split && dma) {
         // the 4-stage 128x128 tile, one workgroup per CU: as many slices as
         // fit one round of workgroups (a second, partial round costs more
         // than the extra slices gain; measured on the batched 128 x 384 x
@@ -403,17 +421,12 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true, const Choice 
         if (splits > ktiles / 4) splits = ktiles / 4;          // keep >= 4 K-tiles per slice
         if (splits > 32) splits = 32;
     } else if (split) {
-        splits = ceil_div(256, tile_count(TILE_64));
-        if (splits > ktiles / 8) splits = ktiles / 8;          // keep >= 8 K-tiles per slice
-        if (splits > 16) splits = 16;
-    } else if (!dma && cls == TILE_64 && tile_count(TILE_64) < 64 && ktiles >= 4 &&
-               p.alpha != 0.0f) {
-        // fp32 with short K on a handful of tiles (256^3: 16 tiles of 8
-        // K-tiles): each K-tile of the register-staged loop waits for its
-        // loads, so a slice of one or two K-tiles per workgroup on 8x the
-        // workgroups, plus the reduction, beats the long loop on 16 CUs
-        splits = ceil_div(128, tile_count(TILE_64));
-        if (splits > ktiles) splits = ktiles;
+        // the register-staged loop waits out a memory round trip per K-tile:
+        // short slices (about two K-tiles) on up to 512 workgroups
+        splits = ceil_div(ktiles, 2);
+        const int64_t cap = 512 / tile_count(TILE_64);
+        if (splits > cap) splits = cap;
+        if (splits > 64) splits = 64;
     }
     if (splits < 1) splits = 1;
     // at most 16 output columns and K-contiguous A rows: the vector-ALU
@@ -434,6 +447,9 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true, const Choice 
         else if (strcmp(env, "dma128") == 0) cls = dma ? TILE_128_DMA : cls;
         else if (strcmp(env, "dma128x4") == 0) cls = dma ? TILE_128_DMA4 : cls;
         else if (strcmp(env, "thin") == 0) cls = thin_ok ? TILE_THIN : cls;
+        else if (strcmp(env, "64ks") == 0) cls = TILE_64_KS;
+        else if (strcmp(env, "32ks") == 0) cls = TILE_32_KS;
+        else if (strcmp(env, "16ks") == 0) cls = TILE_16_KS;
         else cls = v == 256 ? TILE_256 : v == 128 ? TILE_128 : v == 64 ? TILE_64 : cls;
         splits = 1;   // a forced class splits only when TCGEMM_SPLITS says so
     }
@@ -1040,10 +1056,11 @@ std::vector<Choice> tune_candidates(const Problem &p) {
     make_plan(p, &base);
     const int64_t s0 = base.swap ? 1 : base.splits;
     const bool dma = dma_types(p);
-    const int classes_dma[] = {TILE_256_DMA, TILE_256_DMA8, TILE_128_DMA, TILE_128_DMA4, TILE_64};
-    const int classes_f32[] = {TILE_256, TILE_128, TILE_64};
+    const int classes_dma[] = {TILE_256_DMA, TILE_256_DMA8, TILE_128_DMA, TILE_128_DMA4, TILE_64,
+                               TILE_64_KS, TILE_32_KS, TILE_16_KS};
+    const int classes_f32[] = {TILE_256, TILE_128, TILE_64, TILE_64_KS, TILE_32_KS, TILE_16_KS};
     const int *cl = dma ? classes_dma : classes_f32;
-    const int ncl = dma ? 5 : 3;
+    const int ncl = dma ? 8 : 6;
     for (int i = 0; i < ncl; ++i) {
         c.push_back(Choice{cl[i], 1, 0});
         if (splits_ok(cl[i]) && s0 > 1)

@@ -87,6 +87,84 @@ def test_padded_leading_dims(a, c):
     check(p, "padded2")
 
 
+# ---------------------------------------------------------------- K split among the waves
+KS_TILES = ["64ks", "32ks", "16ks"]
+KS_NAME = {"64ks": "_64x64_ks", "32ks": "_32x32_ks", "16ks": "_16x16_ks"}
+
+
+def ks_check(p, label, tile, **envs):
+    """Run p with a tile whose waves split K forced, and check that it is
+    the kernel that ran."""
+    import dense_gemm_tiled_amd as tg
+    res = check(p, label, TCGEMM_TILE=tile, **envs)
+    assert tg.last_kernel().endswith(KS_NAME[tile]), tg.last_kernel()
+    return res
+
+
+@pytest.mark.parametrize("tile", KS_TILES)
+@pytest.mark.parametrize("ta,tb", LAYOUTS, ids=[lay(*l) for l in LAYOUTS])
+@pytest.mark.parametrize("a,c", PAIRS, ids=["%s-%s" % pc for pc in PAIRS])
+def test_ks_kernel_ragged(a, c, ta, tb, tile):
+    """M, N and K ragged (K leaves a partial 16-byte chunk), several tiles,
+    a K of 6..25 K-tiles so the four waves get unequal shares; alpha = 0.5
+    and beta = 1 for floats."""
+    check_k = {"f32": 777, "f16": 1553, "bf16": 1553, "i8": 3105}[a]
+    ks_check(problem(a, c, 150, 131, check_k, ta, tb), "ks ragged", tile)
+    ks_check(problem(a, c, 129, 190, 197, ta, tb), "ks ragged short", tile)
+
+
+@pytest.mark.parametrize("tile", KS_TILES)
+@pytest.mark.parametrize("a,c", PAIRS, ids=["%s-%s" % pc for pc in PAIRS])
+def test_ks_kernel_fewer_k_tiles_than_waves(a, c, tile):
+    """K of one or two K-tiles: the idle waves contribute zero partial tiles;
+    beta = 0 with a NaN-filled C, which must not be read."""
+    ks_check(problem(a, c, 64, 64, 5, alpha=1.0, beta=0.0, c_dist="nan"), "ks one tile", tile)
+    ks_check(problem(a, c, 100, 70, 150, True, True, alpha=1.0, beta=0.0, c_dist="nan"),
+             "ks two tiles", tile)
+
+
+@pytest.mark.parametrize("tile", KS_TILES)
+@pytest.mark.parametrize("a,c,ta,tb", [("f32", "f32", False, False), ("bf16", "f32", True, False),
+                                       ("f16", "f16", False, True), ("i8", "i32", True, True)])
+def test_ks_kernel_batched_padded(a, c, ta, tb, tile):
+    """Batched problems with odd padded leading dims."""
+    M, N, K = 130, 100, 900
+    p = problem(a, c, M, N, K, ta, tb, batch=3, lda=(M if ta else K) + 3,
+                ldb=(K if tb else N) + 5, ldc=N + 7)
+    ks_check(p, "ks batched", tile)
+
+
+@pytest.mark.parametrize("tile", KS_TILES)
+@pytest.mark.parametrize("a,c", [("f32", "f32"), ("bf16", "f32"), ("f16", "f16")])
+def test_ks_kernel_exact_regime_bitwise(a, c, tile):
+    """Integer inputs in [-4, 4]: every partial sum and their sum in wave
+    order are exact, so the result is bit-equal to the oracle."""
+    p = problem(a, c, 256, 192, 1024, False, False, alpha=1.0, beta=0.0, dist="small_int",
+                scale=4.0, c_dist="zeros")
+    A, B, C = workloads.make_inputs(p)
+    say("GPU case: ks exact", a, c, tile)
+    with env(TCGEMM_TILE=tile):
+        got = run_library(p, A, B, C)
+    import dense_gemm_tiled_amd as tg
+    assert tg.last_kernel().endswith(KS_NAME[tile]), tg.last_kernel()
+    ref = oracle_full(p, A, B, C)
+    assert np.array_equal(got.view(np.uint8), ref.out.view(np.uint8))
+
+
+def test_ks_kernel_is_the_small_problem_plan_and_deterministic():
+    """fp32 256^3 (16 tiles of 64 x 64, 8 K-tiles) plans onto the 16 x 16
+    K-split tile with no workspace, and two runs give the same bits."""
+    import dense_gemm_tiled_amd as tg
+    p = workloads.get("sgemm_nn_256")
+    A, B, C = workloads.make_inputs(p)
+    say("GPU case: ks plan", p.name)
+    r1 = run_library(p, A, B, C)
+    assert tg.last_kernel() == "gemm_f32_nn_16x16_ks", tg.last_kernel()
+    r2 = run_library(p, A, B, C)
+    assert np.array_equal(r1.view(np.uint8), r2.view(np.uint8))
+    compare(p, r1, oracle_full(p, A, B, C), C_in=C, label="ks plan")
+
+
 # ---------------------------------------------------------------- direct-to-LDS kernel
 DMA_PAIRS = [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32"), ("i8", "i32")]
 
@@ -422,10 +500,22 @@ def test_dma_epilogue_rows_past_m(a, c, epi, tile):
 
 
 @pytest.mark.parametrize("ta,tb", LAYOUTS, ids=[lay(*l) for l in LAYOUTS])
-@pytest.mark.parametrize("tile", [256, 128, 64])
+@pytest.mark.parametrize("tile", [256, 128, 64, "64ks", "16ks"])
 def test_epilogue_register_staged_f32(tile, ta, tb):
     p = problem("f32", "f32", 300, 270, 197, ta, tb)
-    epi_check(p, "gelu_tanh", "epi f32 tile%d" % tile, TCGEMM_TILE=tile)
+    epi_check(p, "gelu_tanh", "epi f32 tile%s" % tile, TCGEMM_TILE=tile)
+
+
+@pytest.mark.parametrize("tile", KS_TILES)
+@pytest.mark.parametrize("act", ["relu", "gelu_tanh"])
+@pytest.mark.parametrize("a,c", [("bf16", "bf16"), ("f16", "f32")])
+def test_epilogue_ks_kernel(a, c, act, tile):
+    """The fused epilogue on the K-split small tiles, batched with one bias
+    vector per problem."""
+    import dense_gemm_tiled_amd as tg
+    p = problem(a, c, 130, 200, 1100, True, False, batch=2)
+    epi_check(p, act, "epi ks", shared=False, TCGEMM_TILE=tile)
+    assert tg.last_kernel().endswith(KS_NAME[tile]), tg.last_kernel()
 
 
 @pytest.mark.parametrize("act", ACTS)
@@ -516,11 +606,11 @@ def test_i8_dequant_dma_kernels(c, ta, tb, tile):
     assert tg.last_kernel().endswith(DMA_NAME[tile]), tg.last_kernel()
 
 
-@pytest.mark.parametrize("tile", [256, 128, 64])
+@pytest.mark.parametrize("tile", [256, 128, 64, "64ks", "32ks"])
 @pytest.mark.parametrize("c", DEQ_OUT)
 def test_i8_dequant_register_staged(c, tile):
     p = deq_problem(c, 300, 270, 197, True, False)
-    deq_check(p, "dequant tile%d" % tile, TCGEMM_TILE=tile)
+    deq_check(p, "dequant tile%s" % tile, TCGEMM_TILE=tile)
 
 
 @pytest.mark.parametrize("c", DEQ_OUT)

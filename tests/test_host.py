@@ -336,11 +336,24 @@ def test_plan_other_workloads():
     assert pl["workspace_bytes"] == 4096 * 4096 + 3 * 4096
     assert plan_of(workloads.get("f16_tn_4096"))["kernel"] == "gemm_f16_tn_256x256_dma"
     assert plan_of(workloads.get("f16_nt_4096"))["kernel"] == "gemm_f16_nt_256x256_dma"
-    # fp32 256^3: 16 tiles of 64 x 64 with 8 K-tiles each, split into 8
-    # slices of one K-tile (128 workgroups) and reduced
+    # fp32 256^3: 16 tiles of 64 x 64 with 8 K-tiles each.  The 4 waves of
+    # a workgroup take every 4th K-tile each, on 16 x 16 tiles (256
+    # workgroups): one launch, no workspace
     pl = plan_of(workloads.get("sgemm_nn_256"))
-    assert pl["kernel"] == "gemm_f32_nn_64x64+splitk_reduce", pl["kernel"]
-    assert pl["splits"] == 8 and pl["grid"] == 128, pl
+    assert pl["kernel"] == "gemm_f32_nn_16x16_ks", pl["kernel"]
+    assert pl["splits"] == 1 and pl["grid"] == 256 and pl["launches"] == 1, pl
+    assert pl["workspace_bytes"] == 0, pl
+    # 36 tiles of 64 x 64 give 144 of 32 x 32
+    mid = plan_of(workloads.get("sgemm_nn_256").with_(M=384, N=384))
+    assert mid["kernel"] == "gemm_f32_nn_32x32_ks" and mid["grid"] == 144, mid
+    # the same small output with a tall K splits K across workgroups, in
+    # slices of two K-tiles on up to 512 workgroups
+    tall = plan_of(workloads.get("sgemm_nn_256").with_(K=8192))
+    assert tall["kernel"] == "gemm_f32_nn_64x64+splitk_reduce", tall["kernel"]
+    assert tall["splits"] == 32 and tall["grid"] == 512, tall
+    # and a 16-bit small problem with a short K takes the K-split tile too
+    small = plan_of(workloads.Problem("small", 256, 256, 512, "bf16", "bf16"))
+    assert small["kernel"] == "gemm_bf16_nn_16x16_ks", small["kernel"]
     z = plan_of(workloads.get("bf16_nn_4096").with_(alpha=0.0, beta=2.0))
     assert z["kernel"] == "scale_c" and z["launches"] == 1
 
