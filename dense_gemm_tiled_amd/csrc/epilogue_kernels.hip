@@ -32,58 +32,55 @@ __device__ inline __amdgpu_buffer_rsrc_t c_row_rsrc(const EpilogueArgs &a, int z
 // Split-K reduction: C = round(alpha * sum_s partial[s] + beta * C_old), the
 // slices summed in ascending s so the result is the same on every run; the
 // fused epilogue, when one is on, runs here (the partials have none).
-// One thread per 4 consecutive outputs of a row.
+// One thread per 4 consecutive outputs of a row; the workgroups of one
+// problem never straddle the next, so the problem's partial sums are one
+// workgroup-uniform buffer (no per-lane resource).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const EpilogueArgs a) {
     const int nq = (a.N + 3) / 4;
-    const int64_t total = (int64_t)a.batch * a.M * nq;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= total) return;
-    const int z = (int)(idx / ((int64_t)a.M * nq));
-    const int64_t rem = idx - (int64_t)z * a.M * nq;
+    const int64_t per = (int64_t)a.M * nq;          // threads of one problem
+    const int64_t bpp = (per + 255) / 256;          // workgroups per problem
+    const int z = (int)(blockIdx.x / bpp);
+    const int64_t rem = (int64_t)(blockIdx.x % bpp) * 256 + threadIdx.x;
+    if (z >= a.batch || rem >= per) return;
     const int m = (int)(rem / nq), n = (int)(rem % nq) * 4;
     const int nvalid = a.N - n;
     const int64_t plane = (int64_t)a.M * a.N;
     const char *wsz = static_cast<const char *>(a.ws) + (int64_t)z * a.splits * plane * 4;
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(wsz, (int64_t)a.splits * plane * 4);
-    // C's row m as a buffer of its N values: offsets stay small for a C of
-    // any size, and nothing past column N is written
-    const __amdgpu_buffer_rsrc_t rc = c_row_rsrc(a, z, m);
-    const int coff = n * dt_size(a.c_dtype);
     const bool wvec = (a.N % 4) == 0;
     const bool cvec = a.c_vec_ok != 0;
     float s4[4] = {0.f, 0.f, 0.f, 0.f};
+    int i4[4] = {0, 0, 0, 0};
     if (a.acc_is_int) {
         // exact int32 sums; int32 out as they are, a float out (int8 with a
         // dequantization scale) through the float epilogue below
-        int i4[4] = {0, 0, 0, 0};
         for (int s = 0; s < a.splits; ++s) {
             const int off = (int)((s * plane + (int64_t)m * a.N + n) * 4);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 if (e < nvalid) i4[e] += (int)__builtin_amdgcn_raw_buffer_load_b32(rw, off + 4 * e, 0, 0);
         }
-        if (a.c_dtype == DT_I32) {
-            store_i4(rc, coff, nvalid, cvec, i4);
-            return;
-        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) s4[e] = (float)i4[e];
     } else {
         int s = 0;
         if (wvec && nvalid >= 4) {
-            // groups of 8 slices: the 8 loads are in flight together, the adds
+            // groups of up to 16 slices: a group's loads are in flight
+            // together (one memory round trip for up to 16 slices), the adds
             // still run in ascending s
             const int plane_b = (int)(plane * 4);
             const int off0 = (int)(((int64_t)m * a.N + n) * 4);
-            for (; s + 8 <= a.splits; s += 8) {
-                u32x4 w[8];
+            for (; s < a.splits; s += 16) {
+                u32x4 w[16];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) w[u] = ld128(rw, off0 + (s + u) * plane_b);
+                for (int u = 0; u < 16; ++u)
+                    if (s + u < a.splits) w[u] = ld128(rw, off0 + (s + u) * plane_b);
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
+                for (int u = 0; u < 16; ++u)
+                    if (s + u < a.splits)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) s4[e] += as_f32(w[u][e]);
+                        for (int e = 0; e < 4; ++e) s4[e] += as_f32(w[u][e]);
             }
         }
         for (; s < a.splits; ++s) {
@@ -100,11 +97,24 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const EpilogueArgs a
             }
         }
     }
-    switch (a.c_dtype) {
-    case DT_F32: finish4<DT_F32>(rc, coff, nvalid, cvec, a.alpha, a.beta, s4, epi_of<DT_F32>(a, z), n); break;
-    case DT_BF16: finish4<DT_BF16>(rc, coff, nvalid, cvec, a.alpha, a.beta, s4, epi_of<DT_BF16>(a, z), n); break;
-    default: finish4<DT_F16>(rc, coff, nvalid, cvec, a.alpha, a.beta, s4, epi_of<DT_F16>(a, z), n); break;
-    }
+    auto finish = [&](const __amdgpu_buffer_rsrc_t &rc, int coff) {
+        switch (a.c_dtype) {
+        case DT_I32: store_i4(rc, coff, nvalid, cvec, i4); break;
+        case DT_F32: finish4<DT_F32>(rc, coff, nvalid, cvec, a.alpha, a.beta, s4, epi_of<DT_F32>(a, z), n); break;
+        case DT_BF16: finish4<DT_BF16>(rc, coff, nvalid, cvec, a.alpha, a.beta, s4, epi_of<DT_BF16>(a, z), n); break;
+        default: finish4<DT_F16>(rc, coff, nvalid, cvec, a.alpha, a.beta, s4, epi_of<DT_F16>(a, z), n); break;
+        }
+    };
+    // C: the problem's whole C as one workgroup-uniform buffer when every
+    // offset in it fits 31 bits, else row m as a buffer of its N values
+    // (offsets stay small for a C of any size); nothing past column N is
+    // written either way
+    const int64_t ces = dt_size(a.c_dtype);
+    if (((int64_t)(a.M - 1) * a.ldc + a.N) * ces <= 0x7FFFFFFF)
+        finish(make_rsrc(static_cast<char *>(a.C) + (int64_t)z * a.stride_c * ces, a.c_extent),
+               (int)(((int64_t)m * a.ldc + n) * ces));
+    else
+        finish(c_row_rsrc(a, z, m), (int)(n * ces));
 }
 
 // alpha == 0: C = beta * C (beta == 0 writes zeros without reading C), then
@@ -233,8 +243,8 @@ hipError_t tcg_launch_pack_rows(const PackArgs &args, hipStream_t stream) {
 }
 
 hipError_t tcg_launch_splitk_reduce(const EpilogueArgs &args, hipStream_t stream) {
-    const int64_t total = (int64_t)args.batch * args.M * ((args.N + 3) / 4);
-    const int64_t blocks = (total + 255) / 256;
+    const int64_t per = (int64_t)args.M * ((args.N + 3) / 4);
+    const int64_t blocks = (per + 255) / 256 * args.batch;
     if (blocks <= 0 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, args);
     return hipGetLastError();

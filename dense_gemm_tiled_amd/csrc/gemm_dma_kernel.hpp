@@ -337,10 +337,11 @@ constexpr int op_begin(int q, int n, int qn) { return (q * n + qn - 1) / qn; }
 constexpr int EPI_PLAIN = 0, EPI_BETA = 1, EPI_FUSED = 2;
 
 // BM x BN tile, NW waves (2 along M, NW/2 along N), OCC workgroups per CU;
-// EPI: one of the epilogue variants above; NST LDS stages (2 or 4): tiles
-// kt+1 .. kt+NST-1 are in flight while tile kt is computed -- or NST = 5:
-// a ring of five slots of one operand tile each (BM == BN; 160 KiB for the
-// 256 x 256 tile), see below; MS: the MFMA output block (16 or 32).
+// EPI: one of the epilogue variants above; NST LDS stages (2, 4 or 5): tiles
+// kt+1 .. kt+NST-1 are in flight while tile kt is computed -- except that
+// NST = 5 where five stages do not fit (the 256 x 256 tile) means a ring of
+// five slots of one operand tile each (BM == BN; 160 KiB), see below; MS:
+// the MFMA output block (16 or 32).
 //
 // The ring.  Operand tiles are items: item 2t is A of K-tile t, item 2t+1
 // its B, held in slot item % 5.  At the barrier in the middle of K-tile t
@@ -383,8 +384,9 @@ void gemm_dma_kernel(const GemmArgs args) {
     using Mma = MmaAsm<DT, MS>;
     using Acc = typename Mma::Acc;
 
-    static_assert(NST == 2 || NST == 4 || NST == 5, "2 or 4 stages, or the ring of 5 slots");
-    constexpr bool RING = NST == 5;
+    static_assert(NST == 2 || NST == 4 || NST == 5, "2, 4 or 5 stages, or the ring of 5 slots");
+    constexpr int kLdsMax = 160 * 1024;
+    constexpr bool RING = NST == 5 && 5 * STAGE > kLdsMax;
     static_assert(!RING || BM == BN, "the ring's slots hold either operand tile");
     constexpr int SLOT = A_BYTES;                        // ring: one operand tile
     constexpr int LDS_BYTES = RING ? 5 * SLOT : NST * STAGE;
@@ -547,10 +549,12 @@ void gemm_dma_kernel(const GemmArgs args) {
     // own at the start, their loads issued ahead of the first tiles' (the
     // epilogue then reads them with no wait; the loop's barriers publish them)
     constexpr int EPI_LDS = EPI == EPI_FUSED && OUT != DT_I32 && OUT != OUT_PARTIAL ? 2 * BN : 1;
-    // (declared only where used: the ring takes all 160 KiB of LDS, and the
-    // fused ring kernel stages them in its first slot once the loop is done)
+    // (declared only where used; where the stages take all 160 KiB of LDS --
+    // the ring, five 128 x 128 stages -- the bias and scales wait in
+    // registers and go into the first stage once the loop is done)
+    constexpr bool EPI_AFTER = EPI_LDS > 1 && LDS_BYTES + EPI_LDS * 4 > kLdsMax;
     float *epi_smem = nullptr;
-    if constexpr (EPI_LDS > 1 && RING) {
+    if constexpr (EPI_AFTER) {
         epi_smem = reinterpret_cast<float *>(smem);
     } else if constexpr (EPI_LDS > 1) {
         __shared__ __attribute__((aligned(16))) float epi_buf[EPI_LDS];
@@ -606,16 +610,6 @@ void gemm_dma_kernel(const GemmArgs args) {
         }
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" :::
                          "memory");
-        if constexpr (EPI_LDS > 1) {
-            // every wave is done with the slots: the bias and alpha * scale
-            // (held in registers through the loop) go into the first one
-            asm volatile("s_barrier" ::: "memory");
-            if (tid < BN) {
-                epi_smem[tid] = epi_b;
-                epi_smem[BN + tid] = args.alpha * epi_s;
-            }
-            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        }
       }
     } else if (nkt > 0) {
 #pragma unroll
@@ -627,7 +621,7 @@ void gemm_dma_kernel(const GemmArgs args) {
         // tile 0 landed (tiles 1 .. NST-1 may still be in flight: the loop
         // barriers wait for them); the waves without loads have none in flight
         wait_barrier_vm<(NST - 1) * ND>();
-        if constexpr (EPI_LDS > 1) {
+        if constexpr (EPI_LDS > 1 && !EPI_AFTER) {
             if (tid < BN) {
                 epi_smem[tid] = epi_b;
                 epi_smem[BN + tid] = args.alpha * epi_s;
@@ -648,6 +642,17 @@ void gemm_dma_kernel(const GemmArgs args) {
         // last MFMA results need wait states before the accumulators are read
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" :::
                          "memory");
+    }
+    if constexpr (EPI_AFTER) {
+        // every wave is done with the stages: the bias and alpha * scale
+        // (held in registers through the loop) go into the first one (also
+        // with no K-tile at all, so the epilogue reads what it expects)
+        asm volatile("s_barrier" ::: "memory");
+        if (tid < BN) {
+            epi_smem[tid] = epi_b;
+            epi_smem[BN + tid] = args.alpha * epi_s;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
 #pragma unroll
     for (int i = 0; i < FM; ++i)

@@ -34,10 +34,11 @@ hipError_t launch_one(const GemmArgs &args, int64_t grid, hipStream_t stream) {
         constexpr int T = tile_shape(CLS).bm;
         constexpr int NW = CLS == TILE_256_DMA8 ? 8 : 4;
         constexpr int OCC = CLS == TILE_128_DMA ? 2 : 1;
-        // LDS: 4 stages for split-K slices; the 256 x 256 tile with 4 waves
-        // as the ring of 5 slots (measured on the same box, the ring ran
-        // 0.5-1.5 % faster than 2 stages on the bf16 NN, fp16 TN and int8 NN
-        // 4096^3 shapes, the same on fp16 NT)
+        // LDS: 4 stages for split-K slices (5, all 160 KiB, measured no
+        // faster on the batched 128 x 384 x 16384 split-K shape); the 256 x
+        // 256 tile with 4 waves as the ring of 5 slots (measured on the same
+        // box, the ring ran 0.5-1.5 % faster than 2 stages on the bf16 NN,
+        // fp16 TN and int8 NN 4096^3 shapes, the same on fp16 NT)
         constexpr int NST = CLS == TILE_128_DMA4 ? 4 : CLS == TILE_256_DMA ? 5 : 2;
         // 16 x 16 MFMA blocks: the 32 x 32 form measured 6-8 % slower on the
         // 256 x 256 tile (4096^3 bf16 NN, fp16 TN and NT)
