@@ -176,15 +176,22 @@ def _context(device: int) -> int:
     return h
 
 
-def _torch_stream(device: int, stream=None) -> Tuple[int, int]:
+def _current_raw_stream(device: int) -> int:
+    """torch's current stream on `device` as a hipStream_t (an int)."""
     import torch
-    if stream is None:
-        stream = torch.cuda.current_stream(device)
-    handle = int(stream.cuda_stream)
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return int(raw(device))
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _torch_stream(device: int, stream=None) -> Tuple[int, int]:
+    handle = _current_raw_stream(device) if stream is None else int(stream.cuda_stream)
     key = (device, handle)
     s = _streams.get(key)
     ctx = _context(device)
     if s is None:
+        import torch
         out = _VP()
         with torch.cuda.device(device):
             _check(load_library().tc_stream_wrap(ctx, _VP(handle), ctypes.byref(out)), ctx)
@@ -303,13 +310,15 @@ def make_epilogue(c, bias=None, activation: Optional[str] = None, col_scale=None
 _desc_cache: Dict[tuple, BatchedDescT] = {}
 
 
-def _desc_of(a, b, c, alpha, beta, transpose_a, transpose_b) -> BatchedDescT:
-    key = (a.dtype, b.dtype, c.dtype, tuple(a.shape), tuple(b.shape), tuple(c.shape),
-           a.stride(), b.stride(), c.stride(), float(alpha), float(beta), bool(transpose_a),
-           bool(transpose_b))
+def _desc_of(a, b, c, alpha, beta, transpose_a, transpose_b):
+    """The descriptor of a call and a ctypes reference to it, cached per
+    (types, shapes, strides, scalars, transposes)."""
+    key = (a.dtype, b.dtype, c.dtype, a.shape, b.shape, c.shape, a.stride(), b.stride(),
+           c.stride(), alpha, beta, transpose_a, transpose_b)
     d = _desc_cache.get(key)
     if d is None:
-        d = make_desc(a, b, c, alpha, beta, transpose_a, transpose_b)
+        desc = make_desc(a, b, c, alpha, beta, transpose_a, transpose_b)
+        d = (desc, ctypes.byref(desc))
         if len(_desc_cache) < 4096:
             _desc_cache[key] = d
     return d
@@ -326,19 +335,18 @@ def gemm(a, b, c, *, alpha: float = 1.0, beta: float = 0.0, transpose_a: bool = 
     (per-column dequantization).  Returns c."""
     if not (a.is_cuda and b.is_cuda and c.is_cuda):
         raise TcGemmError(1, "a, b and c must be GPU tensors")
-    device = c.device.index if c.device.index is not None else 0
-    desc = _desc_of(a, b, c, alpha, beta, transpose_a, transpose_b)
-    lib = load_library()
+    device = c.get_device()
+    desc, dref = _desc_of(a, b, c, alpha, beta, transpose_a, transpose_b)
+    lib = _lib if _lib is not None else load_library()
     ctx, s = _torch_stream(device, stream)
     if bias is None and activation is None and col_scale is None:
-        st = lib.tc_gemm_batched_async(ctx, ctypes.byref(desc), _VP(a.data_ptr()),
-                                       _VP(b.data_ptr()), _VP(c.data_ptr()), s)
+        st = lib.tc_gemm_batched_async(ctx, dref, a.data_ptr(), b.data_ptr(), c.data_ptr(), s)
     else:
         ep = make_epilogue(c, bias, activation, col_scale)
-        st = lib.tc_gemm_epilogue_async(ctx, ctypes.byref(desc), ctypes.byref(ep),
-                                        _VP(a.data_ptr()), _VP(b.data_ptr()),
-                                        _VP(c.data_ptr()), s)
-    _check(st, ctx)
+        st = lib.tc_gemm_epilogue_async(ctx, dref, ctypes.byref(ep), a.data_ptr(), b.data_ptr(),
+                                        c.data_ptr(), s)
+    if st != 0:
+        _check(st, ctx)
     return c
 
 

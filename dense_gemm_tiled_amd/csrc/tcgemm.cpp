@@ -22,6 +22,8 @@
 #include <utility>
 #include <vector>
 
+#include <unistd.h>   // environ
+
 #include "tc_internal.h"
 
 using namespace tcg;
@@ -260,8 +262,38 @@ void operand_shape(const Problem &p, int w, int64_t *rows, int64_t *cols) {
     *cols = mc ? mn : p.K;
 }
 
+// Tuning knobs (environment variables TCGEMM_*, unset in normal use).  An
+// entry point reads them all in one pass over the environment when it starts
+// (KnobScope); the planner then looks them up here instead of calling getenv
+// for each (a getenv walks the whole environment).  Outside a scope the
+// lookup falls back to getenv.
+enum Knob { K_TILE, K_SPLITS, K_BAND, K_EDGE, K_GEMV, K_PACK_UNALIGNED, NUM_KNOBS };
+const char *const kKnobName[NUM_KNOBS] = {"TCGEMM_TILE", "TCGEMM_SPLITS", "TCGEMM_BAND",
+                                          "TCGEMM_EDGE", "TCGEMM_GEMV", "TCGEMM_PACK_UNALIGNED"};
+thread_local const char *t_knob[NUM_KNOBS];
+thread_local int t_knob_depth = 0;
+
+struct KnobScope {
+    KnobScope() {
+        if (t_knob_depth++ > 0) return;
+        for (int k = 0; k < NUM_KNOBS; ++k) t_knob[k] = nullptr;
+        for (char **e = environ; e && *e; ++e) {
+            if (strncmp(*e, "TCGEMM_", 7) != 0) continue;
+            for (int k = 0; k < NUM_KNOBS; ++k) {
+                const size_t n = strlen(kKnobName[k]);
+                if (strncmp(*e, kKnobName[k], n) == 0 && (*e)[n] == '=') t_knob[k] = *e + n + 1;
+            }
+        }
+    }
+    ~KnobScope() { --t_knob_depth; }
+    KnobScope(const KnobScope &) = delete;
+    KnobScope &operator=(const KnobScope &) = delete;
+};
+
+const char *knob(Knob k) { return t_knob_depth > 0 ? t_knob[k] : getenv(kKnobName[k]); }
+
 bool pack_unaligned() {
-    const char *env = getenv("TCGEMM_PACK_UNALIGNED");
+    const char *env = knob(K_PACK_UNALIGNED);
     return !env || atoi(env) != 0;
 }
 
@@ -366,8 +398,8 @@ bool gemv_route(const Problem &p, const Choice *ch) {
     if (!gemv_eligible(p)) return false;
     if (ch && ch->gemv >= 0) return ch->gemv == 1;
     if (ch && ch->cls >= 0) return false;                       // a chosen class
-    if (getenv("TCGEMM_TILE")) return false;                    // a forced class
-    if (const char *env = getenv("TCGEMM_GEMV"))                // tuning knob: 0 disables
+    if (knob(K_TILE)) return false;                    // a forced class
+    if (const char *env = knob(K_GEMV))                // tuning knob: 0 disables
         if (atoi(env) == 0) return false;
     return true;
 }
@@ -440,7 +472,7 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true, const Choice 
     }
     if (dma && cls == TILE_256) cls = TILE_256_DMA;
     if (dma && cls == TILE_128) cls = TILE_128_DMA;
-    if (const char *env = getenv("TCGEMM_TILE")) {
+    if (const char *env = knob(K_TILE)) {
         const int v = atoi(env);
         if (strcmp(env, "dma") == 0) cls = dma ? TILE_256_DMA : cls;
         else if (strcmp(env, "dma8") == 0) cls = dma ? TILE_256_DMA8 : cls;
@@ -453,7 +485,7 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true, const Choice 
         else cls = v == 256 ? TILE_256 : v == 128 ? TILE_128 : v == 64 ? TILE_64 : cls;
         splits = 1;   // a forced class splits only when TCGEMM_SPLITS says so
     }
-    if (const char *env = getenv("TCGEMM_SPLITS")) {
+    if (const char *env = knob(K_SPLITS)) {
         const int64_t forced = atoi(env);
         if (forced > 0 && p.alpha != 0.0f) splits = forced > ktiles ? ktiles : forced;
     }
@@ -481,7 +513,7 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true, const Choice 
     pl->k_per_split = (int32_t)kps;
     pl->grid = tiles * splits;
     pl->band = 8;
-    if (const char *env = getenv("TCGEMM_BAND")) pl->band = atoi(env);   // tuning knob
+    if (const char *env = knob(K_BAND)) pl->band = atoi(env);   // tuning knob
     const bool aligned[2] = {true, true};
     layout_workspace(p, pl, aligned);
 
@@ -492,7 +524,7 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true, const Choice 
     // saves a round.
     pl->edge = 0;
     pl->edge_at = 0;
-    const char *env_edge = getenv("TCGEMM_EDGE");   // tuning knob: 0 disables
+    const char *env_edge = knob(K_EDGE);   // tuning knob: 0 disables
     if (allow_edge && p.alpha != 0.0f && (cls == TILE_256_DMA || cls == TILE_256_DMA8) && splits == 1 &&
         !(env_edge && atoi(env_edge) == 0)) {
         auto rounds = [](int64_t t) { return (t + 255) / 256; };
@@ -1138,6 +1170,7 @@ tc_status_t run(tc_context *ctx, const tc_gemm_batched_desc *bd, const void *A, 
                 void *C, tc_stream *s, bool sync, const tc_epilogue *ep = nullptr,
                 bool noalloc = false) {
     if (!ctx) return TC_ERR_INVALID_ARGUMENT;
+    const KnobScope knobs;
     ctx->last_error.clear();
     std::string *err = &ctx->last_error;
     if (!A || !B || !C) return fail(err, TC_ERR_INVALID_ARGUMENT, "A, B and C must be non-NULL");
@@ -1354,6 +1387,7 @@ tc_status_t tc_set_autotune(tc_context *ctx, int enable) {
 int64_t tc_autotune_entries(const tc_context *ctx) { return ctx ? (int64_t)ctx->tuned.size() : 0; }
 
 tc_status_t tc_gemm_plan(tc_context *ctx, const tc_gemm_batched_desc *bd, tc_plan_info *info) {
+    const KnobScope knobs;
     std::string *err = ctx ? &ctx->last_error : &g_plan_error;
     err->clear();
     Problem p;
