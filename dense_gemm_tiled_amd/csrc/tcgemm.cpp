@@ -441,8 +441,26 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true, const Choice 
     // tall K and too few tiles to fill the chip: split K
     const bool split =
         !ks && cls == TILE_64 && tile_count(TILE_64) < 128 && ktiles >= 16 && p.alpha != 0.0f;
+    // 16-bit and int8 outputs of 32 to 191 tiles of 128 x 128 (too few for
+    // that class by the count above; M and N at least 128) run on 128 x 128
+    // direct-to-LDS tiles, not on 64 x 64 tiles of the register-staged loop:
+    // with a long K (32 K-tiles or more) on the 4-stage tile with as many K
+    // slices as fill one round of workgroups, else on the 2-workgroup-per-CU
+    // tile as it is.
+    // Measured, bf16 NN, us per call: 4096 x 512 x 4096 30.3 (2 slices)
+    // against 68.5 on 64 x 64 and 41.0 unsliced; 1024 x 768 x 2048 19.6
+    // against 31.3 and 22.7; 1024^3 12.4 unsliced against 16.1 on 64 x 64
+    // and 19.1 with slices; int8 2048 x 512 x 2048 12.3 unsliced against 21.6.
+    const bool mid = !ks && !split && dma && cls == TILE_64 && tile_count(TILE_128) >= 32 &&
+                     p.M >= 128 && p.N >= 128 && p.alpha != 0.0f;
     if (ks) {
         cls = ks_cls;
+    } else if (mid) {
+        splits = ktiles >= 32 ? 256 / tile_count(TILE_128_DMA4) : 1;
+        if (splits > ktiles / 4) splits = ktiles / 4;          // keep >= 4 K-tiles per slice
+        if (splits > 32) splits = 32;
+        cls = splits >= 2 ? TILE_128_DMA4 : TILE_128;          // TILE_128 -> TILE_128_DMA below
+        if (splits < 2) splits = 1;
     } else if (split && dma) {
         // the 4-stage 128x128 tile, one workgroup per CU: as many slices as
         // fit one round of workgroups (a second, partial round costs more

@@ -358,6 +358,26 @@ def test_plan_other_workloads():
     assert z["kernel"] == "scale_c" and z["launches"] == 1
 
 
+def test_plan_mid_size_outputs():
+    """16-bit and int8 outputs of 32 to 191 tiles of 128 x 128 run on the
+    128 x 128 direct-to-LDS tiles: K-sliced on the 4-stage tile to fill one
+    round of workgroups when K has 32 K-tiles or more, else unsliced on the
+    two-per-CU tile; fp32 keeps the register-staged tiles."""
+    P = workloads.Problem
+    pl = plan_of(P("m", 4096, 512, 4096, "bf16", "bf16"))
+    assert pl["kernel"] == "gemm_bf16_nn_128x128_dma4+splitk_reduce", pl["kernel"]
+    assert pl["splits"] == 2 and pl["grid"] == 256, pl
+    pl = plan_of(P("m", 2048, 512, 4096, "bf16", "bf16"))
+    assert pl["splits"] == 4 and pl["grid"] == 256, pl
+    pl = plan_of(P("m", 1024, 768, 2048, "bf16", "f32"))
+    assert pl["kernel"].endswith("128x128_dma4+splitk_reduce") and pl["splits"] == 5, pl
+    for shape in [(1024, 1024, 1024, "bf16", "bf16"), (2048, 512, 2048, "i8", "i32"),
+                  (3072, 512, 1024, "f16", "f16")]:
+        pl = plan_of(P("m", *shape))
+        assert pl["kernel"].endswith("_128x128_dma") and pl["splits"] == 1, (shape, pl)
+    assert plan_of(P("m", 1024, 1024, 1024, "f32", "f32"))["kernel"] == "gemm_f32_nn_64x64"
+
+
 def test_plan_dma_eligibility():
     """The direct-to-LDS classes take 16-bit and int8 inputs.  An operand whose
     row pitch, batch stride or row length (K for K-contiguous operands, M or N
