@@ -417,7 +417,11 @@ def test_plan_edge_split():
     assert plan_of(base.with_(N=4104))["kernel"] == main + "|transpose_b+gemm_bf16_nn_thin"
     assert plan_of(base.with_(M=4100))["kernel"] == main + "|gemm_bf16_nn_128x128_dma4+splitk_reduce"
     assert plan_of(base.with_(N=4096 + 128))["kernel"].startswith(main + "|")
-    assert plan_of(base.with_(N=4096 + 136))["kernel"] == main            # strip > half a tile
+    # a strip over half a tile: no edge split; the 17th tile column would be
+    # a second round of 256 x 256 tiles, so the 128 x 128 tile runs it all
+    assert plan_of(base.with_(N=4096 + 136))["kernel"] == "gemm_bf16_nn_128x128_dma"
+    assert plan_of(base.with_(N=4096 + 256))["kernel"] == "gemm_bf16_nn_128x128_dma"
+    assert plan_of(base.with_(M=4096 + 1024, N=4096 + 1024))["kernel"] == main   # 400 tiles
     assert plan_of(base.with_(M=3072, N=4104))["kernel"] == main          # 204 tiles: one round
     pl = plan_of(base.with_(N=4104))
     assert pl["tiles_m"] == 16 and pl["tiles_n"] == 16 and pl["grid"] > 256
