@@ -57,7 +57,7 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--settle", type=float, default=0.5,
                     help="seconds of untimed steps before the warm-up (clock ramp)")
-    ap.add_argument("--clock-window", type=float, default=0.4,
+    ap.add_argument("--clock-window", type=float, default=2.5,
                     help="seconds of untimed steps after the timing, while clocks are sampled")
     ap.add_argument("--table", action="store_true",
                     help="measure every workload and print a table (not the one-line contract)")
@@ -92,6 +92,8 @@ def smi_sampler(interval: float) -> None:
             if not isinstance(pw, (int, float)) or not 0 < pw < 65535:
                 pw = m.get("average_socket_power")
             rec["power_w"] = pw if isinstance(pw, (int, float)) and 0 < pw < 65535 else None
+            act = m.get("average_gfx_activity")
+            rec["activity"] = act if isinstance(act, (int, float)) and 0 <= act <= 100 else None
         except Exception as e:  # noqa: BLE001
             rec["error"] = str(e)
         print(json.dumps(rec), flush=True)
@@ -127,8 +129,14 @@ def stop_sampler(proc, windows):
             pass
     errs = [r["error"] for r in recs if "error" in r]
     inside = [r for r in recs if "t" in r and any(a <= r["t"] <= b for a, b in windows)]
-    res = {"samples": len(inside), "source": "amdsmi gpu metrics, every 50 ms, "
-                                              "while steps run"}
+    # the driver refreshes these metrics about once a second, so a sample
+    # taken early in the window can still describe the idle time before it:
+    # keep the samples whose activity reading says the GPU was busy
+    busy = [r for r in inside if (r.get("activity") or 0) >= 90]
+    res = {"samples": len(inside), "busy_samples": len(busy),
+           "source": "amdsmi gpu metrics (refreshed about once a second), sampled every 50 ms "
+                     "while steps run; clock and power of the samples with activity >= 90 %"}
+    inside = busy
     for key in ("sclk_mhz", "power_w"):
         v = np.array([r[key] for r in inside if r.get(key) is not None], dtype=float)
         res[key] = ({"p50": float(np.median(v)), "min": float(v.min()), "max": float(v.max())}
