@@ -378,6 +378,19 @@ def test_plan_mid_size_outputs():
     assert plan_of(P("m", 1024, 1024, 1024, "f32", "f32"))["kernel"] == "gemm_f32_nn_64x64"
 
 
+def test_plan_tile_not_mostly_padding():
+    """A class is taken only when its tile is less than half empty along M
+    and N: a batch of 128 x 128 problems fills the chip with 256 x 256
+    tiles by count, but each would be three quarters padding."""
+    P = workloads.Problem
+    pl = plan_of(P("b", 128, 128, 128, "f32", "f32", batch=256))
+    assert pl["kernel"] == "gemm_f32_nn_128x128" and pl["grid"] == 256, pl
+    pl = plan_of(P("b", 128, 128, 128, "bf16", "bf16", batch=256))
+    assert pl["kernel"] == "gemm_bf16_nn_128x128_dma", pl
+    # 200 rows: a 256-row tile is 22 % padding, still taken
+    assert plan_of(P("w", 200, 65536, 256, "bf16", "bf16"))["kernel"] == "gemm_bf16_nn_256x256_dma"
+
+
 def test_plan_dma_eligibility():
     """The direct-to-LDS classes take 16-bit and int8 inputs.  An operand whose
     row pitch, batch stride or row length (K for K-contiguous operands, M or N
