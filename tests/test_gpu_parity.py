@@ -909,6 +909,25 @@ def full_case(name, **over):
     return p, A, B, C, got
 
 
+@pytest.mark.parametrize("M,N,K,a,c,batch,want", [
+    # mid-size output, long K: 2 K slices on the 4-stage 128 x 128 tile
+    (4096, 512, 4096, "bf16", "bf16", 1, "gemm_bf16_nn_128x128_dma4+splitk_reduce"),
+    # mid-size output, short K: the 128 x 128 tile unsliced
+    (1024, 1024, 1024, "i8", "i32", 1, "gemm_i8_nn_128x128_dma"),
+    # whole tiles just past one round of 256 x 256: the 128 x 128 tile
+    (4096, 4352, 1024, "bf16", "f32", 1, "gemm_bf16_nn_128x128_dma"),
+    # a batch of problems smaller than a 256 x 256 tile
+    (128, 128, 128, "f32", "f32", 256, "gemm_f32_nn_128x128"),
+])
+def test_planner_choices(M, N, K, a, c, batch, want):
+    """The planner's own choices for mid-size, just-past-a-round and batched
+    small outputs, whole results against the oracle (alpha = 0.5 and
+    beta = 1 for floats)."""
+    import dense_gemm_tiled_amd as tg
+    check(problem(a, c, M, N, K, batch=batch), "planner %s" % want)
+    assert tg.last_kernel() == want, tg.last_kernel()
+
+
 def test_workload_sgemm_nn_256():
     p, A, B, C, got = full_case("sgemm_nn_256")
     compare(p, got, oracle_full(p, A, B, C), label=p.name)
