@@ -131,6 +131,29 @@ __device__ inline void dma16(i32x4 rsrc, uint32_t lds, int voff) {
                  : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc)
                  : "memory", "m0");
 }
+
+// The same loads in groups of kLoadGroup sharing one M0 write: the
+// instruction's immediate offset is added to both the buffer offset and the
+// LDS address, so load j of a group (M0 = the group's first 1 KiB) takes
+// offset j KiB and a buffer offset j KiB lower.  set_m0 writes M0 with an
+// SALU add; the caller issues another instruction (an MFMA) before the first
+// load of the group, the one wait state such a load needs after an SALU
+// write of M0.
+constexpr int kLoadGroup = 4;
+__device__ inline void set_m0(uint32_t lds, uint32_t off) {
+    asm volatile("s_add_u32 m0, %0, %1"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "s"(__builtin_amdgcn_readfirstlane(off))
+                 : "m0");
+}
+__device__ inline void dma16_m0(i32x4 rsrc, int voff, int j) {
+    switch (j) {
+    case 0: asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc) : "memory"); break;
+    case 1: asm volatile("buffer_load_dwordx4 %0, %1, 0 offen offset:1024 lds" ::"v"(voff), "s"(rsrc) : "memory"); break;
+    case 2: asm volatile("buffer_load_dwordx4 %0, %1, 0 offen offset:2048 lds" ::"v"(voff), "s"(rsrc) : "memory"); break;
+    default: asm volatile("buffer_load_dwordx4 %0, %1, 0 offen offset:3072 lds" ::"v"(voff), "s"(rsrc) : "memory"); break;
+    }
+}
 #pragma clang diagnostic pop
 
 // Wait for this wave's LDS reads and all but its newest VM loads, then for
@@ -318,7 +341,10 @@ struct FragReader {
             }
             out = u32x4{(u32)lo[0], (u32)lo[1], (u32)hi[0], (u32)hi[1]};
         } else {
-            out = *(const TCG_LDS u32x4 *)(size_t)(tile + base[ks] + i * MS * kLdsRowBytes);
+            // the block offset as a constant pointer step, so that it becomes
+            // the instruction's immediate offset
+            const TCG_LDS char *p = (const TCG_LDS char *)(size_t)(tile + base[ks]);
+            out = *(const TCG_LDS u32x4 *)(p + i * MS * kLdsRowBytes);
         }
     }
 };
@@ -329,6 +355,57 @@ struct FragReader {
 // n goes after MFMA (o * QN) / n, so MFMA q is followed by operations
 // op_begin(q) .. op_begin(q + 1) - 1.
 constexpr int op_begin(int q, int n, int qn) { return (q * n + qn - 1) / qn; }
+
+// The ring's sub-steps interleave reads and loads, alternating (load first)
+// while both remain, then the rest of the longer kind: op o is load
+// ring_op_load(o) or read ring_op_read(o) (-1: the other kind).
+constexpr int ring_op_load(int o, int nl, int nr) {
+    const int pair = 2 * (nl < nr ? nl : nr);
+    if (o < pair) return (o & 1) == 0 ? o >> 1 : -1;
+    return nl > nr ? o - pair + nr : -1;
+}
+constexpr int ring_op_read(int o, int nl, int nr) {
+    const int pair = 2 * (nl < nr ? nl : nr);
+    if (o < pair) return (o & 1) == 1 ? o >> 1 : -1;
+    return nl > nr ? -1 : o - pair + nl;
+}
+// M0 moves to a load group before the MFMA that precedes the group's first
+// load, so no other load may sit between that MFMA and the group's first
+// load.
+constexpr bool ring_groups_ok(int nl, int nr, int qn) {
+    for (int q = 0; q < qn; ++q) {
+        bool load_seen = false;
+        for (int o = op_begin(q, nl + nr, qn); o < op_begin(q + 1, nl + nr, qn); ++o) {
+            const int d = ring_op_load(o, nl, nr);
+            if (d < 0) continue;
+            if (d % kLoadGroup == 0 && load_seen) return false;
+            load_seen = true;
+        }
+    }
+    return nl % kLoadGroup == 0;
+}
+
+// Buffer source of one operand's K-tiles in the ring: the resource of the
+// next tile to load (based at the tile's origin, ranging to the end of the
+// operand, at most 2^31 - 1 bytes), advanced one K-tile at a time with scalar
+// adds.  Only tiles whose origin lies inside the operand are loaded, so the
+// range left is never empty.  Device addresses have 48 bits, so the base's
+// high word fits the resource's 16-bit field as it is.
+struct RingSrc {
+    uint64_t base, rem, step;   // tile address, bytes left to the end, bytes per K-tile
+    __device__ inline i32x4 rsrc() const {
+        const uint32_t n = (rem >> 31) != 0 ? 0x7FFFFFFFu : (uint32_t)rem;
+        return i32x4{(int)(uint32_t)base, (int)(uint32_t)(base >> 32), (int)n, kRsrcWord3};
+    }
+    __device__ inline void advance() {
+        base += step;
+        rem -= step;
+    }
+};
+
+// Buffer offset of load j of a group, whose immediate offset adds j KiB
+// (unsigned arithmetic: an out-of-range offset stays out of range).
+__device__ inline int group_voff(int off, int j) { return (int)((uint32_t)off - (uint32_t)(j * 1024)); }
 
 // Epilogue variants of the kernel: beta == 0 and no fused epilogue; beta != 0
 // (16-bit C tiles staged through LDS); the fused epilogue (bias and
@@ -442,6 +519,18 @@ void gemm_dma_kernel(const GemmArgs args) {
         s.kv = min(BK, k_hi - k0);
         return s;
     };
+    // ring: the source of an operand's tile 2 (origin k_lo + 2 BK), from
+    // which the loop advances one K-tile at a time
+    [[maybe_unused]] auto ring_src = [&](const char *base, int64_t extent, bool mc, int64_t ld,
+                                         int mn0) {
+        const int64_t k0 = k_lo + 2 * BK;
+        const int64_t org = mc ? (k0 * ld + mn0) * ES : ((int64_t)mn0 * ld + k0) * ES;
+        RingSrc r;
+        r.base = (uint64_t)(base + org);
+        r.rem = (uint64_t)(extent - org);
+        r.step = (uint64_t)(mc ? (int64_t)BK * ld * ES : (int64_t)BK * ES);
+        return r;
+    };
     // ring: load d of an A item (0 .. LPA-1) or a B item (0 .. LPB-1) into
     // slot address `slot`
     [[maybe_unused]] auto dma_a = [&](const TileSrc &s, uint32_t slot, int d) {
@@ -523,24 +612,27 @@ void gemm_dma_kernel(const GemmArgs args) {
 
     // The ring's sub-steps: MFMAs on one register set, NR fragment reads into
     // the other, and NL loads, the reads and loads alternating while both
-    // remain (loads first).  rd(r) and ld(d) issue read r and load d.
+    // remain (loads first).  rd(r) and ld(d) issue read r and load d; grp(g)
+    // points M0 at load group g, before the MFMA that precedes the group's
+    // first load.
     [[maybe_unused]] auto ring_sub = [&](auto nl_tag, const u32x4 (&af)[KSUB][FM],
-                                         const u32x4 (&bf)[KSUB][FN], auto &&rd, auto &&ld) {
+                                         const u32x4 (&bf)[KSUB][FN], auto &&rd, auto &&ld,
+                                         auto &&grp) {
         constexpr int NL = decltype(nl_tag)::value;
+        static_assert(ring_groups_ok(NL, NR, QN), "a load group starts first in its MFMA gap");
 #pragma unroll
         for (int q = 0; q < QN; ++q) {
+#pragma unroll
+            for (int o = op_begin(q, NL + NR, QN); o < op_begin(q + 1, NL + NR, QN); ++o) {
+                const int d = ring_op_load(o, NL, NR);
+                if (d >= 0 && d % kLoadGroup == 0) grp(d / kLoadGroup);
+            }
             mma(q, af, bf);
 #pragma unroll
             for (int o = op_begin(q, NL + NR, QN); o < op_begin(q + 1, NL + NR, QN); ++o) {
-                const int pair = 2 * (NL < NR ? NL : NR);
-                if (o < pair) {
-                    if ((o & 1) == 0) ld(o >> 1);
-                    else rd(o >> 1);
-                } else if (NL > NR) {
-                    ld(o - pair + NR);
-                } else {
-                    rd(o - pair + NL);
-                }
+                const int d = ring_op_load(o, NL, NR);
+                if (d >= 0) ld(d);
+                else rd(ring_op_read(o, NL, NR));
             }
         }
     };
@@ -581,33 +673,64 @@ void gemm_dma_kernel(const GemmArgs args) {
         wait_barrier_vm<LPA + LPB>();
 #pragma unroll
         for (int r = 0; r < NR; ++r) read2(lds, lds + SLOT, 0, r, a0, b0);
-        // slot numbers of items 2kt .. 2kt+4, advanced by 2 (mod 5) per tile
-        int s_a = 0, s_b = 1, s_an = 2, s_bn = 3, s_ld = 4;
-        for (int kt = 0; kt < nkt; ++kt) {
-            const uint32_t a_at = lds + s_a * SLOT, b_at = lds + s_b * SLOT;
-            const uint32_t an_at = lds + s_an * SLOT, bn_at = lds + s_bn * SLOT;
-            const uint32_t ld_at = lds + s_ld * SLOT;
-            const TileSrc s2 = tile_src(kt + 2);
+        // Sources of the loaded tiles from tile 2 on, advanced one K-tile per
+        // iteration; only tiles inside the K slice are loaded (the last two
+        // iterations load nothing).
+        RingSrc ga = ring_src(Ab, args.a_extent, A_MC, args.lda, m0);
+        RingSrc gb = ring_src(Bb, args.b_extent, B_MC, args.ldb, n0);
+        // M0 offsets of this wave's load groups inside a slot
+        const uint32_t wofs_a = dwave * LPA * 1024, wofs_b = dwave * LPB * 1024;
+        // slot addresses of items 2kt .. 2kt+4, advanced by 2 (mod 5) per tile
+        uint32_t s_a = lds, s_b = lds + SLOT, s_an = lds + 2 * SLOT, s_bn = lds + 3 * SLOT,
+                 s_ld = lds + 4 * SLOT;
+        auto iter = [&](int kt, auto with_loads) {
+            constexpr bool WL = decltype(with_loads)::value;
+            const uint32_t a_at = s_a, b_at = s_b, an_at = s_an, bn_at = s_bn, ld_at = s_ld;
+            const int kv = min(BK, k_hi - (k_lo + (kt + 2) * BK));
             // sub-step 0: reads of sub-step 1 from tile kt, A of tile kt+2
-            ring_sub(std::integral_constant<int, LPA>{}, a0, b0,
-                     [&](int r) { read2(a_at, b_at, 1, r, a1, b1); },
-                     [&](int d) { dma_a(s2, ld_at, d); });
+            {
+                const i32x4 ra = ga.rsrc();
+                ring_sub(std::integral_constant<int, WL ? LPA : 0>{}, a0, b0,
+                         [&](int r) { read2(a_at, b_at, 1, r, a1, b1); },
+                         [&](int d) {
+                             if (loads)
+                                 dma16_m0(ra, group_voff(la.template offset<KMASK>(d, kv), d % kLoadGroup),
+                                          d % kLoadGroup);
+                         },
+                         [&](int g) {
+                             if (loads) set_m0(ld_at, wofs_a + g * kLoadGroup * 1024);
+                         });
+            }
+            if constexpr (WL) ga.advance();
             // tile kt+1 landed (only A of tile kt+2 may be in flight); every
             // wave is done with the slots of tile kt
-            wait_barrier_vm<LPA>();
+            wait_barrier_vm<WL ? LPA : 0>();
             // sub-step 1: reads of tile kt+1's sub-step 0, B of tile kt+2
             // into the slot of tile kt's A
-            ring_sub(std::integral_constant<int, LPB>{}, a1, b1,
-                     [&](int r) { read2(an_at, bn_at, 0, r, a0, b0); },
-                     [&](int d) { dma_b(s2, a_at, d); });
+            {
+                const i32x4 rb = gb.rsrc();
+                ring_sub(std::integral_constant<int, WL ? LPB : 0>{}, a1, b1,
+                         [&](int r) { read2(an_at, bn_at, 0, r, a0, b0); },
+                         [&](int d) {
+                             if (loads)
+                                 dma16_m0(rb, group_voff(lb.template offset<KMASK>(d, kv), d % kLoadGroup),
+                                          d % kLoadGroup);
+                         },
+                         [&](int g) {
+                             if (loads) set_m0(a_at, wofs_b + g * kLoadGroup * 1024);
+                         });
+            }
+            if constexpr (WL) gb.advance();
             // items 2kt+2 .. 2kt+6 are in slots s_an, s_bn, s_ld, s_a, s_b
-            const int o_a = s_a, o_b = s_b;
-            s_a = s_an;
-            s_b = s_bn;
-            s_an = s_ld;
-            s_bn = o_a;
-            s_ld = o_b;
-        }
+            s_a = an_at;
+            s_b = bn_at;
+            s_an = ld_at;
+            s_bn = a_at;
+            s_ld = b_at;
+        };
+        int kt = 0;
+        for (; kt < nkt - 2; ++kt) iter(kt, std::true_type{});
+        for (; kt < nkt; ++kt) iter(kt, std::false_type{});
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" :::
                          "memory");
       }
