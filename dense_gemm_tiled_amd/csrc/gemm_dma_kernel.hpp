@@ -138,13 +138,14 @@ __device__ inline void dma16(i32x4 rsrc, uint32_t lds, int voff) {
 // offset j KiB and a buffer offset j KiB lower.  set_m0 writes M0 with an
 // SALU add; the caller issues another instruction (an MFMA) before the first
 // load of the group, the one wait state such a load needs after an SALU
-// write of M0.
+// write of M0.  (The add writes SCC, so SCC is listed as clobbered: the
+// compiler must not keep a comparison in it across the statement.)
 constexpr int kLoadGroup = 4;
 __device__ inline void set_m0(uint32_t lds, uint32_t off) {
     asm volatile("s_add_u32 m0, %0, %1"
                  :
                  : "s"(__builtin_amdgcn_readfirstlane(lds)), "s"(__builtin_amdgcn_readfirstlane(off))
-                 : "m0");
+                 : "m0", "scc");
 }
 __device__ inline void dma16_m0(i32x4 rsrc, int voff, int j) {
     switch (j) {
