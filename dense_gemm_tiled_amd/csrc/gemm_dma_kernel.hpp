@@ -386,16 +386,18 @@ constexpr bool ring_groups_ok(int nl, int nr, int qn) {
     return nl % kLoadGroup == 0;
 }
 
-// Buffer source of one operand's K-tiles in the ring: the resource of the
-// next tile to load (based at the tile's origin, ranging to the end of the
-// operand, at most 2^31 - 1 bytes), advanced one K-tile at a time with scalar
-// adds.  Only tiles whose origin lies inside the operand are loaded, so the
-// range left is never empty.  Device addresses have 48 bits, so the base's
-// high word fits the resource's 16-bit field as it is.
+// Buffer source of one operand's K-tiles: the resource of the next tile to
+// load (based at the tile's origin, ranging to the end of the operand, at
+// most 2^31 - 1 bytes), advanced one K-tile at a time with scalar adds.  A
+// tile inside the K slice has its origin inside the operand, so its range is
+// never empty.  Device addresses have 48 bits, so the base's high word fits
+// the resource's 16-bit field as it is.
 struct RingSrc {
     uint64_t base, rem, step;   // tile address, bytes left to the end, bytes per K-tile
-    __device__ inline i32x4 rsrc() const {
-        const uint32_t n = (rem >> 31) != 0 ? 0x7FFFFFFFu : (uint32_t)rem;
+    // inside: the tile lies inside the K slice (else an empty range: its
+    // loads fetch nothing and fill their LDS with zeros)
+    __device__ inline i32x4 rsrc(bool inside = true) const {
+        const uint32_t n = !inside ? 0u : (rem >> 31) != 0 ? 0x7FFFFFFFu : (uint32_t)rem;
         return i32x4{(int)(uint32_t)base, (int)(uint32_t)(base >> 32), (int)n, kRsrcWord3};
     }
     __device__ inline void advance() {
@@ -520,11 +522,11 @@ void gemm_dma_kernel(const GemmArgs args) {
         s.kv = min(BK, k_hi - k0);
         return s;
     };
-    // ring: the source of an operand's tile 2 (origin k_lo + 2 BK), from
-    // which the loop advances one K-tile at a time
-    [[maybe_unused]] auto ring_src = [&](const char *base, int64_t extent, bool mc, int64_t ld,
-                                         int mn0) {
-        const int64_t k0 = k_lo + 2 * BK;
+    // the source of an operand's tile t0 (origin k_lo + t0 BK), from which the
+    // loop advances one K-tile at a time
+    [[maybe_unused]] auto ring_src = [&](int t0, const char *base, int64_t extent, bool mc,
+                                         int64_t ld, int mn0) {
+        const int64_t k0 = k_lo + (int64_t)t0 * BK;
         const int64_t org = mc ? (k0 * ld + mn0) * ES : ((int64_t)mn0 * ld + k0) * ES;
         RingSrc r;
         r.base = (uint64_t)(base + org);
@@ -587,30 +589,6 @@ void gemm_dma_kernel(const GemmArgs args) {
                 read(cur, 1, r, a1, b1);
         }
     };
-    // Sub-step 1: MFMAs on (a1, b1); the loads of tile kt+NST into `cur` and
-    // the reads of the next tile's sub-step 0, alternating.  Past the last
-    // tile the loads are empty (zero-fill a stage nobody reads) and the reads
-    // return stale data nobody uses, so the loop body has no branch.
-    auto sub1 = [&](uint32_t cur, uint32_t nxt, const TileSrc &s) {
-#pragma unroll
-        for (int q = 0; q < QN; ++q) {
-            mma(q, a1, b1);
-#pragma unroll
-            for (int o = op_begin(q, ND + NR, QN); o < op_begin(q + 1, ND + NR, QN); ++o) {
-                // o -> (load or read, index): alternate while both remain
-                const int pair = 2 * (ND < NR ? ND : NR);
-                if (o < pair) {
-                    if ((o & 1) == 0) dma(s, cur, o >> 1);
-                    else read(nxt, 0, o >> 1, a0, b0);
-                } else if (ND > NR) {
-                    dma(s, cur, o - pair + NR);
-                } else {
-                    read(nxt, 0, o - pair + ND, a0, b0);
-                }
-            }
-        }
-    };
-
     // The ring's sub-steps: MFMAs on one register set, NR fragment reads into
     // the other, and NL loads, the reads and loads alternating while both
     // remain (loads first).  rd(r) and ld(d) issue read r and load d; grp(g)
@@ -677,8 +655,8 @@ void gemm_dma_kernel(const GemmArgs args) {
         // Sources of the loaded tiles from tile 2 on, advanced one K-tile per
         // iteration; only tiles inside the K slice are loaded (the last two
         // iterations load nothing).
-        RingSrc ga = ring_src(Ab, args.a_extent, A_MC, args.lda, m0);
-        RingSrc gb = ring_src(Bb, args.b_extent, B_MC, args.ldb, n0);
+        RingSrc ga = ring_src(2, Ab, args.a_extent, A_MC, args.lda, m0);
+        RingSrc gb = ring_src(2, Bb, args.b_extent, B_MC, args.ldb, n0);
         // M0 offsets of this wave's load groups inside a slot
         const uint32_t wofs_a = dwave * LPA * 1024, wofs_b = dwave * LPB * 1024;
         // slot addresses of items 2kt .. 2kt+4, advanced by 2 (mod 5) per tile
@@ -753,6 +731,13 @@ void gemm_dma_kernel(const GemmArgs args) {
         }
 #pragma unroll
         for (int r = 0; r < NR; ++r) read(lds, 0, r, a0, b0);
+        // sources of tile NST on, advanced one K-tile per iteration (tiles
+        // past the K slice: empty ranges)
+        RingSrc ga = ring_src(NST, Ab, args.a_extent, A_MC, args.lda, m0);
+        RingSrc gb = ring_src(NST, Bb, args.b_extent, B_MC, args.ldb, n0);
+        // M0 offsets of this wave's load groups inside a stage
+        static_assert(LPA % kLoadGroup == 0 && LPB % kLoadGroup == 0, "whole load groups per operand");
+        const uint32_t wofs_a = dwave * LPA * 1024, wofs_b = A_BYTES + dwave * LPB * 1024;
         for (int kt = 0; kt < nkt; ++kt) {
             const uint32_t cur = lds + (kt % NST) * STAGE;
             const uint32_t nxt = lds + ((kt + 1) % NST) * STAGE;
@@ -760,7 +745,30 @@ void gemm_dma_kernel(const GemmArgs args) {
             // tile kt+1 landed for every wave (tiles up to kt+NST-1 may still
             // be in flight); every wave is done with `cur`
             wait_barrier_vm<(NST - 2) * ND>();
-            sub1(cur, nxt, tile_src(kt + NST));
+            // sub-step 1: MFMAs on (a1, b1), the reads of tile kt+1's
+            // sub-step 0 and the loads of tile kt+NST into `cur` (A, then B),
+            // a group of loads per M0 write
+            const bool inside = kt + NST < nkt;
+            const int kv = min(BK, k_hi - (k_lo + (kt + NST) * BK));
+            const i32x4 ra = ga.rsrc(inside), rb = gb.rsrc(inside);
+            ring_sub(std::integral_constant<int, ND>{}, a1, b1,
+                     [&](int r) { read(nxt, 0, r, a0, b0); },
+                     [&](int d) {
+                         if (!loads) return;
+                         if (d < LPA)
+                             dma16_m0(ra, group_voff(la.template offset<KMASK>(d, kv), d % kLoadGroup),
+                                      d % kLoadGroup);
+                         else
+                             dma16_m0(rb, group_voff(lb.template offset<KMASK>(d - LPA, kv), d % kLoadGroup),
+                                      d % kLoadGroup);
+                     },
+                     [&](int g) {
+                         if (!loads) return;
+                         if (g * kLoadGroup < LPA) set_m0(cur, wofs_a + g * kLoadGroup * 1024);
+                         else set_m0(cur, wofs_b + (g * kLoadGroup - LPA) * 1024);
+                     });
+            ga.advance();
+            gb.advance();
         }
         // no load may still be writing LDS when the workgroup ends, and the
         // last MFMA results need wait states before the accumulators are read
