@@ -867,41 +867,45 @@ void gemm_dma_kernel(const GemmArgs args) {
     }
     [[maybe_unused]] const EpiState ep = make_epi<OUT == DT_I32 ? DT_F32 : OUT>(args, z, N);
     // Interior tiles whose C rows are whole 16-byte chunks store through LDS:
-    // each wave writes its tile, CH rows at a time, into a region of its own
+    // each wave writes its tile, SCH rows at a time, into a region of its own
     // (rows padded by 16 values, so the writes of 16 rows spread over the
     // banks), then reads it back 16 bytes per lane along the rows and stores
     // whole row pieces (measured on the 256 x 256 tile, bf16 4096^3: the
     // 16 x 32-byte pieces of a block per store took 3.6 us longer per call
-    // than 16-byte pieces along rows).  pack(i, j, q, w): the CES words of
-    // the 4 values of block (i, j), group q, in C's type.  Rows past M start
-    // past the store range of `rc` (see below), so their stores are dropped.
+    // than 16-byte pieces along rows).  col(j, q) runs before the values of
+    // column group (j, q) are packed; pack(i, j, q, w): the CES words of the 4
+    // values of block (i, j), group q, in C's type.  Rows past M start past
+    // the store range of `rc` (see below), so their stores are dropped.  The
+    // regions start past the bias and scales that the fused epilogue keeps at
+    // the start of the stages.
     constexpr int SROW = WTN * CES, SPITCH = SROW + 16 * CES;
-    constexpr int SREGION = LDS_BYTES / NW;
+    constexpr int SBASE = EPI_AFTER ? (EPI_LDS * 4 + 1023) / 1024 * 1024 : 0;
+    constexpr int SREGION = (LDS_BYTES - SBASE) / NW / 16 * 16;
     constexpr int SCH = (WTM * SPITCH <= SREGION) ? WTM : (WTM / 2 * SPITCH <= SREGION) ? WTM / 2
                       : (WTM / 4 * SPITCH <= SREGION) ? WTM / 4 : WTM / 8;
     static_assert(SCH >= MS && SCH * SPITCH <= SREGION && WTM % SCH == 0, "staging band fits");
     constexpr int SLPR = SROW / 16, SRPI = 64 / SLPR;   // lanes per row, rows per read
-    [[maybe_unused]] auto staged_store = [&](auto &&pack) {
+    [[maybe_unused]] auto staged_store = [&](auto &&col, auto &&pack) {
         // every wave is done with the stages and no load is still writing them
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        TCG_LDS char *reg = (TCG_LDS char *)(size_t)(lds + wave * SREGION);
+        TCG_LDS char *reg = (TCG_LDS char *)(size_t)(lds + SBASE + wave * SREGION);
 #pragma unroll
         for (int c0 = 0; c0 < WTM; c0 += SCH) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int r = ml_of(i) - wm * WTM - c0;
-                if (i * MS < c0 || i * MS >= c0 + SCH) continue;
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
+                for (int q = 0; q < NG; ++q) {
+                    col(j, q);
 #pragma unroll
-                    for (int q = 0; q < NG; ++q) {
+                    for (int i = c0 / MS; i < (c0 + SCH) / MS; ++i) {
                         u32 w[CES];
                         pack(i, j, q, w);
-                        TCG_LDS char *at = reg + r * SPITCH + (nl_of(j, q) - wn * WTN) * CES;
+                        TCG_LDS char *at =
+                            reg + (ml_of(i) - wm * WTM - c0) * SPITCH + (nl_of(j, q) - wn * WTN) * CES;
                         if constexpr (CES == 2) *(TCG_LDS u32x2 *)at = u32x2{w[0], w[1]};
                         else *(TCG_LDS u32x4 *)at = u32x4{w[0], w[1], w[2], w[3]};
                     }
-            }
+                }
             // the LDS runs one wave's accesses in order: the reads below see
             // the writes above, and the next band's writes follow these reads
 #pragma unroll
@@ -955,7 +959,32 @@ void gemm_dma_kernel(const GemmArgs args) {
                 }
         }
     };
+    // the same through LDS for 16-byte C rows: act(acc * (alpha * scale) + bias)
+    [[maybe_unused]] auto fused_staged = [&](auto act_tag) {
+        constexpr int ACT = decltype(act_tag)::value;
+        float b[4], sa[4];
+        staged_store([&](int j, int q) { read_epi4(epi_smem, BN, nl_of(j, q), b, sa); },
+                     [&](int i, int j, int q, u32 (&w)[CES]) {
+                         float v[4];
+#pragma unroll
+                         for (int e = 0; e < 4; ++e)
+                             v[e] = act1<ACT>(__builtin_fmaf((float)acc[i][j][4 * q + e], sa[e], b[e]));
+                         if constexpr (CES == 4) {
+#pragma unroll
+                             for (int e = 0; e < 4; ++e) w[e] = as_u32(v[e]);
+                         } else {
+                             w[0] = pack2_16<OUT>(v[0], v[1]);
+                             w[1] = pack2_16<OUT>(v[2], v[3]);
+                         }
+                     });
+    };
     if constexpr (EPI_LDS > 1) {
+        if (interior && beta == 0.f && args.c_dma_ok) {
+            if (ep.act == ACT_GELU_TANH) fused_staged(std::integral_constant<int, ACT_GELU_TANH>{});
+            else if (ep.act == ACT_RELU) fused_staged(std::integral_constant<int, ACT_RELU>{});
+            else fused_staged(std::integral_constant<int, ACT_NONE>{});
+            return;
+        }
         if (interior && beta == 0.f) {
             if (ep.act == ACT_GELU_TANH) fused_interior(std::integral_constant<int, ACT_GELU_TANH>{});
             else if (ep.act == ACT_RELU) fused_interior(std::integral_constant<int, ACT_RELU>{});
@@ -965,7 +994,7 @@ void gemm_dma_kernel(const GemmArgs args) {
     }
     if constexpr (EPI == EPI_PLAIN && OUT != OUT_PARTIAL) {
         if (interior && args.c_dma_ok) {
-            staged_store([&](int i, int j, int q, u32 (&w)[CES]) {
+            staged_store([](int, int) {}, [&](int i, int j, int q, u32 (&w)[CES]) {
                 if constexpr (OUT == DT_I32) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) w[e] = (u32)acc[i][j][4 * q + e];
