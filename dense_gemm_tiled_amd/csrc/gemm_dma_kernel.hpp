@@ -800,6 +800,59 @@ void gemm_dma_kernel(const GemmArgs args) {
     auto nl_of = [&](int j, int q) {
         return wn * WTN + j * MS + (MS == 16 ? 4 * (lane >> 4) : 8 * q + 4 * (lane >> 5));
     };
+    constexpr int CES = dt_size(OUT == OUT_PARTIAL ? DT_F32 : OUT);
+    // Interior tiles whose output rows are whole 16-byte chunks store through
+    // LDS (C, or the split-K partial sums, rows ld values apart, at r):
+    // each wave writes its tile, SCH rows at a time, into a region of its own
+    // (rows padded by 16 values, so the writes of 16 rows spread over the
+    // banks), then reads it back 16 bytes per lane along the rows and stores
+    // whole row pieces (measured on the 256 x 256 tile, bf16 4096^3: the
+    // 16 x 32-byte pieces of a block per store took 3.6 us longer per call
+    // than 16-byte pieces along rows).  col(j, q) runs before the values of
+    // column group (j, q) are packed; pack(i, j, q, w): the CES words of the 4
+    // values of block (i, j), group q, in the output's type.  Rows past M
+    // start past the store range of r, so their stores are dropped.  The
+    // regions start past the bias and scales that the fused epilogue keeps at
+    // the start of the stages.
+    constexpr int SROW = WTN * CES, SPITCH = SROW + 16 * CES;
+    constexpr int SBASE = EPI_AFTER ? (EPI_LDS * 4 + 1023) / 1024 * 1024 : 0;
+    constexpr int SREGION = (LDS_BYTES - SBASE) / NW / 16 * 16;
+    constexpr int SCH = (WTM * SPITCH <= SREGION) ? WTM : (WTM / 2 * SPITCH <= SREGION) ? WTM / 2
+                      : (WTM / 4 * SPITCH <= SREGION) ? WTM / 4 : WTM / 8;
+    static_assert(SCH >= MS && SCH * SPITCH <= SREGION && WTM % SCH == 0, "staging band fits");
+    constexpr int SLPR = SROW / 16, SRPI = 64 / SLPR;   // lanes per row, rows per read
+    [[maybe_unused]] auto staged_store = [&](__amdgpu_buffer_rsrc_t r, int ld, auto &&col, auto &&pack) {
+        // every wave is done with the stages and no load is still writing them
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        TCG_LDS char *reg = (TCG_LDS char *)(size_t)(lds + SBASE + wave * SREGION);
+#pragma unroll
+        for (int c0 = 0; c0 < WTM; c0 += SCH) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < NG; ++q) {
+                    col(j, q);
+#pragma unroll
+                    for (int i = c0 / MS; i < (c0 + SCH) / MS; ++i) {
+                        u32 w[CES];
+                        pack(i, j, q, w);
+                        TCG_LDS char *at =
+                            reg + (ml_of(i) - wm * WTM - c0) * SPITCH + (nl_of(j, q) - wn * WTN) * CES;
+                        if constexpr (CES == 2) *(TCG_LDS u32x2 *)at = u32x2{w[0], w[1]};
+                        else *(TCG_LDS u32x4 *)at = u32x4{w[0], w[1], w[2], w[3]};
+                    }
+                }
+            // the LDS runs one wave's accesses in order: the reads below see
+            // the writes above, and the next band's writes follow these reads
+#pragma unroll
+            for (int t = 0; t < SCH / SRPI; ++t) {
+                const int row = t * SRPI + lane / SLPR, ch = lane % SLPR;
+                const u32x4 d = *(const TCG_LDS u32x4 *)(reg + row * SPITCH + ch * 16);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    d, r, (wm * WTM + c0 + row) * ld * CES + wn * WTN * CES + ch * 16, 0, 0);
+            }
+        }
+    };
     if constexpr (OUT == OUT_PARTIAL) {
         // raw fp32 / int32 partial sums of this K slice: workspace plane g
         char *wsb = static_cast<char *>(args.ws) +
@@ -807,6 +860,16 @@ void gemm_dma_kernel(const GemmArgs args) {
         const int64_t ws_ext = (int64_t)(M - m0) * N * 4 - (int64_t)n0 * 4;
         const __amdgpu_buffer_rsrc_t rw = make_rsrc(wsb, ws_ext);
         const bool vec = (N % 4) == 0;
+        if (vec && n0 + BN <= N) {
+            staged_store(rw, N, [](int, int) {}, [&](int i, int j, int q, u32 (&w)[CES]) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (DT == DT_I8) w[e] = (u32)acc[i][j][4 * q + e];
+                    else w[e] = as_u32(acc[i][j][4 * q + e]);
+                }
+            });
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int ml = ml_of(i);
@@ -829,7 +892,6 @@ void gemm_dma_kernel(const GemmArgs args) {
         }
         return;
     }
-    constexpr int CES = dt_size(OUT == OUT_PARTIAL ? DT_F32 : OUT);
     const int64_t c_org = ((int64_t)m0 * args.ldc + n0) * CES;
     char *Cb = static_cast<char *>(args.C) + z * args.stride_c * CES + c_org;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cb, args.c_extent - c_org);
@@ -866,57 +928,6 @@ void gemm_dma_kernel(const GemmArgs args) {
         }
     }
     [[maybe_unused]] const EpiState ep = make_epi<OUT == DT_I32 ? DT_F32 : OUT>(args, z, N);
-    // Interior tiles whose C rows are whole 16-byte chunks store through LDS:
-    // each wave writes its tile, SCH rows at a time, into a region of its own
-    // (rows padded by 16 values, so the writes of 16 rows spread over the
-    // banks), then reads it back 16 bytes per lane along the rows and stores
-    // whole row pieces (measured on the 256 x 256 tile, bf16 4096^3: the
-    // 16 x 32-byte pieces of a block per store took 3.6 us longer per call
-    // than 16-byte pieces along rows).  col(j, q) runs before the values of
-    // column group (j, q) are packed; pack(i, j, q, w): the CES words of the 4
-    // values of block (i, j), group q, in C's type.  Rows past M start past
-    // the store range of `rc` (see below), so their stores are dropped.  The
-    // regions start past the bias and scales that the fused epilogue keeps at
-    // the start of the stages.
-    constexpr int SROW = WTN * CES, SPITCH = SROW + 16 * CES;
-    constexpr int SBASE = EPI_AFTER ? (EPI_LDS * 4 + 1023) / 1024 * 1024 : 0;
-    constexpr int SREGION = (LDS_BYTES - SBASE) / NW / 16 * 16;
-    constexpr int SCH = (WTM * SPITCH <= SREGION) ? WTM : (WTM / 2 * SPITCH <= SREGION) ? WTM / 2
-                      : (WTM / 4 * SPITCH <= SREGION) ? WTM / 4 : WTM / 8;
-    static_assert(SCH >= MS && SCH * SPITCH <= SREGION && WTM % SCH == 0, "staging band fits");
-    constexpr int SLPR = SROW / 16, SRPI = 64 / SLPR;   // lanes per row, rows per read
-    [[maybe_unused]] auto staged_store = [&](auto &&col, auto &&pack) {
-        // every wave is done with the stages and no load is still writing them
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        TCG_LDS char *reg = (TCG_LDS char *)(size_t)(lds + SBASE + wave * SREGION);
-#pragma unroll
-        for (int c0 = 0; c0 < WTM; c0 += SCH) {
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int q = 0; q < NG; ++q) {
-                    col(j, q);
-#pragma unroll
-                    for (int i = c0 / MS; i < (c0 + SCH) / MS; ++i) {
-                        u32 w[CES];
-                        pack(i, j, q, w);
-                        TCG_LDS char *at =
-                            reg + (ml_of(i) - wm * WTM - c0) * SPITCH + (nl_of(j, q) - wn * WTN) * CES;
-                        if constexpr (CES == 2) *(TCG_LDS u32x2 *)at = u32x2{w[0], w[1]};
-                        else *(TCG_LDS u32x4 *)at = u32x4{w[0], w[1], w[2], w[3]};
-                    }
-                }
-            // the LDS runs one wave's accesses in order: the reads below see
-            // the writes above, and the next band's writes follow these reads
-#pragma unroll
-            for (int t = 0; t < SCH / SRPI; ++t) {
-                const int row = t * SRPI + lane / SLPR, ch = lane % SLPR;
-                const u32x4 d = *(const TCG_LDS u32x4 *)(reg + row * SPITCH + ch * 16);
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    d, rc, (wm * WTM + c0 + row) * ldc * CES + wn * WTN * CES + ch * 16, 0, 0);
-            }
-        }
-    };
     // A tile whose columns lie inside C, with vector-aligned rows, and no
     // C_old to read: every block is stored whole, so the store sequence is
     // straight-line code with no per-block bounds or alignment branches
@@ -963,7 +974,7 @@ void gemm_dma_kernel(const GemmArgs args) {
     [[maybe_unused]] auto fused_staged = [&](auto act_tag) {
         constexpr int ACT = decltype(act_tag)::value;
         float b[4], sa[4];
-        staged_store([&](int j, int q) { read_epi4(epi_smem, BN, nl_of(j, q), b, sa); },
+        staged_store(rc, ldc, [&](int j, int q) { read_epi4(epi_smem, BN, nl_of(j, q), b, sa); },
                      [&](int i, int j, int q, u32 (&w)[CES]) {
                          float v[4];
 #pragma unroll
@@ -994,7 +1005,7 @@ void gemm_dma_kernel(const GemmArgs args) {
     }
     if constexpr (EPI == EPI_PLAIN && OUT != OUT_PARTIAL) {
         if (interior && args.c_dma_ok) {
-            staged_store([](int, int) {}, [&](int i, int j, int q, u32 (&w)[CES]) {
+            staged_store(rc, ldc, [](int, int) {}, [&](int i, int j, int q, u32 (&w)[CES]) {
                 if constexpr (OUT == DT_I32) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) w[e] = (u32)acc[i][j][4 * q + e];
