@@ -172,22 +172,25 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const PackArgs a) {
         else if (a.bt_es == 2) tail = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
         else tail = __builtin_amdgcn_raw_buffer_load_b8(rs, off, 0, 0);
     }
-    const int chunks = (int)(a.dst_pitch / 16);
-    // eight chunks per lane in flight before their stores: a row of up to
-    // 8 KiB costs one memory round trip
-    for (int c0 = threadIdx.x & 63; c0 < chunks; c0 += 512) {
+    const int chunks = (int)(a.dst_pitch / 16), full = a.row_bytes / 16;
+    // the whole chunks, eight per lane in flight before their stores (a row
+    // of up to 8 KiB costs one memory round trip); no partial chunk among
+    // them, so the loads go out with no branch between them
+    for (int c0 = lane; c0 < full; c0 += 512) {
         u32x4 v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int c = c0 + 64 * u;
-            const int nb = a.row_bytes - 16 * c;
-            v[u] = u32x4{0u, 0u, 0u, 0u};
-            if (nb >= 16) v[u] = ld128(rs, 16 * c);
-            else if (nb > 0) v[u] = ld_partial<1>(rs, 16 * c, nb);
-        }
+        for (int u = 0; u < 8; ++u)
+            if (c0 + 64 * u < full) v[u] = ld128(rs, 16 * (c0 + 64 * u));
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-            if (c0 + 64 * u < chunks) *reinterpret_cast<u32x4 *>(dst + 16 * (c0 + 64 * u)) = v[u];
+            if (c0 + 64 * u < full) *reinterpret_cast<u32x4 *>(dst + 16 * (c0 + 64 * u)) = v[u];
+    }
+    // the partial chunk at the end of the row (byte by byte) and the zero
+    // padding up to the pitch
+    for (int c = full + lane; c < chunks; c += 64) {
+        const int nb = a.row_bytes - 16 * c;
+        const u32x4 v = nb > 0 ? ld_partial<1>(rs, 16 * c, nb) : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4 *>(dst + 16 * c) = v;
     }
     if (lane < (a.bt ? a.bt_cols : 0)) {
         char *d = static_cast<char *>(a.bt) + z * a.bt_stride + (int64_t)lane * a.bt_pitch +
