@@ -26,7 +26,15 @@
 //     with the gfx950 transposing LDS reads (ds_read_b64_tr_b16 / _b8),
 //     which hand every lane the K-run of one column -- no transpose pass and
 //     no register shuffles (tensorcore "GEMM", "Transposes": a transpose is a
-//     choice of strides).
+//     choice of strides);
+//   * few instructions besides the MFMAs: a wave issues one instruction per 4
+//     cycles and an MFMA block takes 16, so a run of more than three other
+//     instructions holds up the matrix core.  The loads go four to an M0
+//     write (their immediate offset moves the LDS address and the buffer
+//     offset alike), and the next tile's buffer resources advance by one
+//     K-tile with scalar adds;
+//   * interior tiles whose output rows are whole 16-byte chunks are stored
+//     through LDS, 16 bytes per lane along the rows.
 //
 // The MFMAs, the LDS-bound loads and the barrier are inline assembly.  The
 // accumulators are pinned to AGPRs (operand constraint "+a", destination =
