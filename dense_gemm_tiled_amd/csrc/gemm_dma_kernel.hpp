@@ -644,6 +644,15 @@ void gemm_dma_kernel(const GemmArgs args) {
         if (tid < BN)
             load_epi1<OUT>(make_epi<OUT>(args, z, N), n0 + tid, N, epi_b, epi_s);
     }
+    // beta != 0 with a 16-bit C tile inside C: the epilogue reads C_old from
+    // an LDS image of the tile (below).  On the ring with at least three
+    // K-tiles the image's four 64-row quarters load during the last two
+    // iterations, which load no operands, into slots free by then (c_pf);
+    // cq0 .. cq3: LDS addresses of the quarters.
+    constexpr bool C16 = EPI == EPI_BETA && (OUT == DT_F16 || OUT == DT_BF16);
+    [[maybe_unused]] const bool c_pf = C16 && RING && args.beta != 0.f && args.c_dma_ok != 0 &&
+                                       m0 + BM <= M && n0 + BN <= N && nkt >= 3;
+    [[maybe_unused]] uint32_t cq0 = lds, cq1 = lds, cq2 = lds, cq3 = lds;
     if constexpr (RING) {
       if (nkt > 0) {
         // items 0 .. 3 (tiles 0 and 1) into slots 0 .. 3
@@ -670,44 +679,81 @@ void gemm_dma_kernel(const GemmArgs args) {
         // slot addresses of items 2kt .. 2kt+4, advanced by 2 (mod 5) per tile
         uint32_t s_a = lds, s_b = lds + SLOT, s_an = lds + 2 * SLOT, s_bn = lds + 3 * SLOT,
                  s_ld = lds + 4 * SLOT;
-        auto iter = [&](int kt, auto with_loads) {
+        // C quarters (c_pf): load u (0 .. 7) of this wave for quarter q brings
+        // rows 64 q + 2 (8 wave + u) + {0, 1}, row r's 16-byte chunk c at
+        // position c ^ ((r & 15) * 2) of its 512 bytes (the image's layout,
+        // below); the C tile's resource is based at its origin
+        // (without c_pf the resource holds no bytes: the loads bring zeros and
+        // touch no memory, and the tail's code and wait counts stay the same)
+        [[maybe_unused]] i32x4 rcq{};
+        if constexpr (C16) {
+            const int64_t c_org0 = ((int64_t)m0 * args.ldc + n0) * 2;
+            rcq = rsrc4(static_cast<char *>(args.C) + z * args.stride_c * 2 + c_org0,
+                        c_pf ? args.c_extent - c_org0 : 0);
+        }
+        [[maybe_unused]] auto cq_load = [&](int q, int u) {
+            const int r = 64 * q + (dwave * 8 + u) * 2 + lane / 32;
+            const int c = (lane % 32) ^ ((r & 15) * 2);
+            dma16_m0(rcq, group_voff(r * args.ldc * 2 + c * 16, u % kLoadGroup), u % kLoadGroup);
+        };
+        // CPH: 0, or the C quarter loads of the last two iterations (1: quarter
+        // 0 in sub-step 0, quarters 1 and 2 in sub-step 1; 2: quarter 3)
+        auto iter = [&](int kt, auto with_loads, auto cph_tag) {
             constexpr bool WL = decltype(with_loads)::value;
+            constexpr int CPH = decltype(cph_tag)::value;
+            static_assert(CPH == 0 || (!WL && NW == 4 && NDW == NW && LPA == 8 && LPB == 8 && BN == 256),
+                          "C quarters: 8 loads per wave, every wave loading");
             const uint32_t a_at = s_a, b_at = s_b, an_at = s_an, bn_at = s_bn, ld_at = s_ld;
             const int kv = min(BK, k_hi - (k_lo + (kt + 2) * BK));
-            // sub-step 0: reads of sub-step 1 from tile kt, A of tile kt+2
+            // sub-step 0: reads of sub-step 1 from tile kt, A of tile kt+2 (or C
+            // quarter 0 into the slot tile kt+2's A would have taken)
             {
                 const i32x4 ra = ga.rsrc();
-                ring_sub(std::integral_constant<int, WL ? LPA : 0>{}, a0, b0,
+                ring_sub(std::integral_constant<int, WL ? LPA : CPH == 1 ? 8 : 0>{}, a0, b0,
                          [&](int r) { read2(a_at, b_at, 1, r, a1, b1); },
                          [&](int d) {
-                             if (loads)
+                             if constexpr (CPH == 1) cq_load(0, d);
+                             else if (loads)
                                  dma16_m0(ra, group_voff(la.template offset<KMASK>(d, kv), d % kLoadGroup),
                                           d % kLoadGroup);
                          },
                          [&](int g) {
-                             if (loads) set_m0(ld_at, wofs_a + g * kLoadGroup * 1024);
+                             if (CPH == 1 || loads) set_m0(ld_at, wofs_a + g * kLoadGroup * 1024);
                          });
             }
             if constexpr (WL) ga.advance();
-            // tile kt+1 landed (only A of tile kt+2 may be in flight); every
-            // wave is done with the slots of tile kt
-            wait_barrier_vm<WL ? LPA : 0>();
-            // sub-step 1: reads of tile kt+1's sub-step 0, B of tile kt+2
-            // into the slot of tile kt's A
+            // tile kt+1 landed (only A of tile kt+2, or the C quarters, may be
+            // in flight); every wave is done with the slots of tile kt
+            wait_barrier_vm<WL ? LPA : CPH == 1 ? 8 : CPH == 2 ? 24 : 0>();
+            // sub-step 1: reads of tile kt+1's sub-step 0, B of tile kt+2 into
+            // the slot of tile kt's A (or C quarters 1 and 2 into tile kt's two
+            // slots, or quarter 3 into tile kt's A slot)
             {
                 const i32x4 rb = gb.rsrc();
-                ring_sub(std::integral_constant<int, WL ? LPB : 0>{}, a1, b1,
+                ring_sub(std::integral_constant<int, WL ? LPB : CPH == 1 ? 16 : CPH == 2 ? 8 : 0>{}, a1, b1,
                          [&](int r) { read2(an_at, bn_at, 0, r, a0, b0); },
                          [&](int d) {
-                             if (loads)
+                             if constexpr (CPH == 1) cq_load(1 + d / 8, d % 8);
+                             else if constexpr (CPH == 2) cq_load(3, d);
+                             else if (loads)
                                  dma16_m0(rb, group_voff(lb.template offset<KMASK>(d, kv), d % kLoadGroup),
                                           d % kLoadGroup);
                          },
                          [&](int g) {
-                             if (loads) set_m0(a_at, wofs_b + g * kLoadGroup * 1024);
+                             if constexpr (CPH == 1)
+                                 set_m0(g < 2 ? a_at : b_at, wofs_a + (g % 2) * kLoadGroup * 1024);
+                             else if (loads)
+                                 set_m0(a_at, wofs_b + g * kLoadGroup * 1024);
                          });
             }
             if constexpr (WL) gb.advance();
+            if constexpr (CPH == 1) {
+                cq0 = ld_at;
+                cq1 = a_at;
+                cq2 = b_at;
+            } else if constexpr (CPH == 2) {
+                cq3 = a_at;
+            }
             // items 2kt+2 .. 2kt+6 are in slots s_an, s_bn, s_ld, s_a, s_b
             s_a = an_at;
             s_b = bn_at;
@@ -715,9 +761,16 @@ void gemm_dma_kernel(const GemmArgs args) {
             s_bn = a_at;
             s_ld = b_at;
         };
+        using C0 = std::integral_constant<int, 0>;
         int kt = 0;
-        for (; kt < nkt - 2; ++kt) iter(kt, std::true_type{});
-        for (; kt < nkt; ++kt) iter(kt, std::false_type{});
+        for (; kt < nkt - 2; ++kt) iter(kt, std::true_type{}, C0{});
+        if constexpr (C16) {
+            // kt == max(nkt - 2, 0)
+            iter(kt, std::false_type{}, std::integral_constant<int, 1>{});
+            if (kt + 1 < nkt) iter(kt + 1, std::false_type{}, std::integral_constant<int, 2>{});
+        } else {
+            for (; kt < nkt; ++kt) iter(kt, std::false_type{}, C0{});
+        }
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" :::
                          "memory");
       }
@@ -920,7 +973,11 @@ void gemm_dma_kernel(const GemmArgs args) {
     bool c_lds = false;
     if constexpr (EPI == EPI_BETA && (OUT == DT_F16 || OUT == DT_BF16)) {
         c_lds = beta != 0.f && args.c_dma_ok != 0 && m0 + BM <= M && n0 + BN <= N;
-        if (c_lds) {
+        if (c_pf) {
+            // the quarters loaded during the last iterations: every wave's
+            // loads have landed
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        } else if (c_lds) {
             // every wave is done with the operand stages
             asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
             const i32x4 rcc = rsrc4(Cb, args.c_extent - c_org);
@@ -1115,8 +1172,12 @@ void gemm_dma_kernel(const GemmArgs args) {
                         if (c_lds) {
                             // C_old from the LDS image (8 bytes: 4 values)
                             const int cq = (nl * 2) / 16;
-                            const uint32_t a = lds + ml * CRB + ((cq ^ ((ml & 15) * CSW)) << 4) +
-                                               ((nl * 2) & 15);
+                            // the row's place in the image: contiguous, or in
+                            // the slot of its quarter (64 rows)
+                            const int cqi = (wm * WTM + i * MS) / 64;   // the quarter (uniform)
+                            const uint32_t cqa = cqi == 0 ? cq0 : cqi == 1 ? cq1 : cqi == 2 ? cq2 : cq3;
+                            const uint32_t row_at = c_pf ? cqa + (ml % 64) * CRB : lds + ml * CRB;
+                            const uint32_t a = row_at + ((cq ^ ((ml & 15) * CSW)) << 4) + ((nl * 2) & 15);
                             const u32x2 w = *(const TCG_LDS u32x2 *)(size_t)a;
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
