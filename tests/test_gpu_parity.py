@@ -224,6 +224,20 @@ def test_dma_kernel_batched_padded(a, c, ta, tb, tile):
     dma_check(p, "dma batched", tile)
 
 
+@pytest.mark.parametrize("k", [64, 128, 192, 320])
+@pytest.mark.parametrize("ta,tb", [(False, False), (True, False), (False, True)],
+                         ids=["NN", "TN", "NT"])
+@pytest.mark.parametrize("a,c", [("f16", "f16"), ("bf16", "bf16")], ids=["f16-f16", "bf16-bf16"])
+def test_dma_ring_beta_c_tile(a, c, ta, tb, k):
+    """beta = 1 with a 16-bit C on the 256x256 ring tile.  Interior tiles read
+    C_old from an LDS image of the tile: loaded during the loop's last two
+    K-tiles when there are at least three (K = 192, 320), after the loop
+    otherwise (K = 64, 128).  Batch 2 with a padded ldc (rows stay whole
+    16-byte chunks), and one ragged column of tiles, which reads C directly."""
+    p = problem(a, c, 512, 520, k, ta, tb, batch=2, ldc=520 + 8)
+    dma_check(p, "dma ring beta K%d" % k, "dma")
+
+
 @pytest.mark.parametrize("tile", DMA_TILES)
 @pytest.mark.parametrize("a,c", [("bf16", "f32"), ("f16", "f16")])
 def test_dma_kernel_exact_regime_bitwise(a, c, tile):
