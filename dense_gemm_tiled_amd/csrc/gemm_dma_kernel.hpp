@@ -645,14 +645,15 @@ void gemm_dma_kernel(const GemmArgs args) {
             load_epi1<OUT>(make_epi<OUT>(args, z, N), n0 + tid, N, epi_b, epi_s);
     }
     // beta != 0 with a 16-bit C tile inside C: the epilogue reads C_old from
-    // an LDS image of the tile (below).  On the ring with at least three
+    // an LDS image of the tile (below).  On the ring with at least two
     // K-tiles the image's four 64-row quarters load during the last two
     // iterations, which load no operands, into slots free by then (c_pf);
-    // cq0 .. cq3: LDS addresses of the quarters.
+    // cq0 .. cq3: LDS addresses of the quarters, cfree: the fifth slot, free
+    // once the loop is done.
     constexpr bool C16 = EPI == EPI_BETA && (OUT == DT_F16 || OUT == DT_BF16);
     [[maybe_unused]] const bool c_pf = C16 && RING && args.beta != 0.f && args.c_dma_ok != 0 &&
-                                       m0 + BM <= M && n0 + BN <= N && nkt >= 3;
-    [[maybe_unused]] uint32_t cq0 = lds, cq1 = lds, cq2 = lds, cq3 = lds;
+                                       m0 + BM <= M && n0 + BN <= N && nkt >= 2;
+    [[maybe_unused]] uint32_t cq0 = lds, cq1 = lds, cq2 = lds, cq3 = lds, cfree = lds;
     if constexpr (RING) {
       if (nkt > 0) {
         // items 0 .. 3 (tiles 0 and 1) into slots 0 .. 3
@@ -753,6 +754,7 @@ void gemm_dma_kernel(const GemmArgs args) {
                 cq2 = b_at;
             } else if constexpr (CPH == 2) {
                 cq3 = a_at;
+                cfree = b_at;
             }
             // items 2kt+2 .. 2kt+6 are in slots s_an, s_bn, s_ld, s_a, s_b
             s_a = an_at;
@@ -882,19 +884,23 @@ void gemm_dma_kernel(const GemmArgs args) {
                       : (WTM / 4 * SPITCH <= SREGION) ? WTM / 4 : WTM / 8;
     static_assert(SCH >= MS && SCH * SPITCH <= SREGION && WTM % SCH == 0, "staging band fits");
     constexpr int SLPR = SROW / 16, SRPI = 64 / SLPR;   // lanes per row, rows per read
-    [[maybe_unused]] auto staged_store = [&](__amdgpu_buffer_rsrc_t r, int ld, auto &&col, auto &&pack) {
-        // every wave is done with the stages and no load is still writing them
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        TCG_LDS char *reg = (TCG_LDS char *)(size_t)(lds + SBASE + wave * SREGION);
+    // (staged_in: the same into the region at `region`, SCHX rows at a time,
+    // band(c0) first in the band of rows c0 ..)
+    [[maybe_unused]] auto staged_in = [&](auto sch_tag, uint32_t region, __amdgpu_buffer_rsrc_t r, int ld,
+                                          auto &&band, auto &&col, auto &&pack) {
+        constexpr int SCHX = decltype(sch_tag)::value;
+        static_assert(SCHX >= MS && WTM % SCHX == 0, "staging band");
+        TCG_LDS char *reg = (TCG_LDS char *)(size_t)region;
 #pragma unroll
-        for (int c0 = 0; c0 < WTM; c0 += SCH) {
+        for (int c0 = 0; c0 < WTM; c0 += SCHX) {
+            band(c0);
 #pragma unroll
             for (int j = 0; j < FN; ++j)
 #pragma unroll
                 for (int q = 0; q < NG; ++q) {
                     col(j, q);
 #pragma unroll
-                    for (int i = c0 / MS; i < (c0 + SCH) / MS; ++i) {
+                    for (int i = c0 / MS; i < (c0 + SCHX) / MS; ++i) {
                         u32 w[CES];
                         pack(i, j, q, w);
                         TCG_LDS char *at =
@@ -906,13 +912,19 @@ void gemm_dma_kernel(const GemmArgs args) {
             // the LDS runs one wave's accesses in order: the reads below see
             // the writes above, and the next band's writes follow these reads
 #pragma unroll
-            for (int t = 0; t < SCH / SRPI; ++t) {
+            for (int t = 0; t < SCHX / SRPI; ++t) {
                 const int row = t * SRPI + lane / SLPR, ch = lane % SLPR;
                 const u32x4 d = *(const TCG_LDS u32x4 *)(reg + row * SPITCH + ch * 16);
                 __builtin_amdgcn_raw_buffer_store_b128(
                     d, r, (wm * WTM + c0 + row) * ld * CES + wn * WTN * CES + ch * 16, 0, 0);
             }
         }
+    };
+    [[maybe_unused]] auto staged_store = [&](__amdgpu_buffer_rsrc_t r, int ld, auto &&col, auto &&pack) {
+        // every wave is done with the stages and no load is still writing them
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        staged_in(std::integral_constant<int, SCH>{}, lds + SBASE + wave * SREGION, r, ld, [](int) {}, col,
+                  pack);
     };
     if constexpr (OUT == OUT_PARTIAL) {
         // raw fp32 / int32 partial sums of this K slice: workspace plane g
@@ -971,13 +983,70 @@ void gemm_dma_kernel(const GemmArgs args) {
     constexpr int CSW = CRB >= 512 ? 2 : 1;
     static_assert(BM * CRB <= LDS_BYTES, "the C tile fits the operand stages");
     bool c_lds = false;
-    if constexpr (EPI == EPI_BETA && (OUT == DT_F16 || OUT == DT_BF16)) {
-        c_lds = beta != 0.f && args.c_dma_ok != 0 && m0 + BM <= M && n0 + BN <= N;
+    // v = beta * C_old + alpha * acc for the 4 values of tile row ml, columns
+    // nl .. nl+3, C_old from the tile's LDS image, the row at LDS address
+    // row_at (its 16-byte chunks swizzled by the row's low bits)
+    // (c_old4: the 8 bytes of C_old; beta4: v from them)
+    [[maybe_unused]] auto c_old4 = [&](uint32_t row_at, int ml, int nl) {
+        const int cq = (nl * 2) / 16;
+        const uint32_t a = row_at + ((cq ^ ((ml & 15) * CSW)) << 4) + ((nl * 2) & 15);
+        return *(const TCG_LDS u32x2 *)(size_t)a;
+    };
+    [[maybe_unused]] auto beta4 = [&](u32x2 w, float (&v)[4]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const u32 h = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            const float old = OUT == DT_BF16 ? from_bf16_bits(h) : from_f16_bits(h);
+            v[e] = __builtin_fmaf(beta, old, v[e] * alpha);
+        }
+    };
+    [[maybe_unused]] auto beta_lds4 = [&](uint32_t row_at, int ml, int nl, float (&v)[4]) {
+        beta4(c_old4(row_at, ml, nl), v);
+    };
+    if constexpr (EPI == EPI_BETA && (OUT == DT_F16 || OUT == DT_BF16) && RING) {
         if (c_pf) {
             // the quarters loaded during the last iterations: every wave's
-            // loads have landed
+            // loads have landed.  The results go out along rows through the
+            // fifth slot, a quarter of it per wave (the quarters hold C_old
+            // meanwhile).  The ring's other tiles read C_old from C itself.
             asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        } else if (c_lds) {
+            constexpr int SREG_C = SLOT / NW / 16 * 16;
+            constexpr int SCH_C = (WTM / 4 * SPITCH <= SREG_C) ? WTM / 4
+                                : (WTM / 8 * SPITCH <= SREG_C) ? WTM / 8 : MS;
+            static_assert(SCH_C * SPITCH <= SREG_C, "staging band fits a quarter slot");
+            // the wave's rows span two quarters: the first and second, or the
+            // third and fourth
+            static_assert(BM == 256 && WTM == 128, "two C quarters per wave");
+            const uint32_t qw0 = wm == 0 ? cq0 : cq2, qw1 = wm == 0 ? cq1 : cq3;
+            // a band's C_old is read before its first write to the staging
+            // region, so that the reads go out together
+            constexpr int BI = SCH_C / MS;
+            u32x2 cold[BI][FN][NG];
+            staged_in(std::integral_constant<int, SCH_C>{}, cfree + wave * SREG_C, rc, ldc,
+                      [&](int c0) {
+#pragma unroll
+                          for (int ib = 0; ib < BI; ++ib) {
+                              const int i = c0 / MS + ib, ml = ml_of(i);
+                              const uint32_t row_at = (i * MS < 64 ? qw0 : qw1) + (ml % 64) * CRB;
+#pragma unroll
+                              for (int j = 0; j < FN; ++j)
+#pragma unroll
+                                  for (int q = 0; q < NG; ++q) cold[ib][j][q] = c_old4(row_at, ml, nl_of(j, q));
+                          }
+                      },
+                      [](int, int) {}, [&](int i, int j, int q, u32 (&w)[CES]) {
+                          float v[4];
+#pragma unroll
+                          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+                          beta4(cold[i % BI][j][q], v);
+                          w[0] = pack2_16<OUT>(v[0], v[1]);
+                          w[1] = pack2_16<OUT>(v[2], v[3]);
+                      });
+            return;
+        }
+    } else if constexpr (EPI == EPI_BETA && (OUT == DT_F16 || OUT == DT_BF16)) {
+        c_lds = beta != 0.f && args.c_dma_ok != 0 && m0 + BM <= M && n0 + BN <= N;
+        if (c_lds) {
             // every wave is done with the operand stages
             asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
             const i32x4 rcc = rsrc4(Cb, args.c_extent - c_org);
@@ -1171,20 +1240,7 @@ void gemm_dma_kernel(const GemmArgs args) {
                     if constexpr (EPI == EPI_BETA && (OUT == DT_F16 || OUT == DT_BF16)) {
                         if (c_lds) {
                             // C_old from the LDS image (8 bytes: 4 values)
-                            const int cq = (nl * 2) / 16;
-                            // the row's place in the image: contiguous, or in
-                            // the slot of its quarter (64 rows)
-                            const int cqi = (wm * WTM + i * MS) / 64;   // the quarter (uniform)
-                            const uint32_t cqa = cqi == 0 ? cq0 : cqi == 1 ? cq1 : cqi == 2 ? cq2 : cq3;
-                            const uint32_t row_at = c_pf ? cqa + (ml % 64) * CRB : lds + ml * CRB;
-                            const uint32_t a = row_at + ((cq ^ ((ml & 15) * CSW)) << 4) + ((nl * 2) & 15);
-                            const u32x2 w = *(const TCG_LDS u32x2 *)(size_t)a;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const u32 h = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                                const float old = OUT == DT_BF16 ? from_bf16_bits(h) : from_f16_bits(h);
-                                v[e] = __builtin_fmaf(beta, old, v[e] * alpha);
-                            }
+                            beta_lds4(lds + ml * CRB, ml, nl, v);
                             store_c4<OUT>(rc, off, 4, true, v);
                             continue;
                         }

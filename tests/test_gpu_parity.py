@@ -229,11 +229,12 @@ def test_dma_kernel_batched_padded(a, c, ta, tb, tile):
                          ids=["NN", "TN", "NT"])
 @pytest.mark.parametrize("a,c", [("f16", "f16"), ("bf16", "bf16")], ids=["f16-f16", "bf16-bf16"])
 def test_dma_ring_beta_c_tile(a, c, ta, tb, k):
-    """beta = 1 with a 16-bit C on the 256x256 ring tile.  Interior tiles read
-    C_old from an LDS image of the tile: loaded during the loop's last two
-    K-tiles when there are at least three (K = 192, 320), after the loop
-    otherwise (K = 64, 128).  Batch 2 with a padded ldc (rows stay whole
-    16-byte chunks), and one ragged column of tiles, which reads C directly."""
+    """beta = 1 with a 16-bit C on the 256x256 ring tile.  With at least two
+    K-tiles (K = 128, 192, 320) interior tiles read C_old from an LDS image
+    of the tile loaded during the loop's last two K-tiles, and store through
+    LDS along rows; with one (K = 64) they read C directly.  Batch 2 with a
+    padded ldc (rows stay whole 16-byte chunks), and one ragged column of
+    tiles, which reads C directly."""
     p = problem(a, c, 512, 520, k, ta, tb, batch=2, ldc=520 + 8)
     dma_check(p, "dma ring beta K%d" % k, "dma")
 
