@@ -63,6 +63,8 @@ def parse():
                     help="measure every workload and print a table (not the one-line contract)")
     ap.add_argument("--fused-compare", action="store_true",
                     help="fused bias+GELU against unfused passes, interleaved")
+    ap.add_argument("--layout-table", action="store_true",
+                    help="4096^3 over layouts, bf16/fp16 and beta 0/1, interleaved")
     ap.add_argument("--smi-sampler", type=float, default=0.0, help=argparse.SUPPRESS)
     return ap.parse_args()
 
@@ -403,6 +405,49 @@ def run_fused_compare(args):
                       "blocks_per_round": 2, "calls_per_block": 10}), flush=True)
 
 
+def run_layout_table(args):
+    """4096^3 with alpha = 0.5 over the four layouts, bf16 and fp16 inputs
+    (output in the input type) and beta 0 and 1, interleaved in one process:
+    8 rounds, each a block of 20 back-to-back calls of every case in turn,
+    each block between two events; four input sets in rotation (bell-shaped
+    random A and B scaled by 0.02, C unscaled)."""
+    import torch
+    import dense_gemm_tiled_amd as tg
+    torch.cuda.set_device(0)
+    tg.load_library()
+    n = 4096
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234)
+    types = {"bf16": torch.bfloat16, "f16": torch.float16}
+    sets = {k: [tuple(torch.randn(n, n, device="cuda", generator=gen).mul_(sc).to(t)
+                      for sc in (0.02, 0.02, 1.0)) for _ in range(4)]
+            for k, t in types.items()}
+    cases = [(dt, beta, ta, tb) for dt in types for beta in (0.0, 1.0)
+             for ta in (False, True) for tb in (False, True)]
+
+    def stepper(case):
+        dt, beta, ta, tb = case
+
+        def step(i):
+            a, b, c = sets[dt][i % 4]
+            tg.gemm(a, b, c, alpha=0.5, beta=beta, transpose_a=ta, transpose_b=tb)
+        return step
+
+    steps = {cs: stepper(cs) for cs in cases}
+    for f in steps.values():
+        settle(f, 0.1)
+    res = {cs: [] for cs in cases}
+    for _ in range(8):
+        for cs, f in steps.items():
+            res[cs].extend(block_times(f, 1, 20).tolist())
+    print("| | NN | NT | TN | TT |")
+    print("|---|---|---|---|---|")
+    for dt in types:
+        for beta in (0.0, 1.0):
+            row = [np.median(res[(dt, beta, ta, tb)]) for ta in (False, True) for tb in (False, True)]
+            print("| %s, beta = %g | %s |" % (dt, beta, " | ".join("%.1f" % v for v in row)), flush=True)
+
+
 def pcts(x):
     x = np.asarray(x, dtype=float)
     return {"p10": float(np.percentile(x, 10)), "p50": float(np.percentile(x, 50)),
@@ -419,6 +464,9 @@ def main():
         return
     if args.fused_compare:
         run_fused_compare(args)
+        return
+    if args.layout_table:
+        run_layout_table(args)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
