@@ -33,8 +33,12 @@
 //     write (their immediate offset moves the LDS address and the buffer
 //     offset alike), and the next tile's buffer resources advance by one
 //     K-tile with scalar adds;
-//   * interior tiles whose output rows are whole 16-byte chunks are stored
-//     through LDS, 16 bytes per lane along the rows.
+//   * interior tiles are stored through LDS, 16 bytes per lane along the
+//     rows (32-bit outputs where C's rows are whole 16-byte chunks);
+//   * with beta != 0 and a 16-bit C, an interior tile of the 256 x 256 ring
+//     loads its C tile into LDS during the last two K-tiles (which load no
+//     operands), into slots those K-tiles free, and stages its results in
+//     the one slot left over.
 //
 // The MFMAs, the LDS-bound loads and the barrier are inline assembly.  The
 // accumulators are pinned to AGPRs (operand constraint "+a", destination =
@@ -876,7 +880,11 @@ void gemm_dma_kernel(const GemmArgs args) {
     // values of block (i, j), group q, in the output's type.  Rows past M
     // start past the store range of r, so their stores are dropped.  The
     // regions start past the bias and scales that the fused epilogue keeps at
-    // the start of the stages.
+    // the start of the stages.  16-bit outputs take this path also where C's
+    // rows do not start on 16-byte boundaries (the stores are unaligned then,
+    // which the GPU allows; int8 4093 x 4099 x 4096 dequantized into bf16 at
+    // ldc = 4099: 78.2 -> 71.7 us per call); 32-bit ones only where they do
+    // (int32 out at ldc = 4099: no gain, the main kernel 1 % slower).
     constexpr int SROW = WTN * CES, SPITCH = SROW + 16 * CES;
     constexpr int SBASE = EPI_AFTER ? (EPI_LDS * 4 + 1023) / 1024 * 1024 : 0;
     constexpr int SREGION = (LDS_BYTES - SBASE) / NW / 16 * 16;
@@ -1124,7 +1132,7 @@ void gemm_dma_kernel(const GemmArgs args) {
                      });
     };
     if constexpr (EPI_LDS > 1) {
-        if (interior && beta == 0.f && args.c_dma_ok) {
+        if (interior && beta == 0.f && (CES == 2 || args.c_dma_ok)) {
             if (ep.act == ACT_GELU_TANH) fused_staged(std::integral_constant<int, ACT_GELU_TANH>{});
             else if (ep.act == ACT_RELU) fused_staged(std::integral_constant<int, ACT_RELU>{});
             else fused_staged(std::integral_constant<int, ACT_NONE>{});
@@ -1138,7 +1146,7 @@ void gemm_dma_kernel(const GemmArgs args) {
         }
     }
     if constexpr (EPI == EPI_PLAIN && OUT != OUT_PARTIAL) {
-        if (interior && args.c_dma_ok) {
+        if (interior && (CES == 2 || args.c_dma_ok)) {
             staged_store(rc, ldc, [](int, int) {}, [&](int i, int j, int q, u32 (&w)[CES]) {
                 if constexpr (OUT == DT_I32) {
 #pragma unroll
