@@ -13,12 +13,13 @@ namespace {
 
 // Output types that exist for this input type (include/tcgemm.h lists the
 // supported tuples); split-K partials only for the classes the planner
-// splits (64x64 and the 128x128 tiles); the direct-to-LDS classes only for
-// 16-bit and int8 inputs.
+// splits (64x64, the 128x128 tiles and the 256x256 ring); the direct-to-LDS
+// classes only for 16-bit and int8 inputs.
 constexpr bool out_ok(int cls, int out) {
     if (is_dma_class(cls) && TCG_DT == DT_F32) return false;
     if (out == OUT_PARTIAL)
-        return cls == TILE_64 || cls == TILE_128 || cls == TILE_128_DMA || cls == TILE_128_DMA4;
+        return cls == TILE_64 || cls == TILE_128 || cls == TILE_128_DMA || cls == TILE_128_DMA4 ||
+               cls == TILE_256_DMA;
     if (cls == TILE_THIN) return false;
     // int8 into a float output: the dequantizing fused epilogue only
     if (TCG_DT == DT_I8) return out == DT_I32 || out == DT_F32 || out == DT_F16 || out == DT_BF16;

@@ -251,7 +251,8 @@ bool dma_types(const Problem &p) { return p.dt == TC_F16 || p.dt == TC_BF16 || p
 
 // Tile classes whose kernel can write split-K partial sums.
 bool splits_ok(int cls) {
-    return cls == TILE_64 || cls == TILE_128 || cls == TILE_128_DMA || cls == TILE_128_DMA4;
+    return cls == TILE_64 || cls == TILE_128 || cls == TILE_128_DMA || cls == TILE_128_DMA4 ||
+           cls == TILE_256_DMA;
 }
 
 // Rows and columns (elements) of operand w (0 = A, 1 = B) as stored.
@@ -445,6 +446,17 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true, const Choice 
         if (!strip && r128 < r256) cls = TILE_128;
     }
     int64_t splits = 1;
+    // 16-bit and int8 outputs of 129 to 191 tiles of 128 x 128 (M and N at
+    // least 256) and a long K: too many of those tiles for a K split of them
+    // to fit one round of workgroups, too few to fill the chip unsplit.  The
+    // 256 x 256 ring takes them with as many K slices as fit one round, at
+    // least 16 K-tiles per slice and at least 192 workgroups.
+    const int64_t t256 = tile_count(TILE_256), t128 = tile_count(TILE_128);
+    int64_t s256 = t256 > 0 ? 256 / t256 : 0;
+    if (s256 > ktiles / 16) s256 = ktiles / 16;
+    if (s256 > 32) s256 = 32;
+    const bool wide_split = dma && cls == TILE_64 && t128 > 128 && p.M >= 256 && p.N >= 256 &&
+                            p.alpha != 0.0f && s256 >= 2 && t256 * s256 >= 192;
     // Few tiles (under 128 of 64 x 64) and a short K: the 4 waves of a
     // workgroup take every 4th K-tile each and add their partial tiles in
     // LDS (each K-tile of the register-staged loop would wait out a memory
@@ -457,12 +469,12 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true, const Choice 
     // for 8 slices of split-K plus the reduction; fp32 256 x 256 x 1024:
     // 8.6 against 10.4 us.
     const int ks_cls = tile_count(TILE_32_KS) >= 128 ? TILE_32_KS : TILE_16_KS;
-    const bool ks = cls == TILE_64 && tile_count(TILE_64) < 128 && ktiles >= 4 &&
+    const bool ks = !wide_split && cls == TILE_64 && tile_count(TILE_64) < 128 && ktiles >= 4 &&
                     p.alpha != 0.0f &&
                     (ktiles < 16 || (!dma && ktiles <= 32 && tile_count(ks_cls) >= 256));
     // tall K and too few tiles to fill the chip: split K
     const bool split =
-        !ks && cls == TILE_64 && tile_count(TILE_64) < 128 && ktiles >= 16 && p.alpha != 0.0f;
+        !wide_split && !ks && cls == TILE_64 && tile_count(TILE_64) < 128 && ktiles >= 16 && p.alpha != 0.0f;
     // 16-bit and int8 outputs of 32 to 191 tiles of 128 x 128 (too few for
     // that class by the count above; M and N at least 128) run on 128 x 128
     // direct-to-LDS tiles, not on 64 x 64 tiles of the register-staged loop:
@@ -473,9 +485,12 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true, const Choice 
     // against 68.5 on 64 x 64 and 41.0 unsliced; 1024 x 768 x 2048 19.6
     // against 31.3 and 22.7; 1024^3 12.4 unsliced against 16.1 on 64 x 64
     // and 19.1 with slices; int8 2048 x 512 x 2048 12.3 unsliced against 21.6.
-    const bool mid = !ks && !split && dma && cls == TILE_64 && tile_count(TILE_128) >= 32 &&
+    const bool mid = !wide_split && !ks && !split && dma && cls == TILE_64 && tile_count(TILE_128) >= 32 &&
                      p.M >= 128 && p.N >= 128 && p.alpha != 0.0f;
-    if (ks) {
+    if (wide_split) {
+        cls = TILE_256;                                          // TILE_256 -> TILE_256_DMA below
+        splits = s256;
+    } else if (ks) {
         cls = ks_cls;
     } else if (mid) {
         splits = ktiles >= 32 ? 256 / tile_count(TILE_128_DMA4) : 1;

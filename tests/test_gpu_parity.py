@@ -224,6 +224,21 @@ def test_dma_kernel_batched_padded(a, c, ta, tb, tile):
     dma_check(p, "dma batched", tile)
 
 
+@pytest.mark.parametrize("a,c,ta,tb", [("bf16", "bf16", False, False), ("f16", "f32", True, False),
+                                       ("i8", "i32", False, True)],
+                         ids=["bf16-bf16-NN", "f16-f32-TN", "i8-i32-NT"])
+def test_dma_ring_split_k(a, c, ta, tb):
+    """Split-K on the 256x256 ring by the planner's own choice: 169 tiles of
+    128 x 128 (1664 x 1544, ragged in M and N on the 256 tile) and a K of 96
+    K-tiles, so 5 slices of 19 to 20 -- the partial sums and their reduction
+    against the oracle."""
+    import dense_gemm_tiled_amd as tg
+    k = 96 * (128 if a == "i8" else 64)
+    p = problem(a, c, 1664, 1544, k, ta, tb)
+    check(p, "ring split-K")
+    assert tg.last_kernel().endswith("_256x256_dma+splitk_reduce"), tg.last_kernel()
+
+
 @pytest.mark.parametrize("k", [64, 128, 192, 320])
 @pytest.mark.parametrize("ta,tb", [(False, False), (True, False), (False, True)],
                          ids=["NN", "TN", "NT"])
@@ -255,14 +270,15 @@ def test_dma_kernel_exact_regime_bitwise(a, c, tile):
     assert np.array_equal(got.view(np.uint8), ref.out.view(np.uint8))
 
 
-@pytest.mark.parametrize("tile", ["dma128", "dma128x4"])
+@pytest.mark.parametrize("tile", ["dma128", "dma128x4", "dma"])
 @pytest.mark.parametrize("splits", [3, 5])
 @pytest.mark.parametrize("ta,tb", LAYOUTS, ids=[lay(*l) for l in LAYOUTS])
 @pytest.mark.parametrize("a,c", DMA_PAIRS, ids=["%s-%s" % pc for pc in DMA_PAIRS])
 def test_dma128_split_k(a, c, ta, tb, splits, tile):
-    """Split-K on the 128x128 direct-to-LDS tiles (2 and 4 LDS stages): 2 x 2
-    tiles ragged in M and N, batch 2, a K whose last slice is shorter and
-    ends in a partial tile; alpha = 0.5 and beta = 1 for floats."""
+    """Split-K on the 128x128 direct-to-LDS tiles (2 and 4 LDS stages) and
+    the 256x256 ring: 2 x 2 tiles ragged in M and N (one ragged tile on the
+    ring), batch 2, a K whose last slice is shorter and ends in a partial
+    tile; alpha = 0.5 and beta = 1 for floats."""
     if a == "i8":
         p = problem(a, c, 144, 208, 1104, ta, tb, batch=2)
     else:

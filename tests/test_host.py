@@ -378,6 +378,27 @@ def test_plan_mid_size_outputs():
     assert plan_of(P("m", 1024, 1024, 1024, "f32", "f32"))["kernel"] == "gemm_f32_nn_64x64"
 
 
+def test_plan_wide_split_on_the_256_ring():
+    """129 to 191 tiles of 128 x 128 with a long K: the 256 x 256 ring with as
+    many K slices as fit one round (at least 16 K-tiles each, at least 192
+    workgroups); fewer 128 x 128 tiles keep their own split, a short K stays
+    unsplit."""
+    P = workloads.Problem
+    pl = plan_of(P("w", 1536, 1536, 12288, "bf16", "bf16"))
+    assert pl["kernel"] == "gemm_bf16_nn_256x256_dma+splitk_reduce", pl["kernel"]
+    assert pl["splits"] == 7 and pl["grid"] == 252, pl
+    assert (pl["splits"] - 1) * pl["k_per_split"] < 12288 <= pl["splits"] * pl["k_per_split"]
+    assert pl["k_per_split"] >= 16 * pl["tile_k"]
+    pl = plan_of(P("w", 1280, 1792, 16384, "f16", "f32", transpose_a=True))
+    assert pl["kernel"] == "gemm_f16_tn_256x256_dma+splitk_reduce" and pl["grid"] == 245, pl
+    # 64 tiles of 128 x 128: their own 4-stage split
+    pl = plan_of(P("w", 1024, 1024, 16384, "bf16", "bf16"))
+    assert pl["kernel"] == "gemm_bf16_nn_128x128_dma4+splitk_reduce", pl["kernel"]
+    # too short a K for 16 K-tiles in each of enough slices
+    pl = plan_of(P("w", 1536, 1536, 2048, "bf16", "bf16"))
+    assert pl["kernel"] == "gemm_bf16_nn_128x128_dma" and pl["splits"] == 1, pl
+
+
 def test_plan_tile_not_mostly_padding():
     """A class is taken only when its tile is less than half empty along M
     and N: a batch of 128 x 128 problems fills the chip with 256 x 256
