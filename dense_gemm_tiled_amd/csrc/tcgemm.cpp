@@ -445,6 +445,19 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true, const Choice 
         const double r128 = 0.625 * (double)ceil_div(tile_count(TILE_128), 512);
         if (!strip && r128 < r256) cls = TILE_128;
     }
+    // The same comparison the other way: too few 256 x 256 tiles to be taken
+    // by count (under 192, M and N at least 256) but more 128 x 128 tiles
+    // than two workgroups per CU hold (over 512): one partly filled round of
+    // 256 x 256 tiles costs less than two rounds of 128 x 128.  Measured,
+    // bf16 NN, us per call (256 / 128): 3072^2 x 8192 155.5 / 186.3, 3328 x
+    // 3072 x 8192 141.6 / 177.9, 3072^2 x 4096 82.9 / 98.2; and where 128 x
+    // 128 stays (484 and 400 tiles): 2816^2 x 8192 148.5 / 120.1, 2560^2 x
+    // 8192 141.1 / 101.5.
+    if (dma && cls == TILE_128 && p.M >= 256 && p.N >= 256 && tile_count(TILE_256) <= 256) {
+        const double r256 = (double)ceil_div(tile_count(TILE_256), 256);
+        const double r128 = 0.625 * (double)ceil_div(tile_count(TILE_128), 512);
+        if (r256 < r128) cls = TILE_256;
+    }
     int64_t splits = 1;
     // 16-bit and int8 outputs of 129 to 191 tiles of 128 x 128 (M and N at
     // least 256) and a long K: too many of those tiles for a K split of them

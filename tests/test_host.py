@@ -399,6 +399,19 @@ def test_plan_wide_split_on_the_256_ring():
     assert pl["kernel"] == "gemm_bf16_nn_128x128_dma" and pl["splits"] == 1, pl
 
 
+def test_plan_one_partial_round_of_256_tiles():
+    """Under 192 tiles of 256 x 256 but over 512 of 128 x 128: one partly
+    filled round of 256 x 256 tiles rather than two rounds of 128 x 128;
+    up to 512 of them stay on 128 x 128."""
+    P = workloads.Problem
+    for shape in [(3072, 3072, 8192), (3328, 3072, 8192), (3072, 3072, 4096)]:
+        pl = plan_of(P("r", *shape, "bf16", "bf16"))
+        assert pl["kernel"] == "gemm_bf16_nn_256x256_dma" and pl["grid"] < 192, (shape, pl)
+    for shape in [(2816, 2816, 8192), (2560, 2560, 8192)]:
+        pl = plan_of(P("r", *shape, "bf16", "bf16"))
+        assert pl["kernel"] == "gemm_bf16_nn_128x128_dma", (shape, pl)
+
+
 def test_plan_tile_not_mostly_padding():
     """A class is taken only when its tile is less than half empty along M
     and N: a batch of 128 x 128 problems fills the chip with 256 x 256
