@@ -464,11 +464,18 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true, const Choice 
     // to fit one round of workgroups, too few to fill the chip unsplit.  The
     // 256 x 256 ring takes them with as many K slices as fit one round, at
     // least 16 K-tiles per slice and at least 192 workgroups.
+    // The same for 192 to 256 tiles of 128 x 128 (one workgroup per CU
+    // unsplit, each streaming all of K) when K is long enough that the
+    // partial sums stay a small part of the traffic: at least 25 K-tiles
+    // per slice (8 bytes of partial sums written and read per output and
+    // slice, against 2 K multiply-adds).
     const int64_t t256 = tile_count(TILE_256), t128 = tile_count(TILE_128);
+    const bool few128 = cls == TILE_64 && t128 > 128;
+    const bool one128 = cls == TILE_128 && t128 <= 256;
     int64_t s256 = t256 > 0 ? 256 / t256 : 0;
-    if (s256 > ktiles / 16) s256 = ktiles / 16;
+    if (s256 > ktiles / (few128 ? 16 : 25)) s256 = ktiles / (few128 ? 16 : 25);
     if (s256 > 32) s256 = 32;
-    const bool wide_split = dma && cls == TILE_64 && t128 > 128 && p.M >= 256 && p.N >= 256 &&
+    const bool wide_split = dma && (few128 || one128) && p.M >= 256 && p.N >= 256 &&
                             p.alpha != 0.0f && s256 >= 2 && t256 * s256 >= 192;
     // Few tiles (under 128 of 64 x 64) and a short K: the 4 waves of a
     // workgroup take every 4th K-tile each and add their partial tiles in

@@ -381,7 +381,8 @@ def test_plan_mid_size_outputs():
 def test_plan_wide_split_on_the_256_ring():
     """129 to 191 tiles of 128 x 128 with a long K: the 256 x 256 ring with as
     many K slices as fit one round (at least 16 K-tiles each, at least 192
-    workgroups); fewer 128 x 128 tiles keep their own split, a short K stays
+    workgroups); 192 to 256 of them the same with at least 25 K-tiles per
+    slice; fewer 128 x 128 tiles keep their own split, a short K stays
     unsplit."""
     P = workloads.Problem
     pl = plan_of(P("w", 1536, 1536, 12288, "bf16", "bf16"))
@@ -397,6 +398,14 @@ def test_plan_wide_split_on_the_256_ring():
     # too short a K for 16 K-tiles in each of enough slices
     pl = plan_of(P("w", 1536, 1536, 2048, "bf16", "bf16"))
     assert pl["kernel"] == "gemm_bf16_nn_128x128_dma" and pl["splits"] == 1, pl
+    # 192 to 256 tiles of 128 x 128: split only with at least 25 K-tiles per slice
+    for shape in [(2048, 2048, 16384), (2048, 2048, 8192), (4096, 1024, 8192)]:
+        pl = plan_of(P("w", *shape, "bf16", "bf16"))
+        assert pl["kernel"] == "gemm_bf16_nn_256x256_dma+splitk_reduce", (shape, pl)
+        assert pl["splits"] == 4 and pl["k_per_split"] >= 25 * pl["tile_k"], (shape, pl)
+    for shape in [(4096, 1024, 4096), (2048, 2048, 4096), (2048, 2048, 2048)]:
+        pl = plan_of(P("w", *shape, "bf16", "bf16"))
+        assert pl["kernel"] == "gemm_bf16_nn_128x128_dma" and pl["splits"] == 1, (shape, pl)
 
 
 def test_plan_one_partial_round_of_256_tiles():
