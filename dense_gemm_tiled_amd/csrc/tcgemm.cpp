@@ -616,6 +616,48 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true, const Choice 
             pl->edge_at = (int32_t)(p.M - rm);
         }
     }
+    // Round split.  Past one round of 256 x 256 tiles, the tiles of the last
+    // partial round can cost more than they are worth to the whole launch:
+    // the rows (or columns) of tiles that fill whole rounds then run as one
+    // launch of 256 x 256 tiles and the rest as a second GEMM with a plan of
+    // its own, when the two cost less by the round count used above (a
+    // round of 256 x 256 tiles = 1, of 128 x 128 two per CU = 0.625; 0.05
+    // for the second launch).  Measured, bf16 NN, us per call (whole /
+    // split): 6144 x 4096 x 4096 199.2 / 171.3, 6144^3 379.0 / 358.0, 5120 x
+    // 4096 x 4096 158.6 / 144.9, 4096 x 4352 x 4096 150.7 / 140.7, 6144 x
+    // 4096 x 2048 100.7 / 92.0; 7168 x 4096 x 4096 (no gain by the count)
+    // 189.9 / 188.8.
+    if (pl->edge == 0 && allow_edge && dma && p.alpha != 0.0f && splits == 1 && p.batch == 1 &&
+        (cls == TILE_256_DMA || cls == TILE_128_DMA) && !knob(K_TILE) && !(ch && ch->cls >= 0) &&
+        !(env_edge && atoi(env_edge) == 0)) {
+        auto cost = [](int64_t m, int64_t n) {
+            const int64_t t2 = ceil_div(m, 256) * ceil_div(n, 256), t1 = ceil_div(m, 128) * ceil_div(n, 128);
+            const double r2 = (double)ceil_div(t2, 256), r1 = 0.625 * (double)ceil_div(t1, 512);
+            return r2 < r1 ? r2 : r1;
+        };
+        const int64_t tm = ceil_div(p.M, 256), tn = ceil_div(p.N, 256), t2 = tm * tn;
+        if (t2 > 256 && t2 % 256 != 0) {
+            const int64_t full = t2 / 256 * 256;   // tiles of the whole rounds
+            double best = cost(p.M, p.N) - 0.05;
+            const int64_t rows = full / tn, cols = full / tm;
+            if (rows >= 1 && rows < tm) {
+                const double c = (double)ceil_div(rows * tn, 256) + cost(p.M - rows * 256, p.N);
+                if (c < best) {
+                    best = c;
+                    pl->edge = 2;
+                    pl->edge_at = (int32_t)(rows * 256);
+                }
+            }
+            if (cols >= 1 && cols < tn) {
+                const double c = (double)ceil_div(cols * tm, 256) + cost(p.M, p.N - cols * 256);
+                if (c < best) {
+                    best = c;
+                    pl->edge = 1;
+                    pl->edge_at = (int32_t)(cols * 256);
+                }
+            }
+        }
+    }
 }
 
 // The part [lo, lo + n) of problem p along N (axis 1) or M (axis 2), and the

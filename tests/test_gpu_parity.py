@@ -484,6 +484,20 @@ def test_epilogue_dma_kernels(a, c, tile, act):
     assert tg.last_kernel().endswith(DMA_NAME[tile]), tg.last_kernel()
 
 
+@pytest.mark.parametrize("M,N", [(6144, 4096), (4096, 4232)], ids=["rows", "columns"])
+def test_round_split(M, N):
+    """Past one round of 256x256 tiles, the tiles of the whole rounds run as
+    one launch and the rest as a second GEMM (rows or columns): the plain
+    product with alpha = 0.5 and beta = 1, and the fused bias + GELU, whose
+    bias starts at the second part's first column, against the oracle."""
+    import dense_gemm_tiled_amd as tg
+    p = problem("bf16", "bf16", M, N, 128)
+    check(p, "round split")
+    assert tg.last_kernel().startswith("gemm_bf16_nn_256x256_dma|"), tg.last_kernel()
+    epi_check(p, "gelu_tanh", "round split epilogue")
+    assert tg.last_kernel().startswith("gemm_bf16_nn_256x256_dma|"), tg.last_kernel()
+
+
 # (input, output, epilogue) for rows past M: plain products and the fused forms
 ROWS_PAST_M = [("bf16", "bf16", None), ("f16", "f32", None), ("i8", "i32", None),
                ("bf16", "bf16", "gelu_tanh"), ("f16", "f16", "relu"), ("i8", "bf16", "dequant")]
@@ -945,8 +959,9 @@ def full_case(name, **over):
     (4096, 512, 4096, "bf16", "bf16", 1, "gemm_bf16_nn_128x128_dma4+splitk_reduce"),
     # mid-size output, short K: the 128 x 128 tile unsliced
     (1024, 1024, 1024, "i8", "i32", 1, "gemm_i8_nn_128x128_dma"),
-    # whole tiles just past one round of 256 x 256: the 128 x 128 tile
-    (4096, 4352, 1024, "bf16", "f32", 1, "gemm_bf16_nn_128x128_dma"),
+    # whole tiles just past one round of 256 x 256: the round of 256 x 256
+    # tiles, then the last tile column as a GEMM of its own (round split)
+    (4096, 4352, 1024, "bf16", "f32", 1, "gemm_bf16_nn_256x256_dma|gemm_bf16_nn_128x128_dma"),
     # a batch of problems smaller than a 256 x 256 tile
     (128, 128, 128, "f32", "f32", 256, "gemm_f32_nn_128x128"),
 ])

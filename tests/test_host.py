@@ -466,24 +466,32 @@ def test_plan_dma_eligibility():
 
 def test_plan_edge_split():
     """A thin ragged last tile column (or row) that would cost a second round
-    of 256x256 workgroups runs as a second GEMM; a strip that saves no round,
-    a thick one, or TCGEMM_EDGE=0 keeps one launch."""
+    of 256x256 workgroups runs as a second GEMM, and so do the tiles past the
+    whole rounds when that costs fewer rounds (round split); a strip that
+    saves nothing, or TCGEMM_EDGE=0, keeps one launch."""
     base = workloads.get("bf16_nn_4096")
     main = "gemm_bf16_nn_256x256_dma"
     assert plan_of(base.with_(N=4104))["kernel"] == main + "|transpose_b+gemm_bf16_nn_thin"
     assert plan_of(base.with_(M=4100))["kernel"] == main + "|gemm_bf16_nn_128x128_dma4+splitk_reduce"
     assert plan_of(base.with_(N=4096 + 128))["kernel"].startswith(main + "|")
-    # a strip over half a tile: no edge split; the 17th tile column would be
-    # a second round of 256 x 256 tiles, so the 128 x 128 tile runs it all
-    assert plan_of(base.with_(N=4096 + 136))["kernel"] == "gemm_bf16_nn_128x128_dma"
-    assert plan_of(base.with_(N=4096 + 256))["kernel"] == "gemm_bf16_nn_128x128_dma"
-    assert plan_of(base.with_(M=4096 + 1024, N=4096 + 1024))["kernel"] == main   # 400 tiles
+    # a strip over half a tile, or a whole 17th tile column: the whole
+    # round of 256 x 256 tiles and the rest as a second GEMM (round split)
+    pl = plan_of(base.with_(N=4096 + 136))
+    assert pl["kernel"] == main + "|gemm_bf16_nn_128x128_dma4+splitk_reduce", pl["kernel"]
+    assert plan_of(base.with_(N=4096 + 256))["kernel"].startswith(main + "|")
+    assert plan_of(base.with_(M=4096 + 2048))["kernel"] == main + "|gemm_bf16_nn_128x128_dma"
+    # 400 tiles (20 x 20): 12 rows of tiles fill 240 of one round, the other
+    # 8 rows still take a round of their own -- no gain, one launch
+    assert plan_of(base.with_(M=4096 + 1024, N=4096 + 1024))["kernel"] == main
+    # 448 tiles: one launch costs two rounds, the split two as well
+    assert "|" not in plan_of(base.with_(M=7168))["kernel"]
     assert plan_of(base.with_(M=3072, N=4104))["kernel"] == main          # 204 tiles: one round
     pl = plan_of(base.with_(N=4104))
     assert pl["tiles_m"] == 16 and pl["tiles_n"] == 16 and pl["grid"] > 256
     os.environ["TCGEMM_EDGE"] = "0"
     try:
         assert plan_of(base.with_(N=4104))["kernel"] == main
+        assert plan_of(base.with_(N=4096 + 136))["kernel"] == "gemm_bf16_nn_128x128_dma"
     finally:
         del os.environ["TCGEMM_EDGE"]
     # one partial tile row or column: no strip (there are no whole tiles
