@@ -547,6 +547,19 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true, const Choice 
     }
     if (dma && cls == TILE_256) cls = TILE_256_DMA;
     if (dma && cls == TILE_128) cls = TILE_128_DMA;
+    // 128 x 128 tiles that leave every CU at most one workgroup: the 4-stage
+    // variant, three K-tiles in flight instead of one (the room the 2-stage
+    // variant leaves for a second workgroup per CU has nothing to run).
+    // Measured, bf16 NN, us per call (4 stages / 2): 4096 x 1024 x 4096 37.9
+    // / 47.4, 3072 x 1024 x 3072 27.5 / 34.7, 2048^3 21.8 / 26.4, 2048^2 x
+    // 4096 37.2 / 46.8, 1024^3 11.5 / 13.7, fp16 3072 x 512 x 1024 12.0 /
+    // 14.0, int8 2048 x 512 x 2048 12.3 / 14.5.  With 288 tiles (3072 x 1536
+    // x 2048) the 2-stage tile, two per CU, stays ahead (28.5 against 36.1),
+    // and so it does with under 16 K-tiles, where the deeper pipeline has
+    // little to overlap (fp16 1024^2 x 512 7.7 against 8.2, int8 1024^3 8.5
+    // against 9.1, a batch of 256 bf16 128^3 7.7 against 8.0).
+    if (cls == TILE_128_DMA && splits == 1 && tile_count(TILE_128) <= 256 && ktiles >= 16)
+        cls = TILE_128_DMA4;
     if (const char *env = knob(K_TILE)) {
         const int v = atoi(env);
         if (strcmp(env, "dma") == 0) cls = dma ? TILE_256_DMA : cls;

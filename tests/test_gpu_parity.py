@@ -961,7 +961,7 @@ def full_case(name, **over):
     (1024, 1024, 1024, "i8", "i32", 1, "gemm_i8_nn_128x128_dma"),
     # whole tiles just past one round of 256 x 256: the round of 256 x 256
     # tiles, then the last tile column as a GEMM of its own (round split)
-    (4096, 4352, 1024, "bf16", "f32", 1, "gemm_bf16_nn_256x256_dma|gemm_bf16_nn_128x128_dma"),
+    (4096, 4352, 1024, "bf16", "f32", 1, "gemm_bf16_nn_256x256_dma|gemm_bf16_nn_128x128_dma4"),
     # a batch of problems smaller than a 256 x 256 tile
     (128, 128, 128, "f32", "f32", 256, "gemm_f32_nn_128x128"),
 ])

@@ -371,8 +371,13 @@ def test_plan_mid_size_outputs():
     assert pl["splits"] == 4 and pl["grid"] == 256, pl
     pl = plan_of(P("m", 1024, 768, 2048, "bf16", "f32"))
     assert pl["kernel"].endswith("128x128_dma4+splitk_reduce") and pl["splits"] == 5, pl
+    # unsliced: the 4-stage tile with 16 K-tiles or more (one workgroup per
+    # CU either way), else the 2-stage one
     for shape in [(1024, 1024, 1024, "bf16", "bf16"), (2048, 512, 2048, "i8", "i32"),
                   (3072, 512, 1024, "f16", "f16")]:
+        pl = plan_of(P("m", *shape))
+        assert pl["kernel"].endswith("_128x128_dma4") and pl["splits"] == 1, (shape, pl)
+    for shape in [(1024, 1024, 512, "f16", "f16"), (1024, 1024, 1024, "i8", "i32")]:
         pl = plan_of(P("m", *shape))
         assert pl["kernel"].endswith("_128x128_dma") and pl["splits"] == 1, (shape, pl)
     assert plan_of(P("m", 1024, 1024, 1024, "f32", "f32"))["kernel"] == "gemm_f32_nn_64x64"
@@ -397,7 +402,7 @@ def test_plan_wide_split_on_the_256_ring():
     assert pl["kernel"] == "gemm_bf16_nn_128x128_dma4+splitk_reduce", pl["kernel"]
     # too short a K for 16 K-tiles in each of enough slices
     pl = plan_of(P("w", 1536, 1536, 2048, "bf16", "bf16"))
-    assert pl["kernel"] == "gemm_bf16_nn_128x128_dma" and pl["splits"] == 1, pl
+    assert pl["kernel"] == "gemm_bf16_nn_128x128_dma4" and pl["splits"] == 1, pl
     # 192 to 256 tiles of 128 x 128: split only with at least 25 K-tiles per slice
     for shape in [(2048, 2048, 16384), (2048, 2048, 8192), (4096, 1024, 8192)]:
         pl = plan_of(P("w", *shape, "bf16", "bf16"))
@@ -405,7 +410,7 @@ def test_plan_wide_split_on_the_256_ring():
         assert pl["splits"] == 4 and pl["k_per_split"] >= 25 * pl["tile_k"], (shape, pl)
     for shape in [(4096, 1024, 4096), (2048, 2048, 4096), (2048, 2048, 2048)]:
         pl = plan_of(P("w", *shape, "bf16", "bf16"))
-        assert pl["kernel"] == "gemm_bf16_nn_128x128_dma" and pl["splits"] == 1, (shape, pl)
+        assert pl["kernel"] == "gemm_bf16_nn_128x128_dma4" and pl["splits"] == 1, (shape, pl)
 
 
 def test_plan_one_partial_round_of_256_tiles():
@@ -580,7 +585,10 @@ def test_plan_mid_size_and_split_k_classes():
     direct-to-LDS for 16-bit and int8 inputs; tall K with few tiles splits K
     on that tile (on the 64 x 64 tile for f32)."""
     mid = workloads.Problem("mid", 1536, 2048, 1024, "bf16", "bf16")
-    assert plan_of(mid)["kernel"] == "gemm_bf16_nn_128x128_dma"
+    # 192 tiles, at most one per CU, 16 K-tiles: the 4-stage variant
+    assert plan_of(mid)["kernel"] == "gemm_bf16_nn_128x128_dma4"
+    assert plan_of(mid.with_(K=512))["kernel"] == "gemm_bf16_nn_128x128_dma"
+    assert plan_of(mid.with_(M=3072))["kernel"] == "gemm_bf16_nn_128x128_dma"   # 384 tiles
     assert plan_of(mid.with_(a_dtype="f32", c_dtype="f32"))["kernel"] == "gemm_f32_nn_128x128"
     tall = workloads.Problem("tall", 256, 256, 8192, "f16", "f32")
     pl = plan_of(tall)
