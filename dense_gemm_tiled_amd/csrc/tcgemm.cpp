@@ -475,8 +475,14 @@ void make_plan(const Problem &p, Plan *pl, bool allow_edge = true, const Choice 
     int64_t s256 = t256 > 0 ? 256 / t256 : 0;
     if (s256 > ktiles / (few128 ? 16 : 25)) s256 = ktiles / (few128 ? 16 : 25);
     if (s256 > 32) s256 = 32;
+    // Both only from 160 K-tiles on: below that the unsplit 128 x 128 tile
+    // with 4 stages (one workgroup per CU, see below) is ahead.  Measured,
+    // bf16 NN, us per call (ring split / 4-stage unsplit): 2048^2 x 16384
+    // (256 K-tiles) 130.9 / 143.4, 1536^2 x 12288 (192) 67.5 / 79.9;
+    // 2048^2 x 8192 (128) 82.9 / 74.2, 4096 x 1024 x 8192 75.3 / 63.5,
+    // 1664 x 1544 x 6144 (96) 51.8 / 45.3.
     const bool wide_split = dma && (few128 || one128) && p.M >= 256 && p.N >= 256 &&
-                            p.alpha != 0.0f && s256 >= 2 && t256 * s256 >= 192;
+                            p.alpha != 0.0f && ktiles >= 160 && s256 >= 2 && t256 * s256 >= 192;
     // Few tiles (under 128 of 64 x 64) and a short K: the 4 waves of a
     // workgroup take every 4th K-tile each and add their partial tiles in
     // LDS (each K-tile of the register-staged loop would wait out a memory

@@ -228,13 +228,13 @@ def test_dma_kernel_batched_padded(a, c, ta, tb, tile):
                                        ("i8", "i32", False, True)],
                          ids=["bf16-bf16-NN", "f16-f32-TN", "i8-i32-NT"])
 def test_dma_ring_split_k(a, c, ta, tb):
-    """Split-K on the 256x256 ring by the planner's own choice: 169 tiles of
-    128 x 128 (1664 x 1544, ragged in M and N on the 256 tile) and a K of 96
-    K-tiles, so 5 slices of 19 to 20 -- the partial sums and their reduction
-    against the oracle."""
+    """Split-K on the 256x256 ring by the planner's own choice: 132 tiles of
+    128 x 128 (1408 x 1544, ragged in M and N on the 256 tile) and a K of
+    160 K-tiles, so 6 slices of 26 to 27 -- the partial sums and their
+    reduction against the oracle."""
     import dense_gemm_tiled_amd as tg
-    k = 96 * (128 if a == "i8" else 64)
-    p = problem(a, c, 1664, 1544, k, ta, tb)
+    k = 160 * (128 if a == "i8" else 64)
+    p = problem(a, c, 1408, 1544, k, ta, tb)
     check(p, "ring split-K")
     assert tg.last_kernel().endswith("_256x256_dma+splitk_reduce"), tg.last_kernel()
 

@@ -384,11 +384,11 @@ def test_plan_mid_size_outputs():
 
 
 def test_plan_wide_split_on_the_256_ring():
-    """129 to 191 tiles of 128 x 128 with a long K: the 256 x 256 ring with as
-    many K slices as fit one round (at least 16 K-tiles each, at least 192
-    workgroups); 192 to 256 of them the same with at least 25 K-tiles per
-    slice; fewer 128 x 128 tiles keep their own split, a short K stays
-    unsplit."""
+    """129 to 191 tiles of 128 x 128 with at least 160 K-tiles: the 256 x 256
+    ring with as many K slices as fit one round (at least 16 K-tiles each,
+    at least 192 workgroups); 192 to 256 of them the same with at least 25
+    K-tiles per slice; fewer 128 x 128 tiles keep their own split, a shorter
+    K stays unsplit."""
     P = workloads.Problem
     pl = plan_of(P("w", 1536, 1536, 12288, "bf16", "bf16"))
     assert pl["kernel"] == "gemm_bf16_nn_256x256_dma+splitk_reduce", pl["kernel"]
@@ -400,15 +400,16 @@ def test_plan_wide_split_on_the_256_ring():
     # 64 tiles of 128 x 128: their own 4-stage split
     pl = plan_of(P("w", 1024, 1024, 16384, "bf16", "bf16"))
     assert pl["kernel"] == "gemm_bf16_nn_128x128_dma4+splitk_reduce", pl["kernel"]
-    # too short a K for 16 K-tiles in each of enough slices
+    # too short a K
     pl = plan_of(P("w", 1536, 1536, 2048, "bf16", "bf16"))
     assert pl["kernel"] == "gemm_bf16_nn_128x128_dma4" and pl["splits"] == 1, pl
     # 192 to 256 tiles of 128 x 128: split only with at least 25 K-tiles per slice
-    for shape in [(2048, 2048, 16384), (2048, 2048, 8192), (4096, 1024, 8192)]:
-        pl = plan_of(P("w", *shape, "bf16", "bf16"))
-        assert pl["kernel"] == "gemm_bf16_nn_256x256_dma+splitk_reduce", (shape, pl)
-        assert pl["splits"] == 4 and pl["k_per_split"] >= 25 * pl["tile_k"], (shape, pl)
-    for shape in [(4096, 1024, 4096), (2048, 2048, 4096), (2048, 2048, 2048)]:
+    pl = plan_of(P("w", 2048, 2048, 16384, "bf16", "bf16"))
+    assert pl["kernel"] == "gemm_bf16_nn_256x256_dma+splitk_reduce", pl
+    assert pl["splits"] == 4 and pl["k_per_split"] >= 25 * pl["tile_k"], pl
+    # under 160 K-tiles: the 4-stage 128 x 128 tile unsplit
+    for shape in [(2048, 2048, 8192), (4096, 1024, 8192), (1664, 1544, 6144),
+                  (4096, 1024, 4096), (2048, 2048, 4096), (2048, 2048, 2048)]:
         pl = plan_of(P("w", *shape, "bf16", "bf16"))
         assert pl["kernel"] == "gemm_bf16_nn_128x128_dma4" and pl["splits"] == 1, (shape, pl)
 
