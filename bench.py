@@ -65,6 +65,8 @@ def parse():
                     help="fused bias+GELU against unfused passes, interleaved")
     ap.add_argument("--layout-table", action="store_true",
                     help="4096^3 over layouts, bf16/fp16 and beta 0/1, interleaved")
+    ap.add_argument("--shape-sweep", action="store_true",
+                    help="bf16 NN over a spread of shapes, against torch.mm")
     ap.add_argument("--smi-sampler", type=float, default=0.0, help=argparse.SUPPRESS)
     return ap.parse_args()
 
@@ -448,6 +450,52 @@ def run_layout_table(args):
             print("| %s, beta = %g | %s |" % (dt, beta, " | ".join("%.1f" % v for v in row)), flush=True)
 
 
+SWEEP = [(1024, 1024, 1024), (2048, 2048, 2048), (4096, 4096, 4096), (8192, 8192, 8192),
+         (5120, 5120, 5120), (6144, 6144, 6144), (4096, 4352, 4096), (6144, 4096, 4096),
+         (3072, 3072, 8192), (2048, 2048, 8192), (2048, 2048, 16384), (1536, 1536, 12288),
+         (1024, 1024, 8192), (512, 512, 32768), (4096, 1024, 4096), (3072, 1024, 3072),
+         (8192, 8192, 1024), (16384, 2048, 2048)]
+
+
+def run_shape_sweep(args):
+    """bf16 NN (alpha 1, beta 0) on each shape of SWEEP: this library and
+    torch.mm on the same two input sets (bell-shaped random, unscaled), 10
+    warm-up calls each, then 5 blocks of 10 calls of each between two
+    events; p50 us per call and the planner's kernel chain."""
+    import torch
+    import dense_gemm_tiled_amd as tg
+    torch.cuda.set_device(0)
+    tg.load_library()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3)
+    print("| M×N×K | plan | this library | torch | ratio |")
+    print("|---|---|---|---|---|")
+    for M, N, K in SWEEP:
+        sets = [(torch.randn(M, K, device="cuda", generator=gen).bfloat16(),
+                 torch.randn(K, N, device="cuda", generator=gen).bfloat16(),
+                 torch.empty(M, N, device="cuda").bfloat16()) for _ in range(2)]
+
+        def ours(i):
+            a, b, c = sets[i % 2]
+            tg.gemm(a, b, c)
+
+        def theirs(i):
+            a, b, c = sets[i % 2]
+            torch.mm(a, b, out=c)
+
+        med = {}
+        for name, f in (("ours", ours), ("torch", theirs)):
+            for i in range(10):
+                f(i)
+            med[name] = float(np.median(block_times(f, 5, 10)))
+            if name == "ours":
+                plan = tg.last_kernel()
+        print("| %dx%dx%d | %s | %.1f | %.1f | %.2f |" % (M, N, K, plan, med["ours"], med["torch"],
+                                                         med["ours"] / med["torch"]), flush=True)
+        del sets
+        torch.cuda.empty_cache()
+
+
 def pcts(x):
     x = np.asarray(x, dtype=float)
     return {"p10": float(np.percentile(x, 10)), "p50": float(np.percentile(x, 50)),
@@ -467,6 +515,9 @@ def main():
         return
     if args.layout_table:
         run_layout_table(args)
+        return
+    if args.shape_sweep:
+        run_shape_sweep(args)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
